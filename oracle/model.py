@@ -1,0 +1,229 @@
+"""Oracle forward passes, float64: per-tile block, shared layer, TileShare-k stack.
+
+Pages.  Figure 2 caption: in a shared layer every token has one state;
+normalisation, the QKV projection and QK-normalisation run once per token, as
+do the out-projection and the MLP; attention still runs per released tile
+with the tile's own global token and coordinates; an overlap token's per-tile
+attention outputs are blended with the released weights w-bar, the only
+approximate step.  Table S1: layer 0's Norm1/QKV/QK-RMSNorm are exact once per
+token; RoPE stays per tile on tile coordinates; keys and values of layers >= k
+come from the shared states; the blend of attention outputs happens in every
+layer >= k.  Abstract and Table 1 caption: TileShare-k keeps the first k
+layers per tile (per-tile residual streams).
+
+Readings taken (the design doc lists them with reasons): pre-norm block
+x += Attn(Norm1(x)); x += MLP(Norm2(x)); MLP = fc1 -> exact erf GELU -> fc2;
+LayerNorm for the ViT-style configurations, RMSNorm plus per-head
+QK-RMSNorm for the MiniMax-style ones; eps 1e-6; q|k|v split of the QKV
+output with head h at columns h*hd .. (h+1)*hd; linear weights stored
+[out, in]; the global token is one vector, copied into every tile; at layer k
+the per-tile states are merged with w-bar (global rows stay per tile); the
+tiled baseline is k = L followed by the same merge; no final norm.
+"""
+import math
+
+import numpy as np
+from scipy.special import erf
+
+from . import fp8 as fp8mod
+from .plan import rope_tables
+
+F = np.float64
+
+
+def layer_norm(x, g, b, eps):
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * g + b
+
+
+def rms_norm(x, g, eps):
+    ms = (x * x).mean(axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def gelu(x):
+    """Exact GELU, x * Phi(x) with the normal CDF written through erf."""
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def norm(x, p, which, cfg):
+    g = p[which + "_g"].astype(F)
+    if cfg["norm"] == "ln":
+        return layer_norm(x, g, p[which + "_b"].astype(F), cfg.get("eps", 1e-6))
+    return rms_norm(x, g, cfg.get("eps", 1e-6))
+
+
+def linear(x, w, b, fp8=False):
+    """y = x W^T + b; with ``fp8`` both operands are per-tensor e4m3 fake-quantised."""
+    if fp8:
+        return fp8mod.fp8_linear(x, w, b)
+    return x @ w.astype(F).T + b.astype(F)
+
+
+def rope_rotate(x, cos, sin):
+    """Rotate consecutive pairs (2k, 2k+1) of x [n, hd] by the per-row angles."""
+    a = x[:, 0::2]
+    b = x[:, 1::2]
+    out = np.empty_like(x)
+    out[:, 0::2] = a * cos - b * sin
+    out[:, 1::2] = a * sin + b * cos
+    return out
+
+
+def softmax_attention(q, k, v, scale):
+    s = (q @ k.T) * scale
+    s = s - s.max(axis=-1, keepdims=True)
+    e = np.exp(s)
+    return (e @ v) / e.sum(axis=-1, keepdims=True)
+
+
+def qkv_heads(h, p, cfg, fp8=False):
+    """QKV projection and per-head QK-RMSNorm, once per row of h."""
+    d, hd = cfg["d"], cfg["head_dim"]
+    qkv = linear(h, p["w_qkv"], p["b_qkv"], fp8)
+    q, k, v = qkv[:, :d].copy(), qkv[:, d:2 * d].copy(), qkv[:, 2 * d:].copy()
+    if cfg["qk_norm"]:
+        eps = cfg.get("eps", 1e-6)
+        for hh in range(cfg["n_heads"]):
+            cs = slice(hh * hd, (hh + 1) * hd)
+            q[:, cs] = rms_norm(q[:, cs], p["q_g"].astype(F), eps)
+            k[:, cs] = rms_norm(k[:, cs], p["k_g"].astype(F), eps)
+    return q, k, v
+
+
+def tile_attention(q, k, v, cos_t, sin_t, cfg):
+    """Dense attention of one tile window.
+
+    q, k, v: [n+1, d], rows 0..n-1 the tile's tokens in local raster order,
+    row n its global token.  cos_t/sin_t: [n+1, hd/2] with the identity
+    rotation in the global row.  Returns o [n+1, d].
+    """
+    hd = cfg["head_dim"]
+    out = np.empty_like(q)
+    scale = 1.0 / math.sqrt(hd)
+    for hh in range(cfg["n_heads"]):
+        cs = slice(hh * hd, (hh + 1) * hd)
+        qh = rope_rotate(q[:, cs], cos_t, sin_t)
+        kh = rope_rotate(k[:, cs], cos_t, sin_t)
+        out[:, cs] = softmax_attention(qh, kh, v[:, cs], scale)
+    return out
+
+
+def mlp(x, p, cfg, fp8=False):
+    hid = gelu(linear(x, p["w_1"], p["b_1"], fp8))
+    return linear(hid, p["w_2"], p["b_2"], fp8)
+
+
+class Rope:
+    """Tile-local rotation table with an identity row appended for the global token."""
+
+    def __init__(self, plan, cfg):
+        cos, sin = rope_tables(plan, cfg["ndim"], cfg["head_dim"],
+                               cfg.get("rope_base", 10000.0))
+        P = cfg["head_dim"] // 2
+        self.cos = np.vstack([cos.astype(F), np.ones((1, P))])
+        self.sin = np.vstack([sin.astype(F), np.zeros((1, P))])
+
+
+def per_tile_layer(X, p, cfg, rope):
+    """One released block on one tile's state X [n+1, d] (global row last)."""
+    h = norm(X, p, "norm1", cfg)
+    q, k, v = qkv_heads(h, p, cfg)
+    o = tile_attention(q, k, v, rope.cos, rope.sin, cfg)
+    X = X + linear(o, p["w_o"], p["b_o"])
+    X = X + mlp(norm(X, p, "norm2", cfg), p, cfg)
+    return X
+
+
+def blend(plan, per_tile_rows):
+    """a[p] = sum over the tiles covering p (ascending) of w-bar * row(t, j)."""
+    d = per_tile_rows[0].shape[1]
+    a = np.zeros((plan.n_union, d), dtype=F)
+    for p in range(plan.n_union):
+        for e in range(plan.cover_ptr[p], plan.cover_ptr[p + 1]):
+            t, j = plan.cover_tile[e], plan.cover_local[e]
+            a[p] += F(plan.cover_w[e]) * per_tile_rows[t][j]
+    return a
+
+
+def shared_layer(x, G, p, cfg, plan, rope, fp8=False, blend_after_out=False):
+    """One shared layer.  x [n_union, d] union states, G [n_tiles, d] global rows.
+
+    Norm1/QKV/QK-norm, the out-projection and the MLP run once per row of the
+    union plus the global rows; attention runs per tile over the tile's rows
+    of the shared q/k/v; the per-tile outputs are blended with w-bar.
+    ``blend_after_out`` blends after the out-projection instead (equal by
+    linearity and sum w-bar = 1; used only as a pin).
+    """
+    n = plan.tile_tokens
+    xa = np.vstack([x, G])
+    h = norm(xa, p, "norm1", cfg)
+    q, k, v = qkv_heads(h, p, cfg, fp8)
+    outs = []
+    for t in range(plan.n_tiles):
+        rows = np.concatenate([plan.tile_rows[t].astype(np.int64), [plan.n_union + t]])
+        outs.append(tile_attention(q[rows], k[rows], v[rows], rope.cos, rope.sin, cfg))
+    if blend_after_out:
+        proj = [linear(o, p["w_o"], p["b_o"], fp8) for o in outs]
+        delta = np.vstack([blend(plan, proj), np.stack([pr[n] for pr in proj])])
+    else:
+        a = np.vstack([blend(plan, outs), np.stack([o[n] for o in outs])])
+        delta = linear(a, p["w_o"], p["b_o"], fp8)
+    xa = xa + delta
+    xa = xa + mlp(norm(xa, p, "norm2", cfg), p, cfg, fp8)
+    return xa[: plan.n_union], xa[plan.n_union:]
+
+
+def gather_tiles(plan, x, g):
+    """Per-tile states X_t = [x[tile_rows[t]]; g] as float64."""
+    return [np.vstack([x[plan.tile_rows[t]].astype(F), g.astype(F)[None, :]])
+            for t in range(plan.n_tiles)]
+
+
+def merge(plan, X):
+    """Merge per-tile states into one shared state; global rows stay per tile."""
+    n = plan.tile_tokens
+    return blend(plan, X), np.stack([Xt[n] for Xt in X])
+
+
+def stack_forward(cfg, plan, x, g, layers, k, rope=None):
+    """TileShare-k: layers < k per tile, merge at layer k, layers >= k shared.
+
+    Returns (x_out [n_union, d], g_out [n_tiles, d]) in float64.  k = L is the
+    released tiled decoder (per-tile layers throughout, merged at the end).
+    """
+    rope = rope or Rope(plan, cfg)
+    L = len(layers)
+    fp8 = cfg.get("gemm_shared") == "fp8"
+    if k > 0:
+        X = gather_tiles(plan, x, g)
+        for li in range(k):
+            X = [per_tile_layer(Xt, layers[li], cfg, rope) for Xt in X]
+        xs, G = merge(plan, X)
+    else:
+        xs = x.astype(F)
+        G = np.tile(g.astype(F)[None, :], (plan.n_tiles, 1))
+    for li in range(k, L):
+        xs, G = shared_layer(xs, G, layers[li], cfg, plan, rope, fp8=fp8)
+    return xs, G
+
+
+def tiled_forward(cfg, plan, x, g, layers, rope=None):
+    """Released overlapping-tile decoding, tiles outermost: every tile runs the
+    whole stack on its own window, then the outputs are blended with w-bar."""
+    rope = rope or Rope(plan, cfg)
+    outs = []
+    for t in range(plan.n_tiles):
+        Xt = np.vstack([x[plan.tile_rows[t]].astype(F), g.astype(F)[None, :]])
+        for p in layers:
+            Xt = per_tile_layer(Xt, p, cfg, rope)
+        outs.append(Xt)
+    return merge(plan, outs)
+
+
+def rel_err(got, ref):
+    """max |got - ref| / RMS(ref): the parity metric on the union output."""
+    ref = np.asarray(ref, dtype=F)
+    rms = math.sqrt(float(np.mean(ref * ref)))
+    return float(np.max(np.abs(np.asarray(got, dtype=F) - ref))) / rms

@@ -1,0 +1,270 @@
+"""Pins for the oracle's block, shared layer and TileShare-k stack (CPU).
+
+Each pin checks the oracle against something other than itself: torch's own
+norm / attention / GELU routines, a per-token brute-force formulation, or an
+invariant the pages fix (Figure 2 caption: the blend is the only approximate
+step; Table 1 caption: identical per-tile states stay identical; abstract:
+TileShare-k with every layer per tile is the released tiled decoder).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as Fn
+
+from oracle import model as M
+from oracle.brute import brute_per_tile_layer, brute_shared_layer
+from oracle.plan import Plan, rope_pairs
+from synth import configs, make_inputs
+
+torch.set_default_dtype(torch.float64)
+
+
+def tiny_cfg(ndim=2, norm="ln", qk=False, grid=(1, 4, 6), tile=(1, 4, 4), stride=(1, 2, 2),
+             d=8, heads=2, layers=2, dtype="f32", mlp=16):
+    return dict(name="tiny", ndim=ndim, grid=grid, tile=tile, stride=stride, n_layers=layers,
+                d=d, n_heads=heads, head_dim=d // heads, mlp_hidden=mlp, norm=norm,
+                qk_norm=qk, dtype=dtype, gemm_shared=dtype, seed=3)
+
+
+# --- library-routine pins ---------------------------------------------------
+
+def test_norms_gelu_attention_against_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((7, 12))
+    g = 1 + 0.1 * rng.standard_normal(12)
+    b = 0.1 * rng.standard_normal(12)
+    tx = torch.from_numpy(x)
+    assert np.allclose(M.layer_norm(x, g, b, 1e-6),
+                       Fn.layer_norm(tx, (12,), torch.from_numpy(g), torch.from_numpy(b), 1e-6).numpy(),
+                       atol=1e-13, rtol=0)
+    assert np.allclose(M.rms_norm(x, g, 1e-6),
+                       Fn.rms_norm(tx, (12,), torch.from_numpy(g), 1e-6).numpy(), atol=1e-13, rtol=0)
+    assert np.allclose(M.gelu(x), Fn.gelu(tx, approximate="none").numpy(), atol=1e-14, rtol=0)
+    # exact GELU closed forms
+    assert M.gelu(np.array([0.0]))[0] == 0.0
+    assert math.isclose(M.gelu(np.array([1.0]))[0], 0.5 * (1 + math.erf(1 / math.sqrt(2))), rel_tol=1e-15)
+    q, k, v = (rng.standard_normal((9, 4)) for _ in range(3))
+    ref = Fn.scaled_dot_product_attention(*(torch.from_numpy(a)[None, None] for a in (q, k, v)))[0, 0]
+    assert np.allclose(M.softmax_attention(q, k, v, 0.5), ref.numpy(), atol=1e-13, rtol=0)
+
+
+def _torch_rope(x, pos, counts, base):
+    """RoPE through complex multiplication (torch), independent of the oracle's pair loop."""
+    n, hd = x.shape
+    freqs = torch.cat([base ** (-torch.arange(m, dtype=torch.float64) / m) for m in counts if m])
+    axes = torch.cat([torch.full((m,), ax, dtype=torch.long) for ax, m in enumerate(counts) if m])
+    ang = pos[:, axes].to(torch.float64) * freqs[None, :]
+    # the oracle stores cos/sin rounded to fp32; do the same
+    c = torch.cos(ang).to(torch.float32).to(torch.float64)
+    s = torch.sin(ang).to(torch.float32).to(torch.float64)
+    z = torch.complex(c, s)
+    xc = torch.view_as_complex(x.reshape(n, hd // 2, 2).contiguous())
+    return torch.view_as_real(xc * z).reshape(n, hd)
+
+
+def _torch_vit(cfg, X, layers, pos):
+    """Textbook pre-norm ViT on one window with torch ops; last row is the global token."""
+    d, H, hd = cfg["d"], cfg["n_heads"], cfg["head_dim"]
+    counts = rope_pairs(cfg["ndim"], hd)
+    X = torch.from_numpy(X)
+    pos = torch.from_numpy(pos)
+    n = X.shape[0]
+    for p in layers:
+        tp = {k: torch.from_numpy(v.astype(np.float64)) for k, v in p.items()}
+
+        def nrm(x, w):
+            if cfg["norm"] == "ln":
+                return Fn.layer_norm(x, (d,), tp[w + "_g"], tp[w + "_b"], 1e-6)
+            return Fn.rms_norm(x, (d,), tp[w + "_g"], 1e-6)
+        h = nrm(X, "norm1")
+        qkv = Fn.linear(h, tp["w_qkv"], tp["b_qkv"])
+        q, k, v = qkv.split(d, dim=1)
+        q = q.reshape(n, H, hd)
+        k = k.reshape(n, H, hd)
+        if cfg["qk_norm"]:
+            q = Fn.rms_norm(q, (hd,), tp["q_g"], 1e-6)
+            k = Fn.rms_norm(k, (hd,), tp["k_g"], 1e-6)
+        qs, ks = [], []
+        for hh in range(H):
+            qh = torch.cat([_torch_rope(q[:-1, hh], pos, counts, 10000.0), q[-1:, hh]])
+            kh = torch.cat([_torch_rope(k[:-1, hh], pos, counts, 10000.0), k[-1:, hh]])
+            qs.append(qh)
+            ks.append(kh)
+        qh = torch.stack(qs)[None]
+        kh = torch.stack(ks)[None]
+        vh = v.reshape(n, H, hd).transpose(0, 1).contiguous()[None]
+        o = Fn.scaled_dot_product_attention(qh, kh, vh)[0].transpose(0, 1).reshape(n, d)
+        X = X + Fn.linear(o, tp["w_o"], tp["b_o"])
+        u = Fn.gelu(Fn.linear(nrm(X, "norm2"), tp["w_1"], tp["b_1"]), approximate="none")
+        X = X + Fn.linear(u, tp["w_2"], tp["b_2"])
+    return X.numpy()
+
+
+@pytest.mark.parametrize("ndim,norm,qk", [(2, "ln", False), (3, "rms", True), (3, "ln", False)])
+def test_single_tile_equals_textbook_vit(ndim, norm, qk):
+    grid = (1, 4, 6) if ndim == 2 else (2, 3, 4)
+    cfg = tiny_cfg(ndim=ndim, norm=norm, qk=qk, grid=grid, tile=grid, stride=grid, d=16, heads=2)
+    x, g, layers = make_inputs(cfg)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    assert pl.n_tiles == 1
+    X = np.vstack([x[pl.tile_rows[0]], g[None]]).astype(np.float64)
+    ref = _torch_vit(cfg, X, layers, pl.local_pos)
+    for k in (0, 1, 2):
+        out, G = M.stack_forward(cfg, pl, x, g, layers, k)
+        back = np.empty_like(out)
+        back[pl.tile_rows[0]] = out[pl.tile_rows[0]]
+        assert np.allclose(out[pl.tile_rows[0]], ref[:-1], atol=1e-11, rtol=0)
+        assert np.allclose(G[0], ref[-1], atol=1e-11, rtol=0)
+
+
+# --- invariants the pages fix ---------------------------------------------
+
+@pytest.mark.parametrize("ndim,norm,qk", [(2, "ln", False), (3, "rms", True)])
+def test_k_equals_L_is_tiled_baseline(ndim, norm, qk):
+    grid, tile, stride = ((1, 6, 9), (1, 4, 4), (1, 2, 3)) if ndim == 2 else ((2, 5, 6), (2, 3, 4), (1, 2, 2))
+    cfg = tiny_cfg(ndim=ndim, norm=norm, qk=qk, grid=grid, tile=tile, stride=stride)
+    x, g, layers = make_inputs(cfg)
+    pl = Plan(grid, tile, stride)
+    a, ga = M.stack_forward(cfg, pl, x, g, layers, len(layers))
+    b, gb = M.tiled_forward(cfg, pl, x, g, layers)
+    assert np.array_equal(a, b) and np.array_equal(ga, gb)
+
+
+@pytest.mark.parametrize("ndim", [2, 3])
+def test_zero_overlap_every_k_equals_baseline(ndim):
+    grid, tile = ((1, 4, 8), (1, 4, 4)) if ndim == 2 else ((2, 4, 6), (2, 2, 3))
+    cfg = tiny_cfg(ndim=ndim, norm="rms" if ndim == 3 else "ln", qk=ndim == 3,
+                   grid=grid, tile=tile, stride=tile, layers=3)
+    x, g, layers = make_inputs(cfg)
+    pl = Plan(grid, tile, tile)
+    base, _ = M.tiled_forward(cfg, pl, x, g, layers)
+    for k in range(4):
+        out, _ = M.stack_forward(cfg, pl, x, g, layers, k)
+        assert M.rel_err(out, base) < 1e-12
+    # but the global tokens differ per tile, so they are not merged
+    _, G = M.stack_forward(cfg, pl, x, g, layers, 0)
+    assert not np.allclose(G[0], G[1])
+
+
+def test_identical_per_tile_states_stay_identical():
+    """With W_v = 0 and b_v = 0 attention adds only b_o, so a token's state is the
+    same in every tile; TileShare-0 then equals the tiled baseline to rounding."""
+    cfg = tiny_cfg(ndim=2, grid=(1, 5, 9), tile=(1, 4, 5), stride=(1, 1, 2), layers=3)
+    x, g, layers = make_inputs(cfg)
+    d = cfg["d"]
+    for p in layers:
+        p["w_qkv"][2 * d:] = 0
+        p["b_qkv"][2 * d:] = 0
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    base, _ = M.tiled_forward(cfg, pl, x, g, layers)
+    for k in range(4):
+        out, _ = M.stack_forward(cfg, pl, x, g, layers, k)
+        assert M.rel_err(out, base) < 1e-6     # fp32-rounded w-bar sums to 1 within ~1e-7
+
+
+def test_overlap_makes_tileshare_differ():
+    """Control for the two pins above: with overlap and W_v != 0 the blend is approximate."""
+    cfg = tiny_cfg(ndim=2, grid=(1, 5, 9), tile=(1, 4, 5), stride=(1, 1, 2), layers=2)
+    x, g, layers = make_inputs(cfg, qk_scale=4.0)
+    for p in layers:     # N(0, 0.02) at d = 8 leaves the attention branch tiny
+        for key in ("w_qkv", "w_o"):
+            p[key] *= 20
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    base, _ = M.tiled_forward(cfg, pl, x, g, layers)
+    out, _ = M.stack_forward(cfg, pl, x, g, layers, 0)
+    assert M.rel_err(out, base) > 1e-2
+
+
+def test_blend_before_or_after_out_projection():
+    cfg = tiny_cfg(ndim=3, norm="rms", qk=True, grid=(2, 5, 6), tile=(2, 3, 4), stride=(1, 2, 2))
+    x, g, layers = make_inputs(cfg)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    rope = M.Rope(pl, cfg)
+    G = np.tile(g[None].astype(np.float64), (pl.n_tiles, 1))
+    a, ga = M.shared_layer(x.astype(np.float64), G, layers[0], cfg, pl, rope)
+    b, gb = M.shared_layer(x.astype(np.float64), G, layers[0], cfg, pl, rope, blend_after_out=True)
+    # equal up to the fp32 rounding of w-bar (sum 1 within a few 1e-8)
+    assert M.rel_err(b, a) < 1e-6 and M.rel_err(gb, ga) < 1e-6
+
+
+def test_rope_relativity_in_shared_layer():
+    """In a shared layer q and k are per token, so a pair of non-global tokens that
+    sits in two tiles gets the same score in both (RoPE depends on differences)."""
+    cfg = tiny_cfg(ndim=3, norm="rms", qk=True, grid=(2, 5, 6), tile=(2, 3, 4), stride=(1, 2, 2))
+    x, g, layers = make_inputs(cfg)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    rope = M.Rope(pl, cfg)
+    h = M.norm(x.astype(np.float64), layers[0], "norm1", cfg)
+    q, k, _ = M.qkv_heads(h, layers[0], cfg)
+    hd = cfg["head_dim"]
+    checked = 0
+    for t1 in range(pl.n_tiles):
+        for t2 in range(t1 + 1, pl.n_tiles):
+            common = sorted(set(pl.tile_rows[t1].tolist()) & set(pl.tile_rows[t2].tolist()))
+            if len(common) < 2:
+                continue
+            j1 = {int(p): j for j, p in enumerate(pl.tile_rows[t1])}
+            j2 = {int(p): j for j, p in enumerate(pl.tile_rows[t2])}
+            for a in common[:4]:
+                for b in common[-4:]:
+                    for hh in range(cfg["n_heads"]):
+                        cs = slice(hh * hd, (hh + 1) * hd)
+                        s = []
+                        for jj in (j1, j2):
+                            qa = M.rope_rotate(q[[a], cs], rope.cos[[jj[a]]], rope.sin[[jj[a]]])
+                            kb = M.rope_rotate(k[[b], cs], rope.cos[[jj[b]]], rope.sin[[jj[b]]])
+                            s.append((qa @ kb.T).item())
+                        assert math.isclose(s[0], s[1], rel_tol=0, abs_tol=1e-5)
+                        checked += 1
+    assert checked > 0
+
+
+# --- brute-force per-token loops --------------------------------------------
+
+BRUTE = [
+    dict(ndim=2, norm="ln", qk=False, grid=(1, 4, 6), tile=(1, 4, 4), stride=(1, 2, 2)),
+    dict(ndim=3, norm="rms", qk=True, grid=(2, 3, 4), tile=(2, 2, 3), stride=(1, 1, 1)),
+    dict(ndim=3, norm="ln", qk=False, grid=(3, 4, 4), tile=(2, 3, 3), stride=(1, 2, 2)),
+]
+
+
+@pytest.mark.parametrize("c", BRUTE)
+def test_shared_layer_against_brute_force(c):
+    cfg = tiny_cfg(ndim=c["ndim"], norm=c["norm"], qk=c["qk"], grid=c["grid"], tile=c["tile"],
+                   stride=c["stride"], layers=1)
+    x, g, layers = make_inputs(cfg, qk_scale=3.0)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    rope = M.Rope(pl, cfg)
+    G = np.tile(g[None].astype(np.float64), (pl.n_tiles, 1))
+    G[0] += 0.5   # per-tile global rows that differ
+    a, ga = M.shared_layer(x.astype(np.float64), G, layers[0], cfg, pl, rope)
+    bx, bg = brute_shared_layer(x.astype(np.float64).tolist(), G.tolist(), layers[0], cfg,
+                                cfg["grid"], cfg["tile"], cfg["stride"])
+    assert np.allclose(a, np.array(bx), atol=1e-10, rtol=0)
+    assert np.allclose(ga, np.array(bg), atol=1e-10, rtol=0)
+
+
+@pytest.mark.parametrize("c", BRUTE)
+def test_per_tile_layer_against_brute_force(c):
+    cfg = tiny_cfg(ndim=c["ndim"], norm=c["norm"], qk=c["qk"], grid=c["grid"], tile=c["tile"],
+                   stride=c["stride"], layers=1)
+    x, g, layers = make_inputs(cfg, qk_scale=3.0)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    rope = M.Rope(pl, cfg)
+    X = M.gather_tiles(pl, x, g)
+    for t in range(pl.n_tiles):
+        a = M.per_tile_layer(X[t], layers[0], cfg, rope)
+        b = brute_per_tile_layer(X[t].tolist(), layers[0], cfg, pl.extent)
+        assert np.allclose(a, np.array(b), atol=1e-10, rtol=0)
+
+
+def test_tiny2d_config_runs_and_differs_from_baseline():
+    cfg = configs.get("tiny2d")
+    x, g, layers = make_inputs(cfg)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    base, _ = M.stack_forward(cfg, pl, x, g, layers, 1)
+    ts0, _ = M.stack_forward(cfg, pl, x, g, layers, 0)
+    e = M.rel_err(ts0, base)
+    assert np.all(np.isfinite(ts0)) and 0 < e < 1.0
