@@ -1,0 +1,589 @@
+// C ABI of libtileshare: argument checks, plan upload, workspace layout, and
+// the launch schedule of the per-tile block, the shared layer (TileShare
+// paper page, Figure 2 caption and Table S1) and the TileShare-k stack
+// (abstract, Table 1 caption).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "plan_internal.h"
+#include "ts_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ts_status fail(ts_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+#define TS_HIP(call, what)                                                                  \
+  do {                                                                                      \
+    hipError_t e_ = (call);                                                                 \
+    if (e_ != hipSuccess) return fail(TS_EHIP, std::string(what) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// ---------------------------------------------------------------- profiler
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+struct Profiler {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+thread_local Profiler g_prof;
+
+// Brackets one launch with events when profiling is on.
+struct Scope {
+  hipStream_t s;
+  ProfRec rec;
+  bool active = false;
+  Scope(hipStream_t st, const char* name, double flops, double bytes) : s(st) {
+    if (!g_prof.on) return;
+    rec.name = name;
+    rec.flops = flops;
+    rec.bytes = bytes;
+    rec.a = g_prof.take();
+    rec.b = g_prof.take();
+    if (rec.a && rec.b && hipEventRecord(rec.a, s) == hipSuccess) active = true;
+  }
+  ~Scope() {
+    if (active && hipEventRecord(rec.b, s) == hipSuccess) g_prof.recs.push_back(rec);
+  }
+};
+
+// ------------------------------------------------------------ validation
+int act_bytes(int act) { return act == TS_F32 ? 4 : (act == TS_BF16 ? 2 : 1); }
+
+ts_status check_model(const ts_model_desc* m) {
+  if (!m) return fail(TS_EINVAL, "model is null");
+  if (m->d <= 0 || m->n_heads <= 0 || m->head_dim <= 0 || m->mlp_hidden <= 0 || m->n_layers < 0)
+    return fail(TS_EINVAL, "model sizes must be positive");
+  if (m->d != m->n_heads * m->head_dim) return fail(TS_ESHAPE, "d must equal n_heads * head_dim");
+  if (m->d % 64 != 0 || m->d > 4096) return fail(TS_ESHAPE, "d must be a multiple of 64 and <= 4096");
+  if (m->mlp_hidden % 64 != 0) return fail(TS_ESHAPE, "mlp_hidden must be a multiple of 64");
+  if (m->norm != 0 && m->norm != 1) return fail(TS_EINVAL, "norm must be 0 (LayerNorm) or 1 (RMSNorm)");
+  if (!(m->eps > 0.f)) return fail(TS_EINVAL, "eps must be > 0");
+  if (m->act_dtype == TS_F32) {
+    if (m->head_dim != 32 && m->head_dim != 64)
+      return fail(TS_ESHAPE, "fp32 attention supports head_dim 32 or 64");
+    if (m->gemm_dtype_shared != TS_F32) return fail(TS_EDTYPE, "fp32 models need fp32 shared GEMMs");
+  } else if (m->act_dtype == TS_BF16) {
+    if (m->head_dim != 64 && m->head_dim != 128)
+      return fail(TS_ESHAPE, "bf16 attention supports head_dim 64 or 128");
+    if (m->gemm_dtype_shared != TS_BF16 && m->gemm_dtype_shared != TS_FP8E4M3)
+      return fail(TS_EDTYPE, "bf16 models need bf16 or fp8 shared GEMMs");
+    if (m->gemm_dtype_shared == TS_FP8E4M3 && (m->d % 128 != 0 || m->mlp_hidden % 128 != 0))
+      return fail(TS_ESHAPE, "fp8 GEMMs need d and mlp_hidden multiples of 128");
+  } else {
+    return fail(TS_EDTYPE, "act_dtype must be TS_F32 or TS_BF16");
+  }
+  return TS_OK;
+}
+
+ts_status check_weights(const ts_model_desc* m, const ts_layer_weights* w, bool shared) {
+  if (!w) return fail(TS_EINVAL, "layer weights are null");
+  if (!w->norm1_g || !w->norm2_g || !w->w_qkv || !w->b_qkv || !w->w_o || !w->b_o || !w->w_1 ||
+      !w->b_1 || !w->w_2 || !w->b_2)
+    return fail(TS_EINVAL, "a required weight pointer is null");
+  if (m->norm == 0 && (!w->norm1_b || !w->norm2_b)) return fail(TS_EINVAL, "LayerNorm needs norm biases");
+  if (m->qk_norm && (!w->q_g || !w->k_g)) return fail(TS_EINVAL, "QK-norm needs q_g and k_g");
+  if (shared && m->gemm_dtype_shared == TS_FP8E4M3 &&
+      (!w->w_qkv_f8 || !w->w_o_f8 || !w->w_1_f8 || !w->w_2_f8 || !w->w_scale_f8))
+    return fail(TS_EINVAL, "fp8 shared layers need the e4m3 weights and their scales");
+  return TS_OK;
+}
+
+ts_status check_plan(const ts_plan* p, const ts_model_desc* m) {
+  if (!p) return fail(TS_EINVAL, "plan is null");
+  if (!p->uploaded) return fail(TS_EINVAL, "plan not uploaded (call ts_plan_upload)");
+  if (p->rope_hd != m->head_dim || p->rope_base != m->rope_base)
+    return fail(TS_EINVAL, "plan RoPE table was uploaded for another head_dim or base");
+  return TS_OK;
+}
+
+// ------------------------------------------------------------ workspace
+struct WS {
+  unsigned* amax = nullptr;  // fp8 scratch: amax bits
+  float* sa = nullptr;       // fp8 scratch: activation scale
+  float* X = nullptr;        // fp32 [M_t, d] per-tile states
+  float* xs = nullptr;       // fp32 [M_s, d] shared states
+  void* h = nullptr;         // act [M_max, d] norm / blend output
+  void* big = nullptr;       // act [M_max, max(3d, mlp)] qkv, then MLP hidden
+  void* o = nullptr;         // act [M_t, d] attention output, per-tile layout
+  uint8_t* q8 = nullptr;     // e4m3 [M_s, max(d, mlp)] quantised GEMM operand
+  size_t bytes = 0;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+WS layout(const ts_model_desc* m, const ts_plan* p, bool states, bool per_tile, bool shared_xs,
+          char* base) {
+  const int64_t Mt = int64_t(p->n_tiles) * (p->n + 1);
+  const int64_t Ms = int64_t(p->n_union) + p->n_tiles;
+  const int64_t Mmax = per_tile ? std::max(Mt, Ms) : Ms;
+  const int64_t d = m->d, wide = std::max<int64_t>(3 * d, m->mlp_hidden);
+  const int ab = act_bytes(m->act_dtype);
+  WS w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* r = base ? base + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  char* scratch = take(256);
+  w.amax = (unsigned*)scratch;
+  w.sa = (float*)(scratch + 64);
+  if (states && per_tile) w.X = (float*)take(size_t(Mt * d * 4));
+  if (shared_xs) w.xs = (float*)take(size_t(Ms * d * 4));
+  w.h = take(size_t(Mmax * d * ab));
+  w.big = take(size_t(Mmax * wide * ab));
+  w.o = take(size_t(Mt * d * ab));
+  if (m->gemm_dtype_shared == TS_FP8E4M3) w.q8 = (uint8_t*)take(size_t(Ms * std::max<int64_t>(d, m->mlp_hidden)));
+  w.bytes = off;
+  return w;
+}
+
+// ------------------------------------------------------------ one layer
+struct Ctx {
+  const ts_model_desc* m;
+  const ts_plan* p;
+  hipStream_t s;
+};
+
+double gemm_bytes(int64_t M, int64_t N, int64_t K, int ab, int ob, bool resid) {
+  return double(M * K + N * K) * ab + double(M * N) * ob * (resid ? 2 : 1);
+}
+
+// y = A W^T (+ epilogue) for one projection; fp8 quantises A first.
+ts_status proj(const Ctx& c, const WS& ws, bool f8, const char* role, int epi, const void* A, int64_t M,
+               int N, int K, const void* Wt, const uint8_t* W8, const float* w8scale, const float* bias,
+               void* C) {
+  const int act = c.m->act_dtype;
+  const int ob = (epi == tsk::EPI_RESID || epi == tsk::EPI_F32) ? 4 : act_bytes(act);
+  std::string name = std::string(f8 ? "gemm_fp8[" : (act == TS_F32 ? "gemm_f32[" : "gemm_bf16[")) + role + "]";
+  if (f8) {
+    {
+      Scope sc(c.s, (std::string("fp8_quantize[") + role + "]").c_str(), 0.0,
+               double(M * K) * (2.0 * act_bytes(act) + 1.0));
+      TS_HIP(tsk::fp8_quantize(c.s, act, A, M * K, ws.q8, ws.sa, ws.amax), "fp8 quantize");
+    }
+    Scope sc(c.s, name.c_str(), 2.0 * M * N * K, gemm_bytes(M, N, K, 1, ob, epi == tsk::EPI_RESID));
+    TS_HIP(tsk::gemm(c.s, tsk::ACT_FP8, epi, ws.q8, W8, int(M), N, K, bias, C, ws.sa, w8scale), "fp8 gemm");
+    return TS_OK;
+  }
+  Scope sc(c.s, name.c_str(), 2.0 * M * N * K, gemm_bytes(M, N, K, act_bytes(act), ob, epi == tsk::EPI_RESID));
+  TS_HIP(tsk::gemm(c.s, act, epi, A, Wt, int(M), N, K, bias, C, nullptr, nullptr), "gemm");
+  return TS_OK;
+}
+
+// Window attention of every (tile, head) for one layer.
+ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared, const void* qkv, void* out,
+                           hipStream_t s) {
+  tsk::AttnArgs a;
+  a.qkv = qkv;
+  a.out = out;
+  a.rows = shared ? (const int*)p->d_tile_rows : nullptr;
+  a.n_union = p->n_union;
+  a.d = m->d;
+  a.H = m->n_heads;
+  a.hd = m->head_dim;
+  a.n_tiles = p->n_tiles;
+  a.n = p->n;
+  a.local_pos = (const int*)p->d_local_pos;
+  a.rope = (const float*)p->d_rope;
+  a.maxl = p->rope_maxl;
+  a.pairs_t = p->rope_pairs[0];
+  a.pairs_h = p->rope_pairs[1];
+  const double nn = double(p->n + 1);
+  Scope sc(s, m->act_dtype == TS_F32 ? "attn_f32" : "attn_bf16", 4.0 * nn * nn * m->d * p->n_tiles,
+           double(p->n_tiles) * (p->n + 1) * m->d * 4 * act_bytes(m->act_dtype));
+  TS_HIP(tsk::attention(s, m->act_dtype, a), "attention");
+  return TS_OK;
+}
+
+// One pre-norm block on rows x [M, d] fp32.  shared: M = n_union + n_tiles and
+// attention reads each tile through the plan's row map, then the w-bar blend
+// forms one row per token; otherwise M = n_tiles*(n+1) per-tile rows.
+ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shared, const WS& ws) {
+  const ts_model_desc* m = c.m;
+  const ts_plan* p = c.p;
+  const int act = m->act_dtype;
+  const int ab = act_bytes(act);
+  const int64_t Mt = int64_t(p->n_tiles) * (p->n + 1);
+  const int64_t Ms = int64_t(p->n_union) + p->n_tiles;
+  const int64_t M = shared ? Ms : Mt;
+  const int d = m->d, H = m->n_heads, hd = m->head_dim, dm = m->mlp_hidden;
+  const bool f8 = shared && m->gemm_dtype_shared == TS_FP8E4M3;
+  const bool rms = m->norm == 1;
+  ts_status st;
+
+  {
+    Scope sc(c.s, "norm", 0.0, double(M * d) * (4 + ab));
+    TS_HIP(tsk::norm(c.s, act, rms, x, int(M), d, w.norm1_g, w.norm1_b, m->eps, ws.h), "norm1");
+  }
+  if ((st = proj(c, ws, f8, "qkv", tsk::EPI_BIAS, ws.h, M, 3 * d, d, w.w_qkv, w.w_qkv_f8,
+                 w.w_scale_f8 ? w.w_scale_f8 + 0 : nullptr, w.b_qkv, ws.big)) != TS_OK)
+    return st;
+  if (m->qk_norm) {
+    Scope sc(c.s, "qk_norm", 0.0, double(M * 2 * d) * 2 * ab);
+    TS_HIP(tsk::qk_norm(c.s, act, ws.big, int(M), d, H, hd, w.q_g, w.k_g, m->eps), "qk_norm");
+  }
+  if ((st = window_attention(m, p, shared, ws.big, ws.o, c.s)) != TS_OK) return st;
+  const void* aout = ws.o;
+  if (shared) {
+    Scope sc(c.s, "blend", 0.0, (double(p->n_entries + p->n_tiles) + double(Ms)) * d * ab);
+    TS_HIP(tsk::blend(c.s, act, act, ws.o, d, p->n_union, p->n_tiles, p->n, (const int*)p->d_cover_ptr,
+                      (const int*)p->d_entry_row, (const float*)p->d_cover_w, ws.h,
+                      (char*)ws.h + size_t(p->n_union) * d * ab),
+           "blend");
+    aout = ws.h;
+  }
+  if ((st = proj(c, ws, f8, "out", tsk::EPI_RESID, aout, M, d, d, w.w_o, w.w_o_f8,
+                 w.w_scale_f8 ? w.w_scale_f8 + 1 : nullptr, w.b_o, x)) != TS_OK)
+    return st;
+  {
+    Scope sc(c.s, "norm", 0.0, double(M * d) * (4 + ab));
+    TS_HIP(tsk::norm(c.s, act, rms, x, int(M), d, w.norm2_g, w.norm2_b, m->eps, ws.h), "norm2");
+  }
+  if ((st = proj(c, ws, f8, "fc1", tsk::EPI_BIAS_GELU, ws.h, M, dm, d, w.w_1, w.w_1_f8,
+                 w.w_scale_f8 ? w.w_scale_f8 + 2 : nullptr, w.b_1, ws.big)) != TS_OK)
+    return st;
+  if ((st = proj(c, ws, f8, "fc2", tsk::EPI_RESID, ws.big, M, d, dm, w.w_2, w.w_2_f8,
+                 w.w_scale_f8 ? w.w_scale_f8 + 3 : nullptr, w.b_2, x)) != TS_OK)
+    return st;
+  return TS_OK;
+}
+
+ts_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return fail(TS_EWORKSPACE, "workspace is null");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(TS_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(TS_EWORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes, got " +
+                                   std::to_string(ws_bytes));
+  return TS_OK;
+}
+
+ts_status stack_impl(const ts_model_desc* m, const ts_layer_weights* layers, const ts_plan* p, int32_t k,
+                     const float* x_in, const float* g, float* x_out, float* g_out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  ts_status st;
+  if ((st = check_model(m)) != TS_OK) return st;
+  if ((st = check_plan(p, m)) != TS_OK) return st;
+  if (!layers && m->n_layers > 0) return fail(TS_EINVAL, "layers is null");
+  if (k < 0 || k > m->n_layers) return fail(TS_EINVAL, "k must be in 0..n_layers");
+  if (!x_in || !g || !x_out) return fail(TS_EINVAL, "x_in, g and x_out must be non-null");
+  for (int l = 0; l < m->n_layers; ++l)
+    if ((st = check_weights(m, &layers[l], l >= k)) != TS_OK) return st;
+  const bool per_tile = k > 0;
+  const bool shared_xs = k < m->n_layers;
+  WS w0 = layout(m, p, true, per_tile, shared_xs, nullptr);
+  if ((st = check_ws(ws, ws_bytes, w0.bytes)) != TS_OK) return st;
+  WS w = layout(m, p, true, per_tile, shared_xs, (char*)ws);
+  Ctx c{m, p, (hipStream_t)stream};
+  const int d = m->d;
+  const int64_t Mt = int64_t(p->n_tiles) * (p->n + 1);
+  const int64_t Ms = int64_t(p->n_union) + p->n_tiles;
+  if (per_tile) {
+    {
+      Scope sc(c.s, "gather", 0.0, double(Mt) * d * 8);
+      TS_HIP(tsk::gather(c.s, x_in, g, (const int*)p->d_tile_rows, p->n_tiles, p->n, d, w.X), "gather");
+    }
+    for (int l = 0; l < k; ++l)
+      if ((st = run_layer(c, layers[l], w.X, false, w)) != TS_OK) return st;
+    // merge into one shared state (or the output, for the tiled baseline)
+    float* mu = shared_xs ? w.xs : x_out;
+    float* mg = shared_xs ? w.xs + size_t(p->n_union) * d : g_out;
+    Scope sc(c.s, "merge", 0.0, (double(p->n_entries + p->n_tiles) + double(Ms)) * d * 4);
+    TS_HIP(tsk::blend(c.s, TS_F32, TS_F32, w.X, d, p->n_union, p->n_tiles, p->n, (const int*)p->d_cover_ptr,
+                      (const int*)p->d_entry_row, (const float*)p->d_cover_w, mu, mg),
+           "merge");
+  } else {
+    Scope sc(c.s, "init_shared", 0.0, double(Ms) * d * 8);
+    TS_HIP(tsk::init_shared(c.s, x_in, g, p->n_union, p->n_tiles, d, w.xs), "init");
+  }
+  if (shared_xs) {
+    for (int l = k; l < m->n_layers; ++l)
+      if ((st = run_layer(c, layers[l], w.xs, true, w)) != TS_OK) return st;
+    Scope sc(c.s, "copy_out", 0.0, double(Ms) * d * 8);
+    TS_HIP(tsk::copy_f32(c.s, w.xs, x_out, int64_t(p->n_union) * d), "copy out");
+    if (g_out) TS_HIP(tsk::copy_f32(c.s, w.xs + size_t(p->n_union) * d, g_out, int64_t(p->n_tiles) * d), "copy g");
+  }
+  return TS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ts_abi_version(void) { return TS_ABI_VERSION; }
+const char* ts_last_error(void) { return g_err.c_str(); }
+
+ts_status ts_plan_create(const ts_tiling_desc* desc, ts_plan** out) {
+  if (!desc || !out) return fail(TS_EINVAL, "desc and out must be non-null");
+  *out = nullptr;
+  ts_plan* p = new (std::nothrow) ts_plan();
+  if (!p) return fail(TS_ENOMEM, "host allocation failed");
+  std::string err;
+  try {
+    err = tsplan::build(*desc, *p);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(TS_ENOMEM, "host allocation failed");
+  }
+  if (!err.empty()) {
+    delete p;
+    return fail(TS_EINVAL, err);
+  }
+  *out = p;
+  return TS_OK;
+}
+
+ts_status ts_plan_get_info(const ts_plan* p, ts_plan_info* out) {
+  if (!p || !out) return fail(TS_EINVAL, "plan and out must be non-null");
+  out->n_tiles = p->n_tiles;
+  out->tile_tokens = p->n;
+  out->n_union = p->n_union;
+  out->n_entries = p->n_entries;
+  out->max_cover = p->max_cover;
+  for (int a = 0; a < 3; ++a) out->extent[a] = p->ext[a];
+  return TS_OK;
+}
+
+ts_status ts_plan_export(const ts_plan* p, int32_t* tile_start, int32_t* tile_rows, int32_t* cover_ptr,
+                         int32_t* cover_tile, int32_t* cover_local, float* cover_w) {
+  if (!p) return fail(TS_EINVAL, "plan is null");
+  if (tile_start) std::memcpy(tile_start, p->tile_start.data(), p->tile_start.size() * 4);
+  if (tile_rows) std::memcpy(tile_rows, p->tile_rows.data(), p->tile_rows.size() * 4);
+  if (cover_ptr) std::memcpy(cover_ptr, p->cover_ptr.data(), p->cover_ptr.size() * 4);
+  if (cover_tile) std::memcpy(cover_tile, p->cover_tile.data(), p->cover_tile.size() * 4);
+  if (cover_local) std::memcpy(cover_local, p->cover_local.data(), p->cover_local.size() * 4);
+  if (cover_w) std::memcpy(cover_w, p->cover_w.data(), p->cover_w.size() * 4);
+  return TS_OK;
+}
+
+ts_status ts_plan_export_rope(const ts_plan* p, int32_t head_dim, float rope_base, float* cos_out,
+                              float* sin_out) {
+  if (!p || !cos_out || !sin_out) return fail(TS_EINVAL, "null argument");
+  if (head_dim <= 0 || head_dim % 2 != 0) return fail(TS_EINVAL, "head_dim must be even and positive");
+  std::vector<float> tab;
+  int32_t maxl = 0;
+  tsplan::rope_table(*p, head_dim, rope_base, tab, maxl);
+  int32_t pairs[3];
+  tsplan::rope_pairs(p->desc.ndim, head_dim, pairs);
+  const int32_t P = head_dim / 2;
+  for (int32_t j = 0; j < p->n; ++j) {
+    for (int32_t k = 0; k < P; ++k) {
+      const int ax = k < pairs[0] ? 0 : (k < pairs[0] + pairs[1] ? 1 : 2);
+      const int pos = (p->local_pos[j] >> (10 * ax)) & 1023;
+      cos_out[size_t(j) * P + k] = tab[2 * (size_t(k) * maxl + pos)];
+      sin_out[size_t(j) * P + k] = tab[2 * (size_t(k) * maxl + pos) + 1];
+    }
+  }
+  return TS_OK;
+}
+
+static void free_device(ts_plan* p) {
+  void** ptrs[] = {&p->d_tile_rows, &p->d_cover_ptr, &p->d_entry_row, &p->d_cover_w, &p->d_local_pos, &p->d_rope};
+  for (void** q : ptrs) {
+    if (*q) (void)hipFree(*q);
+    *q = nullptr;
+  }
+  p->uploaded = false;
+}
+
+ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* stream) {
+  if (!p) return fail(TS_EINVAL, "plan is null");
+  if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > 256) return fail(TS_EINVAL, "bad head_dim");
+  std::vector<float> tab;
+  int32_t maxl = 0;
+  tsplan::rope_table(*p, head_dim, rope_base, tab, maxl);
+  if (tab.size() > 4096) return fail(TS_ESHAPE, "RoPE table exceeds 16 KB (head_dim/2 * max extent too large)");
+  std::vector<int32_t> entry_row(p->n_entries);
+  for (int32_t e = 0; e < p->n_entries; ++e) entry_row[e] = p->cover_tile[e] * (p->n + 1) + p->cover_local[e];
+  free_device(p);
+  hipStream_t s = (hipStream_t)stream;
+  struct Item {
+    void** dst;
+    const void* src;
+    size_t bytes;
+  } items[] = {
+      {&p->d_tile_rows, p->tile_rows.data(), p->tile_rows.size() * 4},
+      {&p->d_cover_ptr, p->cover_ptr.data(), p->cover_ptr.size() * 4},
+      {&p->d_entry_row, entry_row.data(), entry_row.size() * 4},
+      {&p->d_cover_w, p->cover_w.data(), p->cover_w.size() * 4},
+      {&p->d_local_pos, p->local_pos.data(), p->local_pos.size() * 4},
+      {&p->d_rope, tab.data(), tab.size() * 4},
+  };
+  for (auto& it : items) {
+    if (hipMalloc(it.dst, std::max<size_t>(it.bytes, 4)) != hipSuccess) {
+      free_device(p);
+      return fail(TS_ENOMEM, "device allocation for the plan failed");
+    }
+    hipError_t e = hipMemcpyAsync(*it.dst, it.src, it.bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) {
+      free_device(p);
+      return fail(TS_EHIP, std::string("plan upload: ") + hipGetErrorString(e));
+    }
+  }
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    free_device(p);
+    return fail(TS_EHIP, std::string("plan upload sync: ") + hipGetErrorString(e));
+  }
+  tsplan::rope_pairs(p->desc.ndim, head_dim, p->rope_pairs);
+  p->rope_hd = head_dim;
+  p->rope_base = rope_base;
+  p->rope_maxl = maxl;
+  p->uploaded = true;
+  return TS_OK;
+}
+
+void ts_plan_destroy(ts_plan* p) {
+  if (!p) return;
+  free_device(p);
+  delete p;
+}
+
+ts_status ts_workspace_size(const ts_model_desc* m, const ts_plan* p, int32_t k, size_t* bytes) {
+  ts_status st;
+  if ((st = check_model(m)) != TS_OK) return st;
+  if (!p || !bytes) return fail(TS_EINVAL, "plan and bytes must be non-null");
+  if (k < 0 || k > m->n_layers) return fail(TS_EINVAL, "k must be in 0..n_layers");
+  // the larger of what the stack (with k) and a single shared layer need
+  WS a = layout(m, p, true, k > 0, k < m->n_layers, nullptr);
+  WS b = layout(m, p, false, false, false, nullptr);
+  *bytes = std::max(a.bytes, b.bytes);
+  return TS_OK;
+}
+
+ts_status ts_shared_layer_forward(const ts_model_desc* m, const ts_layer_weights* w, const ts_plan* p,
+                                  float* x, void* ws, size_t ws_bytes, void* stream) {
+  ts_status st;
+  if ((st = check_model(m)) != TS_OK) return st;
+  if ((st = check_plan(p, m)) != TS_OK) return st;
+  if ((st = check_weights(m, w, true)) != TS_OK) return st;
+  if (!x) return fail(TS_EINVAL, "x is null");
+  WS w0 = layout(m, p, false, false, false, nullptr);
+  if ((st = check_ws(ws, ws_bytes, w0.bytes)) != TS_OK) return st;
+  WS wl = layout(m, p, false, false, false, (char*)ws);
+  Ctx c{m, p, (hipStream_t)stream};
+  return run_layer(c, *w, x, true, wl);
+}
+
+ts_status ts_stack_forward(const ts_model_desc* m, const ts_layer_weights* layers, const ts_plan* p,
+                           int32_t k, const float* x_in, const float* g, float* x_out, float* g_out,
+                           void* ws, size_t ws_bytes, void* stream) {
+  return stack_impl(m, layers, p, k, x_in, g, x_out, g_out, ws, ws_bytes, stream);
+}
+
+ts_status ts_tiled_forward(const ts_model_desc* m, const ts_layer_weights* layers, const ts_plan* p,
+                           const float* x_in, const float* g, float* x_out, float* g_out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!m) return fail(TS_EINVAL, "model is null");
+  return stack_impl(m, layers, p, m->n_layers, x_in, g, x_out, g_out, ws, ws_bytes, stream);
+}
+
+ts_status ts_fp8_quantize(const void* src, int32_t src_dtype, int64_t n, uint8_t* dst, float* scale,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (!src || !dst || !scale) return fail(TS_EINVAL, "null argument");
+  if (src_dtype != TS_F32 && src_dtype != TS_BF16) return fail(TS_EDTYPE, "src_dtype must be TS_F32 or TS_BF16");
+  if (n <= 0) return fail(TS_EINVAL, "n must be positive");
+  ts_status st;
+  if ((st = check_ws(ws, ws_bytes, 256)) != TS_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Scope sc(s, "fp8_quantize", 0.0, double(n) * (2.0 * act_bytes(src_dtype) + 1.0));
+  TS_HIP(tsk::fp8_quantize(s, src_dtype, src, n, dst, scale, (unsigned*)ws), "fp8 quantize");
+  return TS_OK;
+}
+
+ts_status ts_op_gemm(int32_t dtype, int32_t epilogue, const void* a, const void* b, int32_t m, int32_t n,
+                     int32_t k, const float* bias, void* c, const float* scale_a, const float* scale_b,
+                     void* stream) {
+  if (!a || !b || !c) return fail(TS_EINVAL, "a, b and c must be non-null");
+  if (m < 0 || n <= 0 || k <= 0) return fail(TS_EINVAL, "bad GEMM sizes");
+  if (epilogue < 0 || epilogue > 3) return fail(TS_EINVAL, "bad epilogue");
+  if (dtype == TS_BF16 && (k % 64 != 0 || n % 16 != 0)) return fail(TS_ESHAPE, "bf16 GEMM needs k % 64 == 0, n % 16 == 0");
+  if (dtype == TS_FP8E4M3 && (k % 128 != 0 || n % 16 != 0)) return fail(TS_ESHAPE, "fp8 GEMM needs k % 128 == 0, n % 16 == 0");
+  if (dtype == TS_FP8E4M3 && (!scale_a || !scale_b)) return fail(TS_EINVAL, "fp8 GEMM needs both scales");
+  if (dtype != TS_F32 && dtype != TS_BF16 && dtype != TS_FP8E4M3) return fail(TS_EDTYPE, "bad dtype");
+  hipStream_t s = (hipStream_t)stream;
+  const int ab = act_bytes(dtype);
+  const int ob = (epilogue >= 2 || dtype == TS_F32) ? 4 : 2;
+  Scope sc(s, dtype == TS_F32 ? "gemm_f32" : (dtype == TS_BF16 ? "gemm_bf16" : "gemm_fp8"), 2.0 * m * n * k,
+           gemm_bytes(m, n, k, ab, ob, epilogue == TS_EPI_RESIDUAL));
+  TS_HIP(tsk::gemm(s, dtype == TS_F32 ? tsk::ACT_F32 : (dtype == TS_BF16 ? tsk::ACT_BF16 : tsk::ACT_FP8), epilogue,
+                   a, b, m, n, k, bias, c, scale_a, scale_b),
+         "gemm");
+  return TS_OK;
+}
+
+ts_status ts_op_window_attention(const ts_model_desc* m, const ts_plan* p, int32_t shared, const void* qkv,
+                                 void* out, void* stream) {
+  ts_status st;
+  if ((st = check_model(m)) != TS_OK) return st;
+  if ((st = check_plan(p, m)) != TS_OK) return st;
+  if (!qkv || !out) return fail(TS_EINVAL, "qkv and out must be non-null");
+  return window_attention(m, p, shared != 0, qkv, out, (hipStream_t)stream);
+}
+
+ts_status ts_profile_begin(void) {
+  g_prof.on = true;
+  return TS_OK;
+}
+
+ts_status ts_profile_end(ts_kernel_stat* out, int32_t max_records, int32_t* n_records) {
+  g_prof.on = false;
+  std::map<std::string, ts_kernel_stat> agg;
+  std::vector<std::string> order;
+  ts_status result = TS_OK;
+  for (auto& r : g_prof.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      result = fail(TS_EHIP, "profile event query failed");
+    auto it = agg.find(r.name);
+    if (it == agg.end()) {
+      ts_kernel_stat z{};
+      std::snprintf(z.name, sizeof(z.name), "%s", r.name.c_str());
+      it = agg.emplace(r.name, z).first;
+      order.push_back(r.name);
+    }
+    it->second.launches += 1;
+    it->second.total_ms += ms;
+    it->second.flops += r.flops;
+    it->second.bytes += r.bytes;
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  int32_t nrec = 0;
+  for (auto& name : order) {
+    if (out && nrec < max_records) out[nrec] = agg[name];
+    ++nrec;
+  }
+  if (n_records) *n_records = std::min<int32_t>(nrec, max_records);
+  return result;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal layout of ts_plan, shared by the host-only plan builder (plan.cpp,
+// built with the host compiler) and the HIP side (abi.hip).  No HIP types here.
+#pragma once
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/tileshare.h"
+
+struct ts_plan {
+  ts_tiling_desc desc;
+  int32_t n_tiles = 0, n = 0, n_union = 0, n_entries = 0, max_cover = 0;
+  int32_t ext[3] = {1, 1, 1};
+  std::vector<int32_t> axis_starts[3];
+  std::vector<int32_t> tile_start;   // [n_tiles*3]
+  std::vector<int32_t> tile_rows;    // [n_tiles*n]
+  std::vector<int32_t> cover_ptr;    // [n_union+1]
+  std::vector<int32_t> cover_tile;   // [n_entries]
+  std::vector<int32_t> cover_local;  // [n_entries]
+  std::vector<float> cover_w;        // [n_entries]
+  std::vector<int32_t> local_pos;    // [n] packed tau | y<<10 | x<<20
+
+  // device copies (owned; void* to keep HIP out of this header)
+  void* d_tile_rows = nullptr;   // int32 [n_tiles*n]
+  void* d_cover_ptr = nullptr;   // int32 [n_union+1]
+  void* d_entry_row = nullptr;   // int32 [n_entries]: t*(n+1)+local of each entry
+  void* d_cover_w = nullptr;     // fp32 [n_entries]
+  void* d_local_pos = nullptr;   // int32 [n]
+  void* d_rope = nullptr;        // float2 [pairs * rope_maxl] (cos, sin)
+  int32_t rope_hd = 0;
+  float rope_base = 0.f;
+  int32_t rope_maxl = 0;
+  int32_t rope_pairs[3] = {0, 0, 0};
+  bool uploaded = false;
+};
+
+namespace tsplan {
+// Builds every host-side map of the plan; returns an error message or "".
+std::string build(const ts_tiling_desc& desc, ts_plan& p);
+// Pairs per axis for a head size (t, h, w).
+void rope_pairs(int32_t ndim, int32_t head_dim, int32_t out[3]);
+// Compact RoPE table: for pair k and axis position pos, (cos, sin) at
+// tab[2*(k*maxl + pos) + {0,1}], maxl = largest tile extent.
+void rope_table(const ts_plan& p, int32_t head_dim, float base, std::vector<float>& tab,
+                int32_t& maxl);
+}  // namespace tsplan

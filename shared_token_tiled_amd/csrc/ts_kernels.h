@@ -1,0 +1,62 @@
+// Host-side launchers of the HIP kernels (internal to libtileshare).
+// Every launcher validates nothing beyond what its kernel assumes; the
+// C ABI (abi.hip) checks shapes before calling them.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsk {
+
+enum Act { ACT_F32 = 0, ACT_BF16 = 1, ACT_FP8 = 2 };
+
+// GEMM epilogues: C = A B^T (A [M,K], B [N,K], row-major), v = alpha*acc + bias[n]
+enum Epi {
+  EPI_BIAS = 0,      // C (act) = v
+  EPI_BIAS_GELU = 1, // C (act) = GELU(v)
+  EPI_RESID = 2,     // C (fp32) += v   (residual stream, in place)
+  EPI_F32 = 3,       // C (fp32) = v
+};
+
+// ---- elementwise.hip ----
+// y[M,d] (act) = Norm(x[M,d] fp32); rms: RMSNorm(g) else LayerNorm(g, b).
+hipError_t norm(hipStream_t s, int act, bool rms, const float* x, int M, int d, const float* g,
+                const float* b, float eps, void* y);
+// In place per-head RMSNorm of the q and k sections of qkv [M, 3d] (act).
+hipError_t qk_norm(hipStream_t s, int act, void* qkv, int M, int d, int H, int hd, const float* qg,
+                   const float* kg, float eps);
+// out_union[p] = sum_e w[e] * in[entry_row[e]] over cover_ptr[p]..cover_ptr[p+1];
+// out_global[t] = in[t*(n+1)+n] (skipped when out_global is null).
+hipError_t blend(hipStream_t s, int tin, int tout, const void* in, int d, int n_union, int n_tiles,
+                 int n, const int* cover_ptr, const int* entry_row, const float* w, void* out_union,
+                 void* out_global);
+// X[t*(n+1)+j] = x_in[tile_rows[t*n+j]], X[t*(n+1)+n] = g  (fp32)
+hipError_t gather(hipStream_t s, const float* x_in, const float* g, const int* tile_rows, int n_tiles,
+                  int n, int d, float* X);
+// xs[p] = x_in[p] (p < n_union), xs[n_union+t] = g  (fp32)
+hipError_t init_shared(hipStream_t s, const float* x_in, const float* g, int n_union, int n_tiles,
+                       int d, float* xs);
+// dst[i] = src[i], n multiple of 4 (fp32)
+hipError_t copy_f32(hipStream_t s, const float* src, float* dst, int64_t n);
+// e4m3 per-tensor quantisation; amax_slot: 4 bytes of scratch device memory.
+hipError_t fp8_quantize(hipStream_t s, int tin, const void* src, int64_t n, uint8_t* dst,
+                        float* scale_out, unsigned* amax_slot);
+
+// ---- gemm_*.hip ----
+// act: ACT_F32 (fp32 operands), ACT_BF16, ACT_FP8 (e4m3 operands, alpha = *sa * *sb).
+hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, int M, int N, int K,
+                const float* bias, void* C, const float* sa, const float* sb);
+
+// ---- attn_*.hip ----
+struct AttnArgs {
+  const void* qkv;      // [rows, 3d] act
+  void* out;            // [n_tiles*(n+1), d] act, per-tile layout
+  const int* rows;      // [n_tiles*n] grid rows (shared layer) or null (per-tile rows)
+  int n_union;          // global row of tile t = n_union + t when rows != null
+  int d, H, hd, n_tiles, n;
+  const int* local_pos; // [n] packed tau | y<<10 | x<<20
+  const float* rope;    // compact (cos, sin) table [pairs*maxl*2]
+  int maxl, pairs_t, pairs_h;
+};
+hipError_t attention(hipStream_t s, int act, const AttnArgs& a);
+
+}  // namespace tsk

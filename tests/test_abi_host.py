@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+symbol the header declares, builds plans bit-exact to the oracle's, and
+rejects bad arguments with the documented status codes."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import shared_token_tiled_amd as ts
+from oracle.plan import Plan, rope_tables
+from synth import configs
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tileshare.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ts_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ts.lib()
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert ts.ts_abi_version() == 1
+
+
+PLAN_CASES = [(configs.get(n)["ndim"], configs.get(n)["grid"], configs.get(n)["tile"], configs.get(n)["stride"])
+              for n in ("tiny2d", "small_video", "minimax_h3", "vitok4k")] + [
+    (2, (1, 7, 9), (1, 4, 4), (1, 3, 3)),
+    (3, (3, 5, 6), (2, 3, 4), (1, 2, 3)),
+    (3, (2, 6, 6), (2, 6, 3), (2, 6, 3)),
+    (2, (1, 5, 11), (1, 5, 5), (1, 5, 2)),
+    (3, (2, 3, 3), (2, 4, 4), (2, 4, 4)),
+    (2, (1, 13, 29), (1, 6, 7), (1, 4, 5)),
+]
+
+
+@pytest.mark.parametrize("ndim,grid,tile,stride", PLAN_CASES)
+def test_plan_bit_exact_against_oracle(ndim, grid, tile, stride):
+    h = ts.ts_plan_create(ndim, grid, tile, stride)
+    try:
+        info = ts.ts_plan_get_info(h)
+        ref = Plan(grid, tile, stride)
+        assert (info.n_tiles, info.tile_tokens, info.n_union, info.n_entries, info.max_cover) == \
+            (ref.n_tiles, ref.tile_tokens, ref.n_union, ref.n_entries, ref.max_cover)
+        assert tuple(info.extent) == ref.extent
+        st, tr, cp, ct, cl, cw = ts.ts_plan_export(h)
+        assert np.array_equal(st, ref.tile_start_array())
+        assert np.array_equal(tr, ref.tile_rows)
+        assert np.array_equal(cp, ref.cover_ptr)
+        assert np.array_equal(ct, ref.cover_tile)
+        assert np.array_equal(cl, ref.cover_local)
+        assert np.array_equal(cw.view(np.uint32), ref.cover_w.view(np.uint32))   # bit-exact w-bar
+        for hd in (32, 64, 128):
+            c, s = ts.ts_plan_export_rope(h, hd, 10000.0)
+            rc, rs = rope_tables(ref, ndim, hd, 10000.0)
+            assert np.array_equal(c.view(np.uint32), rc.view(np.uint32))
+            assert np.array_equal(s.view(np.uint32), rs.view(np.uint32))
+    finally:
+        ts.ts_plan_destroy(h)
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((4, (1, 2, 3), (1, 2, 3), (1, 1, 1)), "ndim"),
+    ((2, (2, 4, 4), (2, 4, 4), (1, 1, 1)), "2D"),
+    ((3, (2, 4, 4), (2, 0, 4), (1, 1, 1)), ">= 1"),
+    ((3, (2, 4, 4), (2, 4, 4), (1, 1, 0)), ">= 1"),
+])
+def test_plan_rejects_bad_descriptions(args, msg):
+    with pytest.raises(ts.TileShareError, match="TS_EINVAL.*" + msg):
+        ts.ts_plan_create(*args)
+    with pytest.raises(ts.TileShareError, match="n_global"):
+        ts.ts_plan_create(2, (1, 4, 4), (1, 4, 4), (1, 4, 4), n_global=2)
+
+
+def _model(**kw):
+    cfg = dict(configs.get("small_video"))
+    cfg.update(kw)
+    return ts.model_desc(cfg)
+
+
+def test_model_and_workspace_validation_on_host():
+    h = ts.ts_plan_create(3, (4, 12, 20), (4, 12, 12), (4, 8, 8))
+    try:
+        m = _model()
+        n = ts.ts_workspace_size(m, h, 2)
+        assert n > 0 and n % 256 == 0
+        with pytest.raises(ts.TileShareError, match="TS_EINVAL"):
+            ts.ts_workspace_size(m, h, 9)              # k > n_layers
+        with pytest.raises(ts.TileShareError, match="TS_ESHAPE"):
+            ts.ts_workspace_size(_model(d=700, n_heads=7, head_dim=100), h, 0)
+        with pytest.raises(ts.TileShareError, match="TS_ESHAPE"):
+            ts.ts_workspace_size(_model(n_heads=6, head_dim=100), h, 0)   # d != heads*hd
+        with pytest.raises(ts.TileShareError, match="TS_EDTYPE"):
+            ts.ts_workspace_size(_model(dtype="f32", gemm_shared="bf16", head_dim=64), h, 0)
+        # forward calls refuse a plan that was never uploaded, before touching a GPU
+        L = ts.lib()
+        st = L.ts_stack_forward(ctypes.byref(m), None, h, 0, None, None, None, None, None, 0, None)
+        assert st == -1 and b"uploaded" in L.ts_last_error()
+        st = L.ts_shared_layer_forward(ctypes.byref(m), None, h, None, None, 0, None)
+        assert st == -1
+        st = L.ts_fp8_quantize(None, 1, 16, None, None, None, 0, None)
+        assert st == -1
+    finally:
+        ts.ts_plan_destroy(h)

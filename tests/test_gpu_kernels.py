@@ -1,0 +1,155 @@
+"""GPU parity of the building-block kernels against the oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import shared_token_tiled_amd as ts
+from oracle import fp8 as ofp8
+from oracle import model as M
+from oracle.plan import Plan
+from synth import round_bf16
+
+from gpu_helpers import DEV, max_rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+GEMM_SHAPES = [(300, 512, 320), (257, 768, 64), (1000, 256, 1024), (64, 16, 128), (513, 2304, 768)]
+
+
+@pytest.mark.parametrize("M_,N,K", GEMM_SHAPES)
+@pytest.mark.parametrize("epi", [0, 1, 2, 3])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gemm_against_oracle(M_, N, K, epi, dtype):
+    say(f"gemm {dtype} epi={epi} M={M_} N={N} K={K}")
+    r = _rng(M_ + N + K + epi)
+    A = r.standard_normal((M_, K)).astype(np.float32)
+    B = (0.05 * r.standard_normal((N, K))).astype(np.float32)
+    bias = r.standard_normal(N).astype(np.float32)
+    c0 = r.standard_normal((M_, N)).astype(np.float32)
+    if dtype == "bf16":
+        A, B = round_bf16(A), round_bf16(B)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    a = torch.from_numpy(A).to(DEV, tdt)
+    b = torch.from_numpy(B).to(DEV, tdt)
+    bt = torch.from_numpy(bias).to(DEV)
+    out_f32 = epi >= 2 or dtype == "f32"
+    c = torch.from_numpy(c0).to(DEV) if out_f32 else torch.zeros(M_, N, dtype=tdt, device=DEV)
+    ts.ts_op_gemm(ts.TS_F32 if dtype == "f32" else ts.TS_BF16, epi, a, b, bt, c)
+    torch.cuda.synchronize()
+    ref = A.astype(np.float64) @ B.astype(np.float64).T + bias
+    if epi == 1:
+        ref = M.gelu(ref)
+    if epi == 2:
+        ref = ref + c0
+    got = c.float().cpu().numpy()
+    tol = 1e-5 if out_f32 else 1e-2
+    assert max_rel(got, ref) < tol
+
+
+def test_gemm_fp8_against_oracle():
+    say("gemm fp8")
+    r = _rng(7)
+    Mq, N, K = 333, 512, 640
+    A = round_bf16(r.standard_normal((Mq, K)).astype(np.float32))
+    B = round_bf16((0.05 * r.standard_normal((N, K))).astype(np.float32))
+    bias = r.standard_normal(N).astype(np.float32)
+    a = torch.from_numpy(A).to(DEV, torch.bfloat16)
+    b = torch.from_numpy(B).to(DEV, torch.bfloat16)
+    a8 = torch.empty(Mq, K, dtype=torch.uint8, device=DEV)
+    b8 = torch.empty(N, K, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(2, dtype=torch.float32, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    ts.ts_fp8_quantize(a, a8, sc[0:1], ws)
+    ts.ts_fp8_quantize(b, b8, sc[1:2], ws)
+    for epi in (0, 3):
+        c = torch.empty(Mq, N, dtype=torch.float32 if epi == 3 else torch.bfloat16, device=DEV)
+        ts.ts_op_gemm(ts.TS_FP8E4M3, epi, a8, b8, torch.from_numpy(bias).to(DEV), c, sc[0:1], sc[1:2])
+        torch.cuda.synchronize()
+        ref = ofp8.fp8_linear(A, B, bias)
+        assert max_rel(c.float().cpu().numpy(), ref) < (1e-5 if epi == 3 else 1e-2)
+
+
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_fp8_quantize_bit_exact(src):
+    say(f"fp8 quantize {src}")
+    r = _rng(3)
+    x = (r.standard_normal(40003) * 3).astype(np.float32)
+    # values that land exactly on e4m3 midpoints after scaling: s = 448/448 = 1
+    table = ofp8.e4m3_decode_table()
+    fin = np.sort(np.unique(np.abs(table[np.isfinite(table)])))
+    mids = ((fin[:-1] + fin[1:]) / 2).astype(np.float32)
+    x[: len(mids)] = mids
+    x[len(mids): 2 * len(mids)] = -mids
+    x[-1] = 448.0
+    if src == "bf16":
+        x = round_bf16(x)
+    t = torch.from_numpy(x).to(DEV, torch.float32 if src == "f32" else torch.bfloat16)
+    q = torch.empty(x.size, dtype=torch.uint8, device=DEV)
+    s = torch.empty(1, dtype=torch.float32, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    ts.ts_fp8_quantize(t, q, s, ws)
+    torch.cuda.synchronize()
+    s_ref = ofp8.tensor_scale(x)
+    assert s.cpu().numpy()[0] == s_ref
+    codes_ref = ofp8.encode_e4m3(ofp8.round_e4m3(x / s_ref))
+    got = q.cpu().numpy()
+    # +0 / -0 may differ in sign only when the value is zero
+    zero = ofp8.round_e4m3(x / s_ref) == 0
+    assert np.array_equal(got[~zero], codes_ref[~zero])
+    assert np.all((got[zero] & 0x7F) == 0)
+
+
+ATTN_CASES = [
+    # ndim, grid, tile, stride, H, hd, dtype
+    (3, (2, 12, 20), (2, 8, 8), (2, 6, 6), 2, 128, "bf16"),
+    (3, (2, 12, 28), (2, 12, 12), (2, 8, 8), 3, 64, "bf16"),
+    (2, (1, 20, 36), (1, 16, 16), (1, 12, 12), 2, 64, "bf16"),
+    (2, (1, 16, 24), (1, 16, 16), (1, 8, 8), 2, 32, "f32"),
+    (3, (2, 9, 10), (2, 7, 5), (2, 3, 3), 2, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("ndim,grid,tile,stride,H,hd,dtype", ATTN_CASES)
+@pytest.mark.parametrize("shared", [True, False])
+@pytest.mark.parametrize("qk_scale", [1.0, 3.0])
+def test_window_attention_against_oracle(ndim, grid, tile, stride, H, hd, dtype, shared, qk_scale):
+    say(f"attention {dtype} grid={grid} tile={tile} hd={hd} shared={shared} qk_scale={qk_scale}")
+    d = H * hd
+    cfg = dict(ndim=ndim, grid=grid, tile=tile, stride=stride, d=d, n_heads=H, head_dim=hd, mlp_hidden=4 * d,
+               n_layers=1, norm="ln", qk_norm=False, dtype=dtype, gemm_shared=dtype)
+    pl = Plan(grid, tile, stride)
+    n = pl.tile_tokens
+    rows = pl.n_union + pl.n_tiles if shared else pl.n_tiles * (n + 1)
+    r = _rng(11)
+    qkv = r.standard_normal((rows, 3 * d)).astype(np.float32)
+    qkv[:, : 2 * d] *= qk_scale
+    if dtype == "bf16":
+        qkv = round_bf16(qkv)
+    h = ts.ts_plan_create(ndim, grid, tile, stride)
+    try:
+        ts.ts_plan_upload(h, hd)
+        tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+        tq = torch.from_numpy(qkv).to(DEV, tdt)
+        out = torch.zeros(pl.n_tiles * (n + 1), d, dtype=tdt, device=DEV)
+        ts.ts_op_window_attention(ts.model_desc(cfg), h, shared, tq, out)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+    finally:
+        ts.ts_plan_destroy(h)
+    rope = M.Rope(pl, cfg)
+    q64 = qkv.astype(np.float64)
+    errs = []
+    for t in range(pl.n_tiles):
+        if shared:
+            idx = np.concatenate([pl.tile_rows[t].astype(np.int64), [pl.n_union + t]])
+        else:
+            idx = np.arange(t * (n + 1), (t + 1) * (n + 1))
+        ref = M.tile_attention(q64[idx, :d], q64[idx, d:2 * d], q64[idx, 2 * d:], rope.cos, rope.sin, cfg)
+        errs.append(max_rel(got[t * (n + 1):(t + 1) * (n + 1)], ref))
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert max(errs) < tol, errs

@@ -1,0 +1,134 @@
+"""GPU parity of the shared layer, the TileShare-k stack and the tiled baseline
+against the oracle, on seeded inputs at sizes the oracle finishes in seconds
+(several tiles, ragged query and key blocks), plus the invariants of the
+pages checked GPU-against-GPU at the same sizes."""
+import numpy as np
+import pytest
+
+from oracle import model as M
+from oracle.plan import Plan
+from synth import configs, make_inputs
+
+from gpu_helpers import TOL, Run, max_rel, say
+
+pytestmark = pytest.mark.gpu
+
+# Reduced-size versions of the workloads: same block type, head size, norm and
+# tiling pattern (overlap, clamped last tile), fewer tokens / channels / layers.
+REDUCED = {
+    "minimax_h3": dict(grid=(2, 12, 20), tile=(2, 8, 8), stride=(2, 6, 6), d=256, n_heads=2, mlp_hidden=1024,
+                       n_layers=3),
+    "minimax_h3_fp8": dict(grid=(2, 12, 20), tile=(2, 8, 8), stride=(2, 6, 6), d=256, n_heads=2,
+                           mlp_hidden=1024, n_layers=3),
+    "small_video": dict(grid=(2, 12, 28), tile=(2, 12, 12), stride=(2, 8, 8), d=256, n_heads=4, mlp_hidden=1024,
+                        n_layers=2),
+    "vitok4k": dict(grid=(1, 20, 36), tile=(1, 16, 16), stride=(1, 12, 12), d=256, n_heads=4, mlp_hidden=1024,
+                    n_layers=2),
+}
+
+
+def reduced(name):
+    return configs.get(name, **REDUCED[name])
+
+
+def _oracle(cfg, x, g, layers, k):
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    return M.stack_forward(cfg, pl, x, g, layers, k)
+
+
+CASES = [("tiny2d", None, 0), ("tiny2d", None, 1),
+         ("minimax_h3", "r", 0), ("minimax_h3", "r", 1), ("minimax_h3", "r", 3),
+         ("minimax_h3_fp8", "r", 0), ("minimax_h3_fp8", "r", 1),
+         ("small_video", "r", 0), ("small_video", "r", 2),
+         ("vitok4k", "r", 0), ("vitok4k", "r", 2)]
+
+
+@pytest.mark.parametrize("name,size,k", CASES)
+@pytest.mark.parametrize("qk_scale", [1.0, 4.0])
+def test_stack_against_oracle(name, size, k, qk_scale):
+    cfg = configs.get(name) if size is None else reduced(name)
+    say(f"stack {name} {'reduced' if size else 'full'} k={k} qk_scale={qk_scale} grid={cfg['grid']}")
+    x, g, layers = make_inputs(cfg, qk_scale=qk_scale)
+    ref, gref = _oracle(cfg, x, g, layers, k)
+    run = Run(cfg, layers)
+    try:
+        got, ggot = run.stack(x, g, k)
+    finally:
+        run.close()
+    tol = TOL["fp8" if cfg["gemm_shared"] == "fp8" and k < cfg["n_layers"] else cfg["dtype"]]
+    e = max_rel(got, ref)
+    eg = max_rel(ggot, gref)
+    print(f"  max|err|/rms = {e:.3e} (globals {eg:.3e}), tolerance {tol}")
+    assert e < tol and eg < tol
+
+
+@pytest.mark.parametrize("name", ["minimax_h3", "vitok4k", "tiny2d"])
+def test_shared_layer_against_oracle(name):
+    cfg = configs.get(name) if name == "tiny2d" else reduced(name)
+    say(f"shared layer {name}")
+    x, g, layers = make_inputs(cfg, n_layers=1)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    rng = np.random.default_rng(5)
+    G = (np.tile(g[None], (pl.n_tiles, 1)) + 0.1 * rng.standard_normal((pl.n_tiles, cfg["d"]))).astype(np.float32)
+    xa = np.vstack([x, G]).astype(np.float32)
+    ref_x, ref_g = M.shared_layer(x.astype(np.float64), G.astype(np.float64), layers[0], cfg, pl, M.Rope(pl, cfg))
+    run = Run(dict(cfg, n_layers=1), layers)
+    try:
+        got = run.shared_layer(xa)
+    finally:
+        run.close()
+    tol = TOL[cfg["dtype"]]
+    assert max_rel(got[: pl.n_union], ref_x) < tol
+    assert max_rel(got[pl.n_union:], ref_g) < tol
+
+
+def test_repeat_runs_are_bit_identical():
+    cfg = reduced("minimax_h3")
+    say("determinism minimax_h3 reduced")
+    x, g, layers = make_inputs(cfg)
+    run = Run(cfg, layers)
+    try:
+        a, ga = run.stack(x, g, 1)
+        b, gb = run.stack(x, g, 1)
+    finally:
+        run.close()
+    assert np.array_equal(a, b) and np.array_equal(ga, gb)
+
+
+@pytest.mark.parametrize("name", ["minimax_h3", "small_video"])
+def test_zero_overlap_every_k_matches_baseline_on_gpu(name):
+    """Figure 2 caption: the blend is the only approximate step, so without
+    overlap TileShare-k equals per-tile decoding for every k."""
+    base = reduced(name)
+    T = base["grid"][0]
+    cfg = dict(base, grid=(T, 8, 24), tile=(T, 8, 8), stride=(T, 8, 8))
+    say(f"zero overlap {name}")
+    x, g, layers = make_inputs(cfg)
+    run = Run(cfg, layers)
+    try:
+        ref, _ = run.stack(x, g, cfg["n_layers"])
+        for k in range(cfg["n_layers"]):
+            got, _ = run.stack(x, g, k)
+            assert max_rel(got, ref) < 1e-5
+    finally:
+        run.close()
+
+
+def test_identical_states_blend_to_themselves_on_gpu():
+    """Table 1 caption: identical per-tile states stay identical.  With W_v = 0
+    and b_v = 0 every tile's state of a token is the same, so TileShare-0
+    equals the tiled baseline up to the fp32 rounding of w-bar."""
+    cfg = reduced("small_video")
+    say("identical states small_video reduced")
+    x, g, layers = make_inputs(cfg)
+    d = cfg["d"]
+    for p in layers:
+        p["w_qkv"][2 * d:] = 0
+        p["b_qkv"][2 * d:] = 0
+    run = Run(cfg, layers)
+    try:
+        base, _ = run.stack(x, g, cfg["n_layers"])
+        ts0, _ = run.stack(x, g, 0)
+    finally:
+        run.close()
+    assert max_rel(ts0, base) < 1e-5
