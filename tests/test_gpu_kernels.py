@@ -47,8 +47,13 @@ def test_gemm_against_oracle(M_, N, K, epi, dtype):
     if epi == 2:
         ref = ref + c0
     got = c.float().cpu().numpy()
-    tol = 1e-5 if out_f32 else 1e-2
-    assert max_rel(got, ref) < tol
+    if out_f32:
+        assert max_rel(got, ref) < 1e-5
+    else:
+        # fp32 accumulation, then one round-to-nearest to bf16 (half an ulp
+        # is at most 2^-8 of the value)
+        rms = np.sqrt(np.mean(ref * ref))
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * rms)
 
 
 def test_gemm_fp8_against_oracle():
@@ -71,7 +76,12 @@ def test_gemm_fp8_against_oracle():
         ts.ts_op_gemm(ts.TS_FP8E4M3, epi, a8, b8, torch.from_numpy(bias).to(DEV), c, sc[0:1], sc[1:2])
         torch.cuda.synchronize()
         ref = ofp8.fp8_linear(A, B, bias)
-        assert max_rel(c.float().cpu().numpy(), ref) < (1e-5 if epi == 3 else 1e-2)
+        got = c.float().cpu().numpy()
+        rms = np.sqrt(np.mean(ref * ref))
+        # same e4m3 codes on both sides; the MFMA's internal sum of the 64
+        # products of one instruction is not a round-per-add fp32 sum, which
+        # leaves a few 1e-5 of the output RMS
+        assert np.all(np.abs(got - ref) <= (2.0 ** -8 * np.abs(ref) if epi == 0 else 0) + 2e-4 * rms)
 
 
 @pytest.mark.parametrize("src", ["bf16", "f32"])
@@ -143,13 +153,23 @@ def test_window_attention_against_oracle(ndim, grid, tile, stride, H, hd, dtype,
         ts.ts_plan_destroy(h)
     rope = M.Rope(pl, cfg)
     q64 = qkv.astype(np.float64)
-    errs = []
+    row_err, frob = [], []
     for t in range(pl.n_tiles):
         if shared:
             idx = np.concatenate([pl.tile_rows[t].astype(np.int64), [pl.n_union + t]])
         else:
             idx = np.arange(t * (n + 1), (t + 1) * (n + 1))
         ref = M.tile_attention(q64[idx, :d], q64[idx, d:2 * d], q64[idx, 2 * d:], rope.cos, rope.sin, cfg)
-        errs.append(max_rel(got[t * (n + 1):(t + 1) * (n + 1)], ref))
-    tol = 1e-5 if dtype == "f32" else 2e-2
-    assert max(errs) < tol, errs
+        out_t = got[t * (n + 1):(t + 1) * (n + 1)]
+        row_err.append(np.max(np.linalg.norm(out_t - ref, axis=1) / np.linalg.norm(ref, axis=1)))
+        frob.append(np.linalg.norm(out_t - ref) / np.linalg.norm(ref))
+    # bf16: the rotated q and k, the softmax weights and the output are each
+    # rounded to bf16 once; with qk_scale 3 the logits are ~9x larger, so the
+    # rounding of q and k moves them ~9x more.  A wrong row or key would give
+    # per-row errors of order 1.
+    if dtype == "f32":
+        row_tol, frob_tol = 1e-4, 1e-5
+    else:
+        row_tol, frob_tol = (2e-2 if qk_scale == 1.0 else 6e-2), 1e-2
+    print(f"  worst row rel-L2 {max(row_err):.3e}, frobenius {max(frob):.3e}")
+    assert max(row_err) < row_tol and max(frob) < frob_tol, (row_err, frob)
