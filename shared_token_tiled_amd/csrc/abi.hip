@@ -213,9 +213,13 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared
   a.n = p->n;
   a.local_pos = (const int*)p->d_local_pos;
   a.rope = (const float*)p->d_rope;
-  a.maxl = p->rope_maxl;
-  a.pairs_t = p->rope_pairs[0];
-  a.pairs_h = p->rope_pairs[1];
+  a.rope_floats = p->rope_floats;
+  for (int ax = 0; ax < 3; ++ax) {
+    a.pairs[ax] = p->rope_pairs[ax];
+    a.rope_off[ax] = p->rope_off[ax];
+  }
+  if (m->act_dtype == TS_BF16 && m->head_dim == 128 && p->rope_floats > 3776)
+    return fail(TS_ESHAPE, "RoPE table exceeds the 14.75 KB the head_dim-128 attention kernel keeps in LDS");
   const double nn = double(p->n + 1);
   Scope sc(s, m->act_dtype == TS_F32 ? "attn_f32" : "attn_bf16", 4.0 * nn * nn * m->d * p->n_tiles,
            double(p->n_tiles) * (p->n + 1) * m->d * 4 * act_bytes(m->act_dtype));
@@ -388,17 +392,16 @@ ts_status ts_plan_export_rope(const ts_plan* p, int32_t head_dim, float rope_bas
   if (!p || !cos_out || !sin_out) return fail(TS_EINVAL, "null argument");
   if (head_dim <= 0 || head_dim % 2 != 0) return fail(TS_EINVAL, "head_dim must be even and positive");
   std::vector<float> tab;
-  int32_t maxl = 0;
-  tsplan::rope_table(*p, head_dim, rope_base, tab, maxl);
-  int32_t pairs[3];
-  tsplan::rope_pairs(p->desc.ndim, head_dim, pairs);
+  int32_t pairs[3], off[3];
+  tsplan::rope_table(*p, head_dim, rope_base, tab, pairs, off);
   const int32_t P = head_dim / 2;
   for (int32_t j = 0; j < p->n; ++j) {
     for (int32_t k = 0; k < P; ++k) {
       const int ax = k < pairs[0] ? 0 : (k < pairs[0] + pairs[1] ? 1 : 2);
+      const int i = k - (ax == 0 ? 0 : (ax == 1 ? pairs[0] : pairs[0] + pairs[1]));
       const int pos = (p->local_pos[j] >> (10 * ax)) & 1023;
-      cos_out[size_t(j) * P + k] = tab[2 * (size_t(k) * maxl + pos)];
-      sin_out[size_t(j) * P + k] = tab[2 * (size_t(k) * maxl + pos) + 1];
+      cos_out[size_t(j) * P + k] = tab[off[ax] + 2 * (size_t(pos) * pairs[ax] + i)];
+      sin_out[size_t(j) * P + k] = tab[off[ax] + 2 * (size_t(pos) * pairs[ax] + i) + 1];
     }
   }
   return TS_OK;
@@ -417,9 +420,9 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
   if (!p) return fail(TS_EINVAL, "plan is null");
   if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > 256) return fail(TS_EINVAL, "bad head_dim");
   std::vector<float> tab;
-  int32_t maxl = 0;
-  tsplan::rope_table(*p, head_dim, rope_base, tab, maxl);
-  if (tab.size() > 4096) return fail(TS_ESHAPE, "RoPE table exceeds 16 KB (head_dim/2 * max extent too large)");
+  int32_t pairs[3], off[3];
+  tsplan::rope_table(*p, head_dim, rope_base, tab, pairs, off);
+  if (tab.size() > 4096) return fail(TS_ESHAPE, "RoPE table exceeds 16 KB (head_dim/2 * tile extent too large)");
   std::vector<int32_t> entry_row(p->n_entries);
   for (int32_t e = 0; e < p->n_entries; ++e) entry_row[e] = p->cover_tile[e] * (p->n + 1) + p->cover_local[e];
   free_device(p);
@@ -452,10 +455,13 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
     free_device(p);
     return fail(TS_EHIP, std::string("plan upload sync: ") + hipGetErrorString(e));
   }
-  tsplan::rope_pairs(p->desc.ndim, head_dim, p->rope_pairs);
+  for (int a = 0; a < 3; ++a) {
+    p->rope_pairs[a] = pairs[a];
+    p->rope_off[a] = off[a];
+  }
   p->rope_hd = head_dim;
   p->rope_base = rope_base;
-  p->rope_maxl = maxl;
+  p->rope_floats = int32_t(tab.size());
   p->uploaded = true;
   return TS_OK;
 }

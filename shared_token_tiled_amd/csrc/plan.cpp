@@ -139,22 +139,21 @@ void rope_pairs(int32_t ndim, int32_t head_dim, int32_t out[3]) {
 }
 
 void rope_table(const ts_plan& p, int32_t head_dim, float base, std::vector<float>& tab,
-                int32_t& maxl) {
-  int32_t pairs[3];
+                int32_t pairs[3], int32_t off[3]) {
   rope_pairs(p.desc.ndim, head_dim, pairs);
-  maxl = p.ext[0];
-  if (p.ext[1] > maxl) maxl = p.ext[1];
-  if (p.ext[2] > maxl) maxl = p.ext[2];
-  const int32_t P = head_dim / 2;
-  tab.assign(size_t(2) * P * maxl, 0.f);
-  int32_t k = 0;
+  int32_t total = 0;
+  for (int a = 0; a < 3; ++a) {
+    off[a] = total;
+    total += 2 * pairs[a] * p.ext[a];
+  }
+  tab.assign(size_t(total), 0.f);
   for (int a = 0; a < 3; ++a)
-    for (int32_t i = 0; i < pairs[a]; ++i, ++k) {
+    for (int32_t i = 0; i < pairs[a]; ++i) {
       const double inv = std::pow(double(base), double(-i) / double(pairs[a]));
-      for (int32_t pos = 0; pos < maxl; ++pos) {
+      for (int32_t pos = 0; pos < p.ext[a]; ++pos) {
         const double ang = double(pos) * inv;
-        tab[2 * (size_t(k) * maxl + pos)] = float(std::cos(ang));
-        tab[2 * (size_t(k) * maxl + pos) + 1] = float(std::sin(ang));
+        tab[off[a] + 2 * (size_t(pos) * pairs[a] + i)] = float(std::cos(ang));
+        tab[off[a] + 2 * (size_t(pos) * pairs[a] + i) + 1] = float(std::sin(ang));
       }
     }
 }

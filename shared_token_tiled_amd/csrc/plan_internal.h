@@ -26,11 +26,12 @@ struct ts_plan {
   void* d_entry_row = nullptr;   // int32 [n_entries]: t*(n+1)+local of each entry
   void* d_cover_w = nullptr;     // fp32 [n_entries]
   void* d_local_pos = nullptr;   // int32 [n]
-  void* d_rope = nullptr;        // float2 [pairs * rope_maxl] (cos, sin)
+  void* d_rope = nullptr;        // compact per-axis (cos, sin) table, see rope_table
   int32_t rope_hd = 0;
   float rope_base = 0.f;
-  int32_t rope_maxl = 0;
+  int32_t rope_floats = 0;       // floats in the compact table
   int32_t rope_pairs[3] = {0, 0, 0};
+  int32_t rope_off[3] = {0, 0, 0};
   bool uploaded = false;
 };
 
@@ -39,8 +40,9 @@ namespace tsplan {
 std::string build(const ts_tiling_desc& desc, ts_plan& p);
 // Pairs per axis for a head size (t, h, w).
 void rope_pairs(int32_t ndim, int32_t head_dim, int32_t out[3]);
-// Compact RoPE table: for pair k and axis position pos, (cos, sin) at
-// tab[2*(k*maxl + pos) + {0,1}], maxl = largest tile extent.
+// Compact RoPE table: axis a holds pairs[a] rotation pairs over ext[a]
+// positions; the (cos, sin) of pair i of axis a at position pos sits at
+// tab[off[a] + 2*(pos*pairs[a] + i) + {0, 1}].
 void rope_table(const ts_plan& p, int32_t head_dim, float base, std::vector<float>& tab,
-                int32_t& maxl);
+                int32_t pairs[3], int32_t off[3]);
 }  // namespace tsplan

@@ -54,8 +54,11 @@ struct AttnArgs {
   int n_union;          // global row of tile t = n_union + t when rows != null
   int d, H, hd, n_tiles, n;
   const int* local_pos; // [n] packed tau | y<<10 | x<<20
-  const float* rope;    // compact (cos, sin) table [pairs*maxl*2]
-  int maxl, pairs_t, pairs_h;
+  const float* rope;    // compact per-axis (cos, sin) table
+  int rope_floats;      // its length in floats
+  int pairs[3];         // rotation pairs per axis (t, h, w)
+  int rope_off[3];      // float offset of each axis' block: pair i at position pos of
+                        // axis a is (cos, sin) at rope_off[a] + 2*(pos*pairs[a] + i)
 };
 hipError_t attention(hipStream_t s, int act, const AttnArgs& a);
 
