@@ -16,9 +16,13 @@ w-bar.  Readings taken here (listed in the design doc):
 * w-bar: per axis a linear ramp across each overlap with a neighbour
   (lead/trail below), the product over axes, normalised to sum 1 per token;
   computed in float64 in the order written here and rounded once to fp32;
-* RoPE: the head_dim/2 rotation pairs are split over the axes (2D: h, w get
-  half each; 3D: t gets P - 2*floor(P/3), h and w floor(P/3) each); pair i of
-  an axis chunk of m pairs turns by pos * base**(-i/m); cos/sin in float64,
+* RoPE: the P = head_dim/2 rotation pairs are split over the axes in
+  contiguous chunks (t, then h, then w).  3D: h and w get floor(P/3) pairs
+  each and t the rest, except that when P >= 12 and P % 4 == 0 the h and w
+  counts are rounded to the nearest multiple of 4 (halves up), so every group
+  of 4 consecutive pairs (8 dims) belongs to one axis.  2D: h gets P/2 (rounded
+  down to a multiple of 4 when P >= 8 and P % 4 == 0) and w the rest.  Pair i
+  of an axis chunk of m pairs turns by pos * base**(-i/m); cos/sin in float64,
   stored as fp32.  The tile's global token is not rotated.
 """
 import math
@@ -131,9 +135,15 @@ class Plan:
 def rope_pairs(ndim, head_dim):
     """Number of rotation pairs per axis (t, h, w)."""
     P = head_dim // 2
+    aligned = P % 4 == 0
     if ndim == 2:
-        return (0, P // 2, P - P // 2)
+        h = P // 2
+        if aligned and P >= 8:
+            h = 4 * (h // 4)
+        return (0, h, P - h)
     third = P // 3
+    if aligned and P >= 12:
+        third = 4 * ((third + 2) // 4)
     return (P - 2 * third, third, third)
 
 

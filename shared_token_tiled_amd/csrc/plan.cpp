@@ -124,14 +124,22 @@ std::string build(const ts_tiling_desc& d, ts_plan& p) {
   return "";
 }
 
+// Pairs per axis: contiguous chunks t, h, w; 3D h = w = floor(P/3) and t the
+// rest, 2D h = P/2 and w the rest; when P is a multiple of 4 (and P >= 12 in
+// 3D, P >= 8 in 2D) h and w are rounded to multiples of 4 (3D: nearest,
+// halves up; 2D: down) so each group of 4 pairs (8 dims) lies in one axis.
 void rope_pairs(int32_t ndim, int32_t head_dim, int32_t out[3]) {
   const int32_t P = head_dim / 2;
+  const bool aligned = P % 4 == 0;
   if (ndim == 2) {
+    int32_t h = P / 2;
+    if (aligned && P >= 8) h = 4 * (h / 4);
     out[0] = 0;
-    out[1] = P / 2;
-    out[2] = P - P / 2;
+    out[1] = h;
+    out[2] = P - h;
   } else {
-    const int32_t third = P / 3;
+    int32_t third = P / 3;
+    if (aligned && P >= 12) third = 4 * ((third + 2) / 4);
     out[0] = P - 2 * third;
     out[1] = third;
     out[2] = third;
