@@ -176,11 +176,18 @@ double gemm_bytes(int64_t M, int64_t N, int64_t K, int ab, int ob, bool resid) {
   return double(M * K + N * K) * ab + double(M * N) * ob * (resid ? 2 : 1);
 }
 
+// The MFMA GEMM addresses each operand with 32-bit byte offsets.
+bool gemm_offsets_fit(int64_t M, int64_t N, int64_t K, int esz) {
+  return M * K * esz < (int64_t(1) << 32) && N * K * esz < (int64_t(1) << 32);
+}
+
 // y = A W^T (+ epilogue) for one projection; fp8 quantises A first.
 ts_status proj(const Ctx& c, const WS& ws, bool f8, const char* role, int epi, const void* A, int64_t M,
                int N, int K, const void* Wt, const uint8_t* W8, const float* w8scale, const float* bias,
                void* C) {
   const int act = c.m->act_dtype;
+  if (act != TS_F32 && !gemm_offsets_fit(M, N, K, f8 ? 1 : 2))
+    return fail(TS_ESHAPE, std::string("GEMM operand larger than 4 GiB (") + role + ")");
   const int ob = (epi == tsk::EPI_RESID || epi == tsk::EPI_F32) ? 4 : act_bytes(act);
   std::string name = std::string(f8 ? "gemm_fp8[" : (act == TS_F32 ? "gemm_f32[" : "gemm_bf16[")) + role + "]";
   if (f8) {
@@ -218,8 +225,11 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared
     a.pairs[ax] = p->rope_pairs[ax];
     a.rope_off[ax] = p->rope_off[ax];
   }
-  if (m->act_dtype == TS_BF16 && m->head_dim == 128 && p->rope_floats > 3776)
-    return fail(TS_ESHAPE, "RoPE table exceeds the 14.75 KB the head_dim-128 attention kernel keeps in LDS");
+  if (m->act_dtype == TS_BF16) {
+    for (int ax = 0; ax < 3; ++ax)
+      if (p->rope_pairs[ax] % 4 != 0)
+        return fail(TS_ESHAPE, "bf16 attention needs every RoPE axis to hold a multiple of 4 rotation pairs");
+  }
   const double nn = double(p->n + 1);
   Scope sc(s, m->act_dtype == TS_F32 ? "attn_f32" : "attn_bf16", 4.0 * nn * nn * m->d * p->n_tiles,
            double(p->n_tiles) * (p->n + 1) * m->d * 4 * act_bytes(m->act_dtype));
@@ -533,6 +543,8 @@ ts_status ts_op_gemm(int32_t dtype, int32_t epilogue, const void* a, const void*
   if (dtype == TS_BF16 && (k % 64 != 0 || n % 16 != 0)) return fail(TS_ESHAPE, "bf16 GEMM needs k % 64 == 0, n % 16 == 0");
   if (dtype == TS_FP8E4M3 && (k % 128 != 0 || n % 16 != 0)) return fail(TS_ESHAPE, "fp8 GEMM needs k % 128 == 0, n % 16 == 0");
   if (dtype == TS_FP8E4M3 && (!scale_a || !scale_b)) return fail(TS_EINVAL, "fp8 GEMM needs both scales");
+  if (dtype != TS_F32 && !gemm_offsets_fit(m, n, k, dtype == TS_BF16 ? 2 : 1))
+    return fail(TS_ESHAPE, "GEMM operand larger than 4 GiB");
   if (dtype != TS_F32 && dtype != TS_BF16 && dtype != TS_FP8E4M3) return fail(TS_EDTYPE, "bad dtype");
   hipStream_t s = (hipStream_t)stream;
   const int ab = act_bytes(dtype);

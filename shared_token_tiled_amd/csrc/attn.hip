@@ -9,16 +9,18 @@
 // Output rows are written in per-tile layout: row t*(n+1)+i for window token
 // i (i = n is the global token).
 //
-// bf16 kernel (gfx950 MFMA 32x32x16): a workgroup of four wavefronts owns 128
-// query rows of one (tile, head); each wavefront owns 32.  Scores are formed
-// transposed, S^T = K Q^T, so each lane holds one query's scores and the
-// softmax max/sum stay in-lane (plus one exchange with the lane 32 apart);
-// the output is accumulated transposed, O^T = V^T P^T, so the per-query
-// rescale is in-lane too.  K rows are fed to the MFMA in an order that swaps
-// bits 2 and 3 of the row index, which makes the score accumulator layout
-// equal the P^T operand layout of the second MFMA (no shuffles).  K is staged
-// as [key][hd] and V transposed as [hd][key], both with XOR-swizzled 16-byte
-// chunks, double buffered; the RoPE table sits in LDS.
+// bf16 kernel (gfx950 MFMA 32x32x16): a workgroup of eight wavefronts owns
+// 256 query rows of one (tile, head), 32 per wavefront, and stages each block
+// of 64 keys once for all of them.  Scores are formed transposed, S^T = K Q^T,
+// so each lane holds one query's scores and the softmax max/sum stay in-lane
+// (plus one exchange with the lane 32 apart); the output is accumulated
+// transposed, O^T = V^T P^T, so the per-query rescale is in-lane too.  K rows
+// are fed to the MFMA in an order that swaps bits 2 and 3 of the row index,
+// which makes the score accumulator layout equal the P^T operand layout of
+// the second MFMA (no shuffles).  K is staged as [key][hd] (rotated) and V
+// transposed as [hd][key], both with XOR-swizzled 16-byte chunks, double
+// buffered; row indices and positions of the keys are prefetched two blocks
+// ahead into an LDS ring, and the RoPE table sits in LDS.
 #include <cstdlib>
 
 #include "device_common.h"
@@ -123,10 +125,9 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnP p) {
         const int kpos = p.local_pos[j];
         for (int k = 0; k < HD / 2; ++k) {
           const float2 cs = rope_cs(p, p.rope, k, kpos);
-          const float c = cs.x, s = cs.y;
           const float a = kp[2 * k], b = kp[2 * k + 1];
-          Ks[threadIdx.x][2 * k] = a * c - b * s;
-          Ks[threadIdx.x][2 * k + 1] = a * s + b * c;
+          Ks[threadIdx.x][2 * k] = a * cs.x - b * cs.y;
+          Ks[threadIdx.x][2 * k + 1] = a * cs.y + b * cs.x;
         }
         for (int e = 0; e < HD; ++e) Vs[threadIdx.x][e] = vp[e];
       }
@@ -154,56 +155,75 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnP p) {
 }
 
 // ------------------------------------------------------------- bf16 -----
+constexpr int NW = 8;              // wavefronts per workgroup
+constexpr int QB = 32 * NW;        // query rows per workgroup
 constexpr int KB = 64;             // keys per staged block
-// RoPE table floats kept in LDS: 14.75 KB at head_dim 128 (so two workgroups of
-// 80 KB fit in a CU's 160 KB), 16 KB otherwise
-template <int HD> constexpr int rope_lds_floats() { return HD == 128 ? 3776 : 4096; }
+constexpr int ROPE_LDS_FLOATS = 4096;  // 16 KB
 constexpr float RESCALE_LOG2 = 8.0f;   // keep a stale running max until a block exceeds it by 2^8
 
 // Swap bits 2 and 3 of a row index in 0..31.
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// LDS swizzles (16-byte chunk c of row r is stored at chunk c ^ key(r)).
-// Keys: bits 0, 1 and 3 of the key row, so the eight rows one MFMA read
-// phase touches (rows swap23(0..7) = 0-3, 8-11) get eight different keys;
-// for V^T rows, hd ^ (hd >> 3), distinct both for eight consecutive hd rows
-// (fragment reads) and for eight hd rows 8 apart (transposing writes).
-__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+// LDS swizzles (16-byte chunk c of row r is stored at chunk c ^ key(r)).  The
+// LDS has 64 banks of 4 bytes; a 16-byte access is served 16 lanes at a time,
+// so the 16 lanes of one phase must hit 16 different 16-byte bank groups.
+// K rows (HD*2 bytes): the 16 rows one MFMA read phase touches (swap23(0..15)
+// = 0..15) get 16 different keys (head size 128: row & 15; head size 64,
+// 128-byte rows where row parity already selects the half: (row >> 1) & 7).
+// V^T rows (128 bytes): hd ^ (hd >> 3), distinct over the even and over the
+// odd rows of 16 consecutive hd rows (fragment reads) and over hd rows 8 apart
+// (transposing writes).
+template <int HD> __device__ __forceinline__ int kswz(int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); }
 __device__ __forceinline__ int vswz(int hd) { return (hd ^ (hd >> 3)) & 7; }
 
-// Rotate 4 pairs (8 bf16) by the tile-local position `pos` (packed tau|y<<10|x<<20),
-// pairs 4*c .. 4*c+3 of the head, with their descriptors from desc_s.
-__device__ __forceinline__ bf16x8 rope8(const float* rope_s, const int* desc_s, int c, int pos, bf16x8 v) {
-  const i32x4 dsc = *reinterpret_cast<const i32x4*>(desc_s + 4 * c);
+// Table lookup of one 8-dim group (4 rotation pairs of one axis): offset of
+// position 0 in floats, floats per position step, and the axis' bit shift in
+// the packed position.  With every axis holding a multiple of 4 pairs the
+// group's four (cos, sin) pairs are 32 contiguous, 32-byte aligned bytes.
+struct GroupRope {
+  int off, step, shift;
+};
+__device__ __forceinline__ GroupRope group_rope(const AttnP& p, int c) {
+  const int k = 4 * c;
+  const int p0 = p.pairs[0], p01 = p.pairs[0] + p.pairs[1];
+  const int ax = k < p0 ? 0 : (k < p01 ? 1 : 2);
+  const int i = k - (ax == 0 ? 0 : (ax == 1 ? p0 : p01));
+  const int np = ax == 0 ? p.pairs[0] : (ax == 1 ? p.pairs[1] : p.pairs[2]);
+  const int off = ax == 0 ? p.rope_off[0] : (ax == 1 ? p.rope_off[1] : p.rope_off[2]);
+  return GroupRope{off + 2 * i, 2 * np, 10 * ax};
+}
+
+// Rotate one 8-dim group (4 pairs, bf16) by position `pos`.
+__device__ __forceinline__ bf16x8 rope_group(const float* rope_s, GroupRope gr, int pos, bf16x8 v) {
+  const float* cs = rope_s + gr.off + ((pos >> gr.shift) & 1023) * gr.step;
+  const f32x4 c01 = *reinterpret_cast<const f32x4*>(cs);      // (cos, sin) of pairs 0, 1
+  const f32x4 c23 = *reinterpret_cast<const f32x4*>(cs + 4);  // pairs 2, 3
   bf16x8 o;
 #pragma unroll
   for (int q2 = 0; q2 < 4; ++q2) {
-    const float2 cs = rope_at(rope_s, dsc[q2], pos);
+    const float c = q2 < 2 ? c01[2 * q2] : c23[2 * q2 - 4];
+    const float s = q2 < 2 ? c01[2 * q2 + 1] : c23[2 * q2 - 3];
     const float a = float(v[2 * q2]), b = float(v[2 * q2 + 1]);
-    o[2 * q2] = bf16(a * cs.x - b * cs.y);
-    o[2 * q2 + 1] = bf16(a * cs.y + b * cs.x);
+    o[2 * q2] = bf16(a * c - b * s);
+    o[2 * q2 + 1] = bf16(a * s + b * c);
   }
   return o;
 }
 
-// Window attention for the tile tokens (query rows 0..n-1); the global
-// token's own query row is done by k_attn_global_bf16.
-// NQ 32-row query blocks per wavefront, four wavefronts per workgroup.
-template <int HD, int NQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 ? 2 : 1, NQ == 1 ? 2 : 1))) void k_attn_bf16(AttnP p) {
-  constexpr int QW = 32 * NQ;         // query rows per wavefront
-  constexpr int QB = 4 * QW;          // query rows per workgroup
+template <int HD>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(AttnP p) {
+  constexpr int NT = NW * 64;         // threads
   constexpr int HC = HD / 8;          // 16-byte chunks per head row
   constexpr int KROWB = HD * 2;       // bytes per staged key row
-  constexpr int KCPT = HC / 4;        // key chunks per thread (4 threads per key row)
-  constexpr int VSB = KB / 4 * HC;    // V sub-blocks (4 keys x 8 hd), one per thread
+  constexpr int KCPT = HC / 8;        // key chunks per thread (8 threads per key row)
+  constexpr int VSB = KB / 2 * HC;    // V transpose units (2 keys x 8 hd)
   constexpr int NHB = HD / 32;        // 32-row hd blocks of O^T
   constexpr int KSTEPS = HD / 16;     // MFMA k-steps of S^T
+  static_assert(VSB <= NT, "one V unit per thread");
   __shared__ __attribute__((aligned(16))) char Ks[2][KB * KROWB];
   __shared__ __attribute__((aligned(16))) char Vt[2][HD * KB * 2];
-  __shared__ __attribute__((aligned(16))) float rope_s[rope_lds_floats<HD>()];
+  __shared__ __attribute__((aligned(16))) float rope_s[ROPE_LDS_FLOATS];
   __shared__ int idx_s[2][2][KB];     // [slot][row | pos][key]
-  __shared__ __attribute__((aligned(16))) int desc_s[HD / 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -224,11 +244,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 ? 2
   }
   const bf16* qkv = (const bf16*)p.qkv;
   const int64_t ld = 3 * int64_t(p.d);
-  const int kcol = p.d + h * HD, vcol = 2 * p.d + h * HD;
+  const bf16* kbase = qkv + p.d + h * HD;
+  const bf16* vbase = qkv + 2 * p.d + h * HD;
   const int nkb = (n + KB - 1) / KB;
 
-  for (int e = tid; e < p.rope_floats; e += 256) rope_s[e] = p.rope[e];
-  if (tid < HD / 2) desc_s[tid] = rope_desc(p, tid);
+  for (int e = tid; e < p.rope_floats; e += NT) rope_s[e] = p.rope[e];
   // row index and position of key j (clamped into the window)
   auto key_meta = [&](int j, int& row, int& pos) {
     j = min(j, n - 1);
@@ -245,24 +265,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 ? 2
     idx_s[1][1][tid] = p1;
   }
 
-  // staging roles.  K: row kr_row, chunks kpart + 4*i; a wavefront's 64
-  // lanes cover 16 rows, the 8 lanes of one LDS write phase rows m and m+8.
-  // V: keys 4*v_k4 .. +3 of hd chunk v_hc, neighbouring lanes alternating
-  // between two key groups so one 8-byte write phase hits 16 distinct slots.
-  const int kr_row = 16 * wave + (((lane >> 2) & 1) << 3) + (lane >> 3), kpart = lane & 3;
+  // staging roles.  K: row kr_row, chunks kpart + 8*i, 8 threads per row; a
+  // 16-lane write phase covers two rows, chosen 8 apart at head size 128 (so
+  // their keys differ in bit 3) and adjacent at 64 (so their parity differs).
+  // V: keys 2*v_k2, 2*v_k2+1 of hd chunk v_hc (one 4-byte write phase hits
+  // 32 banks twice: a 2-way conflict on 8 small writes per block, cheaper than
+  // the per-lane row reordering that would avoid it).
+  const int lg = lane >> 3;
+  const int kr_row = HD == 128 ? (wave >> 1) * 16 + (wave & 1) * 4 + (lg >> 1) + (lg & 1) * 8 : tid >> 3;
+  const int kpart = tid & 7;
+  GroupRope kgr[KCPT];
+#pragma unroll
+  for (int i = 0; i < KCPT; ++i) kgr[i] = group_rope(p, kpart + 8 * i);
   const bool v_on = tid < VSB;
-  const int v_hc = (tid >> 1) % HC, v_k4 = (tid & 1) + 2 * (tid / (2 * HC));
-  i32x4 kreg[KCPT], vreg[4];
+  const int v_hc = (tid & 7) + 8 * (tid / 256), v_k2 = (tid >> 3) & 31;
+  i32x4 kreg[KCPT], vreg[2];
   auto gload = [&](int slot) {
     const int r = idx_s[slot][0][kr_row];
 #pragma unroll
     for (int i = 0; i < KCPT; ++i)
-      kreg[i] = *reinterpret_cast<const i32x4*>(qkv + r * ld + kcol + (kpart + 4 * i) * 8);
+      kreg[i] = *reinterpret_cast<const i32x4*>(kbase + r * ld + (kpart + 8 * i) * 8);
     if (v_on) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rv = idx_s[slot][0][4 * v_k4 + e];
-        vreg[e] = *reinterpret_cast<const i32x4*>(qkv + rv * ld + vcol + v_hc * 8);
+      for (int e = 0; e < 2; ++e) {
+        const int rv = idx_s[slot][0][2 * v_k2 + e];
+        vreg[e] = *reinterpret_cast<const i32x4*>(vbase + rv * ld + v_hc * 8);
       }
     }
   };
@@ -270,19 +297,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 ? 2
     const int pos = idx_s[slot][1][kr_row];
 #pragma unroll
     for (int i = 0; i < KCPT; ++i) {
-      const int c = kpart + 4 * i;
-      const bf16x8 o = rope8(rope_s, desc_s, c, pos, __builtin_bit_cast(bf16x8, kreg[i]));
-      *reinterpret_cast<bf16x8*>(&Ks[st][kr_row * KROWB + ((c ^ kswz(kr_row)) * 16)]) = o;
+      const int c = kpart + 8 * i;
+      const bf16x8 o = rope_group(rope_s, kgr[i], pos, __builtin_bit_cast(bf16x8, kreg[i]));
+      *reinterpret_cast<bf16x8*>(&Ks[st][kr_row * KROWB + ((c ^ kswz<HD>(kr_row)) * 16)]) = o;
     }
     if (v_on) {
       const bf16x8 v0 = __builtin_bit_cast(bf16x8, vreg[0]), v1 = __builtin_bit_cast(bf16x8, vreg[1]);
-      const bf16x8 v2 = __builtin_bit_cast(bf16x8, vreg[2]), v3 = __builtin_bit_cast(bf16x8, vreg[3]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int hdr = v_hc * 8 + e;
-        const bf16x4 w = {v0[e], v1[e], v2[e], v3[e]};
-        const int chunk = (v_k4 >> 1) ^ vswz(hdr);
-        *reinterpret_cast<bf16x4*>(&Vt[st][hdr * (KB * 2) + chunk * 16 + (v_k4 & 1) * 8]) = w;
+        const bf16 w2[2] = {v0[e], v1[e]};
+        const int chunk = (v_k2 >> 2) ^ vswz(hdr);
+        *reinterpret_cast<uint32_t*>(&Vt[st][hdr * (KB * 2) + chunk * 16 + (v_k2 & 3) * 4]) =
+            __builtin_bit_cast(uint32_t, w2);
       }
     }
   };
@@ -290,38 +317,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 ? 2
   __syncthreads();  // rope_s, idx_s ready
   gload(0);
 
-  // ---- this wavefront's 64 queries: B operand of S^T = K Q^T (hd 16s + 8g + e)
-  const int q0 = qblk * QB + wave * QW + l32;
+  // ---- this wavefront's 32 queries: B operand of S^T = K Q^T (hd 16s + 8g + e)
+  const int qi = qblk * QB + wave * 32 + l32;
   const int grow = window_row(p, t, n);
-  const bf16* kgp = qkv + grow * ld + kcol;
-  const bf16* vgp = qkv + grow * ld + vcol;
+  const bf16* kgp = kbase + grow * ld;
+  const bf16* vgp = vbase + grow * ld;
   const float C = p.scale_log2;
-  bf16x8 qf[NQ][KSTEPS];
-  float m_run[NQ], l_run[NQ];
-  f32x16 oacc[NQ][NHB];
-#pragma unroll
-  for (int qq = 0; qq < NQ; ++qq) {
-    const int qi = min(q0 + 32 * qq, n - 1);
-    const bf16* qp = qkv + window_row(p, t, qi) * ld + h * HD;
-    const int qpos = p.local_pos[qi];
+  bf16x8 qf[KSTEPS];
+  float m_run, l_run;
+  f32x16 oacc[NHB];
+  {
+    const int qc = min(qi, n - 1);
+    const bf16* qp = qkv + window_row(p, t, qc) * ld + h * HD;
+    const int qpos = p.local_pos[qc];
     float sg = 0.f;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       const int hd0 = 16 * s + 8 * g;
-      const bf16x8 r = rope8(rope_s, desc_s, hd0 / 8, qpos, *reinterpret_cast<const bf16x8*>(qp + hd0));
+      const bf16x8 r = rope_group(rope_s, group_rope(p, hd0 / 8), qpos, *reinterpret_cast<const bf16x8*>(qp + hd0));
       const bf16x8 kg = *reinterpret_cast<const bf16x8*>(kgp + hd0);
-      qf[qq][s] = r;
+      qf[s] = r;
 #pragma unroll
       for (int e = 0; e < 8; ++e) sg += float(r[e]) * float(kg[e]);
     }
     sg += __shfl_xor(sg, 32, 64);
     // online softmax state starts from the global key: score sg, weight 1, value v_g
-    m_run[qq] = sg * C;
-    l_run[qq] = g == 0 ? 1.f : 0.f;
+    m_run = sg * C;
+    l_run = g == 0 ? 1.f : 0.f;
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[qq][hb][r] = float(vgp[hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)]);
+      for (int r = 0; r < 16; ++r) oacc[hb][r] = float(vgp[hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)]);
   }
 
   lstore(0, 0);
@@ -335,79 +361,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 ? 2
     if (pre) key_meta((kb + 2) * KB + tid, pre_r, pre_p);
     const char* ks = Ks[cur];
     const char* vt = Vt[cur];
-
     const int j0 = kb * KB;
-    // ---- S^T = K Q^T for the 64 keys: two 32-key chains per query block.
-    // K fragments are read ahead of the MFMAs that use them (the schedule
-    // below keeps four LDS reads in flight).
-    f32x16 sacc[NQ][2];
+
+    // ---- S^T = K Q^T for the 64 keys: two 32-key chains, K fragments read
+    // ahead of the MFMAs that use them (four LDS reads kept in flight)
+    f32x16 sacc[2];
 #pragma unroll
-    for (int qq = 0; qq < NQ; ++qq)
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qq][sb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.f;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         const int kr = sb * 32 + krow_a;
         const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(ks + kr * KROWB + (((2 * s + g) ^ kswz(kr)) * 16));
-#pragma unroll
-        for (int qq = 0; qq < NQ; ++qq)
-          sacc[qq][sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qq][s], sacc[qq][sb], 0, 0, 0);
+            *reinterpret_cast<const bf16x8*>(ks + kr * KROWB + (((2 * s + g) ^ kswz<HD>(kr)) * 16));
+        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sb], 0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
 #pragma unroll
     for (int i = 0; i < 2 * KSTEPS - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NQ, 0);  // MFMA(s) of one fragment
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NQ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     if (j0 + KB > n) {  // keys past the window end (last block only)
 #pragma unroll
-      for (int qq = 0; qq < NQ; ++qq)
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // accumulator row 8(r/4)+4g+(r%4) holds key swap23(that row)
-            const int key = j0 + sb * 32 + swap23(8 * (r >> 2) + 4 * g + (r & 3));
-            if (key >= n) sacc[qq][sb][r] = -INFINITY;
-          }
+        for (int r = 0; r < 16; ++r) {
+          // accumulator row 8(r/4)+4g+(r%4) holds key swap23(that row)
+          const int key = j0 + sb * 32 + swap23(8 * (r >> 2) + 4 * g + (r & 3));
+          if (key >= n) sacc[sb][r] = -INFINITY;
+        }
     }
     // ---- online softmax over the block (one rescale check per block)
-    bf16x8 pf[NQ][4];
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) {
+    bf16x8 pf[4];
+    {
       float mx = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qq][sb][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * C;
       // rescale only when some query's block max passes its running max by 2^8
-      if (__builtin_amdgcn_ballot_w64(mx > m_run[qq] + RESCALE_LOG2) != 0) {
-        const float m_new = fmaxf(m_run[qq], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qq] - m_new);
-        m_run[qq] = m_new;
-        l_run[qq] *= alpha;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_LOG2) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) oacc[qq][hb] *= alpha;
+        for (int hb = 0; hb < NHB; ++hb) oacc[hb] *= alpha;
       }
-      const float mneg = -m_run[qq];
+      const float mneg = -m_run;
       float lsum = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[qq][sb][r], C, mneg));
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[sb][r], C, mneg));
           lsum += pv;
-          pf[qq][sb * 2 + (r >> 3)][r & 7] = bf16(pv);
+          pf[sb * 2 + (r >> 3)][r & 7] = bf16(pv);
         }
-      l_run[qq] += lsum;
+      l_run += lsum;
     }
     // ---- O^T += V^T P^T over four 16-key chunks (NHB independent chains)
 #pragma unroll
@@ -417,18 +435,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 ? 2
         const int hdr = hb * 32 + l32;
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
             vt + hdr * (KB * 2) + (((2 * cc + g) ^ vswz(hdr)) * 16));
-#pragma unroll
-        for (int qq = 0; qq < NQ; ++qq)
-          oacc[qq][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qq][cc], oacc[qq][hb], 0, 0, 0);
+        oacc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], oacc[hb], 0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 4 * NHB - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NQ, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NQ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
     if (kb + 1 < nkb) lstore((kb + 1) & 1, cur ^ 1);
     if (pre) {
       idx_s[cur][0][tid] = pre_r;
@@ -437,22 +454,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 ? 2
     __syncthreads();
   }
 
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (qi >= n) return;
+  const float inv = 1.0f / l_tot;
+  bf16* out = (bf16*)p.out + (int64_t(t) * (n + 1) + qi) * p.d + h * HD;
 #pragma unroll
-  for (int qq = 0; qq < NQ; ++qq) {
-    const int qi = q0 + 32 * qq;
-    const float l_tot = l_run[qq] + __shfl_xor(l_run[qq], 32, 64);
-    if (qi >= n) continue;
-    const float inv = 1.0f / l_tot;
-    bf16* out = (bf16*)p.out + (int64_t(t) * (n + 1) + qi) * p.d + h * HD;
+  for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const bf16x4 w = {bf16(oacc[qq][hb][4 * r4] * inv), bf16(oacc[qq][hb][4 * r4 + 1] * inv),
-                          bf16(oacc[qq][hb][4 * r4 + 2] * inv), bf16(oacc[qq][hb][4 * r4 + 3] * inv)};
-        *reinterpret_cast<bf16x4*>(out + hb * 32 + 8 * r4 + 4 * g) = w;
-      }
-  }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const bf16x4 w = {bf16(oacc[hb][4 * r4] * inv), bf16(oacc[hb][4 * r4 + 1] * inv),
+                        bf16(oacc[hb][4 * r4 + 2] * inv), bf16(oacc[hb][4 * r4 + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(out + hb * 32 + 8 * r4 + 4 * g) = w;
+    }
 }
 
 // The global token's query row of every (tile, head): one workgroup per
@@ -522,16 +535,6 @@ __global__ __launch_bounds__(256) void k_attn_global_bf16(AttnP p) {
   }
 }
 
-// Query rows per wavefront of the bf16 kernel: 32 (two workgroups per CU) or
-// 64 (one); TS_ATTN_ROWS_PER_WAVE overrides the default for measurements.
-int attn_rows_per_wave() {
-  static int v = [] {
-    const char* e = getenv("TS_ATTN_ROWS_PER_WAVE");
-    return (e && atoi(e) == 64) ? 64 : 32;
-  }();
-  return v;
-}
-
 }  // namespace
 
 namespace tsk {
@@ -544,21 +547,18 @@ hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
     const dim3 grid((a.n + 1 + 63) / 64, a.H, a.n_tiles), block(64);
     if (a.hd == 32) hipLaunchKernelGGL(k_attn_f32<32>, grid, block, 0, s, p);
     else if (a.hd == 64) hipLaunchKernelGGL(k_attn_f32<64>, grid, block, 0, s, p);
-    else hipLaunchKernelGGL(k_attn_f32<128>, grid, block, 0, s, p);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
   }
   if (a.n < 1) return hipErrorInvalidValue;
-  const int nq = attn_rows_per_wave() / 32;
-  const dim3 grid(((a.n + 128 * nq - 1) / (128 * nq)) * a.H * a.n_tiles), block(256);
-  const dim3 ggrid(a.H, a.n_tiles);
+  const dim3 grid(((a.n + QB - 1) / QB) * a.H * a.n_tiles), block(NW * 64);
+  const dim3 ggrid(a.H, a.n_tiles), gblock(256);
   if (a.hd == 64) {
-    if (nq == 1) hipLaunchKernelGGL((k_attn_bf16<64, 1>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_attn_bf16<64, 2>), grid, block, 0, s, p);
-    hipLaunchKernelGGL(k_attn_global_bf16<64>, ggrid, block, 0, s, p);
+    hipLaunchKernelGGL(k_attn_bf16<64>, grid, block, 0, s, p);
+    hipLaunchKernelGGL(k_attn_global_bf16<64>, ggrid, gblock, 0, s, p);
   } else if (a.hd == 128) {
-    if (nq == 1) hipLaunchKernelGGL((k_attn_bf16<128, 1>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_attn_bf16<128, 2>), grid, block, 0, s, p);
-    hipLaunchKernelGGL(k_attn_global_bf16<128>, ggrid, block, 0, s, p);
+    hipLaunchKernelGGL(k_attn_bf16<128>, grid, block, 0, s, p);
+    hipLaunchKernelGGL(k_attn_global_bf16<128>, ggrid, gblock, 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }

@@ -3,16 +3,22 @@
 // per token in shared layers).  C[M,N] = A[M,K] B[N,K]^T with fused epilogues
 // (bias, exact GELU, fp32 residual add).
 //
-// bf16 / fp8: MFMA kernels for gfx950.  256x256 output tile per workgroup of
-// four wavefronts (2x2, 128x128 each, 4x4 MFMA 32x32 blocks), K staged through
-// LDS in two buffers with 16-byte chunks XOR-swizzled by row so that both the
-// row-wise global loads and the MFMA fragment reads are conflict free.  Tile
-// ids are remapped so that the workgroups each XCD receives (the hardware
-// deals workgroup b to XCD b % 8) form a compact group of output tiles that
-// share A and B panels in that XCD's L2.  The epilogue goes through LDS so
-// every lane writes 16 contiguous output bytes.
+// bf16 / fp8: MFMA kernels for gfx950.  A workgroup computes a 256x256 output
+// tile; its wavefronts form a 2 x WN grid (WN = 2: four wavefronts of 128x128,
+// one per SIMD; WN = 4: eight of 128x64, two per SIMD so one can issue MFMAs
+// while the other waits).  K is staged through LDS in two 64 KB buffers
+// (128-byte rows: 64 bf16 or 128 fp8 per row) filled straight from global
+// memory (global_load_lds, no staging registers) one K block ahead; 16-byte
+// chunks are XOR-swizzled by row so both the loads and the MFMA fragment reads
+// are free of bank conflicts; fragments of the next k-step are read while the
+// current one's MFMAs run.  Tile ids are remapped so that the workgroups each
+// XCD receives (the hardware deals workgroup b to XCD b % 8) form a compact
+// group of output tiles that share A and B panels in that XCD's L2.  The
+// epilogue goes through LDS so every lane writes 16 contiguous output bytes.
 //
 // fp32: a plain LDS-tiled FMA kernel, used by the fp32 configuration.
+#include <cstdlib>
+
 #include "device_common.h"
 #include "ts_kernels.h"
 
@@ -97,7 +103,6 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmP p) {
 constexpr int BM = 256, BN = 256;
 constexpr int ROWB = 128;  // bytes per staged row: 64 bf16 or 128 fp8
 constexpr int STAGE = (BM + BN) * ROWB;
-constexpr int EPI_LD = 136;  // fp32 row stride of the epilogue staging buffer
 
 __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int nblk = tiles_m * tiles_n;
@@ -114,124 +119,179 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_grp / gsize;
 }
 
-// FP8: e4m3 operands, 32x32x64 MFMA with unit block scales (E8M0 127 = 2^0).
-template <bool FP8>
-__device__ __forceinline__ void mfma_step(const char* sA, const char* sB, int s, int wm, int wn,
-                                          int lane, f32x16 (&acc)[4][4]) {
+// LDS swizzle: 16-byte chunk c of staged row r sits at chunk c ^ swz(r).  The
+// LDS has 64 banks of 4 bytes and serves a 16-byte access 16 lanes at a time;
+// with 128-byte rows a phase's 16 rows split by parity into the two 128-byte
+// halves of the banks, and (r >> 1) & 7 gives the 8 rows of each parity 8
+// different chunks (fragment reads of rows 0..15, writes of rows r, r+1).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// Register fragments of one MFMA k-step for a wavefront's 128 x (32*NB)
+// sub-tile: 4 A and NB B fragments (bf16: 8 values = 16 bytes; fp8: 32
+// values = 32 bytes, two 16-byte chunks).  Any assignment of k to (lane
+// group, element) works as long as A and B use the same one.
+template <bool FP8, int NB> struct Frags;
+template <int NB> struct Frags<false, NB> { bf16x8 a[4], b[NB]; };
+template <int NB> struct Frags<true, NB> { i32x8 a[4], b[NB]; };
+
+template <bool FP8, int NB>
+__device__ __forceinline__ void load_frags(Frags<FP8, NB>& f, const char* sA, const char* sB, int s, int arow,
+                                           int brow, int lane) {
   const int l32 = lane & 31, g = lane >> 5;
-  if (!FP8) {
+  if constexpr (!FP8) {
     // k-step s covers bf16 columns 16s..16s+15: logical chunk 2s + g
-    bf16x8 af[4], bfr[4];
-    const int pc = ((2 * s + g) ^ (lane & 7)) * 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      af[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 128 + i * 32 + l32) * ROWB + pc);
-      bfr[i] = *reinterpret_cast<const bf16x8*>(sB + (wn * 128 + i * 32 + l32) * ROWB + pc);
-    }
+    const int pc = ((2 * s + g) ^ swz(l32)) * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
+      f.a[i] = *reinterpret_cast<const bf16x8*>(sA + (arow + i * 32 + l32) * ROWB + pc);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < NB; ++j)
+      f.b[j] = *reinterpret_cast<const bf16x8*>(sB + (brow + j * 32 + l32) * ROWB + pc);
   } else {
     // k-step s covers fp8 columns 64s..64s+63: logical chunks 4s+g and 4s+2+g
-    i32x8 af[4], bfr[4];
-    const int pc0 = ((4 * s + g) ^ (lane & 7)) * 16;
-    const int pc1 = ((4 * s + 2 + g) ^ (lane & 7)) * 16;
+    const int pc0 = ((4 * s + g) ^ swz(l32)) * 16;
+    const int pc1 = ((4 * s + 2 + g) ^ swz(l32)) * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const char* ra = sA + (wm * 128 + i * 32 + l32) * ROWB;
-      const char* rb = sB + (wn * 128 + i * 32 + l32) * ROWB;
+      const char* ra = sA + (arow + i * 32 + l32) * ROWB;
       const i32x4 a0 = *reinterpret_cast<const i32x4*>(ra + pc0);
       const i32x4 a1 = *reinterpret_cast<const i32x4*>(ra + pc1);
-      const i32x4 b0 = *reinterpret_cast<const i32x4*>(rb + pc0);
-      const i32x4 b1 = *reinterpret_cast<const i32x4*>(rb + pc1);
-      af[i] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      bfr[i] = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      f.a[i] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j], 0, 0,
-                                                                    0, 127, 0, 127);
+    for (int j = 0; j < NB; ++j) {
+      const char* rb = sB + (brow + j * 32 + l32) * ROWB;
+      const i32x4 b0 = *reinterpret_cast<const i32x4*>(rb + pc0);
+      const i32x4 b1 = *reinterpret_cast<const i32x4*>(rb + pc1);
+      f.b[j] = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    }
   }
 }
 
-template <int EPI, bool FP8>
-__global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmP p) {
+// FP8: e4m3 operands, 32x32x64 MFMA with unit block scales (E8M0 127 = 2^0).
+template <bool FP8, int NB>
+__device__ __forceinline__ void mfma_frags(const Frags<FP8, NB>& f, f32x16 (&acc)[4][NB]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if constexpr (!FP8)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0,
+                                                                    127, 0, 127);
+    }
+}
+
+// Scheduling hint for one k-step: MFMAS MFMAs with READS LDS reads spread
+// evenly between them (instruction groups in this order).
+template <int MFMAS, int READS, int I = 0>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (I < MFMAS) {
+    constexpr int PER = (READS + MFMAS - 1) / MFMAS;
+    constexpr int K = (I + 1) * PER <= READS ? PER : (I * PER < READS ? READS - I * PER : 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (K > 0) __builtin_amdgcn_sched_group_barrier(0x100, K, 0);
+    sched_interleave<MFMAS, READS, I + 1>();
+  }
+}
+
+template <int EPI, bool FP8, int WN>
+__global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
+  constexpr int NW = 2 * WN;                 // wavefronts: 2 (M) x WN (N)
+  constexpr int NB = 8 / WN;                 // 32-column MFMA blocks per wavefront
+  constexpr int WCOLS = 32 * NB;             // output columns per wavefront
+  constexpr int LPO = 32 / NW;               // global_load_lds per operand per wavefront
+  constexpr int STEPS = FP8 ? 2 : 4;         // MFMA k-steps per staged K block
+  constexpr int READS = (4 + NB) * (FP8 ? 2 : 1);  // LDS reads per k-step
+  constexpr int MFMAS = 4 * NB;              // MFMAs per k-step
+  constexpr int EPI_LD = WCOLS + 8;          // fp32 row stride of the epilogue staging
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
+  const int arow = wm * 128, brow = wn * WCOLS;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int ESZ = FP8 ? 1 : 2;                 // element bytes
-  const int64_t ldab = int64_t(p.K) * ESZ;     // row pitch of A and B in bytes
+  const int ESZ = FP8 ? 1 : 2;               // element bytes
+  const uint32_t ldab = uint32_t(p.K) * ESZ; // row pitch of A and B in bytes
   const char* A = (const char*)p.A;
   const char* B = (const char*)p.B;
 
-  // Global -> LDS: chunk tid + 256*i is row (tid>>3) + 32*i, 16-byte chunk tid&7.
-  const int lrow = tid >> 3, lkc = tid & 7;
-  const int lds_off = lrow * ROWB + ((lkc ^ (lrow & 7)) * 16);
-  int64_t offA[8], offB[8];
+  // Global -> LDS without registers (global_load_lds_dwordx4: lane l of a
+  // wavefront instruction writes 16 bytes at LDS base + 16*l).  Instruction i
+  // of wavefront w fills staged rows 8*(NW*i+w) .. +7 (1 KB); lane l covers row
+  // 8*(NW*i+w) + (l>>3), LDS slot l&7, and so loads the logical chunk that the
+  // swizzle puts in that slot, (l&7) ^ swz(row) (the same for every i).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int lrow = 8 * wv + (lane >> 3);
+  const int lchunk = (lane & 7) ^ swz(lrow);
+  uint32_t offA[LPO], offB[LPO];  // byte offsets (the host checks they fit)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    offA[i] = int64_t(min(m0 + lrow + 32 * i, p.M - 1)) * ldab + lkc * 16;
-    offB[i] = int64_t(min(n0 + lrow + 32 * i, p.N - 1)) * ldab + lkc * 16;
+  for (int i = 0; i < LPO; ++i) {
+    offA[i] = uint32_t(min(m0 + lrow + 8 * NW * i, p.M - 1)) * ldab + lchunk * 16;
+    offB[i] = uint32_t(min(n0 + lrow + 8 * NW * i, p.N - 1)) * ldab + lchunk * 16;
   }
-  i32x4 ra[8], rb[8];
-  auto gload = [&](int kt) {
-    const int64_t kb = int64_t(kt) * ROWB;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[i] = *reinterpret_cast<const i32x4*>(A + offA[i] + kb);
-      rb[i] = *reinterpret_cast<const i32x4*>(B + offB[i] + kb);
-    }
-  };
-  auto lstore = [&](int st) {
+  auto gload = [&](int kt, int st) {
+    const uint32_t kb = uint32_t(kt) * ROWB;
     char* sA = smem + st * STAGE;
     char* sB = sA + BM * ROWB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<i32x4*>(sA + lds_off + i * 32 * ROWB) = ra[i];
-      *reinterpret_cast<i32x4*>(sB + lds_off + i * 32 * ROWB) = rb[i];
+    for (int i = 0; i < LPO; ++i) {
+      __builtin_amdgcn_global_load_lds((const void*)(A + offA[i] + kb),
+                                       (TS_LDS void*)(sA + (NW * i + wv) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(B + offB[i] + kb),
+                                       (TS_LDS void*)(sB + (NW * i + wv) * 1024), 16, 0, 0);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int KT = p.K * ESZ / ROWB;
-  gload(0);
-  lstore(0);
+  gload(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+    // the other stage was last read in the previous iteration, before its barrier
+    if (kt + 1 < KT) gload(kt + 1, cur ^ 1);
     const char* sA = smem + cur * STAGE;
     const char* sB = sA + BM * ROWB;
-    constexpr int STEPS = FP8 ? 2 : 4;
+    // fragments double buffered in registers: step s+1 is read while step s computes
+    Frags<FP8, NB> fr[2];
+    load_frags<FP8, NB>(fr[0], sA, sB, 0, arow, brow, lane);
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) mfma_step<FP8>(sA, sB, s, wm, wn, lane, acc);
-    if (kt + 1 < KT) lstore(cur ^ 1);
+    for (int s = 0; s < STEPS; ++s) {
+      if (s + 1 < STEPS) load_frags<FP8, NB>(fr[(s + 1) & 1], sA, sB, s + 1, arow, brow, lane);
+      mfma_frags<FP8, NB>(fr[s & 1], acc);
+    }
+    // schedule: the first step's reads, then each step's MFMAs with the next
+    // step's reads spread between them
+    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+#pragma unroll
+    for (int s = 0; s + 1 < STEPS; ++s) sched_interleave<MFMAS, READS>();
+    __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);
+    // this iteration's loads of the next stage must have landed before anyone reads it
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
-  // ---- epilogue: per 32-row block, stage 32x128 fp32 through LDS ----
+  // ---- epilogue: per 32-row block, stage 32 x WCOLS fp32 through LDS ----
   float alpha = 1.0f;
   if (FP8) alpha = (*p.sa) * (*p.sb);
   float* stg = reinterpret_cast<float*>(smem) + wave * (32 * EPI_LD);
   const int l32 = lane & 31, g = lane >> 5;
-  // read-back mapping: lane covers 4 columns c4*4.. of rows rr + 2*it
-  const int c4 = lane & 31, rsub = lane >> 5;
-  const int colb = n0 + wn * 128 + c4 * 4;
+  // read-back mapping: LPR lanes cover one row (4 columns each), RPP rows per pass
+  constexpr int LPR = WCOLS / 4, RPP = 64 / LPR;
+  const int c4 = lane % LPR, rsub = lane / LPR;
+  const int colb = n0 + brow + c4 * 4;
   f32x4 bias4 = {0.f, 0.f, 0.f, 0.f};
   if (p.bias) {
 #pragma unroll
@@ -240,15 +300,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmP p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * g + (r & 3)) * EPI_LD + j * 32 + l32] = acc[i][j][r];
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS writes of this wave done
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int rl = 2 * it + rsub;
-      const int row = m0 + wm * 128 + i * 32 + rl;
+    for (int it = 0; it < 32 / RPP; ++it) {
+      const int rl = RPP * it + rsub;
+      const int row = m0 + arow + i * 32 + rl;
       const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * EPI_LD + c4 * 4);
       if (row < p.M && colb < p.N) {
         f32x4 o;
@@ -270,6 +329,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmP p) {
   }
 }
 
+// Wavefronts along N of the MFMA kernel: 2 (four wavefronts, 128x128 each) or
+// 4 (eight wavefronts, 128x64 each, two per SIMD; the default).
+// TS_GEMM_WAVES_N overrides it for measurements.
+int gemm_waves_n() {
+  static int v = [] {
+    const char* e = getenv("TS_GEMM_WAVES_N");
+    return (e && atoi(e) == 2) ? 2 : 4;
+  }();
+  return v;
+}
+
 }  // namespace
 
 namespace tsk {
@@ -288,22 +358,19 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
     }
     return hipGetLastError();
   }
-  const dim3 grid(((M + BM - 1) / BM) * ((N + BN - 1) / BN)), block(256);
-#define TS_G(E, F8) hipLaunchKernelGGL((k_gemm_mfma<E, F8>), grid, block, 0, s, p)
-  if (act == ACT_BF16) {
-    switch (epi) {
-      case EPI_BIAS: TS_G(EPI_BIAS, false); break;
-      case EPI_BIAS_GELU: TS_G(EPI_BIAS_GELU, false); break;
-      case EPI_RESID: TS_G(EPI_RESID, false); break;
-      default: TS_G(EPI_F32, false); break;
-    }
-  } else {
-    switch (epi) {
-      case EPI_BIAS: TS_G(EPI_BIAS, true); break;
-      case EPI_BIAS_GELU: TS_G(EPI_BIAS_GELU, true); break;
-      case EPI_RESID: TS_G(EPI_RESID, true); break;
-      default: TS_G(EPI_F32, true); break;
-    }
+  const int wn = gemm_waves_n();
+  const dim3 grid(((M + BM - 1) / BM) * ((N + BN - 1) / BN)), block(128 * wn);
+#define TS_G(E, F8)                                                                 \
+  do {                                                                              \
+    if (wn == 2) hipLaunchKernelGGL((k_gemm_mfma<E, F8, 2>), grid, block, 0, s, p); \
+    else hipLaunchKernelGGL((k_gemm_mfma<E, F8, 4>), grid, block, 0, s, p);         \
+  } while (0)
+  const bool f8 = act == ACT_FP8;
+  switch (epi) {
+    case EPI_BIAS: if (f8) TS_G(EPI_BIAS, true); else TS_G(EPI_BIAS, false); break;
+    case EPI_BIAS_GELU: if (f8) TS_G(EPI_BIAS_GELU, true); else TS_G(EPI_BIAS_GELU, false); break;
+    case EPI_RESID: if (f8) TS_G(EPI_RESID, true); else TS_G(EPI_RESID, false); break;
+    default: if (f8) TS_G(EPI_F32, true); else TS_G(EPI_F32, false); break;
   }
 #undef TS_G
   return hipGetLastError();
