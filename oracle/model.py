@@ -78,17 +78,24 @@ def softmax_attention(q, k, v, scale):
     return (e @ v) / e.sum(axis=-1, keepdims=True)
 
 
+def head_rms_norm(z, gain, cfg):
+    """RMSNorm over each head's hd channels of z [rows, d], with gain [hd]."""
+    hd = cfg["head_dim"]
+    z = z.copy()
+    for hh in range(cfg["n_heads"]):
+        cs = slice(hh * hd, (hh + 1) * hd)
+        z[:, cs] = rms_norm(z[:, cs], gain.astype(F), cfg.get("eps", 1e-6))
+    return z
+
+
 def qkv_heads(h, p, cfg, fp8=False):
     """QKV projection and per-head QK-RMSNorm, once per row of h."""
-    d, hd = cfg["d"], cfg["head_dim"]
+    d = cfg["d"]
     qkv = linear(h, p["w_qkv"], p["b_qkv"], fp8)
     q, k, v = qkv[:, :d].copy(), qkv[:, d:2 * d].copy(), qkv[:, 2 * d:].copy()
     if cfg["qk_norm"]:
-        eps = cfg.get("eps", 1e-6)
-        for hh in range(cfg["n_heads"]):
-            cs = slice(hh * hd, (hh + 1) * hd)
-            q[:, cs] = rms_norm(q[:, cs], p["q_g"].astype(F), eps)
-            k[:, cs] = rms_norm(k[:, cs], p["k_g"].astype(F), eps)
+        q = head_rms_norm(q, p["q_g"], cfg)
+        k = head_rms_norm(k, p["k_g"], cfg)
     return q, k, v
 
 
@@ -220,6 +227,126 @@ def tiled_forward(cfg, plan, x, g, layers, rope=None):
             Xt = per_tile_layer(Xt, p, cfg, rope)
         outs.append(Xt)
     return merge(plan, outs)
+
+
+# --- the same layers evaluated only for some output rows ------------------
+#
+# Every step of a block except attention is per row, and a row's attention
+# output depends only on its own query and on its window's keys and values.
+# So one output row of a layer needs the keys and values of every row of the
+# windows it lies in, and nothing else of the other rows.  The functions
+# below evaluate exactly that, with the same operations as the full functions
+# above, so that outputs at the full workload sizes can be checked on a
+# sample of rows.  Per-tensor fp8 scales depend on every row of each GEMM
+# operand, so these functions take the bf16 / fp32 path only.
+
+def attention_rows(q_sel, k, v, local, cos_t, sin_t, cfg):
+    """Rows ``local`` of tile_attention(q, k, v, ...), given only their queries.
+
+    q_sel [len(local), d] are the queries of window rows ``local``; k, v
+    [n+1, d] the whole window (global row last).
+    """
+    hd = cfg["head_dim"]
+    local = np.asarray(local, dtype=np.int64)
+    out = np.empty_like(q_sel)
+    scale = 1.0 / math.sqrt(hd)
+    for hh in range(cfg["n_heads"]):
+        cs = slice(hh * hd, (hh + 1) * hd)
+        qh = rope_rotate(q_sel[:, cs], cos_t[local], sin_t[local])
+        kh = rope_rotate(k[:, cs], cos_t, sin_t)
+        out[:, cs] = softmax_attention(qh, kh, v[:, cs], scale)
+    return out
+
+
+def _kv_and_q(h, q_rows, p, cfg):
+    """Keys and values of every row of h, queries of rows ``q_rows`` only."""
+    d = cfg["d"]
+    w, b = p["w_qkv"], p["b_qkv"]
+    kv = linear(h, w[d:], b[d:])
+    k, v = kv[:, :d].copy(), kv[:, d:].copy()
+    q = linear(h[q_rows], w[:d], b[:d])
+    if cfg["qk_norm"]:
+        q = head_rms_norm(q, p["q_g"], cfg)
+        k = head_rms_norm(k, p["k_g"], cfg)
+    return q, k, v
+
+
+def _finish_rows(x_rows, attn_rows, p, cfg):
+    """Out-projection, residual and MLP of the rows whose attention is known."""
+    xs = x_rows + linear(attn_rows, p["w_o"], p["b_o"])
+    return xs + mlp(norm(xs, p, "norm2", cfg), p, cfg)
+
+
+def _no_fp8(cfg):
+    if cfg.get("gemm_shared") == "fp8":
+        raise ValueError("per-tensor fp8 scales depend on every row; use the full functions")
+
+
+def shared_layer_rows(x, G, p, cfg, plan, rope, sel):
+    """Union rows ``sel`` and every global row of shared_layer(x, G, ...).
+
+    Returns (x_out [len(sel), d], G_out [n_tiles, d]).
+    """
+    _no_fp8(cfg)
+    sel = np.asarray(sel, dtype=np.int64)
+    n, d = plan.tile_tokens, cfg["d"]
+    xa = np.vstack([x, G]).astype(F)
+    h = norm(xa, p, "norm1", cfg)
+    q_rows = np.concatenate([sel, plan.n_union + np.arange(plan.n_tiles)])
+    q, k, v = _kv_and_q(h, q_rows, p, cfg)
+    a = np.zeros((len(q_rows), d), dtype=F)
+    for t in range(plan.n_tiles):
+        win = np.concatenate([plan.tile_rows[t].astype(np.int64), [plan.n_union + t]])
+        which, local, wts = [], [], []
+        for i, r in enumerate(sel):
+            for tt, j, w in plan.cover_of(int(r)):
+                if tt == t:
+                    which.append(i)
+                    local.append(j)
+                    wts.append(w)
+        which.append(len(sel) + t)
+        local.append(n)
+        o = attention_rows(q[which], k[win], v[win], local, rope.cos, rope.sin, cfg)
+        for m in range(len(which) - 1):
+            a[which[m]] += F(np.float32(wts[m])) * o[m]
+        a[len(sel) + t] = o[-1]
+    out = _finish_rows(xa[q_rows], a, p, cfg)
+    return out[: len(sel)], out[len(sel):]
+
+
+def per_tile_layer_rows(X, p, cfg, rope, local):
+    """Rows ``local`` of per_tile_layer(X, ...) for one tile state X [n+1, d]."""
+    local = np.asarray(local, dtype=np.int64)
+    X = np.asarray(X, dtype=F)
+    h = norm(X, p, "norm1", cfg)
+    q, k, v = _kv_and_q(h, local, p, cfg)
+    o = attention_rows(q, k, v, local, rope.cos, rope.sin, cfg)
+    return _finish_rows(X[local], o, p, cfg)
+
+
+def tiled_layer_rows(cfg, plan, x, g, p, sel, rope=None):
+    """Rows ``sel`` and the global rows of one per-tile layer followed by the
+    merge: stack_forward with one layer and k = 1 (the one-layer tiled
+    baseline).  Returns (x_out [len(sel), d], G_out [n_tiles, d])."""
+    rope = rope or Rope(plan, cfg)
+    sel = np.asarray(sel, dtype=np.int64)
+    n, d = plan.tile_tokens, cfg["d"]
+    xs = np.zeros((len(sel), d), dtype=F)
+    G = np.empty((plan.n_tiles, d), dtype=F)
+    for t in range(plan.n_tiles):
+        Xt = np.vstack([x[plan.tile_rows[t]].astype(F), g.astype(F)[None, :]])
+        which, local, wts = [], [], []
+        for i, r in enumerate(sel):
+            for tt, j, w in plan.cover_of(int(r)):
+                if tt == t:
+                    which.append(i)
+                    local.append(j)
+                    wts.append(w)
+        rows = per_tile_layer_rows(Xt, p, cfg, rope, local + [n])
+        for m in range(len(which)):
+            xs[which[m]] += F(np.float32(wts[m])) * rows[m]
+        G[t] = rows[-1]
+    return xs, G
 
 
 def rel_err(got, ref):

@@ -1,0 +1,234 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times, on sampled outputs that the oracle computes one by one.
+
+Each case runs one call of the C ABI over the whole workload (every tile,
+every row, the ragged last query and key blocks) and compares a sample of
+output rows with the oracle's float64 value of exactly those rows: the
+first and last rows, rows on block edges, rows covered by each possible
+number of tiles, the global rows, and seeded random rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import shared_token_tiled_amd as ts
+from oracle import fp8 as ofp8
+from oracle import model as M
+from oracle.plan import Plan
+from synth import configs, make_inputs, round_bf16
+
+from gpu_helpers import DEV, TOL, Run, max_rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(m, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 2, 63, 64, 255, 256, m - 257, m - 256, m - 3, m - 2, m - 1, *extra]
+    rand = rng.choice(m, size=24, replace=False).tolist()
+    return np.array(sorted({r for r in fixed + rand if 0 <= r < m}), dtype=np.int64)
+
+
+def _randn(rng, shape, std=1.0):
+    return (std * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
+
+
+def _union_sample(pl, seed):
+    """Rows covered by each possible number of tiles, plus edges and random rows."""
+    counts = np.diff(pl.cover_ptr)
+    extra = []
+    for c in sorted(set(counts.tolist())):
+        idx = np.nonzero(counts == c)[0]
+        extra += [int(idx[0]), int(idx[len(idx) // 2]), int(idx[-1])]
+    return _sample_rows(pl.n_union, seed, extra)
+
+
+MINIMAX = configs.get("minimax_h3")
+_PL = Plan(MINIMAX["grid"], MINIMAX["tile"], MINIMAX["stride"])
+M_SHARED = _PL.n_union + _PL.n_tiles                 # rows of a shared-layer GEMM
+M_TILED = _PL.n_tiles * (_PL.tile_tokens + 1)        # rows of a per-tile GEMM
+D, DM = MINIMAX["d"], MINIMAX["mlp_hidden"]
+
+# (name, M, N, K, epilogue): the GEMMs of one MiniMax-H3-scale layer
+GEMMS = [("qkv", M_SHARED, 3 * D, D, ts.TS_EPI_BIAS),
+         ("out", M_SHARED, D, D, ts.TS_EPI_RESIDUAL),
+         ("fc1", M_SHARED, DM, D, ts.TS_EPI_BIAS_GELU),
+         ("fc2", M_SHARED, D, DM, ts.TS_EPI_RESIDUAL),
+         ("qkv_per_tile", M_TILED, 3 * D, D, ts.TS_EPI_BIAS)]
+
+
+@pytest.mark.parametrize("name,M_,N,K,epi", GEMMS)
+def test_full_size_gemm_bf16(name, M_, N, K, epi):
+    say(f"full-size gemm bf16 {name} M={M_} N={N} K={K} epi={epi}")
+    r = np.random.default_rng(M_ + N + K)
+    A = round_bf16(_randn(r, (M_, K)))
+    B = round_bf16(_randn(r, (N, K), 0.02))
+    bias = _randn(r, (N,), 0.02)
+    rows = _sample_rows(M_, 1)
+    resid = epi == ts.TS_EPI_RESIDUAL
+    c = torch.from_numpy(_randn(r, (M_, N))).to(DEV) if resid else \
+        torch.empty(M_, N, dtype=torch.bfloat16, device=DEV)
+    c0 = c[rows].cpu().numpy().astype(np.float64) if resid else 0.0
+    a = torch.from_numpy(A).to(DEV, torch.bfloat16)
+    b = torch.from_numpy(B).to(DEV, torch.bfloat16)
+    ts.ts_op_gemm(ts.TS_BF16, epi, a, b, torch.from_numpy(bias).to(DEV), c)
+    torch.cuda.synchronize()
+    got = c[rows].float().cpu().numpy().astype(np.float64)
+    ref = A[rows].astype(np.float64) @ B.astype(np.float64).T + bias
+    if epi == ts.TS_EPI_BIAS_GELU:
+        ref = M.gelu(ref)
+    ref = ref + c0
+    rms = np.sqrt(np.mean(ref * ref))
+    if resid:
+        # fp32 output: K-long fp32 accumulation, relative to the output scale
+        bound = 1e-5 * rms
+    else:
+        # one round to nearest bf16 (half an ulp is at most 2^-8 of the value)
+        bound = 2.0 ** -8 * np.abs(ref) + 1e-4 * rms
+    err = np.abs(got - ref)
+    print(f"  max|err|/rms {err.max() / rms:.3e} over {len(rows)} rows x {N} columns")
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("name,N,K,epi", [("qkv", 3 * D, D, ts.TS_EPI_BIAS),
+                                          ("fc2", D, DM, ts.TS_EPI_F32)])
+def test_full_size_gemm_fp8(name, N, K, epi):
+    """FP8 shared-layer GEMMs at the MiniMax-H3 fp8 shapes.  The per-tensor
+    scales are over the whole operands, which the oracle sees whole; only the
+    product is sampled."""
+    M_ = M_SHARED
+    say(f"full-size gemm fp8 {name} M={M_} N={N} K={K}")
+    r = np.random.default_rng(N + K)
+    A = round_bf16(_randn(r, (M_, K)))
+    A[12345, 77] = 9.5                                  # a clear per-tensor maximum
+    B = round_bf16(_randn(r, (N, K), 0.02))
+    bias = _randn(r, (N,), 0.02)
+    rows = _sample_rows(M_, 2, extra=(12345,))
+    a = torch.from_numpy(A).to(DEV, torch.bfloat16)
+    b = torch.from_numpy(B).to(DEV, torch.bfloat16)
+    a8 = torch.empty(M_, K, dtype=torch.uint8, device=DEV)
+    b8 = torch.empty(N, K, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(2, dtype=torch.float32, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    ts.ts_fp8_quantize(a, a8, sc[0:1], ws)
+    ts.ts_fp8_quantize(b, b8, sc[1:2], ws)
+    c = torch.empty(M_, N, dtype=torch.float32 if epi == ts.TS_EPI_F32 else torch.bfloat16, device=DEV)
+    ts.ts_op_gemm(ts.TS_FP8E4M3, epi, a8, b8, torch.from_numpy(bias).to(DEV), c, sc[0:1], sc[1:2])
+    torch.cuda.synchronize()
+    sa, sb = ofp8.tensor_scale(A), ofp8.tensor_scale(B)
+    s_got = sc.cpu().numpy()
+    assert s_got[0] == sa and s_got[1] == sb
+    qa = ofp8.round_e4m3(A[rows] / sa)
+    qb = ofp8.round_e4m3(B / sb)
+    ref = (qa @ qb.T) * (np.float64(sa) * np.float64(sb)) + bias
+    got = c[rows].float().cpu().numpy().astype(np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    # same e4m3 codes on both sides; the MFMA sums the 64 products of one
+    # instruction in one step, not with a rounding per add
+    bound = (0 if epi == ts.TS_EPI_F32 else 2.0 ** -8 * np.abs(ref)) + 2e-4 * rms
+    err = np.abs(got - ref)
+    print(f"  max|err|/rms {err.max() / rms:.3e}")
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_full_size_window_attention(shared):
+    cfg = MINIMAX
+    pl = _PL
+    n, d = pl.tile_tokens, cfg["d"]
+    rows = pl.n_union + pl.n_tiles if shared else pl.n_tiles * (n + 1)
+    say(f"full-size attention bf16 shared={shared} rows={rows} tiles={pl.n_tiles} n={n}")
+    r = np.random.default_rng(21)
+    qkv = round_bf16(_randn(r, (rows, 3 * d)))
+    h = ts.ts_plan_create(cfg["ndim"], cfg["grid"], cfg["tile"], cfg["stride"])
+    try:
+        ts.ts_plan_upload(h, cfg["head_dim"])
+        out = torch.zeros(pl.n_tiles * (n + 1), d, dtype=torch.bfloat16, device=DEV)
+        ts.ts_op_window_attention(ts.model_desc(cfg), h, shared, torch.from_numpy(qkv).to(DEV, torch.bfloat16), out)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+    finally:
+        ts.ts_plan_destroy(h)
+    rope = M.Rope(pl, cfg)
+    q64 = qkv.astype(np.float64)
+    worst = 0.0
+    for t in range(pl.n_tiles):
+        if shared:
+            win = np.concatenate([pl.tile_rows[t].astype(np.int64), [pl.n_union + t]])
+        else:
+            win = np.arange(t * (n + 1), (t + 1) * (n + 1))
+        local = _sample_rows(n + 1, 30 + t, extra=(n,))
+        ref = M.attention_rows(q64[win[local], :d], q64[win, d:2 * d], q64[win, 2 * d:], local,
+                               rope.cos, rope.sin, cfg)
+        o = got[t * (n + 1) + local]
+        err = np.linalg.norm(o - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        worst = max(worst, float(err.max()))
+    print(f"  worst sampled row rel-L2 {worst:.3e}")
+    # the same per-row bound as the small cases (bf16 q, k, weights and output)
+    assert worst < 2e-2
+
+
+FULL_LAYER = ["minimax_h3", "small_video", "vitok4k"]
+
+
+def _full_inputs(name):
+    cfg = dict(configs.get(name), n_layers=1)
+    x, g, layers = make_inputs(cfg, n_layers=1)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    return cfg, x, g, layers, pl
+
+
+@pytest.mark.parametrize("name", FULL_LAYER)
+def test_full_size_shared_layer(name):
+    cfg, x, g, layers, pl = _full_inputs(name)
+    say(f"full-size shared layer {name} n_union={pl.n_union} tiles={pl.n_tiles}")
+    rng = np.random.default_rng(4)
+    G = (np.tile(g[None], (pl.n_tiles, 1)) + 0.1 * _randn(rng, (pl.n_tiles, cfg["d"]))).astype(np.float32)
+    xa = np.vstack([x, G])
+    run = Run(cfg, layers)
+    try:
+        got = run.shared_layer(xa)
+    finally:
+        run.close()
+    sel = _union_sample(pl, 8)
+    rx, rg = M.shared_layer_rows(x.astype(np.float64), G.astype(np.float64), layers[0], cfg, pl,
+                                 M.Rope(pl, cfg), sel)
+    ex, eg = max_rel(got[sel], rx), max_rel(got[pl.n_union:], rg)
+    # the layer's own contribution, without the residual input
+    ed = max_rel(got[sel] - x[sel], rx - x[sel])
+    print(f"  sampled {len(sel)} rows: out {ex:.3e}, globals {eg:.3e}, layer delta {ed:.3e}")
+    tol = TOL[cfg["dtype"]]
+    assert ex < tol and eg < tol and ed < tol
+
+
+def test_full_size_tiled_layer_and_merge():
+    cfg, x, g, layers, pl = _full_inputs("minimax_h3")
+    say(f"full-size per-tile layer + merge minimax_h3 tiles={pl.n_tiles} n={pl.tile_tokens}")
+    run = Run(cfg, layers)
+    try:
+        got, ggot = run.stack(x, g, 1)
+    finally:
+        run.close()
+    sel = _union_sample(pl, 9)
+    rx, rg = M.tiled_layer_rows(cfg, pl, x, g, layers[0], sel)
+    ex, eg = max_rel(got[sel], rx), max_rel(ggot, rg)
+    ed = max_rel(got[sel] - x[sel], rx - x[sel])
+    print(f"  sampled {len(sel)} rows: out {ex:.3e}, globals {eg:.3e}, layer delta {ed:.3e}")
+    tol = TOL[cfg["dtype"]]
+    assert ex < tol and eg < tol and ed < tol
+
+
+def test_full_size_stack_is_deterministic_and_finite():
+    """TileShare-6 over seven MiniMax-H3-scale layers (six per tile, the merge,
+    one shared), twice: results are bit-identical and finite."""
+    cfg = dict(MINIMAX, n_layers=7)
+    say("full-size stack minimax_h3 L=7 k=6, twice")
+    x, g, layers = make_inputs(cfg, n_layers=7)
+    run = Run(cfg, layers)
+    try:
+        a, ga = run.stack(x, g, 6)
+        b, gb = run.stack(x, g, 6)
+    finally:
+        run.close()
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(ga))
+    assert np.array_equal(a, b) and np.array_equal(ga, gb)

@@ -268,3 +268,72 @@ def test_tiny2d_config_runs_and_differs_from_baseline():
     ts0, _ = M.stack_forward(cfg, pl, x, g, layers, 0)
     e = M.rel_err(ts0, base)
     assert np.all(np.isfinite(ts0)) and 0 < e < 1.0
+
+
+# --- row-restricted evaluation (used for checks at the full workload sizes) --
+
+ROWS_CASES = [
+    dict(ndim=3, norm="rms", qk=True, grid=(2, 12, 20), tile=(2, 8, 8), stride=(2, 6, 6), d=16, heads=2),
+    dict(ndim=2, norm="ln", qk=False, grid=(1, 20, 36), tile=(1, 16, 16), stride=(1, 12, 12), d=16, heads=2),
+    dict(ndim=3, norm="ln", qk=False, grid=(3, 5, 6), tile=(2, 3, 4), stride=(1, 2, 3), d=8, heads=2),
+]
+
+
+def _rows_setup(c):
+    cfg = tiny_cfg(ndim=c["ndim"], norm=c["norm"], qk=c["qk"], grid=c["grid"], tile=c["tile"],
+                   stride=c["stride"], d=c["d"], heads=c["heads"], layers=1, mlp=2 * c["d"])
+    x, g, layers = make_inputs(cfg, qk_scale=2.0)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    rng = np.random.default_rng(9)
+    # first, last, every multiply-covered kind, and random rows, unsorted
+    counts = np.diff(pl.cover_ptr)
+    sel = [pl.n_union - 1, 0]
+    for c_ in sorted(set(counts.tolist())):
+        sel.append(int(np.nonzero(counts == c_)[0][-1]))
+    sel += rng.choice(pl.n_union, size=7, replace=False).tolist()
+    return cfg, x, g, layers, pl, np.array(sel)
+
+
+@pytest.mark.parametrize("c", ROWS_CASES)
+def test_shared_layer_rows_equal_full_layer(c):
+    cfg, x, g, layers, pl, sel = _rows_setup(c)
+    rope = M.Rope(pl, cfg)
+    G = np.tile(g[None].astype(np.float64), (pl.n_tiles, 1))
+    G[-1] -= 0.25
+    full_x, full_g = M.shared_layer(x.astype(np.float64), G, layers[0], cfg, pl, rope)
+    rx, rg = M.shared_layer_rows(x.astype(np.float64), G, layers[0], cfg, pl, rope, sel)
+    assert np.allclose(rx, full_x[sel], atol=1e-12, rtol=0)
+    assert np.allclose(rg, full_g, atol=1e-12, rtol=0)
+
+
+def test_shared_layer_rows_against_brute_force():
+    c = BRUTE[2]
+    cfg = tiny_cfg(ndim=c["ndim"], norm=c["norm"], qk=c["qk"], grid=c["grid"], tile=c["tile"],
+                   stride=c["stride"], layers=1)
+    x, g, layers = make_inputs(cfg, qk_scale=3.0)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    G = np.tile(g[None].astype(np.float64), (pl.n_tiles, 1))
+    sel = np.array([5, 17, 0, pl.n_union - 1])
+    rx, rg = M.shared_layer_rows(x.astype(np.float64), G, layers[0], cfg, pl, M.Rope(pl, cfg), sel)
+    bx, bg = brute_shared_layer(x.astype(np.float64).tolist(), G.tolist(), layers[0], cfg,
+                                cfg["grid"], cfg["tile"], cfg["stride"])
+    assert np.allclose(rx, np.array(bx)[sel], atol=1e-10, rtol=0)
+    assert np.allclose(rg, np.array(bg), atol=1e-10, rtol=0)
+
+
+@pytest.mark.parametrize("c", ROWS_CASES)
+def test_tiled_layer_rows_equal_one_layer_stack(c):
+    cfg, x, g, layers, pl, sel = _rows_setup(c)
+    full_x, full_g = M.stack_forward(cfg, pl, x, g, layers, 1)
+    rx, rg = M.tiled_layer_rows(cfg, pl, x, g, layers[0], sel)
+    assert np.allclose(rx, full_x[sel], atol=1e-12, rtol=0)
+    assert np.allclose(rg, full_g, atol=1e-12, rtol=0)
+
+
+def test_rows_functions_refuse_fp8():
+    cfg = dict(tiny_cfg(layers=1), gemm_shared="fp8")
+    x, g, layers = make_inputs(cfg)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    G = np.tile(g[None].astype(np.float64), (pl.n_tiles, 1))
+    with pytest.raises(ValueError):
+        M.shared_layer_rows(x, G, layers[0], cfg, pl, M.Rope(pl, cfg), [0])
