@@ -472,66 +472,107 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // (head, tile); LPK lanes share one key (lane = rotation pair), each
 // wavefront walks every 4th key group with its own online softmax, and the
 // four partial states are merged through LDS at the end.
+// Global-token query row of one (head, tile): one workgroup of 1024 threads.
+// The window's keys are taken in chunks of GCH.  Score pass: HD/16 threads
+// per key, 16 dims each (two 8-dim RoPE groups, the rotated key rounded to
+// bf16 as the MFMA kernel stages it), summed across those lanes; scores and
+// row indices go to LDS.  Value pass: each thread owns one 8-dim group of the
+// output and a strided subset of the chunk's keys and keeps a running
+// (max-shifted) weighted sum; the chunk max is shared by the workgroup, so
+// every thread rescales by the same factor.  The partial sums are added in
+// LDS at the end.  The global key itself (window row n) has no rotation.
+constexpr int GCH = 4096;
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_global_bf16(AttnP p) {
-  constexpr int LPK = HD / 2;        // lanes per key: one rotation pair each
-  constexpr int KPI = 64 / LPK;      // keys per wavefront step
+__global__ __launch_bounds__(1024) void k_attn_global_bf16(AttnP p) {
+  constexpr int NT = 1024;
+  constexpr int TPK = HD / 16;    // threads per key, score pass
+  constexpr int KPP = NT / TPK;   // keys per score pass
+  constexpr int DG = HD / 8;      // 8-dim groups, value pass
+  constexpr int KG = NT / DG;     // key groups, value pass
+  __shared__ float s_s[GCH];
+  __shared__ int r_s[GCH];
+  __shared__ float red[NT / 64];
+  __shared__ __attribute__((aligned(16))) float acc_s[KG][HD + 4];
+  __shared__ float l_s[KG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int pr = lane % LPK, ksub = lane / LPK;
   const int h = blockIdx.x, t = blockIdx.y, n = p.n;
   const bf16* qkv = (const bf16*)p.qkv;
   const int64_t ld = 3 * int64_t(p.d);
-  const int grow = window_row(p, t, n);
-  const bf16* base = qkv + grow * ld + h * HD + 2 * pr;
-  const float qa = float(base[0]), qb = float(base[1]);   // global query: no rotation
-  const float C = p.scale_log2;
-  // global key first (not rotated)
-  float sg = qa * float(base[p.d]) + qb * float(base[p.d + 1]);
-  sg = group_sum(sg, LPK);
-  float m = sg * C, l = 0.f, a0 = 0.f, a1 = 0.f;
-  if (wave == 0 && ksub == 0) {
-    l = 1.f;
-    a0 = float(base[2 * p.d]);
-    a1 = float(base[2 * p.d + 1]);
+  const int64_t grow = window_row(p, t, n);
+
+  // score-pass role: dims [16*sub, 16*sub + 16) of key slot kk
+  const int sub = tid % TPK, kk = tid / TPK;
+  const bf16* qp = qkv + grow * ld + h * HD + 16 * sub;
+  const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(qp), q1 = *reinterpret_cast<const bf16x8*>(qp + 8);
+  const GroupRope gr0 = group_rope(p, 2 * sub), gr1 = group_rope(p, 2 * sub + 1);
+  // value-pass role: dims [8*dg, 8*dg + 8), keys kg, kg + KG, ...
+  const int dg = tid % DG, kg = tid / DG;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float l = 0.f, m_run = -INFINITY;
+
+  for (int c0 = 0; c0 <= n; c0 += GCH) {
+    const int cnt = min(GCH, n + 1 - c0);
+#pragma unroll 4
+    for (int jj = kk; jj < cnt; jj += KPP) {
+      const int j = c0 + jj;
+      const int64_t r = window_row(p, t, j);
+      const bf16* kp = qkv + r * ld + p.d + h * HD + 16 * sub;
+      bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kp), k1 = *reinterpret_cast<const bf16x8*>(kp + 8);
+      if (j < n) {
+        const int pos = p.local_pos[j];
+        k0 = rope_group(p.rope, gr0, pos, k0);
+        k1 = rope_group(p.rope, gr1, pos, k1);
+      }
+      float sc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sc += float(q0[e]) * float(k0[e]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sc += float(q1[e]) * float(k1[e]);
+#pragma unroll
+      for (int o = 1; o < TPK; o <<= 1) sc += __shfl_xor(sc, o);
+      if (sub == 0) {
+        s_s[jj] = sc * p.scale_log2;
+        r_s[jj] = int(r);
+      }
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int jj = tid; jj < cnt; jj += NT) mx = fmaxf(mx, s_s[jj]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    float cmax = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) cmax = fmaxf(cmax, red[w]);
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll 8
+    for (int jj = kg; jj < cnt; jj += KG) {
+      const float pj = __builtin_amdgcn_exp2f(s_s[jj] - m_new);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qkv + int64_t(r_s[jj]) * ld + 2 * p.d + h * HD + 8 * dg);
+      l += pj;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += pj * float(v[e]);
+    }
+    __syncthreads();   // s_s / r_s are rewritten by the next chunk
   }
-  const int dsc = rope_desc(p, pr);
-  for (int j = wave * KPI + ksub; j < n; j += 4 * KPI) {
-    const int r = window_row(p, t, j);
-    const bf16* kp = qkv + r * ld + p.d + h * HD + 2 * pr;
-    const float2 cs = rope_at(p.rope, dsc, p.local_pos[j]);
-    const float c = cs.x, sn = cs.y;
-    const float ka = float(kp[0]), kb = float(kp[1]);
-    const float kra = float(bf16(ka * c - kb * sn)), krb = float(bf16(ka * sn + kb * c));
-    float sc = group_sum(qa * kra + qb * krb, LPK) * C;
-    const float mn = fmaxf(m, sc);
-    const float al = __builtin_amdgcn_exp2f(m - mn), pj = __builtin_amdgcn_exp2f(sc - mn);
-    l = l * al + pj;
-    a0 = a0 * al + pj * float(kp[p.d]);
-    a1 = a1 * al + pj * float(kp[p.d + 1]);
-    m = mn;
-  }
-  // merge the 4 * KPI partial states
-  __shared__ float ms[4 * KPI], ls[4 * KPI];
-  __shared__ float acc_s[4 * KPI][HD];
-  const int slot = wave * KPI + ksub;
-  if (pr == 0) {
-    ms[slot] = m;
-    ls[slot] = l;
-  }
-  acc_s[slot][2 * pr] = a0;
-  acc_s[slot][2 * pr + 1] = a1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc_s[kg][8 * dg + e] = acc[e];
+  if (dg == 0) l_s[kg] = l;
   __syncthreads();
   if (tid < HD) {
-    float mm = -INFINITY;
-    for (int s = 0; s < 4 * KPI; ++s) mm = fmaxf(mm, ms[s]);
-    float lt = 0.f, at = 0.f;
-    for (int s = 0; s < 4 * KPI; ++s) {
-      const float w = __builtin_amdgcn_exp2f(ms[s] - mm);
-      lt += ls[s] * w;
-      at += acc_s[s][tid] * w;
+    float o = 0.f, lt = 0.f;
+    for (int g = 0; g < KG; ++g) {
+      o += acc_s[g][tid];
+      lt += l_s[g];
     }
     bf16* out = (bf16*)p.out + (int64_t(t) * (n + 1) + n) * p.d + h * HD;
-    out[tid] = bf16(at / lt);
+    out[tid] = bf16(o / lt);
   }
 }
 
@@ -552,7 +593,7 @@ hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
   }
   if (a.n < 1) return hipErrorInvalidValue;
   const dim3 grid(((a.n + QB - 1) / QB) * a.H * a.n_tiles), block(NW * 64);
-  const dim3 ggrid(a.H, a.n_tiles), gblock(256);
+  const dim3 ggrid(a.H, a.n_tiles), gblock(1024);
   if (a.hd == 64) {
     hipLaunchKernelGGL(k_attn_bf16<64>, grid, block, 0, s, p);
     hipLaunchKernelGGL(k_attn_global_bf16<64>, ggrid, gblock, 0, s, p);
