@@ -96,6 +96,26 @@ def cpu_baseline(cfg, k):
                       f"TileShare-{k} decode ({total / 1e12:.1f} TFLOP)"}
 
 
+def measured_traffic(name, workload, k):
+    """HBM bytes per launch of kernel `name` from the committed FETCH_SIZE /
+    WRITE_SIZE summary of this workload, or None when there is none or the
+    kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_ts{k}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    ent = doc.get("kernels", {}).get(name)
+    if ent is None:
+        return None
+    for src, digest in ent["sources"].items():
+        with open(os.path.join(ROOT, src), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return ent["hbm_bytes_per_launch"]
+
+
 def decode_flops(cfg, pl, k):
     """Algorithmic FLOPs of a TileShare-k decode: 2*(3d^2 + d^2 + 2 d dm) per row
     per layer for the projections, 4 (n+1)^2 d per tile per layer for attention."""
@@ -178,17 +198,21 @@ def main():
     stats = sorted(stats, key=lambda r: -r["total_ms"])
     dom = stats[0]
     dt = "fp8" if "fp8" in dom["name"] else ("f32" if "f32" in dom["name"] else "bf16")
+    traffic = measured_traffic(dom["name"], args.config, k)
     if dom["flops"] > 0:
         ach = dom["flops"] / (dom["total_ms"] / 1e3)
         roof = {"kernel": dom["name"], "bound": "mfma", "achieved": ach / 1e12, "peak": PEAK[dt] / 1e12,
-                "unit": "TFLOP/s", "frac": ach / PEAK[dt], "traffic": None,
+                "unit": "TFLOP/s", "frac": ach / PEAK[dt], "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "algorithmic_bytes_per_launch": dom["bytes"] / dom["launches"],
                 "launches_per_step": dom["launches"] / args.steps,
                 "avg_launch_ms": dom["total_ms"] / dom["launches"],
                 "flops_per_launch": dom["flops"] / dom["launches"]}
     else:
         ach = dom["bytes"] / (dom["total_ms"] / 1e3)
         roof = {"kernel": dom["name"], "bound": "hbm", "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9,
-                "unit": "GB/s", "frac": ach / HBM_PEAK, "traffic": None,
+                "unit": "GB/s", "frac": ach / HBM_PEAK, "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "launches_per_step": dom["launches"] / args.steps,
                 "avg_launch_ms": dom["total_ms"] / dom["launches"], "bytes_per_launch": dom["bytes"] / dom["launches"]}
     kernels = {}

@@ -230,10 +230,24 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared
       if (p->rope_pairs[ax] % 4 != 0)
         return fail(TS_ESHAPE, "bf16 attention needs every RoPE axis to hold a multiple of 4 rotation pairs");
   }
-  const double nn = double(p->n + 1);
-  Scope sc(s, m->act_dtype == TS_F32 ? "attn_f32" : "attn_bf16", 4.0 * nn * nn * m->d * p->n_tiles,
-           double(p->n_tiles) * (p->n + 1) * m->d * 4 * act_bytes(m->act_dtype));
-  TS_HIP(tsk::attention(s, m->act_dtype, a), "attention");
+  // algorithmic work: 4 (n+1) d FLOPs per query row (QK^T and PV over the
+  // n+1 keys); bytes: the window's q, k, v rows read once, o written once
+  const double nn = double(p->n + 1), ab = act_bytes(m->act_dtype);
+  if (m->act_dtype == TS_F32) {
+    Scope sc(s, "attn_f32", 4.0 * nn * nn * m->d * p->n_tiles, double(p->n_tiles) * nn * m->d * 4 * ab);
+    TS_HIP(tsk::attention(s, m->act_dtype, a), "attention");
+    return TS_OK;
+  }
+  {
+    Scope sc(s, "attn_bf16", 4.0 * double(p->n) * nn * m->d * p->n_tiles,
+             double(p->n_tiles) * (nn * 3 * m->d + double(p->n) * m->d) * ab);
+    TS_HIP(tsk::attention(s, m->act_dtype, a), "attention");
+  }
+  {
+    Scope sc(s, "attn_global_bf16", 4.0 * nn * m->d * p->n_tiles,
+             double(p->n_tiles) * (nn * 2 * m->d + 2 * m->d) * ab);
+    TS_HIP(tsk::attention_global(s, a), "attention (global rows)");
+  }
   return TS_OK;
 }
 

@@ -580,10 +580,14 @@ __global__ __launch_bounds__(1024) void k_attn_global_bf16(AttnP p) {
 
 namespace tsk {
 
+static AttnP make_params(const AttnArgs& a) {
+  return AttnP{a.qkv, a.out, a.rows, a.n_union, a.d, a.H, a.n_tiles, a.n, a.local_pos, a.rope, a.rope_floats,
+               {a.pairs[0], a.pairs[1], a.pairs[2]}, {a.rope_off[0], a.rope_off[1], a.rope_off[2]},
+               1.4426950408889634f / sqrtf(float(a.hd))};
+}
+
 hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
-  AttnP p{a.qkv, a.out, a.rows, a.n_union, a.d, a.H, a.n_tiles, a.n, a.local_pos, a.rope, a.rope_floats,
-          {a.pairs[0], a.pairs[1], a.pairs[2]}, {a.rope_off[0], a.rope_off[1], a.rope_off[2]},
-          1.4426950408889634f / sqrtf(float(a.hd))};
+  const AttnP p = make_params(a);
   if (act == ACT_F32) {
     const dim3 grid((a.n + 1 + 63) / 64, a.H, a.n_tiles), block(64);
     if (a.hd == 32) hipLaunchKernelGGL(k_attn_f32<32>, grid, block, 0, s, p);
@@ -593,16 +597,19 @@ hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
   }
   if (a.n < 1) return hipErrorInvalidValue;
   const dim3 grid(((a.n + QB - 1) / QB) * a.H * a.n_tiles), block(NW * 64);
-  const dim3 ggrid(a.H, a.n_tiles), gblock(1024);
-  if (a.hd == 64) {
-    hipLaunchKernelGGL(k_attn_bf16<64>, grid, block, 0, s, p);
-    hipLaunchKernelGGL(k_attn_global_bf16<64>, ggrid, gblock, 0, s, p);
-  } else if (a.hd == 128) {
-    hipLaunchKernelGGL(k_attn_bf16<128>, grid, block, 0, s, p);
-    hipLaunchKernelGGL(k_attn_global_bf16<128>, ggrid, gblock, 0, s, p);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (a.hd == 64) hipLaunchKernelGGL(k_attn_bf16<64>, grid, block, 0, s, p);
+  else if (a.hd == 128) hipLaunchKernelGGL(k_attn_bf16<128>, grid, block, 0, s, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t attention_global(hipStream_t s, const AttnArgs& a) {
+  const AttnP p = make_params(a);
+  if (a.n < 1) return hipErrorInvalidValue;
+  const dim3 grid(a.H, a.n_tiles), block(1024);
+  if (a.hd == 64) hipLaunchKernelGGL(k_attn_global_bf16<64>, grid, block, 0, s, p);
+  else if (a.hd == 128) hipLaunchKernelGGL(k_attn_global_bf16<128>, grid, block, 0, s, p);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -60,6 +60,10 @@ struct AttnArgs {
   int rope_off[3];      // float offset of each axis' block: pair i at position pos of
                         // axis a is (cos, sin) at rope_off[a] + 2*(pos*pairs[a] + i)
 };
+// fp32: every window row.  bf16: the n tile-token query rows of every window;
+// the global-token row (window row n) is attention_global's.
 hipError_t attention(hipStream_t s, int act, const AttnArgs& a);
+// bf16 only: the global-token query row of every (tile, head).
+hipError_t attention_global(hipStream_t s, const AttnArgs& a);
 
 }  // namespace tsk
