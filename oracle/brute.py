@@ -91,13 +91,9 @@ def _angles(local, ndim, hd, base):
     """Angle of every pair for a token at tile-local (tau, y, x)."""
     P = hd // 2
     if ndim == 2:
-        h = P // 2 if not (P % 4 == 0 and P >= 8) else (P // 2) // 4 * 4
-        chunks = [(1, h), (2, P - h)]
+        chunks = [(1, P // 2), (2, P - P // 2)]
     else:
-        th = P // 3
-        if P % 4 == 0 and P >= 12:
-            th = (th + 2) // 4 * 4
-        chunks = [(0, P - 2 * th), (1, th), (2, th)]
+        chunks = [(0, P - 2 * (P // 3)), (1, P // 3), (2, P // 3)]
     out = []
     for ax, m in chunks:
         for i in range(m):

@@ -18,12 +18,10 @@ w-bar.  Readings taken here (listed in the design doc):
   computed in float64 in the order written here and rounded once to fp32;
 * RoPE: the P = head_dim/2 rotation pairs are split over the axes in
   contiguous chunks (t, then h, then w).  3D: h and w get floor(P/3) pairs
-  each and t the rest, except that when P >= 12 and P % 4 == 0 the h and w
-  counts are rounded to the nearest multiple of 4 (halves up), so every group
-  of 4 consecutive pairs (8 dims) belongs to one axis.  2D: h gets P/2 (rounded
-  down to a multiple of 4 when P >= 8 and P % 4 == 0) and w the rest.  Pair i
-  of an axis chunk of m pairs turns by pos * base**(-i/m); cos/sin in float64,
-  stored as fp32.  The tile's global token is not rotated.
+  each and t the rest (head_dim 128: 22, 21, 21; head_dim 64: 12, 10, 10).
+  2D: h gets floor(P/2) and w the rest.  Pair i of an axis chunk of m pairs
+  turns by pos * base**(-i/m); cos/sin in float64, stored as fp32.  The
+  tile's global token is not rotated.
 """
 import math
 
@@ -133,17 +131,12 @@ class Plan:
 
 
 def rope_pairs(ndim, head_dim):
-    """Number of rotation pairs per axis (t, h, w)."""
+    """Number of rotation pairs per axis (t, h, w): 2D h and w get P/2 each
+    (w the odd one if P is odd); 3D h and w get floor(P/3) each, t the rest."""
     P = head_dim // 2
-    aligned = P % 4 == 0
     if ndim == 2:
-        h = P // 2
-        if aligned and P >= 8:
-            h = 4 * (h // 4)
-        return (0, h, P - h)
+        return (0, P // 2, P - P // 2)
     third = P // 3
-    if aligned and P >= 12:
-        third = 4 * ((third + 2) // 4)
     return (P - 2 * third, third, third)
 
 

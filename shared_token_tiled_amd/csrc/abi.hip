@@ -224,11 +224,16 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared
   for (int ax = 0; ax < 3; ++ax) {
     a.pairs[ax] = p->rope_pairs[ax];
     a.rope_off[ax] = p->rope_off[ax];
+    a.rope_wbase[ax] = p->rope_wbase[ax];
+    a.rope_wpairs[ax] = p->rope_wpairs[ax];
   }
   if (m->act_dtype == TS_BF16) {
-    for (int ax = 0; ax < 3; ++ax)
-      if (p->rope_pairs[ax] % 4 != 0)
-        return fail(TS_ESHAPE, "bf16 attention needs every RoPE axis to hold a multiple of 4 rotation pairs");
+    // the bf16 kernels rotate 8 dims (4 pairs) at a time and allow a group to
+    // straddle one axis boundary, not two
+    const int b0 = p->rope_pairs[0], b1 = p->rope_pairs[0] + p->rope_pairs[1];
+    for (int g = 0; 4 * g < m->head_dim / 2; ++g)
+      if (b0 > 4 * g && b1 < 4 * g + 4 && p->rope_pairs[1] > 0)
+        return fail(TS_ESHAPE, "bf16 attention: a group of 4 RoPE pairs spans three axes (head_dim too small)");
   }
   // algorithmic work: 4 (n+1) d FLOPs per query row (QK^T and PV over the
   // n+1 keys); bytes: the window's q, k, v rows read once, o written once
@@ -416,16 +421,16 @@ ts_status ts_plan_export_rope(const ts_plan* p, int32_t head_dim, float rope_bas
   if (!p || !cos_out || !sin_out) return fail(TS_EINVAL, "null argument");
   if (head_dim <= 0 || head_dim % 2 != 0) return fail(TS_EINVAL, "head_dim must be even and positive");
   std::vector<float> tab;
-  int32_t pairs[3], off[3];
-  tsplan::rope_table(*p, head_dim, rope_base, tab, pairs, off);
+  int32_t pairs[3], off[3], wbase[3], wpairs[3];
+  tsplan::rope_table(*p, head_dim, rope_base, tab, pairs, off, wbase, wpairs);
   const int32_t P = head_dim / 2;
   for (int32_t j = 0; j < p->n; ++j) {
     for (int32_t k = 0; k < P; ++k) {
       const int ax = k < pairs[0] ? 0 : (k < pairs[0] + pairs[1] ? 1 : 2);
-      const int i = k - (ax == 0 ? 0 : (ax == 1 ? pairs[0] : pairs[0] + pairs[1]));
       const int pos = (p->local_pos[j] >> (10 * ax)) & 1023;
-      cos_out[size_t(j) * P + k] = tab[off[ax] + 2 * (size_t(pos) * pairs[ax] + i)];
-      sin_out[size_t(j) * P + k] = tab[off[ax] + 2 * (size_t(pos) * pairs[ax] + i) + 1];
+      const size_t at = off[ax] + 2 * (size_t(pos) * wpairs[ax] + k - wbase[ax]);
+      cos_out[size_t(j) * P + k] = tab[at];
+      sin_out[size_t(j) * P + k] = tab[at + 1];
     }
   }
   return TS_OK;
@@ -444,8 +449,8 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
   if (!p) return fail(TS_EINVAL, "plan is null");
   if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > 256) return fail(TS_EINVAL, "bad head_dim");
   std::vector<float> tab;
-  int32_t pairs[3], off[3];
-  tsplan::rope_table(*p, head_dim, rope_base, tab, pairs, off);
+  int32_t pairs[3], off[3], wbase[3], wpairs[3];
+  tsplan::rope_table(*p, head_dim, rope_base, tab, pairs, off, wbase, wpairs);
   if (tab.size() > 4096) return fail(TS_ESHAPE, "RoPE table exceeds 16 KB (head_dim/2 * tile extent too large)");
   std::vector<int32_t> entry_row(p->n_entries);
   for (int32_t e = 0; e < p->n_entries; ++e) entry_row[e] = p->cover_tile[e] * (p->n + 1) + p->cover_local[e];
@@ -482,6 +487,8 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
   for (int a = 0; a < 3; ++a) {
     p->rope_pairs[a] = pairs[a];
     p->rope_off[a] = off[a];
+    p->rope_wbase[a] = wbase[a];
+    p->rope_wpairs[a] = wpairs[a];
   }
   p->rope_hd = head_dim;
   p->rope_base = rope_base;

@@ -38,6 +38,8 @@ struct AttnP {
   int rope_floats;
   int pairs[3];
   int rope_off[3];
+  int rope_wbase[3];
+  int rope_wpairs[3];
   float scale_log2;  // log2(e) / sqrt(hd)
 };
 
@@ -46,32 +48,20 @@ __device__ __forceinline__ int window_row(const AttnP& p, int t, int i) {
   return t * (p.n + 1) + i;
 }
 
-// (cos, sin) of rotation pair k of a head at the packed tile-local position
-// pos (tau | y<<10 | x<<20): pair k belongs to axis a with index i inside
-// that axis' chunk, stored at tab[rope_off[a] + 2*(pos_a*pairs[a] + i)].
-__device__ __forceinline__ float2 rope_cs(const AttnP& p, const float* tab, int k, int pos) {
-  const int p0 = p.pairs[0], p01 = p.pairs[0] + p.pairs[1];
-  const int ax = k < p0 ? 0 : (k < p01 ? 1 : 2);
-  const int i = k - (ax == 0 ? 0 : (ax == 1 ? p0 : p01));
-  const int np = ax == 0 ? p.pairs[0] : (ax == 1 ? p.pairs[1] : p.pairs[2]);
-  const int off = ax == 0 ? p.rope_off[0] : (ax == 1 ? p.rope_off[1] : p.rope_off[2]);
-  const int ps = (pos >> (10 * ax)) & 1023;
-  return *reinterpret_cast<const float2*>(tab + off + 2 * (ps * np + i));
+// Axis of rotation pair k (pairs are split over t, h, w in contiguous chunks).
+__device__ __forceinline__ int pair_axis(const AttnP& p, int k) {
+  return k < p.pairs[0] ? 0 : (k < p.pairs[0] + p.pairs[1] ? 1 : 2);
 }
+__device__ __forceinline__ int pick3(const int (&v)[3], int a) { return a == 0 ? v[0] : (a == 1 ? v[1] : v[2]); }
 
-// Packed per-pair lookup descriptor: table offset of position 0 (bits 0..13),
-// floats per position step (bits 14..22), axis (bits 24..25).
-__device__ __forceinline__ int rope_desc(const AttnP& p, int k) {
-  const int p0 = p.pairs[0], p01 = p.pairs[0] + p.pairs[1];
-  const int ax = k < p0 ? 0 : (k < p01 ? 1 : 2);
-  const int i = k - (ax == 0 ? 0 : (ax == 1 ? p0 : p01));
-  const int np = ax == 0 ? p.pairs[0] : (ax == 1 ? p.pairs[1] : p.pairs[2]);
-  const int off = ax == 0 ? p.rope_off[0] : (ax == 1 ? p.rope_off[1] : p.rope_off[2]);
-  return (off + 2 * i) | ((2 * np) << 14) | (ax << 24);
-}
-__device__ __forceinline__ float2 rope_at(const float* tab, int desc, int pos) {
-  const int ps = (pos >> (10 * (desc >> 24))) & 1023;
-  return *reinterpret_cast<const float2*>(tab + (desc & 0x3fff) + ps * ((desc >> 14) & 0x1ff));
+// (cos, sin) of rotation pair k of a head at the packed tile-local position
+// pos (tau | y<<10 | x<<20).  Axis a's block of the compact table spans the
+// pairs [rope_wbase[a], rope_wbase[a] + rope_wpairs[a]) per position.
+__device__ __forceinline__ float2 rope_cs(const AttnP& p, const float* tab, int k, int pos) {
+  const int ax = pair_axis(p, k);
+  const int ps = (pos >> (10 * ax)) & 1023;
+  return *reinterpret_cast<const float2*>(tab + pick3(p.rope_off, ax) +
+                                          2 * (ps * pick3(p.rope_wpairs, ax) + k - pick3(p.rope_wbase, ax)));
 }
 
 // ------------------------------------------------------------- fp32 -----
@@ -176,28 +166,44 @@ __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1)
 template <int HD> __device__ __forceinline__ int kswz(int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); }
 __device__ __forceinline__ int vswz(int hd) { return (hd ^ (hd >> 3)) & 7; }
 
-// Table lookup of one 8-dim group (4 rotation pairs of one axis): offset of
-// position 0 in floats, floats per position step, and the axis' bit shift in
-// the packed position.  With every axis holding a multiple of 4 pairs the
-// group's four (cos, sin) pairs are 32 contiguous, 32-byte aligned bytes.
+// Table lookup of one 8-dim group, rotation pairs 4c .. 4c+3.  Segment 0 is
+// the table block of the axis of pair 4c, segment 1 that of pair 4c+3; the
+// first `split` pairs take segment 0 (split = 4 when the group lies in one
+// axis).  In each block the group's four (cos, sin) pairs are 32 contiguous,
+// 32-byte aligned bytes, so a segment is two 16-byte reads.
 struct GroupRope {
-  int off, step, shift;
+  int off0, step0, shift0;
+  int off1, step1, shift1;
+  int split;
 };
 __device__ __forceinline__ GroupRope group_rope(const AttnP& p, int c) {
   const int k = 4 * c;
-  const int p0 = p.pairs[0], p01 = p.pairs[0] + p.pairs[1];
-  const int ax = k < p0 ? 0 : (k < p01 ? 1 : 2);
-  const int i = k - (ax == 0 ? 0 : (ax == 1 ? p0 : p01));
-  const int np = ax == 0 ? p.pairs[0] : (ax == 1 ? p.pairs[1] : p.pairs[2]);
-  const int off = ax == 0 ? p.rope_off[0] : (ax == 1 ? p.rope_off[1] : p.rope_off[2]);
-  return GroupRope{off + 2 * i, 2 * np, 10 * ax};
+  const int a0 = pair_axis(p, k), a1 = pair_axis(p, k + 3);
+  GroupRope g;
+  g.off0 = pick3(p.rope_off, a0) + 2 * (k - pick3(p.rope_wbase, a0));
+  g.step0 = 2 * pick3(p.rope_wpairs, a0);
+  g.shift0 = 10 * a0;
+  g.off1 = pick3(p.rope_off, a1) + 2 * (k - pick3(p.rope_wbase, a1));
+  g.step1 = 2 * pick3(p.rope_wpairs, a1);
+  g.shift1 = 10 * a1;
+  g.split = a0 == a1 ? 4 : (a0 == 0 ? p.pairs[0] : p.pairs[0] + p.pairs[1]) - k;
+  return g;
 }
 
-// Rotate one 8-dim group (4 pairs, bf16) by position `pos`.
-__device__ __forceinline__ bf16x8 rope_group(const float* rope_s, GroupRope gr, int pos, bf16x8 v) {
-  const float* cs = rope_s + gr.off + ((pos >> gr.shift) & 1023) * gr.step;
-  const f32x4 c01 = *reinterpret_cast<const f32x4*>(cs);      // (cos, sin) of pairs 0, 1
-  const f32x4 c23 = *reinterpret_cast<const f32x4*>(cs + 4);  // pairs 2, 3
+// Rotate one 8-dim group (4 pairs, bf16) by position `pos`; each rotated
+// value is rounded to bf16.
+__device__ __forceinline__ bf16x8 rope_group(const float* tab, const GroupRope& gr, int pos, bf16x8 v) {
+  const float* cs = tab + gr.off0 + ((pos >> gr.shift0) & 1023) * gr.step0;
+  f32x4 c01 = *reinterpret_cast<const f32x4*>(cs);      // (cos, sin) of pairs 0, 1
+  f32x4 c23 = *reinterpret_cast<const f32x4*>(cs + 4);  // pairs 2, 3
+  if (gr.split < 4) {  // pairs split .. 3 belong to the next axis
+    const float* cs1 = tab + gr.off1 + ((pos >> gr.shift1) & 1023) * gr.step1;
+    const f32x4 d01 = *reinterpret_cast<const f32x4*>(cs1);
+    const f32x4 d23 = *reinterpret_cast<const f32x4*>(cs1 + 4);
+    if (gr.split == 1) c01 = f32x4{c01[0], c01[1], d01[2], d01[3]};
+    if (gr.split <= 2) c23 = d23;
+    else c23 = f32x4{c23[0], c23[1], d23[2], d23[3]};
+  }
   bf16x8 o;
 #pragma unroll
   for (int q2 = 0; q2 < 4; ++q2) {
@@ -583,6 +589,8 @@ namespace tsk {
 static AttnP make_params(const AttnArgs& a) {
   return AttnP{a.qkv, a.out, a.rows, a.n_union, a.d, a.H, a.n_tiles, a.n, a.local_pos, a.rope, a.rope_floats,
                {a.pairs[0], a.pairs[1], a.pairs[2]}, {a.rope_off[0], a.rope_off[1], a.rope_off[2]},
+               {a.rope_wbase[0], a.rope_wbase[1], a.rope_wbase[2]},
+               {a.rope_wpairs[0], a.rope_wpairs[1], a.rope_wpairs[2]},
                1.4426950408889634f / sqrtf(float(a.hd))};
 }
 

@@ -125,45 +125,50 @@ std::string build(const ts_tiling_desc& d, ts_plan& p) {
 }
 
 // Pairs per axis: contiguous chunks t, h, w; 3D h = w = floor(P/3) and t the
-// rest, 2D h = P/2 and w the rest; when P is a multiple of 4 (and P >= 12 in
-// 3D, P >= 8 in 2D) h and w are rounded to multiples of 4 (3D: nearest,
-// halves up; 2D: down) so each group of 4 pairs (8 dims) lies in one axis.
+// rest, 2D h = floor(P/2) and w the rest.
 void rope_pairs(int32_t ndim, int32_t head_dim, int32_t out[3]) {
   const int32_t P = head_dim / 2;
-  const bool aligned = P % 4 == 0;
   if (ndim == 2) {
-    int32_t h = P / 2;
-    if (aligned && P >= 8) h = 4 * (h / 4);
     out[0] = 0;
-    out[1] = h;
-    out[2] = P - h;
+    out[1] = P / 2;
+    out[2] = P - P / 2;
   } else {
-    int32_t third = P / 3;
-    if (aligned && P >= 12) third = 4 * ((third + 2) / 4);
-    out[0] = P - 2 * third;
-    out[1] = third;
-    out[2] = third;
+    out[0] = P - 2 * (P / 3);
+    out[1] = P / 3;
+    out[2] = P / 3;
   }
 }
 
-void rope_table(const ts_plan& p, int32_t head_dim, float base, std::vector<float>& tab,
-                int32_t pairs[3], int32_t off[3]) {
+void rope_table(const ts_plan& p, int32_t head_dim, float base, std::vector<float>& tab, int32_t pairs[3],
+                int32_t off[3], int32_t wbase[3], int32_t wpairs[3]) {
   rope_pairs(p.desc.ndim, head_dim, pairs);
-  int32_t total = 0;
+  int32_t total = 0, k0 = 0;
   for (int a = 0; a < 3; ++a) {
+    const int32_t k1 = k0 + pairs[a];
+    wbase[a] = pairs[a] ? (k0 / 4) * 4 : 0;
+    wpairs[a] = pairs[a] ? ((k1 + 3) / 4) * 4 - wbase[a] : 0;
     off[a] = total;
-    total += 2 * pairs[a] * p.ext[a];
+    total += 2 * wpairs[a] * p.ext[a];
+    k0 = k1;
   }
+  // identity (cos 1, sin 0) in the window slots of pairs of other axes
   tab.assign(size_t(total), 0.f);
   for (int a = 0; a < 3; ++a)
+    for (int32_t pos = 0; pos < p.ext[a]; ++pos)
+      for (int32_t w = 0; w < wpairs[a]; ++w) tab[off[a] + 2 * (size_t(pos) * wpairs[a] + w)] = 1.f;
+  k0 = 0;
+  for (int a = 0; a < 3; ++a) {
     for (int32_t i = 0; i < pairs[a]; ++i) {
       const double inv = std::pow(double(base), double(-i) / double(pairs[a]));
+      const int32_t w = k0 + i - wbase[a];
       for (int32_t pos = 0; pos < p.ext[a]; ++pos) {
         const double ang = double(pos) * inv;
-        tab[off[a] + 2 * (size_t(pos) * pairs[a] + i)] = float(std::cos(ang));
-        tab[off[a] + 2 * (size_t(pos) * pairs[a] + i) + 1] = float(std::sin(ang));
+        tab[off[a] + 2 * (size_t(pos) * wpairs[a] + w)] = float(std::cos(ang));
+        tab[off[a] + 2 * (size_t(pos) * wpairs[a] + w) + 1] = float(std::sin(ang));
       }
     }
+    k0 += pairs[a];
+  }
 }
 
 }  // namespace tsplan

@@ -32,6 +32,8 @@ struct ts_plan {
   int32_t rope_floats = 0;       // floats in the compact table
   int32_t rope_pairs[3] = {0, 0, 0};
   int32_t rope_off[3] = {0, 0, 0};
+  int32_t rope_wbase[3] = {0, 0, 0};
+  int32_t rope_wpairs[3] = {0, 0, 0};
   bool uploaded = false;
 };
 
@@ -40,9 +42,13 @@ namespace tsplan {
 std::string build(const ts_tiling_desc& desc, ts_plan& p);
 // Pairs per axis for a head size (t, h, w).
 void rope_pairs(int32_t ndim, int32_t head_dim, int32_t out[3]);
-// Compact RoPE table: axis a holds pairs[a] rotation pairs over ext[a]
-// positions; the (cos, sin) of pair i of axis a at position pos sits at
-// tab[off[a] + 2*(pos*pairs[a] + i) + {0, 1}].
-void rope_table(const ts_plan& p, int32_t head_dim, float base, std::vector<float>& tab,
-                int32_t pairs[3], int32_t off[3]);
+// Compact RoPE table, one block per axis.  Axis a owns the global pairs
+// [k0_a, k0_a + pairs[a]); its block covers the window of pairs
+// [wbase[a], wbase[a] + wpairs[a]), that range widened to whole groups of 4
+// pairs (8 dims), so a group's entries are 32-byte aligned and contiguous.
+// The (cos, sin) of global pair k at position pos of axis a sits at
+// tab[off[a] + 2*(pos*wpairs[a] + k - wbase[a]) + {0, 1}]; window slots of
+// pairs that belong to another axis hold the identity (1, 0).
+void rope_table(const ts_plan& p, int32_t head_dim, float base, std::vector<float>& tab, int32_t pairs[3],
+                int32_t off[3], int32_t wbase[3], int32_t wpairs[3]);
 }  // namespace tsplan

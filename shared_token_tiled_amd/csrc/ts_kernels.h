@@ -56,9 +56,10 @@ struct AttnArgs {
   const int* local_pos; // [n] packed tau | y<<10 | x<<20
   const float* rope;    // compact per-axis (cos, sin) table
   int rope_floats;      // its length in floats
-  int pairs[3];         // rotation pairs per axis (t, h, w)
-  int rope_off[3];      // float offset of each axis' block: pair i at position pos of
-                        // axis a is (cos, sin) at rope_off[a] + 2*(pos*pairs[a] + i)
+  int pairs[3];         // rotation pairs per axis (t, h, w), contiguous chunks in that order
+  int rope_off[3];      // float offset of each axis' block; global pair k at position pos
+  int rope_wbase[3];    // of axis a is (cos, sin) at
+  int rope_wpairs[3];   // rope_off[a] + 2*(pos*rope_wpairs[a] + k - rope_wbase[a])
 };
 // fp32: every window row.  bf16: the n tile-token query rows of every window;
 // the global-token row (window row n) is attention_global's.

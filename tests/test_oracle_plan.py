@@ -109,21 +109,24 @@ def test_plan_against_brute_force(grid, tile, stride):
 
 
 def test_rope_pairs_split():
-    assert rope_pairs(3, 128) == (24, 20, 20)
-    assert rope_pairs(3, 64) == (8, 12, 12)
-    assert rope_pairs(3, 32) == (8, 4, 4)
-    assert rope_pairs(3, 16) == (4, 2, 2)     # P < 12: plain thirds
+    assert rope_pairs(3, 128) == (22, 21, 21)
+    assert rope_pairs(3, 64) == (12, 10, 10)
+    assert rope_pairs(3, 32) == (6, 5, 5)
+    assert rope_pairs(3, 16) == (4, 2, 2)
     assert rope_pairs(3, 4) == (2, 0, 0)
     assert rope_pairs(2, 128) == (0, 32, 32)
     assert rope_pairs(2, 64) == (0, 16, 16)
-    assert rope_pairs(2, 40) == (0, 8, 12)
+    assert rope_pairs(2, 40) == (0, 10, 10)
     assert rope_pairs(2, 32) == (0, 8, 8)
     assert rope_pairs(2, 12) == (0, 3, 3)
+    assert rope_pairs(2, 6) == (0, 1, 2)
     for ndim in (2, 3):
-        for hd in (32, 64, 128):
+        for hd in (6, 32, 40, 64, 128):
             c = rope_pairs(ndim, hd)
             assert sum(c) == hd // 2
-            assert all(v % 4 == 0 for v in c)   # groups of 8 dims stay in one axis
+            assert max(c[1:]) - min(c[1:]) <= 1      # h and w balanced
+            if ndim == 3:
+                assert c[0] >= c[1]                  # t takes the remainder
 
 
 @pytest.mark.parametrize("ndim,grid,tile,stride,hd", [
