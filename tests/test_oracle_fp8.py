@@ -87,3 +87,27 @@ def test_tensor_scale_and_fake_quant():
     q, s = fp8.fake_quant(x)
     rel = np.abs(q * s - x) / np.maximum(np.abs(x), 2.0 ** -6 * s)
     assert np.max(rel) <= 2.0 ** -4 + 1e-6
+
+
+def test_fp8_linear_on_exactly_representable_operands():
+    """Operands already on the e4m3 grid times a power-of-two scale quantise
+    without error, so the scaled GEMM must equal the plain product plus bias;
+    a wrong scale product, a transposed operand or a dropped bias fails."""
+    table = fp8.e4m3_decode_table()
+    fin = table[np.isfinite(table)]
+    rng = np.random.default_rng(4)
+    for sx, sw in ((1.0, 1.0), (2.0, 0.25), (0.5, 8.0)):
+        xq = rng.choice(fin, size=(5, 16))
+        wq = rng.choice(fin, size=(7, 16))
+        xq[0, 0], wq[0, 0] = 448.0, -448.0           # absmax 448 -> scale = sx, sw exactly
+        x, w = (xq * sx).astype(np.float32), (wq * sw).astype(np.float32)
+        b = rng.standard_normal(7)
+        assert fp8.tensor_scale(x) == np.float32(sx) and fp8.tensor_scale(w) == np.float32(sw)
+        got = fp8.fp8_linear(x, w, b)
+        ref = x.astype(np.float64) @ w.astype(np.float64).T + b
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-9)
+    # a non-square, non-symmetric case where a transposed operand cannot pass
+    x = (np.arange(12, dtype=np.float32).reshape(3, 4) - 5) * 0.5
+    w = (np.arange(8, dtype=np.float32).reshape(2, 4) + 1)
+    assert np.allclose(fp8.fp8_linear(x, w, np.zeros(2)), fp8.round_e4m3(x / fp8.tensor_scale(x)) *
+                       fp8.tensor_scale(x) @ (fp8.round_e4m3(w / fp8.tensor_scale(w)) * fp8.tensor_scale(w)).T)
