@@ -71,7 +71,9 @@ typedef struct {
   int32_t tile[3];    /* tile extent per axis */
   int32_t stride[3];  /* tile stride per axis (>= 1) */
   int32_t n_global;   /* global tokens per tile; must be 1 */
-  int32_t blend;      /* 0 = linear-ramp w-bar (the only rule implemented) */
+  int32_t blend;      /* 0 = linear-ramp w-bar; 1 = hard stitching (Table 2,
+                         Table S2): w-bar 1 on the covering tile with the largest
+                         float64 ramp, 0 on the others, ties to the lowest tile */
 } ts_tiling_desc;
 
 typedef struct ts_plan ts_plan; /* opaque, library-owned */
@@ -148,7 +150,8 @@ typedef struct {
   const float* w_scale_f8;                    /* [4] */
 } ts_layer_weights;
 
-/* Bytes of workspace the forward calls below need for (model, plan, k). */
+/* Bytes of workspace the forward calls below need for (model, plan, k);
+ * k = -1 gives what ts_merge_once_forward needs (any l). */
 ts_status ts_workspace_size(const ts_model_desc* model, const ts_plan* plan, int32_t k,
                             size_t* bytes);
 
@@ -184,6 +187,18 @@ ts_status ts_stack_forward(const ts_model_desc* model, const ts_layer_weights* l
 ts_status ts_tiled_forward(const ts_model_desc* model, const ts_layer_weights* layers,
                            const ts_plan* plan, const float* x_in, const float* g, float* x_out,
                            float* g_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Merging once at layer l, then continuing per tile (Figure 3b): layers
+ * 0 .. l-1 run per tile from the gathered input, the per-tile states are
+ * merged with w-bar into one state (global rows stay per tile), every tile
+ * is re-gathered from that state (with its own global row), layers l .. L-1
+ * run per tile, and the outputs are merged as in ts_tiled_forward.  l in
+ * 0..n_layers.  Arguments, layouts and errors as ts_stack_forward; the
+ * workspace is ts_workspace_size(model, plan, -1, ...) bytes; the shared
+ * GEMM dtype is not used (every layer runs per tile). */
+ts_status ts_merge_once_forward(const ts_model_desc* model, const ts_layer_weights* layers,
+                                const ts_plan* plan, int32_t l, const float* x_in, const float* g,
+                                float* x_out, float* g_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Per-tensor e4m3 quantisation (Table S5 "V0 + FP8"; OCP e4m3, round to
  * nearest even, saturation at +-448): scale = max|src| / 448 (1 if all zero),

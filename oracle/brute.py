@@ -36,8 +36,10 @@ def brute_tiles(grid, tile, stride):
     return tiles, ext, [s for s, _ in per_axis]
 
 
-def brute_cover(grid, tile, stride):
-    """{grid row p: [(tile t, local j, Fraction w)]}, exact rational weights."""
+def brute_cover(grid, tile, stride, hard=False):
+    """{grid row p: [(tile t, local j, Fraction w)]}, exact rational weights;
+    with ``hard`` the weight is 1 on the tile of largest ramp (lowest index
+    among equal ones) and 0 elsewhere."""
     T, H, W = grid
     tiles, ext, axis_starts = brute_tiles(grid, tile, stride)
 
@@ -68,8 +70,13 @@ def brute_cover(grid, tile, stride):
                         j = (u[0] * ext[1] + u[1]) * ext[2] + u[2]
                         r = ramp(0, st, u[0]) * ramp(1, sh, u[1]) * ramp(2, sw, u[2])
                         ents.append((t, j, r))
-                tot = sum(r for _, _, r in ents)
-                cover[p] = [(t, j, r / tot) for t, j, r in ents]
+                if hard:
+                    top = max(r for _, _, r in ents)
+                    first = min(t for t, _, r in ents if r == top)
+                    cover[p] = [(t, j, Fraction(1 if t == first else 0)) for t, j, _ in ents]
+                else:
+                    tot = sum(r for _, _, r in ents)
+                    cover[p] = [(t, j, r / tot) for t, j, r in ents]
     return cover, tiles, ext
 
 

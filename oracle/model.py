@@ -349,6 +349,22 @@ def tiled_layer_rows(cfg, plan, x, g, p, sel, rope=None):
     return xs, G
 
 
+def merge_once_forward(cfg, plan, x, g, layers, l, rope=None):
+    """Figure 3b: per-tile layers 0 .. l-1, the per-tile states merged once
+    into one state (global rows kept per tile), every tile re-gathered from
+    it with its own global row, per-tile layers l .. L-1, then the merge of
+    the released decoder.  Returns (x_out, g_out) in float64."""
+    rope = rope or Rope(plan, cfg)
+    X = gather_tiles(plan, x, g)
+    for li in range(l):
+        X = [per_tile_layer(Xt, layers[li], cfg, rope) for Xt in X]
+    xs, G = merge(plan, X)
+    X = [np.vstack([xs[plan.tile_rows[t]], G[t][None, :]]) for t in range(plan.n_tiles)]
+    for li in range(l, len(layers)):
+        X = [per_tile_layer(Xt, layers[li], cfg, rope) for Xt in X]
+    return merge(plan, X)
+
+
 def rel_err(got, ref):
     """max |got - ref| / RMS(ref): the parity metric on the union output."""
     ref = np.asarray(ref, dtype=F)

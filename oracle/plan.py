@@ -16,6 +16,10 @@ w-bar.  Readings taken here (listed in the design doc):
 * w-bar: per axis a linear ramp across each overlap with a neighbour
   (lead/trail below), the product over axes, normalised to sum 1 per token;
   computed in float64 in the order written here and rounded once to fp32;
+* hard stitching (Table 2, Table S2: "Hard stitching"; Table 1 caption: the
+  rule for blending an overlap token's tiles): w-bar is 1 on the covering
+  tile with the largest float64 ramp and 0 on the others, ties to the lowest
+  tile index;
 * RoPE: the P = head_dim/2 rotation pairs are split over the axes in
   contiguous chunks (t, then h, then w).  3D: h and w get floor(P/3) pairs
   each and t the rest (head_dim 128: 22, 21, 21; head_dim 64: 12, 10, 10).
@@ -54,7 +58,7 @@ def axis_ramp(starts, L, i, u):
 class Plan:
     """Plain-Python tiling plan for grid (T, H, W)."""
 
-    def __init__(self, grid, tile, stride, n_global=1):
+    def __init__(self, grid, tile, stride, n_global=1, blend="ramp"):
         if n_global != 1:
             raise ValueError("one global token per tile")
         self.grid = tuple(int(v) for v in grid)
@@ -101,17 +105,33 @@ class Plan:
         for t in range(self.n_tiles):
             for j in range(self.tile_tokens):
                 cover[int(rows[t, j])].append((t, j))
+        if blend not in ("ramp", "hard"):
+            raise ValueError("blend must be 'ramp' or 'hard'")
+        self.blend = blend
         ptr = np.zeros(self.n_union + 1, dtype=np.int32)
         ctile, clocal, cw = [], [], []
         for p in range(self.n_union):
             ent = cover[p]
-            total = 0.0
-            for t, j in ent:
-                total = total + ramp[t, j]
-            for t, j in ent:
-                ctile.append(t)
-                clocal.append(j)
-                cw.append(np.float32(ramp[t, j] / total))
+            if blend == "hard":
+                # hard stitching: the whole weight on the covering tile with the
+                # largest ramp (the token lies deepest inside it), ties to the
+                # lowest tile index (ent is in ascending tile order)
+                best = 0
+                for e in range(1, len(ent)):
+                    if ramp[ent[e]] > ramp[ent[best]]:
+                        best = e
+                for e, (t, j) in enumerate(ent):
+                    ctile.append(t)
+                    clocal.append(j)
+                    cw.append(np.float32(1.0 if e == best else 0.0))
+            else:
+                total = 0.0
+                for t, j in ent:
+                    total = total + ramp[t, j]
+                for t, j in ent:
+                    ctile.append(t)
+                    clocal.append(j)
+                    cw.append(np.float32(ramp[t, j] / total))
             ptr[p + 1] = ptr[p] + len(ent)
         self.cover_ptr = ptr
         self.cover_tile = np.array(ctile, dtype=np.int32)

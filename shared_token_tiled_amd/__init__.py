@@ -80,6 +80,8 @@ def lib():
                                                   _VP, _VP, _VP, ctypes.c_size_t, _VP]),
             "ts_tiled_forward": (ctypes.c_int32, [P(ModelDesc), P(LayerWeights), _VP, _VP, _VP, _VP, _VP, _VP,
                                                   ctypes.c_size_t, _VP]),
+            "ts_merge_once_forward": (ctypes.c_int32, [P(ModelDesc), P(LayerWeights), _VP, ctypes.c_int32, _VP,
+                                                       _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
             "ts_fp8_quantize": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_int64, _VP, _VP, _VP,
                                                  ctypes.c_size_t, _VP]),
             "ts_op_gemm": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _VP, _VP, ctypes.c_int32,
@@ -189,6 +191,13 @@ def ts_tiled_forward(model, layers, plan, x_in, g, x_out, g_out, ws, stream=None
     _check(lib().ts_tiled_forward(ctypes.byref(model), arr, plan, _ptr(x_in), _ptr(g), _ptr(x_out),
                                   _ptr(g_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "ts_tiled_forward")
+
+
+def ts_merge_once_forward(model, layers, plan, l, x_in, g, x_out, g_out, ws, stream=None):
+    arr = (LayerWeights * len(layers))(*layers)
+    _check(lib().ts_merge_once_forward(ctypes.byref(model), arr, plan, l, _ptr(x_in), _ptr(g), _ptr(x_out),
+                                       _ptr(g_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "ts_merge_once_forward")
 
 
 def ts_fp8_quantize(src, dst, scale, ws, stream=None):

@@ -341,7 +341,7 @@ ts_status stack_impl(const ts_model_desc* m, const ts_layer_weights* layers, con
   if (per_tile) {
     {
       Scope sc(c.s, "gather", 0.0, double(Mt) * d * 8);
-      TS_HIP(tsk::gather(c.s, x_in, g, (const int*)p->d_tile_rows, p->n_tiles, p->n, d, w.X), "gather");
+      TS_HIP(tsk::gather(c.s, x_in, g, 0, (const int*)p->d_tile_rows, p->n_tiles, p->n, d, w.X), "gather");
     }
     for (int l = 0; l < k; ++l)
       if ((st = run_layer(c, layers[l], w.X, false, w)) != TS_OK) return st;
@@ -364,6 +364,54 @@ ts_status stack_impl(const ts_model_desc* m, const ts_layer_weights* layers, con
     if (g_out) TS_HIP(tsk::copy_f32(c.s, w.xs + size_t(p->n_union) * d, g_out, int64_t(p->n_tiles) * d), "copy g");
   }
   return TS_OK;
+}
+
+// Figure 3b: per-tile layers 0 .. l-1, one merge of the per-tile states
+// into one state (global rows kept per tile), every tile re-gathered from
+// that state (its own global row included), per-tile layers l .. L-1, and
+// the final merge.
+ts_status merge_once_impl(const ts_model_desc* m, const ts_layer_weights* layers, const ts_plan* p, int32_t l,
+                          const float* x_in, const float* g, float* x_out, float* g_out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  ts_status st;
+  if ((st = check_model(m)) != TS_OK) return st;
+  if ((st = check_plan(p, m)) != TS_OK) return st;
+  if (!layers && m->n_layers > 0) return fail(TS_EINVAL, "layers is null");
+  if (l < 0 || l > m->n_layers) return fail(TS_EINVAL, "l must be in 0..n_layers");
+  if (!x_in || !g || !x_out) return fail(TS_EINVAL, "x_in, g and x_out must be non-null");
+  for (int i = 0; i < m->n_layers; ++i)
+    if ((st = check_weights(m, &layers[i], false)) != TS_OK) return st;
+  WS w0 = layout(m, p, true, true, true, nullptr);
+  if ((st = check_ws(ws, ws_bytes, w0.bytes)) != TS_OK) return st;
+  WS w = layout(m, p, true, true, true, (char*)ws);
+  Ctx c{m, p, (hipStream_t)stream};
+  const int d = m->d;
+  const int64_t Mt = int64_t(p->n_tiles) * (p->n + 1);
+  const int64_t Ms = int64_t(p->n_union) + p->n_tiles;
+  const double merge_bytes = (double(p->n_entries + p->n_tiles) + double(Ms)) * d * 4;
+  auto merge = [&](float* mu, float* mg) -> ts_status {
+    Scope sc(c.s, "merge", 0.0, merge_bytes);
+    TS_HIP(tsk::blend(c.s, TS_F32, TS_F32, w.X, d, p->n_union, p->n_tiles, p->n, (const int*)p->d_cover_ptr,
+                      (const int*)p->d_entry_row, (const float*)p->d_cover_w, mu, mg),
+           "merge");
+    return TS_OK;
+  };
+  {
+    Scope sc(c.s, "gather", 0.0, double(Mt) * d * 8);
+    TS_HIP(tsk::gather(c.s, x_in, g, 0, (const int*)p->d_tile_rows, p->n_tiles, p->n, d, w.X), "gather");
+  }
+  for (int i = 0; i < l; ++i)
+    if ((st = run_layer(c, layers[i], w.X, false, w)) != TS_OK) return st;
+  if ((st = merge(w.xs, w.xs + size_t(p->n_union) * d)) != TS_OK) return st;
+  {
+    Scope sc(c.s, "gather", 0.0, double(Mt) * d * 8);
+    TS_HIP(tsk::gather(c.s, w.xs, w.xs + size_t(p->n_union) * d, d, (const int*)p->d_tile_rows, p->n_tiles,
+                       p->n, d, w.X),
+           "re-gather");
+  }
+  for (int i = l; i < m->n_layers; ++i)
+    if ((st = run_layer(c, layers[i], w.X, false, w)) != TS_OK) return st;
+  return merge(x_out, g_out);
 }
 
 }  // namespace
@@ -507,9 +555,10 @@ ts_status ts_workspace_size(const ts_model_desc* m, const ts_plan* p, int32_t k,
   ts_status st;
   if ((st = check_model(m)) != TS_OK) return st;
   if (!p || !bytes) return fail(TS_EINVAL, "plan and bytes must be non-null");
-  if (k < 0 || k > m->n_layers) return fail(TS_EINVAL, "k must be in 0..n_layers");
-  // the larger of what the stack (with k) and a single shared layer need
-  WS a = layout(m, p, true, k > 0, k < m->n_layers, nullptr);
+  if (k < -1 || k > m->n_layers) return fail(TS_EINVAL, "k must be in -1..n_layers");
+  // the larger of what the stack (with k; -1: ts_merge_once_forward, which
+  // holds per-tile and merged states) and a single shared layer need
+  WS a = k < 0 ? layout(m, p, true, true, true, nullptr) : layout(m, p, true, k > 0, k < m->n_layers, nullptr);
   WS b = layout(m, p, false, false, false, nullptr);
   *bytes = std::max(a.bytes, b.bytes);
   return TS_OK;
@@ -533,6 +582,12 @@ ts_status ts_stack_forward(const ts_model_desc* m, const ts_layer_weights* layer
                            int32_t k, const float* x_in, const float* g, float* x_out, float* g_out,
                            void* ws, size_t ws_bytes, void* stream) {
   return stack_impl(m, layers, p, k, x_in, g, x_out, g_out, ws, ws_bytes, stream);
+}
+
+ts_status ts_merge_once_forward(const ts_model_desc* m, const ts_layer_weights* layers, const ts_plan* p,
+                                int32_t l, const float* x_in, const float* g, float* x_out, float* g_out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return merge_once_impl(m, layers, p, l, x_in, g, x_out, g_out, ws, ws_bytes, stream);
 }
 
 ts_status ts_tiled_forward(const ts_model_desc* m, const ts_layer_weights* layers, const ts_plan* p,

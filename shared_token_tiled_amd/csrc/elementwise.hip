@@ -153,14 +153,14 @@ __global__ __launch_bounds__(256) void k_blend(const TIN* __restrict__ in, int d
 
 // ---- per-tile gather at stack entry (tile states = tile rows + global token)
 __global__ __launch_bounds__(256) void k_gather(const float* __restrict__ x_in,
-                                                const float* __restrict__ g,
+                                                const float* __restrict__ g, int64_t g_stride,
                                                 const int* __restrict__ tile_rows, int n_tiles,
                                                 int n, int d, float* __restrict__ X) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n_tiles * (n + 1)) return;
   const int t = r / (n + 1), j = r % (n + 1);
-  const float* src = j < n ? x_in + size_t(tile_rows[size_t(t) * n + j]) * d : g;
+  const float* src = j < n ? x_in + size_t(tile_rows[size_t(t) * n + j]) * d : g + t * g_stride;
   float* dst = X + size_t(r) * d;
   for (int c = lane; c < (d >> 2); c += 64) store4(dst + 4 * c, load4(src + 4 * c));
 }
@@ -285,9 +285,9 @@ hipError_t blend(hipStream_t s, int tin, int tout, const void* in, int d, int n_
   return hipGetLastError();
 }
 
-hipError_t gather(hipStream_t s, const float* x_in, const float* g, const int* tile_rows, int n_tiles,
+hipError_t gather(hipStream_t s, const float* x_in, const float* g, int64_t g_stride, const int* tile_rows, int n_tiles,
                   int n, int d, float* X) {
-  hipLaunchKernelGGL(k_gather, dim3(blocks_for_rows(n_tiles * (n + 1))), dim3(256), 0, s, x_in, g,
+  hipLaunchKernelGGL(k_gather, dim3(blocks_for_rows(n_tiles * (n + 1))), dim3(256), 0, s, x_in, g, g_stride,
                      tile_rows, n_tiles, n, d, X);
   return hipGetLastError();
 }

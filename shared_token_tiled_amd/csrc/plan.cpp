@@ -43,7 +43,7 @@ static double axis_ramp(const std::vector<int32_t>& st, int32_t L, size_t i, int
 std::string build(const ts_tiling_desc& d, ts_plan& p) {
   if (d.ndim != 2 && d.ndim != 3) return "ndim must be 2 or 3";
   if (d.n_global != 1) return "n_global must be 1";
-  if (d.blend != 0) return "only the linear-ramp blend (blend = 0) is implemented";
+  if (d.blend != 0 && d.blend != 1) return "blend must be 0 (linear ramp) or 1 (hard stitching)";
   for (int a = 0; a < 3; ++a) {
     if (d.grid[a] < 1 || d.tile[a] < 1 || d.stride[a] < 1) return "grid, tile and stride must be >= 1";
   }
@@ -115,11 +115,20 @@ std::string build(const ts_tiling_desc& d, ts_plan& p) {
       p.cover_local[e] = j;
     }
   for (int32_t q = 0; q < p.n_union; ++q) {
+    const int32_t e0 = p.cover_ptr[q], e1 = p.cover_ptr[q + 1];
+    auto r_of = [&](int32_t e) { return ramp[size_t(p.cover_tile[e]) * p.n + p.cover_local[e]]; };
+    if (d.blend == 1) {
+      // hard stitching: weight 1 on the covering tile with the largest ramp
+      // (ties to the lowest tile index, the first in the row's list)
+      int32_t best = e0;
+      for (int32_t e = e0 + 1; e < e1; ++e)
+        if (r_of(e) > r_of(best)) best = e;
+      for (int32_t e = e0; e < e1; ++e) p.cover_w[e] = e == best ? 1.f : 0.f;
+      continue;
+    }
     double total = 0.0;
-    for (int32_t e = p.cover_ptr[q]; e < p.cover_ptr[q + 1]; ++e)
-      total = total + ramp[size_t(p.cover_tile[e]) * p.n + p.cover_local[e]];
-    for (int32_t e = p.cover_ptr[q]; e < p.cover_ptr[q + 1]; ++e)
-      p.cover_w[e] = float(ramp[size_t(p.cover_tile[e]) * p.n + p.cover_local[e]] / total);
+    for (int32_t e = e0; e < e1; ++e) total = total + r_of(e);
+    for (int32_t e = e0; e < e1; ++e) p.cover_w[e] = float(r_of(e) / total);
   }
   return "";
 }

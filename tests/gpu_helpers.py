@@ -20,12 +20,13 @@ class Run:
 
     def __init__(self, cfg, layers, k_max=None):
         self.cfg = cfg
-        self.plan = ts.ts_plan_create(cfg["ndim"], cfg["grid"], cfg["tile"], cfg["stride"])
+        self.plan = ts.ts_plan_create(cfg["ndim"], cfg["grid"], cfg["tile"], cfg["stride"],
+                                      blend=1 if cfg.get("blend", "ramp") == "hard" else 0)
         ts.ts_plan_upload(self.plan, cfg["head_dim"], cfg.get("rope_base", 10000.0))
         self.info = ts.ts_plan_get_info(self.plan)
         self.model = ts.model_desc(dict(cfg, n_layers=len(layers)))
         self.tens, self.structs = ts.device_layers(layers, cfg, DEV)
-        need = max(ts.ts_workspace_size(self.model, self.plan, k) for k in range(len(layers) + 1))
+        need = max(ts.ts_workspace_size(self.model, self.plan, k) for k in range(-1, len(layers) + 1))
         self.ws = torch.empty(need, dtype=torch.uint8, device=DEV)
 
     def close(self):
@@ -41,6 +42,15 @@ class Run:
             ts.ts_tiled_forward(self.model, self.structs, self.plan, xi, gi, xo, go, self.ws)
         else:
             ts.ts_stack_forward(self.model, self.structs, self.plan, k, xi, gi, xo, go, self.ws)
+        torch.cuda.synchronize()
+        return xo.cpu().numpy().astype(np.float64), go.cpu().numpy().astype(np.float64)
+
+    def merge_once(self, x, g, l):
+        xi = torch.as_tensor(x, dtype=torch.float32).to(DEV).contiguous()
+        gi = torch.as_tensor(g, dtype=torch.float32).to(DEV).contiguous()
+        xo = torch.empty_like(xi)
+        go = torch.empty(self.info.n_tiles, self.cfg["d"], dtype=torch.float32, device=DEV)
+        ts.ts_merge_once_forward(self.model, self.structs, self.plan, l, xi, gi, xo, go, self.ws)
         torch.cuda.synchronize()
         return xo.cpu().numpy().astype(np.float64), go.cpu().numpy().astype(np.float64)
 

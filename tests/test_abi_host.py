@@ -41,12 +41,13 @@ PLAN_CASES = [(configs.get(n)["ndim"], configs.get(n)["grid"], configs.get(n)["t
 ]
 
 
+@pytest.mark.parametrize("blend", [0, 1])
 @pytest.mark.parametrize("ndim,grid,tile,stride", PLAN_CASES)
-def test_plan_bit_exact_against_oracle(ndim, grid, tile, stride):
-    h = ts.ts_plan_create(ndim, grid, tile, stride)
+def test_plan_bit_exact_against_oracle(ndim, grid, tile, stride, blend):
+    h = ts.ts_plan_create(ndim, grid, tile, stride, blend=blend)
     try:
         info = ts.ts_plan_get_info(h)
-        ref = Plan(grid, tile, stride)
+        ref = Plan(grid, tile, stride, blend=("ramp", "hard")[blend])
         assert (info.n_tiles, info.tile_tokens, info.n_union, info.n_entries, info.max_cover) == \
             (ref.n_tiles, ref.tile_tokens, ref.n_union, ref.n_entries, ref.max_cover)
         assert tuple(info.extent) == ref.extent
@@ -77,6 +78,8 @@ def test_plan_rejects_bad_descriptions(args, msg):
         ts.ts_plan_create(*args)
     with pytest.raises(ts.TileShareError, match="n_global"):
         ts.ts_plan_create(2, (1, 4, 4), (1, 4, 4), (1, 4, 4), n_global=2)
+    with pytest.raises(ts.TileShareError, match="blend"):
+        ts.ts_plan_create(2, (1, 4, 4), (1, 4, 4), (1, 4, 4), blend=2)
 
 
 def _model(**kw):

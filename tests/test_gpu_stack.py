@@ -32,7 +32,7 @@ def reduced(name):
 
 
 def _oracle(cfg, x, g, layers, k):
-    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"], blend=cfg.get("blend", "ramp"))
     return M.stack_forward(cfg, pl, x, g, layers, k)
 
 
@@ -132,3 +132,48 @@ def test_identical_states_blend_to_themselves_on_gpu():
     finally:
         run.close()
     assert max_rel(ts0, base) < 1e-5
+
+
+HARD = [("tiny2d", None, 0), ("minimax_h3", "r", 0), ("minimax_h3", "r", 1), ("vitok4k", "r", 0)]
+
+
+@pytest.mark.parametrize("name,size,k", HARD)
+def test_hard_stitching_stack_against_oracle(name, size, k):
+    """Hard stitching (Table 2 / Table S2): the same kernels with a one-hot
+    w-bar from the plan."""
+    cfg = dict(configs.get(name) if size is None else reduced(name), blend="hard")
+    say(f"hard stitching stack {name} k={k}")
+    x, g, layers = make_inputs(cfg, qk_scale=2.0)
+    ref, gref = _oracle(cfg, x, g, layers, k)
+    run = Run(cfg, layers)
+    try:
+        got, ggot = run.stack(x, g, k)
+    finally:
+        run.close()
+    tol = TOL["fp8" if cfg["gemm_shared"] == "fp8" and k < cfg["n_layers"] else cfg["dtype"]]
+    e, eg = max_rel(got, ref), max_rel(ggot, gref)
+    print(f"  max|err|/rms = {e:.3e} (globals {eg:.3e}), tolerance {tol}")
+    assert e < tol and eg < tol
+
+
+MERGE_ONCE = [("tiny2d", None, 0), ("tiny2d", None, 1), ("minimax_h3", "r", 1), ("minimax_h3", "r", 2),
+              ("small_video", "r", 1), ("vitok4k", "r", 1)]
+
+
+@pytest.mark.parametrize("name,size,l", MERGE_ONCE)
+def test_merge_once_against_oracle(name, size, l):
+    """Figure 3b: merge the per-tile states once at layer l, then continue per tile."""
+    cfg = configs.get(name) if size is None else reduced(name)
+    say(f"merge once {name} l={l}")
+    x, g, layers = make_inputs(cfg, qk_scale=2.0)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    ref, gref = M.merge_once_forward(cfg, pl, x, g, layers, l)
+    run = Run(cfg, layers)
+    try:
+        got, ggot = run.merge_once(x, g, l)
+    finally:
+        run.close()
+    tol = TOL[cfg["dtype"]]
+    e, eg = max_rel(got, ref), max_rel(ggot, gref)
+    print(f"  max|err|/rms = {e:.3e} (globals {eg:.3e}), tolerance {tol}")
+    assert e < tol and eg < tol

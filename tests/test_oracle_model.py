@@ -337,3 +337,53 @@ def test_rows_functions_refuse_fp8():
     G = np.tile(g[None].astype(np.float64), (pl.n_tiles, 1))
     with pytest.raises(ValueError):
         M.shared_layer_rows(x, G, layers[0], cfg, pl, M.Rope(pl, cfg), [0])
+
+
+# --- merging once at layer l, then per tile (Figure 3b) ----------------------
+
+@pytest.mark.parametrize("ndim", [2, 3])
+def test_merge_once_at_the_ends_is_the_tiled_decoder(ndim):
+    """Merging at l = L merges the already-final states (a second merge of
+    identical per-tile copies, which w-bar summing to 1 leaves unchanged);
+    merging at l = 0 merges copies of the input.  Both equal the released
+    tiled decoder up to the fp32 rounding of w-bar."""
+    if ndim == 2:
+        cfg = tiny_cfg(layers=3)
+    else:
+        cfg = tiny_cfg(ndim=3, norm="rms", qk=True, grid=(3, 5, 6), tile=(2, 3, 4), stride=(1, 2, 3), layers=3)
+    x, g, layers = make_inputs(cfg, qk_scale=2.0)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    base, gbase = M.tiled_forward(cfg, pl, x, g, layers)
+    for l in (0, 3):
+        got, gg = M.merge_once_forward(cfg, pl, x, g, layers, l)
+        assert M.rel_err(got, base) < 1e-6 and M.rel_err(gg, gbase) < 1e-6
+
+
+def test_merge_once_without_overlap_is_the_tiled_decoder():
+    cfg = tiny_cfg(grid=(1, 4, 8), tile=(1, 4, 4), stride=(1, 4, 4), layers=3)
+    x, g, layers = make_inputs(cfg)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    base, _ = M.tiled_forward(cfg, pl, x, g, layers)
+    for l in range(4):
+        got, _ = M.merge_once_forward(cfg, pl, x, g, layers, l)
+        assert np.array_equal(got, base)
+
+
+def test_merge_once_in_the_middle_differs_and_keeps_global_rows_per_tile():
+    cfg = tiny_cfg(layers=3)
+    x, g, layers = make_inputs(cfg, qk_scale=3.0)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    base, _ = M.tiled_forward(cfg, pl, x, g, layers)
+    got, gg = M.merge_once_forward(cfg, pl, x, g, layers, 1)
+    assert 0 < M.rel_err(got, base) < 1.0
+    assert gg.shape == (pl.n_tiles, cfg["d"]) and not np.allclose(gg[0], gg[1])
+    # by hand: the merged state re-enters every tile
+    rope = M.Rope(pl, cfg)
+    X = M.gather_tiles(pl, x, g)
+    X = [M.per_tile_layer(Xt, layers[0], cfg, rope) for Xt in X]
+    xs, G = M.merge(pl, X)
+    X2 = [np.vstack([xs[pl.tile_rows[t]], G[t][None]]) for t in range(pl.n_tiles)]
+    for li in (1, 2):
+        X2 = [M.per_tile_layer(Xt, layers[li], cfg, rope) for Xt in X2]
+    ref, gref = M.merge(pl, X2)
+    assert np.array_equal(got, ref) and np.array_equal(gg, gref)

@@ -156,3 +156,55 @@ def test_rope_tables_against_complex_exponential(ndim, grid, tile, stride, hd):
             s_ab = np.real(np.vdot(zc[b] * k, zc[a] * q))
             rel = np.exp(1j * (pos[a] - pos[b]) * freqs)
             assert math.isclose(s_ab, np.real(np.vdot(k, rel * q)), rel_tol=0, abs_tol=1e-5)
+
+
+# --- hard stitching (Table 2 / Table S2 "Hard stitching") --------------------
+
+@pytest.mark.parametrize("grid,tile,stride", SMALL + [((3, 9, 10), (2, 5, 5), (1, 3, 3)),
+                                                      ((2, 9, 9), (2, 6, 6), (1, 4, 5))])
+def test_hard_stitching_against_brute_force(grid, tile, stride):
+    """One-hot w-bar on the tile of largest ramp, ties to the lowest index, in
+    exact rational arithmetic; the maps are those of the ramp plan."""
+    pl = Plan(grid, tile, stride, blend="hard")
+    soft = Plan(grid, tile, stride)
+    cover, _, _ = brute_cover(grid, tile, stride, hard=True)
+    assert np.array_equal(pl.cover_ptr, soft.cover_ptr)
+    assert np.array_equal(pl.cover_tile, soft.cover_tile)
+    assert np.array_equal(pl.cover_local, soft.cover_local)
+    for p in range(pl.n_union):
+        got = pl.cover_of(p)
+        exp = cover[p]
+        assert [(t, j) for t, j, _ in got] == [(t, j) for t, j, _ in exp]
+        assert [w for _, _, w in got] == [float(w) for _, _, w in exp]
+        assert sum(w for _, _, w in got) == 1.0
+
+
+def test_tiny2d_hard_stitching_splits_the_band_in_the_middle():
+    """Columns 8..15 are covered by both tiles with ramps (16-c)/9 (tile 0)
+    and (c-7)/9 (tile 1): columns 8..11 go to tile 0, 12..15 to tile 1."""
+    pl = Plan((1, 16, 24), (1, 16, 16), (1, 8, 8), blend="hard")
+    for y in range(16):
+        for c in range(24):
+            ent = pl.cover_of(y * 24 + c)
+            owner = [t for t, _, w in ent if w == 1.0]
+            assert len(owner) == 1 and all(w in (0.0, 1.0) for _, _, w in ent)
+            assert owner[0] == (0 if c <= 11 else 1)
+
+
+def test_hard_stitching_tie_goes_to_lowest_tile():
+    """An even overlap of 2 columns (tile 4, stride 2): column 2 of the grid has
+    ramps 2/3 (tile 0, trailing) and 1/3 (tile 1, leading), column 3 has 1/3 and
+    2/3; with overlap 1 (tile 3, stride 2) the shared column has 1/2 and 1/2,
+    a tie, and goes to the lower tile."""
+    pl = Plan((1, 1, 5), (1, 1, 3), (1, 1, 2), blend="hard")   # starts 0, 2; overlap 1 at column 2
+    ent = pl.cover_of(2)
+    assert [t for t, _, _ in ent] == [0, 1]
+    assert [w for _, _, w in ent] == [1.0, 0.0]
+    pl2 = Plan((1, 1, 6), (1, 1, 4), (1, 1, 2), blend="hard")  # starts 0, 2; overlap 2 at columns 2, 3
+    assert [w for _, _, w in pl2.cover_of(2)] == [1.0, 0.0]
+    assert [w for _, _, w in pl2.cover_of(3)] == [0.0, 1.0]
+
+
+def test_blend_rule_is_validated():
+    with pytest.raises(ValueError):
+        Plan((1, 4, 4), (1, 4, 4), (1, 4, 4), blend="soft")
