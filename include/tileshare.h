@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define TS_ABI_VERSION 1
+#define TS_ABI_VERSION 2
 
 typedef int32_t ts_status;
 #define TS_OK 0
@@ -128,7 +128,17 @@ typedef struct {
   int32_t act_dtype;  /* TS_F32 or TS_BF16: GEMM operands and attention */
   int32_t gemm_dtype_shared; /* act_dtype, or TS_FP8E4M3 (act_dtype bf16) for
                                 the GEMMs of shared layers */
+  /* FP8 scope (Table S2 "FP8 MLP layers only", "TileShare-4 + FP8"; Table S5
+   * "V0 + FP8"), used when gemm_dtype_shared is TS_FP8E4M3: */
+  int32_t fp8_gemms;    /* which GEMMs run in e4m3: TS_FP8_QKV | TS_FP8_OUT |
+                           TS_FP8_FC1 | TS_FP8_FC2; 0 = all four */
+  int32_t fp8_per_tile; /* 1: per-tile layers (and the tiled decoder) use the
+                           same fp8 GEMMs; 0: only shared layers */
 } ts_model_desc;
+#define TS_FP8_QKV 1
+#define TS_FP8_OUT 2
+#define TS_FP8_FC1 4
+#define TS_FP8_FC2 8
 
 /* Device pointers of one pre-norm block (Table S1 order):
  * x += W_o Attn(Norm1(x)) + b_o;  x += W_2 GELU(W_1 Norm2(x) + b_1) + b_2,

@@ -61,6 +61,28 @@ def linear(x, w, b, fp8=False):
     return x @ w.astype(F).T + b.astype(F)
 
 
+ALL_GEMMS = ("qkv", "out", "fc1", "fc2")
+
+
+def f8(fp8, gemm):
+    """Whether GEMM `gemm` runs in fp8: ``fp8`` is a bool (all four GEMMs) or
+    a collection of GEMM names."""
+    if isinstance(fp8, bool):
+        return fp8
+    return gemm in fp8
+
+
+def fp8_scope(cfg, shared):
+    """The fp8 GEMMs of a shared (or per-tile) layer.  Table S2 names "FP8 MLP
+    layers only" and "TileShare-4 + FP8", Table S5 "V0 + FP8"; the pages fix
+    neither the GEMMs nor the layers, so the configuration states them:
+    "fp8_gemms" (default all four) in shared layers, and in per-tile layers
+    too when "fp8_per_tile" is set."""
+    if cfg.get("gemm_shared") != "fp8" or not (shared or cfg.get("fp8_per_tile", False)):
+        return ()
+    return tuple(cfg.get("fp8_gemms") or ALL_GEMMS)
+
+
 def rope_rotate(x, cos, sin):
     """Rotate consecutive pairs (2k, 2k+1) of x [n, hd] by the per-row angles."""
     a = x[:, 0::2]
@@ -91,7 +113,7 @@ def head_rms_norm(z, gain, cfg):
 def qkv_heads(h, p, cfg, fp8=False):
     """QKV projection and per-head QK-RMSNorm, once per row of h."""
     d = cfg["d"]
-    qkv = linear(h, p["w_qkv"], p["b_qkv"], fp8)
+    qkv = linear(h, p["w_qkv"], p["b_qkv"], f8(fp8, "qkv"))
     q, k, v = qkv[:, :d].copy(), qkv[:, d:2 * d].copy(), qkv[:, 2 * d:].copy()
     if cfg["qk_norm"]:
         q = head_rms_norm(q, p["q_g"], cfg)
@@ -118,8 +140,8 @@ def tile_attention(q, k, v, cos_t, sin_t, cfg):
 
 
 def mlp(x, p, cfg, fp8=False):
-    hid = gelu(linear(x, p["w_1"], p["b_1"], fp8))
-    return linear(hid, p["w_2"], p["b_2"], fp8)
+    hid = gelu(linear(x, p["w_1"], p["b_1"], f8(fp8, "fc1")))
+    return linear(hid, p["w_2"], p["b_2"], f8(fp8, "fc2"))
 
 
 class Rope:
@@ -141,6 +163,23 @@ def per_tile_layer(X, p, cfg, rope):
     X = X + linear(o, p["w_o"], p["b_o"])
     X = X + mlp(norm(X, p, "norm2", cfg), p, cfg)
     return X
+
+
+def per_tile_layers(X, p, cfg, rope, fp8=()):
+    """The released block on every tile, the tiles batched as one operand
+    per GEMM (Table S5 "V0, batched"): equal to per_tile_layer on each tile,
+    except that fp8 GEMMs (``fp8``) take one per-tensor scale over all
+    tiles' rows."""
+    if not fp8:
+        return [per_tile_layer(Xt, p, cfg, rope) for Xt in X]
+    n1 = X[0].shape[0]
+    allx = np.vstack(X)
+    q, k, v = qkv_heads(norm(allx, p, "norm1", cfg), p, cfg, fp8)
+    o = np.vstack([tile_attention(q[t * n1:(t + 1) * n1], k[t * n1:(t + 1) * n1], v[t * n1:(t + 1) * n1],
+                                  rope.cos, rope.sin, cfg) for t in range(len(X))])
+    allx = allx + linear(o, p["w_o"], p["b_o"], f8(fp8, "out"))
+    allx = allx + mlp(norm(allx, p, "norm2", cfg), p, cfg, fp8)
+    return [allx[t * n1:(t + 1) * n1] for t in range(len(X))]
 
 
 def blend(plan, per_tile_rows):
@@ -172,11 +211,11 @@ def shared_layer(x, G, p, cfg, plan, rope, fp8=False, blend_after_out=False):
         rows = np.concatenate([plan.tile_rows[t].astype(np.int64), [plan.n_union + t]])
         outs.append(tile_attention(q[rows], k[rows], v[rows], rope.cos, rope.sin, cfg))
     if blend_after_out:
-        proj = [linear(o, p["w_o"], p["b_o"], fp8) for o in outs]
+        proj = [linear(o, p["w_o"], p["b_o"], f8(fp8, "out")) for o in outs]
         delta = np.vstack([blend(plan, proj), np.stack([pr[n] for pr in proj])])
     else:
         a = np.vstack([blend(plan, outs), np.stack([o[n] for o in outs])])
-        delta = linear(a, p["w_o"], p["b_o"], fp8)
+        delta = linear(a, p["w_o"], p["b_o"], f8(fp8, "out"))
     xa = xa + delta
     xa = xa + mlp(norm(xa, p, "norm2", cfg), p, cfg, fp8)
     return xa[: plan.n_union], xa[plan.n_union:]
@@ -202,17 +241,16 @@ def stack_forward(cfg, plan, x, g, layers, k, rope=None):
     """
     rope = rope or Rope(plan, cfg)
     L = len(layers)
-    fp8 = cfg.get("gemm_shared") == "fp8"
     if k > 0:
         X = gather_tiles(plan, x, g)
         for li in range(k):
-            X = [per_tile_layer(Xt, layers[li], cfg, rope) for Xt in X]
+            X = per_tile_layers(X, layers[li], cfg, rope, fp8_scope(cfg, False))
         xs, G = merge(plan, X)
     else:
         xs = x.astype(F)
         G = np.tile(g.astype(F)[None, :], (plan.n_tiles, 1))
     for li in range(k, L):
-        xs, G = shared_layer(xs, G, layers[li], cfg, plan, rope, fp8=fp8)
+        xs, G = shared_layer(xs, G, layers[li], cfg, plan, rope, fp8=fp8_scope(cfg, True))
     return xs, G
 
 
@@ -220,6 +258,11 @@ def tiled_forward(cfg, plan, x, g, layers, rope=None):
     """Released overlapping-tile decoding, tiles outermost: every tile runs the
     whole stack on its own window, then the outputs are blended with w-bar."""
     rope = rope or Rope(plan, cfg)
+    if fp8_scope(cfg, False):   # fp8 scales span the batch of tiles
+        X = gather_tiles(plan, x, g)
+        for p in layers:
+            X = per_tile_layers(X, p, cfg, rope, fp8_scope(cfg, False))
+        return merge(plan, X)
     outs = []
     for t in range(plan.n_tiles):
         Xt = np.vstack([x[plan.tile_rows[t]].astype(F), g.astype(F)[None, :]])
@@ -355,13 +398,14 @@ def merge_once_forward(cfg, plan, x, g, layers, l, rope=None):
     it with its own global row, per-tile layers l .. L-1, then the merge of
     the released decoder.  Returns (x_out, g_out) in float64."""
     rope = rope or Rope(plan, cfg)
+    scope = fp8_scope(cfg, False)
     X = gather_tiles(plan, x, g)
     for li in range(l):
-        X = [per_tile_layer(Xt, layers[li], cfg, rope) for Xt in X]
+        X = per_tile_layers(X, layers[li], cfg, rope, scope)
     xs, G = merge(plan, X)
     X = [np.vstack([xs[plan.tile_rows[t]], G[t][None, :]]) for t in range(plan.n_tiles)]
     for li in range(l, len(layers)):
-        X = [per_tile_layer(Xt, layers[li], cfg, rope) for Xt in X]
+        X = per_tile_layers(X, layers[li], cfg, rope, scope)
     return merge(plan, X)
 
 

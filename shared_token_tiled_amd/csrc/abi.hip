@@ -94,12 +94,20 @@ ts_status check_model(const ts_model_desc* m) {
       return fail(TS_ESHAPE, "bf16 attention supports head_dim 64 or 128");
     if (m->gemm_dtype_shared != TS_BF16 && m->gemm_dtype_shared != TS_FP8E4M3)
       return fail(TS_EDTYPE, "bf16 models need bf16 or fp8 shared GEMMs");
+    if (m->fp8_gemms < 0 || m->fp8_gemms > 15) return fail(TS_EINVAL, "fp8_gemms must be a mask of TS_FP8_* bits");
+    if (m->fp8_per_tile != 0 && m->fp8_per_tile != 1) return fail(TS_EINVAL, "fp8_per_tile must be 0 or 1");
     if (m->gemm_dtype_shared == TS_FP8E4M3 && (m->d % 128 != 0 || m->mlp_hidden % 128 != 0))
       return fail(TS_ESHAPE, "fp8 GEMMs need d and mlp_hidden multiples of 128");
   } else {
     return fail(TS_EDTYPE, "act_dtype must be TS_F32 or TS_BF16");
   }
   return TS_OK;
+}
+
+// fp8 scope: mask of the GEMMs that run in e4m3 in a shared (or per-tile) layer
+int fp8_mask(const ts_model_desc* m, bool shared) {
+  if (m->gemm_dtype_shared != TS_FP8E4M3 || !(shared || m->fp8_per_tile)) return 0;
+  return m->fp8_gemms ? m->fp8_gemms : (TS_FP8_QKV | TS_FP8_OUT | TS_FP8_FC1 | TS_FP8_FC2);
 }
 
 ts_status check_weights(const ts_model_desc* m, const ts_layer_weights* w, bool shared) {
@@ -109,9 +117,10 @@ ts_status check_weights(const ts_model_desc* m, const ts_layer_weights* w, bool 
     return fail(TS_EINVAL, "a required weight pointer is null");
   if (m->norm == 0 && (!w->norm1_b || !w->norm2_b)) return fail(TS_EINVAL, "LayerNorm needs norm biases");
   if (m->qk_norm && (!w->q_g || !w->k_g)) return fail(TS_EINVAL, "QK-norm needs q_g and k_g");
-  if (shared && m->gemm_dtype_shared == TS_FP8E4M3 &&
-      (!w->w_qkv_f8 || !w->w_o_f8 || !w->w_1_f8 || !w->w_2_f8 || !w->w_scale_f8))
-    return fail(TS_EINVAL, "fp8 shared layers need the e4m3 weights and their scales");
+  const int f8 = fp8_mask(m, shared);
+  if (f8 && (!w->w_scale_f8 || ((f8 & TS_FP8_QKV) && !w->w_qkv_f8) || ((f8 & TS_FP8_OUT) && !w->w_o_f8) ||
+             ((f8 & TS_FP8_FC1) && !w->w_1_f8) || ((f8 & TS_FP8_FC2) && !w->w_2_f8)))
+    return fail(TS_EINVAL, "fp8 GEMMs need their e4m3 weights and the weight scales");
   return TS_OK;
 }
 
@@ -160,7 +169,8 @@ WS layout(const ts_model_desc* m, const ts_plan* p, bool states, bool per_tile, 
   w.h = take(size_t(Mmax * d * ab));
   w.big = take(size_t(Mmax * wide * ab));
   w.o = take(size_t(Mt * d * ab));
-  if (m->gemm_dtype_shared == TS_FP8E4M3) w.q8 = (uint8_t*)take(size_t(Ms * std::max<int64_t>(d, m->mlp_hidden)));
+  if (m->gemm_dtype_shared == TS_FP8E4M3)
+    w.q8 = (uint8_t*)take(size_t((m->fp8_per_tile ? Mmax : Ms) * std::max<int64_t>(d, m->mlp_hidden)));
   w.bytes = off;
   return w;
 }
@@ -268,7 +278,7 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
   const int64_t Ms = int64_t(p->n_union) + p->n_tiles;
   const int64_t M = shared ? Ms : Mt;
   const int d = m->d, H = m->n_heads, hd = m->head_dim, dm = m->mlp_hidden;
-  const bool f8 = shared && m->gemm_dtype_shared == TS_FP8E4M3;
+  const int f8 = fp8_mask(m, shared);
   const bool rms = m->norm == 1;
   ts_status st;
 
@@ -276,7 +286,7 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
     Scope sc(c.s, "norm", 0.0, double(M * d) * (4 + ab));
     TS_HIP(tsk::norm(c.s, act, rms, x, int(M), d, w.norm1_g, w.norm1_b, m->eps, ws.h), "norm1");
   }
-  if ((st = proj(c, ws, f8, "qkv", tsk::EPI_BIAS, ws.h, M, 3 * d, d, w.w_qkv, w.w_qkv_f8,
+  if ((st = proj(c, ws, (f8 & TS_FP8_QKV) != 0, "qkv", tsk::EPI_BIAS, ws.h, M, 3 * d, d, w.w_qkv, w.w_qkv_f8,
                  w.w_scale_f8 ? w.w_scale_f8 + 0 : nullptr, w.b_qkv, ws.big)) != TS_OK)
     return st;
   if (m->qk_norm) {
@@ -293,17 +303,17 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
            "blend");
     aout = ws.h;
   }
-  if ((st = proj(c, ws, f8, "out", tsk::EPI_RESID, aout, M, d, d, w.w_o, w.w_o_f8,
+  if ((st = proj(c, ws, (f8 & TS_FP8_OUT) != 0, "out", tsk::EPI_RESID, aout, M, d, d, w.w_o, w.w_o_f8,
                  w.w_scale_f8 ? w.w_scale_f8 + 1 : nullptr, w.b_o, x)) != TS_OK)
     return st;
   {
     Scope sc(c.s, "norm", 0.0, double(M * d) * (4 + ab));
     TS_HIP(tsk::norm(c.s, act, rms, x, int(M), d, w.norm2_g, w.norm2_b, m->eps, ws.h), "norm2");
   }
-  if ((st = proj(c, ws, f8, "fc1", tsk::EPI_BIAS_GELU, ws.h, M, dm, d, w.w_1, w.w_1_f8,
+  if ((st = proj(c, ws, (f8 & TS_FP8_FC1) != 0, "fc1", tsk::EPI_BIAS_GELU, ws.h, M, dm, d, w.w_1, w.w_1_f8,
                  w.w_scale_f8 ? w.w_scale_f8 + 2 : nullptr, w.b_1, ws.big)) != TS_OK)
     return st;
-  if ((st = proj(c, ws, f8, "fc2", tsk::EPI_RESID, ws.big, M, d, dm, w.w_2, w.w_2_f8,
+  if ((st = proj(c, ws, (f8 & TS_FP8_FC2) != 0, "fc2", tsk::EPI_RESID, ws.big, M, d, dm, w.w_2, w.w_2_f8,
                  w.w_scale_f8 ? w.w_scale_f8 + 3 : nullptr, w.b_2, x)) != TS_OK)
     return st;
   return TS_OK;

@@ -177,3 +177,32 @@ def test_merge_once_against_oracle(name, size, l):
     e, eg = max_rel(got, ref), max_rel(ggot, gref)
     print(f"  max|err|/rms = {e:.3e} (globals {eg:.3e}), tolerance {tol}")
     assert e < tol and eg < tol
+
+
+FP8_SCOPE = [
+    # (k, fp8 GEMMs, per-tile layers too): the tiled decoder with fp8 MLPs
+    # ("FP8 MLP layers only"), TileShare with fp8 MLPs in every layer, and
+    # TileShare with all four GEMMs fp8 in shared layers only
+    (3, ("fc1", "fc2"), True),
+    (1, ("fc1", "fc2"), True),
+    (1, ("qkv", "out", "fc1", "fc2"), False),
+    (0, ("out", "fc2"), False),
+]
+
+
+@pytest.mark.parametrize("k,gemms,per_tile", FP8_SCOPE)
+def test_fp8_scope_against_oracle(k, gemms, per_tile):
+    """Table S2 ("FP8 MLP layers only", "TileShare-4 + FP8") and Table S5
+    ("V0 + FP8"): which GEMMs run in e4m3, and whether per-tile layers do."""
+    cfg = dict(reduced("minimax_h3_fp8"), fp8_gemms=gemms, fp8_per_tile=per_tile)
+    say(f"fp8 scope k={k} gemms={gemms} per_tile={per_tile}")
+    x, g, layers = make_inputs(cfg)
+    ref, gref = _oracle(cfg, x, g, layers, k)
+    run = Run(cfg, layers)
+    try:
+        got, ggot = run.stack(x, g, k)
+    finally:
+        run.close()
+    e, eg = max_rel(got, ref), max_rel(ggot, gref)
+    print(f"  max|err|/rms = {e:.3e} (globals {eg:.3e}), tolerance {TOL['fp8']}")
+    assert e < TOL["fp8"] and eg < TOL["fp8"]

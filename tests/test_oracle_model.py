@@ -387,3 +387,38 @@ def test_merge_once_in_the_middle_differs_and_keeps_global_rows_per_tile():
         X2 = [M.per_tile_layer(Xt, layers[li], cfg, rope) for Xt in X2]
     ref, gref = M.merge(pl, X2)
     assert np.array_equal(got, ref) and np.array_equal(gg, gref)
+
+
+# --- fp8 scope ------------------------------------------------------------------
+
+def test_fp8_scope_selects_gemms_and_layers():
+    cfg = dict(tiny_cfg(), gemm_shared="fp8")
+    assert M.fp8_scope(cfg, True) == M.ALL_GEMMS and M.fp8_scope(cfg, False) == ()
+    cfg2 = dict(cfg, fp8_gemms=("fc1", "fc2"), fp8_per_tile=True)
+    assert M.fp8_scope(cfg2, True) == ("fc1", "fc2") == M.fp8_scope(cfg2, False)
+    assert M.fp8_scope(dict(tiny_cfg(), fp8_per_tile=True), False) == ()
+    assert M.f8(True, "qkv") and not M.f8(False, "qkv")
+    assert M.f8(("fc1",), "fc1") and not M.f8(("fc1",), "out")
+
+
+def test_batched_per_tile_layers_equal_per_tile_layers_in_bf16_and_fp8():
+    """Without fp8 the batched form is the per-tile block row for row; with fp8
+    it quantises each GEMM operand once over all tiles: a per-tile call with the
+    scales of the batch gives the same rows."""
+    cfg = tiny_cfg(ndim=3, norm="rms", qk=True, grid=(3, 5, 6), tile=(2, 3, 4), stride=(1, 2, 3), layers=1)
+    x, g, layers = make_inputs(cfg, qk_scale=2.0)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    rope = M.Rope(pl, cfg)
+    X = M.gather_tiles(pl, x, g)
+    a = M.per_tile_layers(X, layers[0], cfg, rope)
+    for t in range(pl.n_tiles):
+        assert np.allclose(a[t], M.per_tile_layer(X[t], layers[0], cfg, rope), atol=1e-12, rtol=0)
+    # MLP-only fp8 on a batch of two identical tiles equals fp8 on one tile
+    # (absmax and hence scales are unchanged by duplicating rows)
+    Y = [X[0], X[0].copy()]
+    b = M.per_tile_layers(Y, layers[0], cfg, rope, ("fc1", "fc2"))
+    c = M.per_tile_layers([X[0]], layers[0], cfg, rope, ("fc1", "fc2"))
+    assert np.allclose(b[0], c[0], atol=1e-12, rtol=0) and np.allclose(b[1], c[0], atol=1e-12, rtol=0)
+    # and the MLP-only fp8 result differs from bf16 by a quantisation-sized amount
+    e = M.rel_err(c[0], a[0])
+    assert 1e-4 < e < 0.2
