@@ -81,18 +81,22 @@ def cpu_baseline(cfg, k):
     pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
     x, g, layers = make_inputs(cfg, n_layers=1)
     rope = M.Rope(pl, cfg)
-    X = M.gather_tiles(pl, x, g)[0]
-    t0 = time.perf_counter()
-    M.per_tile_layer(X, layers[0], cfg, rope)
-    dt = time.perf_counter() - t0
+    X = M.gather_tiles(pl, x, g)
+    # one per-tile block on successive tile windows until about 10 s of CPU work
+    dt, windows = 0.0, 0
+    while windows < pl.n_tiles and dt < 10.0:
+        t0 = time.perf_counter()
+        M.per_tile_layer(X[windows], layers[0], cfg, rope)
+        dt += time.perf_counter() - t0
+        windows += 1
     d, n1 = cfg["d"], pl.tile_tokens + 1
     lin = 2.0 * (3 * d * d + d * d + 2 * d * cfg["mlp_hidden"])
-    sample_flops = lin * n1 + 4.0 * n1 * n1 * d
+    sample_flops = windows * (lin * n1 + 4.0 * n1 * n1 * d)
     total = decode_flops(cfg, pl, k)
     est = dt * total / sample_flops
     return {"value": pl.n_union / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one per-tile block of {cfg['name']} on one tile window ({n1} rows, d={d}), float64 numpy, "
-                      f"{dt:.2f} s for {sample_flops / 1e12:.3f} TFLOP; scaled by FLOPs to the whole "
+            "sample": f"one per-tile block of {cfg['name']} on {windows} tile window(s) ({n1} rows each, d={d}), "
+                      f"float64 numpy, {dt:.2f} s for {sample_flops / 1e12:.3f} TFLOP; scaled by FLOPs to the whole "
                       f"TileShare-{k} decode ({total / 1e12:.1f} TFLOP)"}
 
 
@@ -136,6 +140,13 @@ def main():
     ap.add_argument("--k", type=int, default=None, help="per-tile depth (default: the config's TileShare-k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline", action="store_true", help="skip timing the tiled baseline")
+    ap.add_argument("--blend", choices=("ramp", "hard"), default="ramp",
+                    help="w-bar rule: linear ramps (default) or hard stitching")
+    ap.add_argument("--merge-once", type=int, default=None, metavar="L",
+                    help="time merge-once-at-layer-L-then-per-tile instead of TileShare-k")
+    ap.add_argument("--fp8-gemms", default=None,
+                    help="comma list of the fp8 GEMMs (qkv,out,fc1,fc2) for fp8 configurations")
+    ap.add_argument("--fp8-per-tile", action="store_true", help="fp8 GEMMs in per-tile layers too")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path's sharding across "
@@ -147,24 +158,32 @@ def main():
     from synth import configs
 
     cfg = configs.get(args.config)
+    if args.fp8_gemms:
+        cfg["fp8_gemms"] = tuple(args.fp8_gemms.split(","))
+    cfg["fp8_per_tile"] = args.fp8_per_tile
     k = cfg["k_values"][0] if args.k is None else args.k
     L = cfg["n_layers"]
     dev = "cuda"
     torch.cuda.set_device(0)
-    log(f"bench: {args.config} TileShare-{k} vs tiled, steps={args.steps} warmup={args.warmup}")
-    plan = ts.ts_plan_create(cfg["ndim"], cfg["grid"], cfg["tile"], cfg["stride"])
+    log(f"bench: {args.config} {'merge-once' if args.merge_once is not None else f'TileShare-{k}'} vs tiled, "
+        f"steps={args.steps} warmup={args.warmup}")
+    plan = ts.ts_plan_create(cfg["ndim"], cfg["grid"], cfg["tile"], cfg["stride"],
+                             blend=1 if args.blend == "hard" else 0)
     ts.ts_plan_upload(plan, cfg["head_dim"], cfg.get("rope_base", 10000.0))
     info = ts.ts_plan_get_info(plan)
     model = ts.model_desc(cfg)
     x, g, tens, structs = device_inputs(cfg, cfg.get("seed", 0), dev)
-    ws_bytes = max(ts.ts_workspace_size(model, plan, k), ts.ts_workspace_size(model, plan, L))
+    ws_bytes = max(ts.ts_workspace_size(model, plan, kk) for kk in (k, L, -1))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     xo = torch.empty_like(x)
     go = torch.empty(info.n_tiles, cfg["d"], device=dev)
     torch.cuda.synchronize()
 
     def step_ts():
-        ts.ts_stack_forward(model, structs, plan, k, x, g, xo, go, ws)
+        if args.merge_once is not None:
+            ts.ts_merge_once_forward(model, structs, plan, args.merge_once, x, g, xo, go, ws)
+        else:
+            ts.ts_stack_forward(model, structs, plan, k, x, g, xo, go, ws)
 
     def step_base():
         ts.ts_tiled_forward(model, structs, plan, x, g, xo, go, ws)
@@ -185,8 +204,12 @@ def main():
         stats = ts.ts_profile_end() if profile else None
         return e0.elapsed_time(e1) / steps, stats
 
-    ms_ts, stats = timed(step_ts, args.steps, args.warmup, True)
-    log(f"bench: TileShare-{k}: {ms_ts:.2f} ms/step")
+    # the step time is taken without per-kernel events; the same number of
+    # steps then runs again with the library's HIP events around every
+    # kernel for the per-kernel figures and the roofline
+    ms_ts, _ = timed(step_ts, args.steps, args.warmup, False)
+    ms_prof, stats = timed(step_ts, args.steps, 0, True)
+    log(f"bench: TileShare-{k}: {ms_ts:.2f} ms/step ({ms_prof:.2f} with per-kernel events)")
     ms_base = None
     if not args.no_baseline:
         ms_base, _ = timed(step_base, args.steps, 1, False)
@@ -224,14 +247,23 @@ def main():
     pl_flops = None
     from oracle.plan import Plan  # FLOP count needs only the tile counts
     pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
-    pl_flops = decode_flops(cfg, pl, k)
+    pl_flops = decode_flops(cfg, pl, L if args.merge_once is not None else k)
+    mode = (f"merge once at layer {args.merge_once}, then per tile" if args.merge_once is not None
+            else f"TileShare-{k}")
+    extras = []
+    if args.blend == "hard":
+        extras.append("hard stitching")
+    if cfg["gemm_shared"] == "fp8":
+        extras.append(f"fp8 GEMMs {','.join(cfg.get('fp8_gemms') or ('qkv', 'out', 'fc1', 'fc2'))} in shared"
+                      + (" and per-tile" if args.fp8_per_tile else "") + " layers")
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_ts, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8" if cfg["gemm_shared"] == "fp8" else cfg["dtype"], "data": "synthetic",
-        "config": {"workload": f"{args.config} TileShare-{k}: grid {'x'.join(map(str, cfg['grid']))}, tiles "
+        "config": {"workload": f"{args.config} {mode}: grid {'x'.join(map(str, cfg['grid']))}, tiles "
                                f"{'x'.join(map(str, cfg['tile']))} stride {cfg['stride'][-1]}, {L} blocks d={cfg['d']} "
-                               f"{cfg['n_heads']}x{cfg['head_dim']} heads, MLP {cfg['mlp_hidden']} GELU",
+                               f"{cfg['n_heads']}x{cfg['head_dim']} heads, MLP {cfg['mlp_hidden']} GELU"
+                               + "".join(f"; {e}" for e in extras),
                    "k": k, "tokens_per_step": tok, "n_tiles": info.n_tiles, "tile_tokens": info.tile_tokens,
                    "parallelism": "single GPU"},
         "tiled_baseline": None if ms_base is None else {"ms_per_step": round(ms_base, 3),
@@ -241,6 +273,7 @@ def main():
         "frac_of_bf16_peak": round(pl_flops / (ms_ts / 1e3) / PEAK["bf16"], 4),
         "roofline": roof,
         "kernels": kernels,
+        "profiled_ms_per_step": round(ms_prof, 3),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
