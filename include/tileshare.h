@@ -210,6 +210,24 @@ ts_status ts_merge_once_forward(const ts_model_desc* model, const ts_layer_weigh
                                 const ts_plan* plan, int32_t l, const float* x_in, const float* g,
                                 float* x_out, float* g_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Partial sharing with per-tile residual streams (Table 1 top, Table S7):
+ * layers 0 .. k-1 run per tile; from layer k on every tile keeps its own
+ * residual stream and only the operations in `share` run once per token,
+ * attention always per tile.  A shared operation takes the w-bar blend of
+ * the tiles' states as input (for TS_SHARE_O: the blend of their attention
+ * outputs) and adds its result to every tile's stream; global rows stay
+ * per tile.  The outputs are merged as in ts_tiled_forward.  share = 0 is the
+ * tiled decoder; all three bits follow TileShare-k.  bf16 / fp32 GEMMs only
+ * (TS_EUNSUPPORTED for fp8 models).  Arguments, layouts and errors as
+ * ts_stack_forward; workspace ts_workspace_size(model, plan, -1, ...). */
+#define TS_SHARE_Q 1 /* Norm1, QKV projection, QK-norm */
+#define TS_SHARE_O 2 /* out-projection */
+#define TS_SHARE_M 4 /* Norm2 and MLP */
+ts_status ts_partial_share_forward(const ts_model_desc* model, const ts_layer_weights* layers,
+                                   const ts_plan* plan, int32_t k, int32_t share, const float* x_in,
+                                   const float* g, float* x_out, float* g_out, void* ws, size_t ws_bytes,
+                                   void* stream);
+
 /* Per-tensor e4m3 quantisation (Table S5 "V0 + FP8"; OCP e4m3, round to
  * nearest even, saturation at +-448): scale = max|src| / 448 (1 if all zero),
  * dst[i] = e4m3(clamp(src[i] / scale, -448, 448)).  src: device, n elements of

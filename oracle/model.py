@@ -409,6 +409,56 @@ def merge_once_forward(cfg, plan, x, g, layers, l, rope=None):
     return merge(plan, X)
 
 
+def partial_share_forward(cfg, plan, x, g, layers, k, share, rope=None):
+    """Table 1 (top) and Table S7: from layer k on every tile keeps its own
+    residual stream and only the operations in ``share`` run once per token;
+    attention always runs per tile.  ``share`` holds any of "q" (Norm1, QKV,
+    QK-norm), "o" (out-projection) and "m" (Norm2 and MLP).
+
+    Reading: a shared operation takes the token's w-bar blend of the tiles'
+    states as its input (for "o": the blend of the tiles' attention outputs)
+    and adds its one result to every tile's stream; global rows stay per tile.
+    With every operation shared the blended state follows TileShare-k, with
+    none the tiled decoder; the pages state "q + m" = all and, at k = 0,
+    "o" alone = TileShare-0.  Returns the final merge (x_out, g_out)."""
+    rope = rope or Rope(plan, cfg)
+    n = plan.tile_tokens
+    X = gather_tiles(plan, x, g)
+    for li in range(k):
+        X = per_tile_layers(X, layers[li], cfg, rope)
+
+    def blended(rows):
+        u, G = merge(plan, rows)
+        return np.vstack([u, G])                      # [n_union + n_tiles, d]
+
+    def add_to_tiles(delta):
+        return [X[t] + np.vstack([delta[plan.tile_rows[t]], delta[plan.n_union + t][None, :]])
+                for t in range(plan.n_tiles)]
+
+    for li in range(k, len(layers)):
+        p = layers[li]
+        if "q" in share:
+            q, kk, v = qkv_heads(norm(blended(X), p, "norm1", cfg), p, cfg)
+            outs = []
+            for t in range(plan.n_tiles):
+                rows = np.concatenate([plan.tile_rows[t].astype(np.int64), [plan.n_union + t]])
+                outs.append(tile_attention(q[rows], kk[rows], v[rows], rope.cos, rope.sin, cfg))
+        else:
+            outs = []
+            for Xt in X:
+                q, kk, v = qkv_heads(norm(Xt, p, "norm1", cfg), p, cfg)
+                outs.append(tile_attention(q, kk, v, rope.cos, rope.sin, cfg))
+        if "o" in share:
+            X = add_to_tiles(linear(blended(outs), p["w_o"], p["b_o"]))
+        else:
+            X = [X[t] + linear(outs[t], p["w_o"], p["b_o"]) for t in range(plan.n_tiles)]
+        if "m" in share:
+            X = add_to_tiles(mlp(norm(blended(X), p, "norm2", cfg), p, cfg))
+        else:
+            X = [Xt + mlp(norm(Xt, p, "norm2", cfg), p, cfg) for Xt in X]
+    return merge(plan, X)
+
+
 def rel_err(got, ref):
     """max |got - ref| / RMS(ref): the parity metric on the union output."""
     ref = np.asarray(ref, dtype=F)

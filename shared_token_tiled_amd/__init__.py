@@ -83,6 +83,9 @@ def lib():
                                                   ctypes.c_size_t, _VP]),
             "ts_merge_once_forward": (ctypes.c_int32, [P(ModelDesc), P(LayerWeights), _VP, ctypes.c_int32, _VP,
                                                        _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+            "ts_partial_share_forward": (ctypes.c_int32, [P(ModelDesc), P(LayerWeights), _VP, ctypes.c_int32,
+                                                          ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                                                          _VP]),
             "ts_fp8_quantize": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_int64, _VP, _VP, _VP,
                                                  ctypes.c_size_t, _VP]),
             "ts_op_gemm": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _VP, _VP, ctypes.c_int32,
@@ -199,6 +202,17 @@ def ts_merge_once_forward(model, layers, plan, l, x_in, g, x_out, g_out, ws, str
     _check(lib().ts_merge_once_forward(ctypes.byref(model), arr, plan, l, _ptr(x_in), _ptr(g), _ptr(x_out),
                                        _ptr(g_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "ts_merge_once_forward")
+
+
+TS_SHARE_Q, TS_SHARE_O, TS_SHARE_M = 1, 2, 4
+
+
+def ts_partial_share_forward(model, layers, plan, k, share, x_in, g, x_out, g_out, ws, stream=None):
+    arr = (LayerWeights * len(layers))(*layers)
+    _check(lib().ts_partial_share_forward(ctypes.byref(model), arr, plan, k, share, _ptr(x_in), _ptr(g),
+                                          _ptr(x_out), _ptr(g_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                          _stream(stream)),
+           "ts_partial_share_forward")
 
 
 def ts_fp8_quantize(src, dst, scale, ws, stream=None):

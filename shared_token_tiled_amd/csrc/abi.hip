@@ -319,6 +319,90 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
   return TS_OK;
 }
 
+// A layer on per-tile residual streams X [Mt, d] fp32 whose operations in
+// `share` (TS_SHARE_Q: Norm1, QKV, QK-norm; TS_SHARE_O: out-projection;
+// TS_SHARE_M: Norm2 and MLP) run once per token on the w-bar blend of the
+// tiles' states (for the out-projection: of their attention outputs) and add
+// their one result to every tile's stream (Table 1, Table S7).  Attention
+// always runs per tile.
+ts_status run_layer_partial(const Ctx& c, const ts_layer_weights& w, float* X, int share, const WS& ws) {
+  const ts_model_desc* m = c.m;
+  const ts_plan* p = c.p;
+  const int act = m->act_dtype;
+  const int ab = act_bytes(act);
+  const int64_t Mt = int64_t(p->n_tiles) * (p->n + 1);
+  const int64_t Ms = int64_t(p->n_union) + p->n_tiles;
+  const int d = m->d, H = m->n_heads, hd = m->head_dim, dm = m->mlp_hidden;
+  const bool rms = m->norm == 1;
+  const bool sq = share & TS_SHARE_Q, so = share & TS_SHARE_O, sm = share & TS_SHARE_M;
+  float* xg = ws.xs + size_t(p->n_union) * d;  // global rows of a blend into xs
+  ts_status st;
+  auto blend_states = [&]() -> ts_status {   // xs = w-bar blend of the streams
+    Scope sc(c.s, "blend", 0.0, (double(p->n_entries + p->n_tiles) + double(Ms)) * d * 4);
+    TS_HIP(tsk::blend(c.s, TS_F32, TS_F32, X, d, p->n_union, p->n_tiles, p->n, (const int*)p->d_cover_ptr,
+                      (const int*)p->d_entry_row, (const float*)p->d_cover_w, ws.xs, xg),
+           "blend");
+    return TS_OK;
+  };
+  auto add_back = [&]() -> ts_status {        // every stream += its token's row of xs
+    Scope sc(c.s, "add_to_tiles", 0.0, double(Mt) * d * 12);
+    TS_HIP(tsk::add_to_tiles(c.s, X, ws.xs, (const int*)p->d_tile_rows, p->n_union, p->n_tiles, p->n, d),
+           "add to tiles");
+    return TS_OK;
+  };
+
+  // Norm1, QKV, QK-norm, attention
+  const int64_t Mq = sq ? Ms : Mt;
+  if (sq && (st = blend_states()) != TS_OK) return st;
+  {
+    Scope sc(c.s, "norm", 0.0, double(Mq * d) * (4 + ab));
+    TS_HIP(tsk::norm(c.s, act, rms, sq ? ws.xs : X, int(Mq), d, w.norm1_g, w.norm1_b, m->eps, ws.h), "norm1");
+  }
+  if ((st = proj(c, ws, false, "qkv", tsk::EPI_BIAS, ws.h, Mq, 3 * d, d, w.w_qkv, nullptr, nullptr, w.b_qkv,
+                 ws.big)) != TS_OK)
+    return st;
+  if (m->qk_norm) {
+    Scope sc(c.s, "qk_norm", 0.0, double(Mq * 2 * d) * 2 * ab);
+    TS_HIP(tsk::qk_norm(c.s, act, ws.big, int(Mq), d, H, hd, w.q_g, w.k_g, m->eps), "qk_norm");
+  }
+  if ((st = window_attention(m, p, sq, ws.big, ws.o, c.s)) != TS_OK) return st;
+  // out-projection
+  if (so) {
+    {
+      Scope sc(c.s, "blend", 0.0, (double(p->n_entries + p->n_tiles) + double(Ms)) * d * ab);
+      TS_HIP(tsk::blend(c.s, act, act, ws.o, d, p->n_union, p->n_tiles, p->n, (const int*)p->d_cover_ptr,
+                        (const int*)p->d_entry_row, (const float*)p->d_cover_w, ws.h,
+                        (char*)ws.h + size_t(p->n_union) * d * ab),
+             "blend");
+    }
+    if ((st = proj(c, ws, false, "out", tsk::EPI_F32, ws.h, Ms, d, d, w.w_o, nullptr, nullptr, w.b_o, ws.xs)) !=
+        TS_OK)
+      return st;
+    if ((st = add_back()) != TS_OK) return st;
+  } else if ((st = proj(c, ws, false, "out", tsk::EPI_RESID, ws.o, Mt, d, d, w.w_o, nullptr, nullptr, w.b_o, X)) !=
+             TS_OK) {
+    return st;
+  }
+  // Norm2 and MLP
+  const int64_t Mm = sm ? Ms : Mt;
+  if (sm && (st = blend_states()) != TS_OK) return st;
+  {
+    Scope sc(c.s, "norm", 0.0, double(Mm * d) * (4 + ab));
+    TS_HIP(tsk::norm(c.s, act, rms, sm ? ws.xs : X, int(Mm), d, w.norm2_g, w.norm2_b, m->eps, ws.h), "norm2");
+  }
+  if ((st = proj(c, ws, false, "fc1", tsk::EPI_BIAS_GELU, ws.h, Mm, dm, d, w.w_1, nullptr, nullptr, w.b_1,
+                 ws.big)) != TS_OK)
+    return st;
+  if (sm) {
+    // the blended state in xs has been consumed by Norm2: xs takes the MLP result
+    if ((st = proj(c, ws, false, "fc2", tsk::EPI_F32, ws.big, Ms, d, dm, w.w_2, nullptr, nullptr, w.b_2,
+                   ws.xs)) != TS_OK)
+      return st;
+    return add_back();
+  }
+  return proj(c, ws, false, "fc2", tsk::EPI_RESID, ws.big, Mt, d, dm, w.w_2, nullptr, nullptr, w.b_2, X);
+}
+
 ts_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (!ws) return fail(TS_EWORKSPACE, "workspace is null");
   if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(TS_EWORKSPACE, "workspace must be 256-byte aligned");
@@ -422,6 +506,44 @@ ts_status merge_once_impl(const ts_model_desc* m, const ts_layer_weights* layers
   for (int i = l; i < m->n_layers; ++i)
     if ((st = run_layer(c, layers[i], w.X, false, w)) != TS_OK) return st;
   return merge(x_out, g_out);
+}
+
+// Table 1 (top) / Table S7: per-tile layers 0 .. k-1, then per-tile residual
+// streams with the operations in `share` run once per token, then the merge.
+ts_status partial_share_impl(const ts_model_desc* m, const ts_layer_weights* layers, const ts_plan* p, int32_t k,
+                             int32_t share, const float* x_in, const float* g, float* x_out, float* g_out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  ts_status st;
+  if ((st = check_model(m)) != TS_OK) return st;
+  if ((st = check_plan(p, m)) != TS_OK) return st;
+  if (m->gemm_dtype_shared == TS_FP8E4M3) return fail(TS_EUNSUPPORTED, "partial sharing runs bf16 / fp32 GEMMs only");
+  if (!layers && m->n_layers > 0) return fail(TS_EINVAL, "layers is null");
+  if (k < 0 || k > m->n_layers) return fail(TS_EINVAL, "k must be in 0..n_layers");
+  if (share < 0 || share > (TS_SHARE_Q | TS_SHARE_O | TS_SHARE_M))
+    return fail(TS_EINVAL, "share must be a mask of TS_SHARE_* bits");
+  if (!x_in || !g || !x_out) return fail(TS_EINVAL, "x_in, g and x_out must be non-null");
+  for (int i = 0; i < m->n_layers; ++i)
+    if ((st = check_weights(m, &layers[i], false)) != TS_OK) return st;
+  WS w0 = layout(m, p, true, true, true, nullptr);
+  if ((st = check_ws(ws, ws_bytes, w0.bytes)) != TS_OK) return st;
+  WS w = layout(m, p, true, true, true, (char*)ws);
+  Ctx c{m, p, (hipStream_t)stream};
+  const int d = m->d;
+  const int64_t Mt = int64_t(p->n_tiles) * (p->n + 1);
+  const int64_t Ms = int64_t(p->n_union) + p->n_tiles;
+  {
+    Scope sc(c.s, "gather", 0.0, double(Mt) * d * 8);
+    TS_HIP(tsk::gather(c.s, x_in, g, 0, (const int*)p->d_tile_rows, p->n_tiles, p->n, d, w.X), "gather");
+  }
+  for (int i = 0; i < k; ++i)
+    if ((st = run_layer(c, layers[i], w.X, false, w)) != TS_OK) return st;
+  for (int i = k; i < m->n_layers; ++i)
+    if ((st = run_layer_partial(c, layers[i], w.X, share, w)) != TS_OK) return st;
+  Scope sc(c.s, "merge", 0.0, (double(p->n_entries + p->n_tiles) + double(Ms)) * d * 4);
+  TS_HIP(tsk::blend(c.s, TS_F32, TS_F32, w.X, d, p->n_union, p->n_tiles, p->n, (const int*)p->d_cover_ptr,
+                    (const int*)p->d_entry_row, (const float*)p->d_cover_w, x_out, g_out),
+         "merge");
+  return TS_OK;
 }
 
 }  // namespace
@@ -598,6 +720,12 @@ ts_status ts_merge_once_forward(const ts_model_desc* m, const ts_layer_weights* 
                                 int32_t l, const float* x_in, const float* g, float* x_out, float* g_out, void* ws,
                                 size_t ws_bytes, void* stream) {
   return merge_once_impl(m, layers, p, l, x_in, g, x_out, g_out, ws, ws_bytes, stream);
+}
+
+ts_status ts_partial_share_forward(const ts_model_desc* m, const ts_layer_weights* layers, const ts_plan* p,
+                                   int32_t k, int32_t share, const float* x_in, const float* g, float* x_out,
+                                   float* g_out, void* ws, size_t ws_bytes, void* stream) {
+  return partial_share_impl(m, layers, p, k, share, x_in, g, x_out, g_out, ws, ws_bytes, stream);
 }
 
 ts_status ts_tiled_forward(const ts_model_desc* m, const ts_layer_weights* layers, const ts_plan* p,

@@ -165,6 +165,20 @@ __global__ __launch_bounds__(256) void k_gather(const float* __restrict__ x_in,
   for (int c = lane; c < (d >> 2); c += 64) store4(dst + 4 * c, load4(src + 4 * c));
 }
 
+// X[t*(n+1)+j] += delta[tile_rows[t*n+j]], X[t*(n+1)+n] += delta[n_union+t]:
+// one per-token result added to every tile's copy of the token.
+__global__ __launch_bounds__(256) void k_add_to_tiles(float* __restrict__ X, const float* __restrict__ delta,
+                                                      const int* __restrict__ tile_rows, int n_union,
+                                                      int n_tiles, int n, int d) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n_tiles * (n + 1)) return;
+  const int t = r / (n + 1), j = r % (n + 1);
+  const float* src = delta + size_t(j < n ? tile_rows[size_t(t) * n + j] : n_union + t) * d;
+  float* dst = X + size_t(r) * d;
+  for (int c = lane; c < (d >> 2); c += 64) store4(dst + 4 * c, load4(dst + 4 * c) + load4(src + 4 * c));
+}
+
 __global__ __launch_bounds__(256) void k_init_shared(const float* __restrict__ x_in,
                                                      const float* __restrict__ g, int n_union,
                                                      int n_tiles, int d, float* __restrict__ xs) {
@@ -289,6 +303,13 @@ hipError_t gather(hipStream_t s, const float* x_in, const float* g, int64_t g_st
                   int n, int d, float* X) {
   hipLaunchKernelGGL(k_gather, dim3(blocks_for_rows(n_tiles * (n + 1))), dim3(256), 0, s, x_in, g, g_stride,
                      tile_rows, n_tiles, n, d, X);
+  return hipGetLastError();
+}
+
+hipError_t add_to_tiles(hipStream_t s, float* X, const float* delta, const int* tile_rows, int n_union,
+                        int n_tiles, int n, int d) {
+  hipLaunchKernelGGL(k_add_to_tiles, dim3(blocks_for_rows(n_tiles * (n + 1))), dim3(256), 0, s, X, delta,
+                     tile_rows, n_union, n_tiles, n, d);
   return hipGetLastError();
 }
 

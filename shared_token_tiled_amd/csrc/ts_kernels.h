@@ -29,6 +29,9 @@ hipError_t qk_norm(hipStream_t s, int act, void* qkv, int M, int d, int H, int h
 hipError_t blend(hipStream_t s, int tin, int tout, const void* in, int d, int n_union, int n_tiles,
                  int n, const int* cover_ptr, const int* entry_row, const float* w, void* out_union,
                  void* out_global);
+// X[t*(n+1)+j] += delta[tile_rows[t*n+j]], X[t*(n+1)+n] += delta[n_union+t]  (fp32)
+hipError_t add_to_tiles(hipStream_t s, float* X, const float* delta, const int* tile_rows, int n_union,
+                        int n_tiles, int n, int d);
 // X[t*(n+1)+j] = x_in[tile_rows[t*n+j]], X[t*(n+1)+n] = g + t*g_stride  (fp32;
 // g_stride 0: one global row for every tile)
 hipError_t gather(hipStream_t s, const float* x_in, const float* g, int64_t g_stride, const int* tile_rows,

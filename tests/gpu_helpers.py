@@ -54,6 +54,18 @@ class Run:
         torch.cuda.synchronize()
         return xo.cpu().numpy().astype(np.float64), go.cpu().numpy().astype(np.float64)
 
+    def partial_share(self, x, g, k, share):
+        """share: a set of "q", "o", "m"."""
+        mask = (ts.TS_SHARE_Q if "q" in share else 0) | (ts.TS_SHARE_O if "o" in share else 0) | \
+            (ts.TS_SHARE_M if "m" in share else 0)
+        xi = torch.as_tensor(x, dtype=torch.float32).to(DEV).contiguous()
+        gi = torch.as_tensor(g, dtype=torch.float32).to(DEV).contiguous()
+        xo = torch.empty_like(xi)
+        go = torch.empty(self.info.n_tiles, self.cfg["d"], dtype=torch.float32, device=DEV)
+        ts.ts_partial_share_forward(self.model, self.structs, self.plan, k, mask, xi, gi, xo, go, self.ws)
+        torch.cuda.synchronize()
+        return xo.cpu().numpy().astype(np.float64), go.cpu().numpy().astype(np.float64)
+
     def shared_layer(self, x_all, layer_index=0):
         xa = torch.as_tensor(x_all, dtype=torch.float32).to(DEV).contiguous()
         ts.ts_shared_layer_forward(self.model, self.structs[layer_index], self.plan, xa, self.ws)

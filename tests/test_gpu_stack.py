@@ -206,3 +206,30 @@ def test_fp8_scope_against_oracle(k, gemms, per_tile):
     e, eg = max_rel(got, ref), max_rel(ggot, gref)
     print(f"  max|err|/rms = {e:.3e} (globals {eg:.3e}), tolerance {TOL['fp8']}")
     assert e < TOL["fp8"] and eg < TOL["fp8"]
+
+
+PARTIAL = [("tiny2d", None, 0, "o"), ("tiny2d", None, 0, "qm"),
+           ("minimax_h3", "r", 1, "q"), ("minimax_h3", "r", 1, "o"), ("minimax_h3", "r", 1, "m"),
+           ("minimax_h3", "r", 0, "qo"), ("minimax_h3", "r", 1, "qom"), ("minimax_h3", "r", 2, ""),
+           ("vitok4k", "r", 0, "om"), ("small_video", "r", 1, "qm")]
+
+
+@pytest.mark.parametrize("name,size,k,share", PARTIAL)
+def test_partial_sharing_against_oracle(name, size, k, share):
+    """Table 1 (top) and Table S7: per-tile residual streams from layer k with
+    the listed operations (q: Norm1/QKV/QK-norm, o: out-projection, m: MLP)
+    run once per token on the blended state."""
+    cfg = configs.get(name) if size is None else reduced(name)
+    say(f"partial sharing {name} k={k} share={share!r}")
+    x, g, layers = make_inputs(cfg, qk_scale=2.0)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    ref, gref = M.partial_share_forward(cfg, pl, x, g, layers, k, set(share))
+    run = Run(cfg, layers)
+    try:
+        got, ggot = run.partial_share(x, g, k, set(share))
+    finally:
+        run.close()
+    tol = TOL[cfg["dtype"]]
+    e, eg = max_rel(got, ref), max_rel(ggot, gref)
+    print(f"  max|err|/rms = {e:.3e} (globals {eg:.3e}), tolerance {tol}")
+    assert e < tol and eg < tol

@@ -422,3 +422,67 @@ def test_batched_per_tile_layers_equal_per_tile_layers_in_bf16_and_fp8():
     # and the MLP-only fp8 result differs from bf16 by a quantisation-sized amount
     e = M.rel_err(c[0], a[0])
     assert 1e-4 < e < 0.2
+
+
+# --- partial sharing with per-tile residual streams (Table 1, Table S7) --------
+
+def _ps_setup(layers=3, qk=3.0):
+    cfg = tiny_cfg(ndim=3, norm="rms", qk=True, grid=(3, 5, 6), tile=(2, 3, 4), stride=(1, 2, 3), layers=layers)
+    x, g, lay = make_inputs(cfg, qk_scale=qk)
+    return cfg, x, g, lay, Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+
+
+@pytest.mark.parametrize("k", [0, 1, 3])
+def test_partial_sharing_extremes(k):
+    """Nothing shared is the tiled decoder; everything shared keeps the blended
+    state on TileShare-k's path, so the final merge equals TileShare-k."""
+    cfg, x, g, layers, pl = _ps_setup()
+    base, gbase = M.tiled_forward(cfg, pl, x, g, layers)
+    none, gnone = M.partial_share_forward(cfg, pl, x, g, layers, k, set())
+    assert M.rel_err(none, base) < 1e-12 and M.rel_err(gnone, gbase) < 1e-12
+    ts, gts = M.stack_forward(cfg, pl, x, g, layers, k)
+    allx, gall = M.partial_share_forward(cfg, pl, x, g, layers, k, {"q", "o", "m"})
+    # equal up to the fp32 rounding of w-bar: the broadcast deltas re-enter the
+    # blend with weight sum 1 + O(2^-24)
+    assert M.rel_err(allx, ts) < 1e-6 and M.rel_err(gall, gts) < 1e-6
+
+
+@pytest.mark.parametrize("k", [0, 2])
+def test_partial_sharing_q_plus_m_equals_all(k):
+    """Table S7: sharing q and m is equivalent to sharing everything (the
+    out-projection is linear and w-bar sums to 1, so only blends of it are
+    ever read)."""
+    cfg, x, g, layers, pl = _ps_setup()
+    a, ga = M.partial_share_forward(cfg, pl, x, g, layers, k, {"q", "m"})
+    b, gb = M.partial_share_forward(cfg, pl, x, g, layers, k, {"q", "o", "m"})
+    assert M.rel_err(a, b) < 1e-6 and M.rel_err(ga, gb) < 1e-6
+
+
+def test_partial_sharing_o_only_at_k0_is_tileshare0():
+    """Table 1 footnote: with only the out-projection shared at k = 0 the
+    per-tile states stay identical, so the result equals TileShare-0."""
+    cfg, x, g, layers, pl = _ps_setup()
+    a, ga = M.partial_share_forward(cfg, pl, x, g, layers, 0, {"o"})
+    b, gb = M.stack_forward(cfg, pl, x, g, layers, 0)
+    assert M.rel_err(a, b) < 1e-6 and M.rel_err(ga, gb) < 1e-6
+
+
+def test_partial_sharing_single_ops_differ_and_zero_overlap_is_exact():
+    cfg, x, g, layers, pl = _ps_setup()
+    for p in layers:   # large enough layer updates that the approximation shows
+        p["w_qkv"] = p["w_qkv"] * 20
+        p["w_o"] = p["w_o"] * 20
+        p["w_1"] = p["w_1"] * 10
+    base, _ = M.tiled_forward(cfg, pl, x, g, layers)
+    outs = {}
+    for share in ({"q"}, {"o"}, {"m"}, {"q", "o"}):
+        outs[tuple(sorted(share))], _ = M.partial_share_forward(cfg, pl, x, g, layers, 1, share)
+        assert M.rel_err(outs[tuple(sorted(share))], base) > 1e-6
+    assert M.rel_err(outs[("q",)], outs[("m",)]) > 1e-6
+    cfg0 = tiny_cfg(grid=(1, 4, 8), tile=(1, 4, 4), stride=(1, 4, 4), layers=2)
+    x0, g0, l0 = make_inputs(cfg0)
+    p0 = Plan(cfg0["grid"], cfg0["tile"], cfg0["stride"])
+    b0, _ = M.tiled_forward(cfg0, p0, x0, g0, l0)
+    for share in ({"q"}, {"o"}, {"m"}, {"q", "o", "m"}):
+        got, _ = M.partial_share_forward(cfg0, p0, x0, g0, l0, 0, share)
+        assert M.rel_err(got, b0) < 1e-12
