@@ -120,15 +120,20 @@ def measured_traffic(name, workload, k):
     return ent["hbm_bytes_per_launch"]
 
 
-def decode_flops(cfg, pl, k):
+def decode_flops(cfg, pl, k, share="qom"):
     """Algorithmic FLOPs of a TileShare-k decode: 2*(3d^2 + d^2 + 2 d dm) per row
-    per layer for the projections, 4 (n+1)^2 d per tile per layer for attention."""
+    per layer for the projections, 4 (n+1)^2 d per tile per layer for attention.
+    ``share``: the operations that run once per token from layer k on (q: QKV,
+    o: out-projection, m: MLP); the others run on every tile's rows."""
     d, dm, L = cfg["d"], cfg["mlp_hidden"], cfg["n_layers"]
-    lin = 2.0 * (3 * d * d + d * d + 2 * d * dm)
     mt = pl.n_tiles * (pl.tile_tokens + 1)
     ms = pl.n_union + pl.n_tiles
     attn = 4.0 * (pl.tile_tokens + 1) ** 2 * d * pl.n_tiles
-    return k * (lin * mt + attn) + (L - k) * (lin * ms + attn)
+    per_tile = 2.0 * (3 * d * d + d * d + 2 * d * dm) * mt + attn
+    later = attn
+    for op, fl in (("q", 2.0 * 3 * d * d), ("o", 2.0 * d * d), ("m", 2.0 * 2 * d * dm)):
+        later += fl * (ms if op in share else mt)
+    return k * per_tile + (L - k) * later
 
 
 def main():
@@ -147,6 +152,8 @@ def main():
     ap.add_argument("--fp8-gemms", default=None,
                     help="comma list of the fp8 GEMMs (qkv,out,fc1,fc2) for fp8 configurations")
     ap.add_argument("--fp8-per-tile", action="store_true", help="fp8 GEMMs in per-tile layers too")
+    ap.add_argument("--partial-share", default=None, metavar="OPS",
+                    help="time partial sharing from layer k with per-tile streams; OPS from q, o, m (e.g. qo)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path's sharding across "
@@ -179,9 +186,14 @@ def main():
     go = torch.empty(info.n_tiles, cfg["d"], device=dev)
     torch.cuda.synchronize()
 
+    share_mask = sum(b for c, b in (("q", ts.TS_SHARE_Q), ("o", ts.TS_SHARE_O), ("m", ts.TS_SHARE_M))
+                     if args.partial_share and c in args.partial_share)
+
     def step_ts():
         if args.merge_once is not None:
             ts.ts_merge_once_forward(model, structs, plan, args.merge_once, x, g, xo, go, ws)
+        elif args.partial_share is not None:
+            ts.ts_partial_share_forward(model, structs, plan, k, share_mask, x, g, xo, go, ws)
         else:
             ts.ts_stack_forward(model, structs, plan, k, x, g, xo, go, ws)
 
@@ -247,9 +259,11 @@ def main():
     pl_flops = None
     from oracle.plan import Plan  # FLOP count needs only the tile counts
     pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
-    pl_flops = decode_flops(cfg, pl, L if args.merge_once is not None else k)
+    pl_flops = (decode_flops(cfg, pl, L) if args.merge_once is not None else
+                decode_flops(cfg, pl, k, args.partial_share if args.partial_share is not None else "qom"))
     mode = (f"merge once at layer {args.merge_once}, then per tile" if args.merge_once is not None
-            else f"TileShare-{k}")
+            else (f"per-tile streams from layer {k} sharing {args.partial_share or 'nothing'}"
+                  if args.partial_share is not None else f"TileShare-{k}"))
     extras = []
     if args.blend == "hard":
         extras.append("hard stitching")
