@@ -142,6 +142,8 @@ struct WS {
   void* big = nullptr;       // act [M_max, max(3d, mlp)] qkv, then MLP hidden
   void* o = nullptr;         // act [M_t, d] attention output, per-tile layout
   uint8_t* q8 = nullptr;     // e4m3 [M_s, max(d, mlp)] quantised GEMM operand
+  float* gpart = nullptr;    // fp32 split states of the global-token attention rows
+  int64_t gpart_floats = 0;
   size_t bytes = 0;
 };
 
@@ -171,6 +173,10 @@ WS layout(const ts_model_desc* m, const ts_plan* p, bool states, bool per_tile, 
   w.o = take(size_t(Mt * d * ab));
   if (m->gemm_dtype_shared == TS_FP8E4M3)
     w.q8 = (uint8_t*)take(size_t((m->fp8_per_tile ? Mmax : Ms) * std::max<int64_t>(d, m->mlp_hidden)));
+  if (m->act_dtype == TS_BF16) {  // up to 64 splits of each global row's keys
+    w.gpart_floats = int64_t(p->n_tiles) * m->n_heads * 64 * (m->head_dim + 2);
+    w.gpart = (float*)take(size_t(w.gpart_floats * 4));
+  }
   w.bytes = off;
   return w;
 }
@@ -217,7 +223,7 @@ ts_status proj(const Ctx& c, const WS& ws, bool f8, const char* role, int epi, c
 
 // Window attention of every (tile, head) for one layer.
 ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared, const void* qkv, void* out,
-                           hipStream_t s) {
+                           hipStream_t s, float* gscratch = nullptr, int64_t gscratch_floats = 0) {
   tsk::AttnArgs a;
   a.qkv = qkv;
   a.out = out;
@@ -261,7 +267,7 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared
   {
     Scope sc(s, "attn_global_bf16", 4.0 * nn * m->d * p->n_tiles,
              double(p->n_tiles) * (nn * 2 * m->d + 2 * m->d) * ab);
-    TS_HIP(tsk::attention_global(s, a), "attention (global rows)");
+    TS_HIP(tsk::attention_global(s, a, gscratch, gscratch_floats), "attention (global rows)");
   }
   return TS_OK;
 }
@@ -293,7 +299,7 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
     Scope sc(c.s, "qk_norm", 0.0, double(M * 2 * d) * 2 * ab);
     TS_HIP(tsk::qk_norm(c.s, act, ws.big, int(M), d, H, hd, w.q_g, w.k_g, m->eps), "qk_norm");
   }
-  if ((st = window_attention(m, p, shared, ws.big, ws.o, c.s)) != TS_OK) return st;
+  if ((st = window_attention(m, p, shared, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats)) != TS_OK) return st;
   const void* aout = ws.o;
   if (shared) {
     Scope sc(c.s, "blend", 0.0, (double(p->n_entries + p->n_tiles) + double(Ms)) * d * ab);
@@ -365,7 +371,7 @@ ts_status run_layer_partial(const Ctx& c, const ts_layer_weights& w, float* X, i
     Scope sc(c.s, "qk_norm", 0.0, double(Mq * 2 * d) * 2 * ab);
     TS_HIP(tsk::qk_norm(c.s, act, ws.big, int(Mq), d, H, hd, w.q_g, w.k_g, m->eps), "qk_norm");
   }
-  if ((st = window_attention(m, p, sq, ws.big, ws.o, c.s)) != TS_OK) return st;
+  if ((st = window_attention(m, p, sq, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats)) != TS_OK) return st;
   // out-projection
   if (so) {
     {

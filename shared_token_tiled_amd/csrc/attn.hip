@@ -21,6 +21,7 @@
 // transposed as [hd][key], both with XOR-swizzled 16-byte chunks, double
 // buffered; row indices and positions of the keys are prefetched two blocks
 // ahead into an LDS ring, and the RoPE table sits in LDS.
+#include <algorithm>
 #include <cstdlib>
 
 #include "device_common.h"
@@ -474,23 +475,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
 }
 
-// The global token's query row of every (tile, head): one workgroup per
-// (head, tile); LPK lanes share one key (lane = rotation pair), each
-// wavefront walks every 4th key group with its own online softmax, and the
-// four partial states are merged through LDS at the end.
-// Global-token query row of one (head, tile): one workgroup of 1024 threads.
-// The window's keys are taken in chunks of GCH.  Score pass: HD/16 threads
-// per key, 16 dims each (two 8-dim RoPE groups, the rotated key rounded to
-// bf16 as the MFMA kernel stages it), summed across those lanes; scores and
-// row indices go to LDS.  Value pass: each thread owns one 8-dim group of the
+// Global-token query row of one (head, tile), over the window keys
+// [j_begin, j_end) of split blockIdx.z (key n is the global key itself, not
+// rotated).  Keys are taken in chunks of GCH.  Score pass: HD/16 threads per
+// key, 16 dims each (two 8-dim RoPE groups, the rotated key rounded to bf16 as
+// the MFMA kernel stages it), summed across those lanes; scores and row
+// indices go to LDS.  Value pass: each thread owns one 8-dim group of the
 // output and a strided subset of the chunk's keys and keeps a running
 // (max-shifted) weighted sum; the chunk max is shared by the workgroup, so
 // every thread rescales by the same factor.  The partial sums are added in
-// LDS at the end.  The global key itself (window row n) has no rotation.
-constexpr int GCH = 4096;
-template <int HD>
-__global__ __launch_bounds__(1024) void k_attn_global_bf16(AttnP p) {
-  constexpr int NT = 1024;
+// LDS at the end.  With one split the row is written; with several, each
+// split leaves its state (max m, weight sum l, unnormalised output o[HD], in
+// the exp2 domain) in `part` for k_attn_global_merge.
+constexpr int GCH = 1024;
+template <int HD, int NT>
+__global__ __launch_bounds__(NT) void k_attn_global_bf16(AttnP p, int split_keys, float* part) {
   constexpr int TPK = HD / 16;    // threads per key, score pass
   constexpr int KPP = NT / TPK;   // keys per score pass
   constexpr int DG = HD / 8;      // 8-dim groups, value pass
@@ -502,6 +501,7 @@ __global__ __launch_bounds__(1024) void k_attn_global_bf16(AttnP p) {
   __shared__ float l_s[KG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, t = blockIdx.y, n = p.n;
+  const int j_begin = blockIdx.z * split_keys, j_end = min(j_begin + split_keys, n + 1);
   const bf16* qkv = (const bf16*)p.qkv;
   const int64_t ld = 3 * int64_t(p.d);
   const int64_t grow = window_row(p, t, n);
@@ -516,8 +516,8 @@ __global__ __launch_bounds__(1024) void k_attn_global_bf16(AttnP p) {
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float l = 0.f, m_run = -INFINITY;
 
-  for (int c0 = 0; c0 <= n; c0 += GCH) {
-    const int cnt = min(GCH, n + 1 - c0);
+  for (int c0 = j_begin; c0 < j_end; c0 += GCH) {
+    const int cnt = min(GCH, j_end - c0);
 #pragma unroll 4
     for (int jj = kk; jj < cnt; jj += KPP) {
       const int j = c0 + jj;
@@ -577,9 +577,36 @@ __global__ __launch_bounds__(1024) void k_attn_global_bf16(AttnP p) {
       o += acc_s[g][tid];
       lt += l_s[g];
     }
-    bf16* out = (bf16*)p.out + (int64_t(t) * (n + 1) + n) * p.d + h * HD;
-    out[tid] = bf16(o / lt);
+    if (part) {
+      float* st = part + ((int64_t(t) * p.H + h) * gridDim.z + blockIdx.z) * (HD + 2);
+      if (tid == 0) {
+        st[0] = m_run;
+        st[1] = lt;
+      }
+      st[2 + tid] = o;
+    } else {
+      bf16* out = (bf16*)p.out + (int64_t(t) * (n + 1) + n) * p.d + h * HD;
+      out[tid] = bf16(o / lt);
+    }
   }
+}
+
+// Merge the splits' states of one (head, tile) global row: with M the largest
+// split max, out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+template <int HD>
+__global__ __launch_bounds__(HD) void k_attn_global_merge(AttnP p, int splits, const float* part) {
+  const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const float* st = part + (int64_t(t) * p.H + h) * splits * (HD + 2);
+  float mx = -INFINITY;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, st[s * (HD + 2)]);
+  float o = 0.f, lt = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float w = __builtin_amdgcn_exp2f(st[s * (HD + 2)] - mx);
+    lt += st[s * (HD + 2) + 1] * w;
+    o += st[s * (HD + 2) + 2 + tid] * w;
+  }
+  bf16* out = (bf16*)p.out + (int64_t(t) * (p.n + 1) + p.n) * p.d + h * HD;
+  out[tid] = bf16(o / lt);
 }
 
 }  // namespace
@@ -611,13 +638,39 @@ hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
   return hipGetLastError();
 }
 
-hipError_t attention_global(hipStream_t s, const AttnArgs& a) {
+int attention_global_splits(const AttnArgs& a, int64_t scratch_floats) {
+  // about GLOBAL_WGS workgroups over the chip, splits of at least 128 keys
+  static const int target = [] {
+    const char* e = getenv("TS_GLOBAL_WGS");
+    return e ? std::max(64, atoi(e)) : 2048;
+  }();
+  int splits = (target + a.H * a.n_tiles - 1) / (a.H * a.n_tiles);
+  splits = std::min(splits, std::max(1, (a.n + 1) / 128));
+  while (splits > 1 && int64_t(a.n_tiles) * a.H * splits * (a.hd + 2) > scratch_floats) --splits;
+  return std::max(1, std::min(splits, 64));
+}
+
+hipError_t attention_global(hipStream_t s, const AttnArgs& a, float* scratch, int64_t scratch_floats) {
   const AttnP p = make_params(a);
-  if (a.n < 1) return hipErrorInvalidValue;
-  const dim3 grid(a.H, a.n_tiles), block(1024);
-  if (a.hd == 64) hipLaunchKernelGGL(k_attn_global_bf16<64>, grid, block, 0, s, p);
-  else if (a.hd == 128) hipLaunchKernelGGL(k_attn_global_bf16<128>, grid, block, 0, s, p);
-  else return hipErrorInvalidValue;
+  if (a.n < 1 || (a.hd != 64 && a.hd != 128)) return hipErrorInvalidValue;
+  const int splits = scratch ? attention_global_splits(a, scratch_floats) : 1;
+  if (splits == 1) {
+    const dim3 grid(a.H, a.n_tiles, 1);
+    if (a.hd == 64) hipLaunchKernelGGL((k_attn_global_bf16<64, 1024>), grid, dim3(1024), 0, s, p, a.n + 1, nullptr);
+    else hipLaunchKernelGGL((k_attn_global_bf16<128, 1024>), grid, dim3(1024), 0, s, p, a.n + 1, nullptr);
+    return hipGetLastError();
+  }
+  int split_keys = (a.n + 1 + splits - 1) / splits;
+  split_keys = (split_keys + 63) / 64 * 64;
+  const int used = (a.n + 1 + split_keys - 1) / split_keys;   // every split holds >= 1 key
+  const dim3 grid(a.H, a.n_tiles, used);
+  if (a.hd == 64) {
+    hipLaunchKernelGGL((k_attn_global_bf16<64, 256>), grid, dim3(256), 0, s, p, split_keys, scratch);
+    hipLaunchKernelGGL(k_attn_global_merge<64>, dim3(a.H, a.n_tiles), dim3(64), 0, s, p, used, scratch);
+  } else {
+    hipLaunchKernelGGL((k_attn_global_bf16<128, 256>), grid, dim3(256), 0, s, p, split_keys, scratch);
+    hipLaunchKernelGGL(k_attn_global_merge<128>, dim3(a.H, a.n_tiles), dim3(128), 0, s, p, used, scratch);
+  }
   return hipGetLastError();
 }
 

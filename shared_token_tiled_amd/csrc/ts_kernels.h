@@ -68,7 +68,10 @@ struct AttnArgs {
 // fp32: every window row.  bf16: the n tile-token query rows of every window;
 // the global-token row (window row n) is attention_global's.
 hipError_t attention(hipStream_t s, int act, const AttnArgs& a);
-// bf16 only: the global-token query row of every (tile, head).
-hipError_t attention_global(hipStream_t s, const AttnArgs& a);
+// bf16 only: the global-token query row of every (tile, head).  With
+// scratch (fp32, scratch_floats long) the keys are split over several
+// workgroups per row and merged by a second kernel; without, one workgroup
+// per row.
+hipError_t attention_global(hipStream_t s, const AttnArgs& a, float* scratch, int64_t scratch_floats);
 
 }  // namespace tsk
