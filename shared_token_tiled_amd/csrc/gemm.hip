@@ -18,6 +18,7 @@
 //
 // fp32: a plain LDS-tiled FMA kernel, used by the fp32 configuration.
 #include <cstdlib>
+#include <cstring>
 
 #include "device_common.h"
 #include "ts_kernels.h"
@@ -39,10 +40,35 @@ struct GemmP {
   int M, N, K;
 };
 
-template <int EPI>
+// GELU x Phi(x) = x (1 + erf(x / sqrt 2)) / 2 with erf from Abramowitz and
+// Stegun, Handbook of Mathematical Functions, eq. 7.1.28: for z >= 0,
+// erf(z) = 1 - (1 + a1 z + ... + a6 z^6)^-16, absolute error <= 3e-7 (about
+// 2e-6 in fp32 arithmetic, i.e. <= 6e-7 on the GELU value, far below the
+// bf16 rounding of the MFMA GEMMs' outputs).  One reciprocal and 11 FMA/MUL,
+// no branches; large z overflows the power to +inf and gives erf = 1 exactly.
+__device__ __forceinline__ float gelu_as(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  float q = fmaf(z, 0.0000430638f, 0.0002765672f);
+  q = fmaf(q, z, 0.0001520143f);
+  q = fmaf(q, z, 0.0092705272f);
+  q = fmaf(q, z, 0.0422820123f);
+  q = fmaf(q, z, 0.0705230784f);
+  q = fmaf(q, z, 1.0f);
+  q *= q;
+  q *= q;
+  q *= q;
+  q *= q;
+  const float e = 1.0f - __builtin_amdgcn_rcpf(q);  // erf(|x| / sqrt 2)
+  const float hx = 0.5f * x;
+  return fmaf(hx, copysignf(e, x), hx);
+}
+
+// FAST: GELU through gelu_as (MFMA kernels); otherwise the library erf
+// (the fp32 kernel).
+template <int EPI, bool FAST = false>
 __device__ __forceinline__ float epi_value(float acc, float alpha, float bias) {
   float v = fmaf(acc, alpha, bias);
-  if (EPI == EPI_BIAS_GELU) v = gelu_erf(v);
+  if (EPI == EPI_BIAS_GELU) v = FAST ? gelu_as(v) : gelu_erf(v);
   return v;
 }
 
@@ -196,6 +222,58 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
+// Epilogue of one wavefront's 128 x (32*NB) accumulator tile at (row0, col0):
+// each 32-row block goes through the wavefront's own LDS staging area (32
+// rows of 32*NB + 8 floats) so that every lane then writes 16 contiguous
+// output bytes (4 columns) with the bias / GELU / residual applied.
+template <int EPI, bool FP8, int NB>
+__device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4][NB], float* stg, int row0,
+                                           int col0, int lane) {
+  constexpr int WCOLS = 32 * NB, EPI_LD = WCOLS + 8;
+  float alpha = 1.0f;
+  if (FP8) alpha = (*p.sa) * (*p.sb);
+  const int l32 = lane & 31, g = lane >> 5;
+  // read-back mapping: LPR lanes cover one row (4 columns each), RPP rows per pass
+  constexpr int LPR = WCOLS / 4, RPP = 64 / LPR;
+  const int c4 = lane % LPR, rsub = lane / LPR;
+  const int colb = col0 + c4 * 4;
+  f32x4 bias4 = {0.f, 0.f, 0.f, 0.f};
+  if (p.bias) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bias4[e] = colb + e < p.N ? p.bias[colb + e] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * g + (r & 3)) * EPI_LD + j * 32 + l32] = acc[i][j][r];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < 32 / RPP; ++it) {
+      const int rl = RPP * it + rsub;
+      const int row = row0 + i * 32 + rl;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * EPI_LD + c4 * 4);
+      if (row < p.M && colb < p.N) {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, bias4[e]);
+        const int64_t off = int64_t(row) * p.N + colb;
+        if (EPI == EPI_RESID) {
+          float* C = (float*)p.C;
+          const f32x4 old = load4(C + off);
+          store4(C + off, old + o);
+        } else if (EPI == EPI_F32) {
+          store4((float*)p.C + off, o);
+        } else {
+          store4((bf16*)p.C + off, o);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 template <int EPI, bool FP8, int WN>
 __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
   constexpr int NW = 2 * WN;                 // wavefronts: 2 (M) x WN (N)
@@ -205,7 +283,6 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
   constexpr int STEPS = FP8 ? 2 : 4;         // MFMA k-steps per staged K block
   constexpr int READS = (4 + NB) * (FP8 ? 2 : 1);  // LDS reads per k-step
   constexpr int MFMAS = 4 * NB;              // MFMAs per k-step
-  constexpr int EPI_LD = WCOLS + 8;          // fp32 row stride of the epilogue staging
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -254,79 +331,148 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // Main loop, rotated so that no wavefront idles on LDS latency after the
+  // per-block barrier: fragments are double buffered in registers (step s+1
+  // is read while step s computes), and the last k-step of stage kt computes
+  // after the barrier, from registers, while the first fragments of stage
+  // kt+1 are read.  The barrier therefore only has to follow this wavefront's
+  // reads of stage kt and its loads into stage kt+1; right after it, stage kt
+  // is free for the loads of block kt+2.
   const int KT = p.K * ESZ / ROWB;
   gload(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (KT > 1) gload(1, 1);
+  Frags<FP8, NB> fr[2];
+  load_frags<FP8, NB>(fr[0], smem, smem + BM * ROWB, 0, arow, brow, lane);
+  static_assert(STEPS % 2 == 0, "the last step's fragments sit in fr[1]");
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    // the other stage was last read in the previous iteration, before its barrier
-    if (kt + 1 < KT) gload(kt + 1, cur ^ 1);
     const char* sA = smem + cur * STAGE;
     const char* sB = sA + BM * ROWB;
-    // fragments double buffered in registers: step s+1 is read while step s computes
-    Frags<FP8, NB> fr[2];
-    load_frags<FP8, NB>(fr[0], sA, sB, 0, arow, brow, lane);
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      if (s + 1 < STEPS) load_frags<FP8, NB>(fr[(s + 1) & 1], sA, sB, s + 1, arow, brow, lane);
+    for (int s = 0; s + 1 < STEPS; ++s) {
+      load_frags<FP8, NB>(fr[(s + 1) & 1], sA, sB, s + 1, arow, brow, lane);
       mfma_frags<FP8, NB>(fr[s & 1], acc);
     }
-    // schedule: the first step's reads, then each step's MFMAs with the next
-    // step's reads spread between them
-    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
 #pragma unroll
     for (int s = 0; s + 1 < STEPS; ++s) sched_interleave<MFMAS, READS>();
-    __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);
-    // this iteration's loads of the next stage must have landed before anyone reads it
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // this wavefront's loads of stage kt+1 have landed and its reads of stage
+    // kt are done; after the barrier the same holds for every wavefront
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
+    if (kt + 2 < KT) gload(kt + 2, cur);
+    if (kt + 1 < KT) {
+      const char* nA = smem + (cur ^ 1) * STAGE;
+      load_frags<FP8, NB>(fr[0], nA, nA + BM * ROWB, 0, arow, brow, lane);
+    }
+    mfma_frags<FP8, NB>(fr[1], acc);
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 * LPO, 0);  // global -> LDS loads
+    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);    // next stage's first fragments
+    __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);    // this stage's last k-step
   }
 
   // ---- epilogue: per 32-row block, stage 32 x WCOLS fp32 through LDS ----
-  float alpha = 1.0f;
-  if (FP8) alpha = (*p.sa) * (*p.sb);
-  float* stg = reinterpret_cast<float*>(smem) + wave * (32 * EPI_LD);
+  store_tile<EPI, FP8, NB>(p, acc, reinterpret_cast<float*>(smem) + wave * (32 * (WCOLS + 8)), m0 + arow,
+                           n0 + brow, lane);
+}
+
+// Rows of C past the last full 256-row tile when there are at most 32 of
+// them (the TileShare row counts are multiples of 256 plus one global-token
+// row per tile window): one 32 x 32 output block per workgroup, K split over
+// its 8 wavefronts (128-byte k-groups dealt round robin, four in flight per
+// wavefront), operands read straight from global memory (each row's 128 bytes
+// of a k-group by the two lanes that own it), partial sums reduced through
+// LDS, then the same epilogue as the tile kernels.
+template <int EPI, bool FP8>
+__global__ __launch_bounds__(512) void k_gemm_rows(GemmP p) {
+  constexpr int NWR = 8, UNR = 4;
+  __shared__ float red[NWR][32][33];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  // read-back mapping: LPR lanes cover one row (4 columns each), RPP rows per pass
-  constexpr int LPR = WCOLS / 4, RPP = 64 / LPR;
-  const int c4 = lane % LPR, rsub = lane / LPR;
-  const int colb = n0 + brow + c4 * 4;
-  f32x4 bias4 = {0.f, 0.f, 0.f, 0.f};
-  if (p.bias) {
+  const int n0 = blockIdx.x * 32;
+  const int ESZ = FP8 ? 1 : 2;
+  const int64_t ld = int64_t(p.K) * ESZ;
+  const char* ar = (const char*)p.A + int64_t(min(l32, p.M - 1)) * ld;
+  const char* br = (const char*)p.B + int64_t(min(n0 + l32, p.N - 1)) * ld;
+  // byte offsets of this lane's four 16-byte chunks in a k-group: bf16 k-step
+  // j takes chunk j (k 16j + 8g ..); fp8 k-step j2 takes chunks 2j2, 2j2+1
+  // (k 64 j2 + 32 g ..); A and B use the same assignment
+  int co[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bias4[e] = colb + e < p.N ? p.bias[colb + e] : 0.f;
-  }
+  for (int j = 0; j < 4; ++j) co[j] = FP8 ? 64 * (j >> 1) + 32 * g + 16 * (j & 1) : 32 * j + 16 * g;
+  const int KT = p.K * ESZ / ROWB;
+  f32x16 acc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int kg0 = wave; kg0 < KT; kg0 += NWR * UNR) {
+    i32x4 a[UNR][4], b[UNR][4];
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int u = 0; u < UNR; ++u) {
+      const int kg = kg0 + u * NWR;
+      if (kg < KT) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * g + (r & 3)) * EPI_LD + j * 32 + l32] = acc[i][j][r];
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int it = 0; it < 32 / RPP; ++it) {
-      const int rl = RPP * it + rsub;
-      const int row = m0 + arow + i * 32 + rl;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * EPI_LD + c4 * 4);
-      if (row < p.M && colb < p.N) {
-        f32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI>(v[e], alpha, bias4[e]);
-        const int64_t off = int64_t(row) * p.N + colb;
-        if (EPI == EPI_RESID) {
-          float* C = (float*)p.C;
-          const f32x4 old = load4(C + off);
-          store4(C + off, old + o);
-        } else if (EPI == EPI_F32) {
-          store4((float*)p.C + off, o);
-        } else {
-          store4((bf16*)p.C + off, o);
+        for (int j = 0; j < 4; ++j) {
+          a[u][j] = *reinterpret_cast<const i32x4*>(ar + int64_t(kg) * ROWB + co[j]);
+          b[u][j] = *reinterpret_cast<const i32x4*>(br + int64_t(kg) * ROWB + co[j]);
         }
       }
     }
-    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (kg0 + u * NWR >= KT) break;
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[u][j]),
+                                                        __builtin_bit_cast(bf16x8, b[u][j]), acc, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+          const i32x4 a0 = a[u][2 * j2], a1 = a[u][2 * j2 + 1], b0 = b[u][2 * j2], b1 = b[u][2 * j2 + 1];
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]},
+              i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]}, acc, 0, 0, 0, 127, 0, 127);
+        }
+      }
+    }
   }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[wave][8 * (r >> 2) + 4 * g + (r & 3)][l32] = acc[r];
+  __syncthreads();
+  if (tid < 256) {
+    const int row = tid >> 3, c = (tid & 7) * 4, col = n0 + c;
+    if (row < p.M && col < p.N) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NWR; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += red[w][row][c + e];
+      const float alpha = FP8 ? (*p.sa) * (*p.sb) : 1.0f;
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, p.bias ? p.bias[col + e] : 0.f);
+      const int64_t off = int64_t(row) * p.N + col;
+      if (EPI == EPI_RESID) {
+        float* C = (float*)p.C;
+        store4(C + off, load4(C + off) + o);
+      } else if (EPI == EPI_F32) {
+        store4((float*)p.C + off, o);
+      } else {
+        store4((bf16*)p.C + off, o);
+      }
+    }
+  }
+}
+
+// Compute units of the current device (for the tile-round count).
+int device_cus() {
+  static int v = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    return n;
+  }();
+  return v;
 }
 
 // Wavefronts along N of the MFMA kernel: 2 (four wavefronts, 128x128 each) or
@@ -347,8 +493,8 @@ namespace tsk {
 hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, int M, int N, int K,
                 const float* bias, void* C, const float* sa, const float* sb) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  GemmP p{A, B, C, bias, sa, sb, M, N, K};
   if (act == ACT_F32) {
+    GemmP p{A, B, C, bias, sa, sb, M, N, K};
     const dim3 grid((N + FT - 1) / FT, (M + FT - 1) / FT), block(256);
     switch (epi) {
       case EPI_BIAS: hipLaunchKernelGGL(k_gemm_f32<EPI_BIAS>, grid, block, 0, s, p); break;
@@ -358,14 +504,30 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
     }
     return hipGetLastError();
   }
-  const int wn = gemm_waves_n();
-  const dim3 grid(((M + BM - 1) / BM) * ((N + BN - 1) / BN)), block(128 * wn);
-#define TS_G(E, F8)                                                                 \
-  do {                                                                              \
-    if (wn == 2) hipLaunchKernelGGL((k_gemm_mfma<E, F8, 2>), grid, block, 0, s, p); \
-    else hipLaunchKernelGGL((k_gemm_mfma<E, F8, 4>), grid, block, 0, s, p);         \
-  } while (0)
   const bool f8 = act == ACT_FP8;
+  const int esz = f8 ? 1 : 2, osz = (epi == EPI_RESID || epi == EPI_F32) ? 4 : 2;
+  // Ragged rows (M % 256 <= 32) go to k_gemm_rows when that saves a round of
+  // 256x256 tiles over the device's compute units (TS_GEMM_ROWS=always: in
+  // every such case, for tests).
+  const int tiles_n = (N + BN - 1) / BN, R = M % BM;
+  int Mm = M;
+  if (R != 0 && R <= 32) {
+    const char* e = getenv("TS_GEMM_ROWS");
+    const int64_t ncu = device_cus();
+    const int64_t all = int64_t((M + BM - 1) / BM) * tiles_n, full = int64_t(M / BM) * tiles_n;
+    if ((e && strcmp(e, "always") == 0) || (full > 0 && (full + ncu - 1) / ncu < (all + ncu - 1) / ncu)) Mm = M - R;
+  }
+  GemmP pm{A, B, C, bias, sa, sb, Mm, N, K};
+  GemmP pt{(const char*)A + int64_t(Mm) * K * esz, B, (char*)C + int64_t(Mm) * N * osz, bias, sa, sb, M - Mm, N, K};
+  const int wn = gemm_waves_n();
+  const dim3 grid(((Mm + BM - 1) / BM) * tiles_n), block(128 * wn), tgrid((N + 31) / 32);
+#define TS_G(E, F8)                                                                      \
+  do {                                                                                   \
+    if (Mm == 0) {                                                                       \
+    } else if (wn == 2) hipLaunchKernelGGL((k_gemm_mfma<E, F8, 2>), grid, block, 0, s, pm); \
+    else hipLaunchKernelGGL((k_gemm_mfma<E, F8, 4>), grid, block, 0, s, pm);              \
+    if (Mm < M) hipLaunchKernelGGL((k_gemm_rows<E, F8>), tgrid, dim3(512), 0, s, pt);     \
+  } while (0)
   switch (epi) {
     case EPI_BIAS: if (f8) TS_G(EPI_BIAS, true); else TS_G(EPI_BIAS, false); break;
     case EPI_BIAS_GELU: if (f8) TS_G(EPI_BIAS_GELU, true); else TS_G(EPI_BIAS_GELU, false); break;

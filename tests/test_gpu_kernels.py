@@ -56,6 +56,52 @@ def test_gemm_against_oracle(M_, N, K, epi, dtype):
         assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * rms)
 
 
+@pytest.mark.parametrize("M_", [5, 512 + 7, 256 + 32])
+@pytest.mark.parametrize("epi", [0, 1, 2, 3])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_gemm_ragged_rows_kernel(M_, epi, dtype, monkeypatch):
+    """Rows past the last full 256-row tile through the ragged-row kernel
+    (forced here; the library takes it when it saves a round of tiles): every
+    epilogue, both MFMA dtypes, N not a multiple of its 32-column blocks, K
+    spanning several k-groups per wavefront."""
+    monkeypatch.setenv("TS_GEMM_ROWS", "always")
+    N, K = 80, (1280 if dtype == "bf16" else 2304)
+    say(f"gemm ragged rows {dtype} epi={epi} M={M_} N={N} K={K}")
+    r = _rng(M_ + epi)
+    A = round_bf16(r.standard_normal((M_, K)).astype(np.float32))
+    B = round_bf16((0.05 * r.standard_normal((N, K))).astype(np.float32))
+    bias = r.standard_normal(N).astype(np.float32)
+    c0 = r.standard_normal((M_, N)).astype(np.float32)
+    a = torch.from_numpy(A).to(DEV, torch.bfloat16)
+    b = torch.from_numpy(B).to(DEV, torch.bfloat16)
+    out_f32 = epi >= 2
+    c = torch.from_numpy(c0).to(DEV) if out_f32 else torch.zeros(M_, N, dtype=torch.bfloat16, device=DEV)
+    if dtype == "bf16":
+        ts.ts_op_gemm(ts.TS_BF16, epi, a, b, torch.from_numpy(bias).to(DEV), c)
+        ref = A.astype(np.float64) @ B.astype(np.float64).T + bias
+    else:
+        a8 = torch.empty(M_, K, dtype=torch.uint8, device=DEV)
+        b8 = torch.empty(N, K, dtype=torch.uint8, device=DEV)
+        sc = torch.empty(2, dtype=torch.float32, device=DEV)
+        ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+        ts.ts_fp8_quantize(a, a8, sc[0:1], ws)
+        ts.ts_fp8_quantize(b, b8, sc[1:2], ws)
+        ts.ts_op_gemm(ts.TS_FP8E4M3, epi, a8, b8, torch.from_numpy(bias).to(DEV), c, sc[0:1], sc[1:2])
+        ref = ofp8.fp8_linear(A, B, bias)
+    torch.cuda.synchronize()
+    if epi == 1:
+        ref = M.gelu(ref)
+    if epi == 2:
+        ref = ref + c0
+    got = c.float().cpu().numpy()
+    rms = np.sqrt(np.mean(ref * ref))
+    # bf16 products are exact and summed in fp32 (1e-5); fp8: the MFMA's
+    # internal sum of one instruction's 64 products (2e-4); bf16 outputs add
+    # one round to nearest (2^-8 of the value)
+    bound = (1e-5 if dtype == "bf16" else 2e-4) * rms + (0 if out_f32 else 2.0 ** -8 * np.abs(ref))
+    assert np.all(np.abs(got - ref) <= bound)
+
+
 def test_gemm_fp8_against_oracle():
     say("gemm fp8")
     r = _rng(7)
