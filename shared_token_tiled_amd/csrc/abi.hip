@@ -221,9 +221,30 @@ ts_status proj(const Ctx& c, const WS& ws, bool f8, const char* role, int epi, c
   return TS_OK;
 }
 
-// Window attention of every (tile, head) for one layer.
-ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared, const void* qkv, void* out,
-                           hipStream_t s, float* gscratch = nullptr, int64_t gscratch_floats = 0) {
+// RoPE coordinates of the rows of a shared-layout (n_union + n_tiles rows)
+// or per-tile-layout (n_tiles*(n+1) rows) qkv array.
+tsk::RopeRows rope_rows(const ts_plan* p, bool shared) {
+  tsk::RopeRows r;
+  r.shared = shared;
+  r.n_union = p->n_union;
+  r.n = p->n;
+  r.n_tiles = p->n_tiles;
+  r.tile_start = (const int*)p->d_tile_start;
+  r.local_pos = (const int*)p->d_local_pos;
+  r.tab = (const float*)p->d_rope_glob;
+  for (int a = 0; a < 3; ++a) {
+    r.grid[a] = p->desc.grid[a];
+    r.off[a] = p->rope_glob_off[a];
+    r.pairs[a] = p->rope_pairs[a];
+  }
+  return r;
+}
+
+// Window attention of every (tile, head) for one layer.  rope: q and k are
+// as the QKV projection (and QK-norm) left them and the kernels rotate them
+// by tile-local positions; otherwise qk_prep has rotated them already.
+ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared, bool rope, const void* qkv,
+                           void* out, hipStream_t s, float* gscratch = nullptr, int64_t gscratch_floats = 0) {
   tsk::AttnArgs a;
   a.qkv = qkv;
   a.out = out;
@@ -243,7 +264,7 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared
     a.rope_wbase[ax] = p->rope_wbase[ax];
     a.rope_wpairs[ax] = p->rope_wpairs[ax];
   }
-  if (m->act_dtype == TS_BF16) {
+  if (rope && m->act_dtype == TS_BF16) {
     // the bf16 kernels rotate 8 dims (4 pairs) at a time and allow a group to
     // straddle one axis boundary, not two
     const int b0 = p->rope_pairs[0], b1 = p->rope_pairs[0] + p->rope_pairs[1];
@@ -256,18 +277,18 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared
   const double nn = double(p->n + 1), ab = act_bytes(m->act_dtype);
   if (m->act_dtype == TS_F32) {
     Scope sc(s, "attn_f32", 4.0 * nn * nn * m->d * p->n_tiles, double(p->n_tiles) * nn * m->d * 4 * ab);
-    TS_HIP(tsk::attention(s, m->act_dtype, a), "attention");
+    TS_HIP(tsk::attention(s, m->act_dtype, a, rope), "attention");
     return TS_OK;
   }
   {
     Scope sc(s, "attn_bf16", 4.0 * double(p->n) * nn * m->d * p->n_tiles,
              double(p->n_tiles) * (nn * 3 * m->d + double(p->n) * m->d) * ab);
-    TS_HIP(tsk::attention(s, m->act_dtype, a), "attention");
+    TS_HIP(tsk::attention(s, m->act_dtype, a, rope), "attention");
   }
   {
     Scope sc(s, "attn_global_bf16", 4.0 * nn * m->d * p->n_tiles,
              double(p->n_tiles) * (nn * 2 * m->d + 2 * m->d) * ab);
-    TS_HIP(tsk::attention_global(s, a, gscratch, gscratch_floats), "attention (global rows)");
+    TS_HIP(tsk::attention_global(s, a, rope, gscratch, gscratch_floats), "attention (global rows)");
   }
   return TS_OK;
 }
@@ -295,11 +316,14 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
   if ((st = proj(c, ws, (f8 & TS_FP8_QKV) != 0, "qkv", tsk::EPI_BIAS, ws.h, M, 3 * d, d, w.w_qkv, w.w_qkv_f8,
                  w.w_scale_f8 ? w.w_scale_f8 + 0 : nullptr, w.b_qkv, ws.big)) != TS_OK)
     return st;
-  if (m->qk_norm) {
-    Scope sc(c.s, "qk_norm", 0.0, double(M * 2 * d) * 2 * ab);
-    TS_HIP(tsk::qk_norm(c.s, act, ws.big, int(M), d, H, hd, w.q_g, w.k_g, m->eps), "qk_norm");
+  {
+    Scope sc(c.s, "qk_prep", 0.0, double(M * 2 * d) * 2 * ab);
+    TS_HIP(tsk::qk_prep(c.s, act, ws.big, int(M), d, H, hd, m->qk_norm ? w.q_g : nullptr, w.k_g, m->eps,
+                        rope_rows(p, shared)),
+           "qk_prep");
   }
-  if ((st = window_attention(m, p, shared, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats)) != TS_OK) return st;
+  if ((st = window_attention(m, p, shared, false, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats)) != TS_OK)
+    return st;
   const void* aout = ws.o;
   if (shared) {
     Scope sc(c.s, "blend", 0.0, (double(p->n_entries + p->n_tiles) + double(Ms)) * d * ab);
@@ -367,11 +391,13 @@ ts_status run_layer_partial(const Ctx& c, const ts_layer_weights& w, float* X, i
   if ((st = proj(c, ws, false, "qkv", tsk::EPI_BIAS, ws.h, Mq, 3 * d, d, w.w_qkv, nullptr, nullptr, w.b_qkv,
                  ws.big)) != TS_OK)
     return st;
-  if (m->qk_norm) {
-    Scope sc(c.s, "qk_norm", 0.0, double(Mq * 2 * d) * 2 * ab);
-    TS_HIP(tsk::qk_norm(c.s, act, ws.big, int(Mq), d, H, hd, w.q_g, w.k_g, m->eps), "qk_norm");
+  {
+    Scope sc(c.s, "qk_prep", 0.0, double(Mq * 2 * d) * 2 * ab);
+    TS_HIP(tsk::qk_prep(c.s, act, ws.big, int(Mq), d, H, hd, m->qk_norm ? w.q_g : nullptr, w.k_g, m->eps,
+                        rope_rows(p, sq)),
+           "qk_prep");
   }
-  if ((st = window_attention(m, p, sq, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats)) != TS_OK) return st;
+  if ((st = window_attention(m, p, sq, false, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats)) != TS_OK) return st;
   // out-projection
   if (so) {
     {
@@ -623,7 +649,8 @@ ts_status ts_plan_export_rope(const ts_plan* p, int32_t head_dim, float rope_bas
 }
 
 static void free_device(ts_plan* p) {
-  void** ptrs[] = {&p->d_tile_rows, &p->d_cover_ptr, &p->d_entry_row, &p->d_cover_w, &p->d_local_pos, &p->d_rope};
+  void** ptrs[] = {&p->d_tile_rows, &p->d_cover_ptr, &p->d_entry_row, &p->d_cover_w,
+                   &p->d_local_pos, &p->d_rope,      &p->d_rope_glob, &p->d_tile_start};
   for (void** q : ptrs) {
     if (*q) (void)hipFree(*q);
     *q = nullptr;
@@ -638,6 +665,9 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
   int32_t pairs[3], off[3], wbase[3], wpairs[3];
   tsplan::rope_table(*p, head_dim, rope_base, tab, pairs, off, wbase, wpairs);
   if (tab.size() > 4096) return fail(TS_ESHAPE, "RoPE table exceeds 16 KB (head_dim/2 * tile extent too large)");
+  std::vector<float> gtab;
+  int32_t goff[3];
+  tsplan::rope_table_global(*p, head_dim, rope_base, gtab, goff);
   std::vector<int32_t> entry_row(p->n_entries);
   for (int32_t e = 0; e < p->n_entries; ++e) entry_row[e] = p->cover_tile[e] * (p->n + 1) + p->cover_local[e];
   free_device(p);
@@ -653,6 +683,8 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
       {&p->d_cover_w, p->cover_w.data(), p->cover_w.size() * 4},
       {&p->d_local_pos, p->local_pos.data(), p->local_pos.size() * 4},
       {&p->d_rope, tab.data(), tab.size() * 4},
+      {&p->d_rope_glob, gtab.data(), gtab.size() * 4},
+      {&p->d_tile_start, p->tile_start.data(), p->tile_start.size() * 4},
   };
   for (auto& it : items) {
     if (hipMalloc(it.dst, std::max<size_t>(it.bytes, 4)) != hipSuccess) {
@@ -675,6 +707,7 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
     p->rope_off[a] = off[a];
     p->rope_wbase[a] = wbase[a];
     p->rope_wpairs[a] = wpairs[a];
+    p->rope_glob_off[a] = goff[a];
   }
   p->rope_hd = head_dim;
   p->rope_base = rope_base;
@@ -783,7 +816,7 @@ ts_status ts_op_window_attention(const ts_model_desc* m, const ts_plan* p, int32
   if ((st = check_model(m)) != TS_OK) return st;
   if ((st = check_plan(p, m)) != TS_OK) return st;
   if (!qkv || !out) return fail(TS_EINVAL, "qkv and out must be non-null");
-  return window_attention(m, p, shared != 0, qkv, out, (hipStream_t)stream);
+  return window_attention(m, p, shared != 0, true, qkv, out, (hipStream_t)stream);
 }
 
 ts_status ts_profile_begin(void) {

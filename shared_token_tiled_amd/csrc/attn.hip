@@ -67,7 +67,7 @@ __device__ __forceinline__ float2 rope_cs(const AttnP& p, const float* tab, int 
 
 // ------------------------------------------------------------- fp32 -----
 // One thread per query row, keys staged through LDS 64 at a time.
-template <int HD>
+template <int HD, bool ROPE>
 __global__ __launch_bounds__(64) void k_attn_f32(AttnP p) {
   __shared__ float Ks[64][HD + 1];
   __shared__ float Vs[64][HD + 1];
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnP p) {
 #pragma unroll
   for (int k = 0; k < HD / 2; ++k) {
     float c = 1.f, s = 0.f;
-    if (pos >= 0) {
+    if (ROPE && pos >= 0) {
       const float2 cs = rope_cs(p, p.rope, k, pos);
       c = cs.x;
       s = cs.y;
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnP p) {
         const float* vp = qkv + r * ld + 2 * p.d + h * HD;
         const int kpos = p.local_pos[j];
         for (int k = 0; k < HD / 2; ++k) {
-          const float2 cs = rope_cs(p, p.rope, k, kpos);
+          const float2 cs = ROPE ? rope_cs(p, p.rope, k, kpos) : make_float2(1.f, 0.f);
           const float a = kp[2 * k], b = kp[2 * k + 1];
           Ks[threadIdx.x][2 * k] = a * cs.x - b * cs.y;
           Ks[threadIdx.x][2 * k + 1] = a * cs.y + b * cs.x;
@@ -217,7 +217,7 @@ __device__ __forceinline__ bf16x8 rope_group(const float* tab, const GroupRope& 
   return o;
 }
 
-template <int HD>
+template <int HD, bool ROPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(AttnP p) {
   constexpr int NT = NW * 64;         // threads
   constexpr int HC = HD / 8;          // 16-byte chunks per head row
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   static_assert(VSB <= NT, "one V unit per thread");
   __shared__ __attribute__((aligned(16))) char Ks[2][KB * KROWB];
   __shared__ __attribute__((aligned(16))) char Vt[2][HD * KB * 2];
-  __shared__ __attribute__((aligned(16))) float rope_s[ROPE_LDS_FLOATS];
+  __shared__ __attribute__((aligned(16))) float rope_s[ROPE ? ROPE_LDS_FLOATS : 4];
   __shared__ int idx_s[2][2][KB];     // [slot][row | pos][key]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -255,12 +255,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bf16* vbase = qkv + 2 * p.d + h * HD;
   const int nkb = (n + KB - 1) / KB;
 
-  for (int e = tid; e < p.rope_floats; e += NT) rope_s[e] = p.rope[e];
+  if (ROPE)
+    for (int e = tid; e < p.rope_floats; e += NT) rope_s[e] = p.rope[e];
   // row index and position of key j (clamped into the window)
   auto key_meta = [&](int j, int& row, int& pos) {
     j = min(j, n - 1);
     row = window_row(p, t, j);
-    pos = p.local_pos[j];
+    pos = ROPE ? p.local_pos[j] : 0;
   };
   if (tid < KB) {
     int r0, p0, r1, p1;
@@ -287,11 +288,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bool v_on = tid < VSB;
   const int v_hc = (tid & 7) + 8 * (tid / 256), v_k2 = (tid >> 3) & 31;
   i32x4 kreg[KCPT], vreg[2];
+  // without RoPE, K goes straight from global memory to LDS (global_load_lds:
+  // lane l of a wavefront instruction writes 16 bytes at LDS base + 16*l):
+  // instruction i of wavefront w fills bytes [(w*KDI + i) KB, +1 KB) of the
+  // stage, i.e. row b / KROWB, slot (b % KROWB) / 16 for lane byte b, and the
+  // lane loads the logical chunk the swizzle puts in that slot
+  constexpr int KDI = KB * KROWB / 1024 / NW;  // K DMA instructions per wavefront
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto gload = [&](int slot) {
-    const int r = idx_s[slot][0][kr_row];
+    if constexpr (!ROPE) {
 #pragma unroll
-    for (int i = 0; i < KCPT; ++i)
-      kreg[i] = *reinterpret_cast<const i32x4*>(kbase + r * ld + (kpart + 8 * i) * 8);
+      for (int i = 0; i < KDI; ++i) {
+        const int b = (wv * KDI + i) * 1024 + 16 * lane;
+        const int row = b / KROWB, c = ((b % KROWB) / 16) ^ kswz<HD>(row);
+        const int r = idx_s[slot][0][row];
+        __builtin_amdgcn_global_load_lds((const void*)(kbase + r * ld + c * 8),
+                                         (TS_LDS void*)(&Ks[slot][(wv * KDI + i) * 1024]), 16, 0, 0);
+      }
+    } else {
+      const int r = idx_s[slot][0][kr_row];
+#pragma unroll
+      for (int i = 0; i < KCPT; ++i)
+        kreg[i] = *reinterpret_cast<const i32x4*>(kbase + r * ld + (kpart + 8 * i) * 8);
+    }
     if (v_on) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -301,12 +320,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
   auto lstore = [&](int slot, int st) {
-    const int pos = idx_s[slot][1][kr_row];
+    if constexpr (ROPE) {
+      const int pos = idx_s[slot][1][kr_row];
 #pragma unroll
-    for (int i = 0; i < KCPT; ++i) {
-      const int c = kpart + 8 * i;
-      const bf16x8 o = rope_group(rope_s, kgr[i], pos, __builtin_bit_cast(bf16x8, kreg[i]));
-      *reinterpret_cast<bf16x8*>(&Ks[st][kr_row * KROWB + ((c ^ kswz<HD>(kr_row)) * 16)]) = o;
+      for (int i = 0; i < KCPT; ++i) {
+        const int c = kpart + 8 * i;
+        const bf16x8 o = rope_group(rope_s, kgr[i], pos, __builtin_bit_cast(bf16x8, kreg[i]));
+        *reinterpret_cast<bf16x8*>(&Ks[st][kr_row * KROWB + ((c ^ kswz<HD>(kr_row)) * 16)]) = o;
+      }
     }
     if (v_on) {
       const bf16x8 v0 = __builtin_bit_cast(bf16x8, vreg[0]), v1 = __builtin_bit_cast(bf16x8, vreg[1]);
@@ -341,7 +362,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       const int hd0 = 16 * s + 8 * g;
-      const bf16x8 r = rope_group(rope_s, group_rope(p, hd0 / 8), qpos, *reinterpret_cast<const bf16x8*>(qp + hd0));
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qp + hd0);
+      const bf16x8 r = ROPE ? rope_group(rope_s, group_rope(p, hd0 / 8), qpos, qv) : qv;
       const bf16x8 kg = *reinterpret_cast<const bf16x8*>(kgp + hd0);
       qf[s] = r;
 #pragma unroll
@@ -358,6 +380,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 
   lstore(0, 0);
+  if (!ROPE) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's K DMA landed
   __syncthreads();
   const int krow_a = swap23(l32);  // key row this lane feeds as MFMA A row
   for (int kb = 0; kb < nkb; ++kb) {
@@ -458,6 +481,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       idx_s[cur][0][tid] = pre_r;
       idx_s[cur][1][tid] = pre_p;
     }
+    if (!ROPE) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
@@ -488,7 +512,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // split leaves its state (max m, weight sum l, unnormalised output o[HD], in
 // the exp2 domain) in `part` for k_attn_global_merge.
 constexpr int GCH = 1024;
-template <int HD, int NT>
+template <int HD, int NT, bool ROPE>
 __global__ __launch_bounds__(NT) void k_attn_global_bf16(AttnP p, int split_keys, float* part) {
   constexpr int TPK = HD / 16;    // threads per key, score pass
   constexpr int KPP = NT / TPK;   // keys per score pass
@@ -524,7 +548,7 @@ __global__ __launch_bounds__(NT) void k_attn_global_bf16(AttnP p, int split_keys
       const int64_t r = window_row(p, t, j);
       const bf16* kp = qkv + r * ld + p.d + h * HD + 16 * sub;
       bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kp), k1 = *reinterpret_cast<const bf16x8*>(kp + 8);
-      if (j < n) {
+      if (ROPE && j < n) {
         const int pos = p.local_pos[j];
         k0 = rope_group(p.rope, gr0, pos, k0);
         k1 = rope_group(p.rope, gr1, pos, k1);
@@ -621,20 +645,32 @@ static AttnP make_params(const AttnArgs& a) {
                1.4426950408889634f / sqrtf(float(a.hd))};
 }
 
-hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
+hipError_t attention(hipStream_t s, int act, const AttnArgs& a, bool rope) {
   const AttnP p = make_params(a);
   if (act == ACT_F32) {
     const dim3 grid((a.n + 1 + 63) / 64, a.H, a.n_tiles), block(64);
-    if (a.hd == 32) hipLaunchKernelGGL(k_attn_f32<32>, grid, block, 0, s, p);
-    else if (a.hd == 64) hipLaunchKernelGGL(k_attn_f32<64>, grid, block, 0, s, p);
-    else return hipErrorInvalidValue;
+    if (a.hd == 32) {
+      if (rope) hipLaunchKernelGGL((k_attn_f32<32, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((k_attn_f32<32, false>), grid, block, 0, s, p);
+    } else if (a.hd == 64) {
+      if (rope) hipLaunchKernelGGL((k_attn_f32<64, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((k_attn_f32<64, false>), grid, block, 0, s, p);
+    } else {
+      return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
   if (a.n < 1) return hipErrorInvalidValue;
   const dim3 grid(((a.n + QB - 1) / QB) * a.H * a.n_tiles), block(NW * 64);
-  if (a.hd == 64) hipLaunchKernelGGL(k_attn_bf16<64>, grid, block, 0, s, p);
-  else if (a.hd == 128) hipLaunchKernelGGL(k_attn_bf16<128>, grid, block, 0, s, p);
-  else return hipErrorInvalidValue;
+  if (a.hd == 64) {
+    if (rope) hipLaunchKernelGGL((k_attn_bf16<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_attn_bf16<64, false>), grid, block, 0, s, p);
+  } else if (a.hd == 128) {
+    if (rope) hipLaunchKernelGGL((k_attn_bf16<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_attn_bf16<128, false>), grid, block, 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -650,14 +686,19 @@ int attention_global_splits(const AttnArgs& a, int64_t scratch_floats) {
   return std::max(1, std::min(splits, 64));
 }
 
-hipError_t attention_global(hipStream_t s, const AttnArgs& a, float* scratch, int64_t scratch_floats) {
+hipError_t attention_global(hipStream_t s, const AttnArgs& a, bool rope, float* scratch, int64_t scratch_floats) {
   const AttnP p = make_params(a);
   if (a.n < 1 || (a.hd != 64 && a.hd != 128)) return hipErrorInvalidValue;
   const int splits = scratch ? attention_global_splits(a, scratch_floats) : 1;
+#define TS_GL(HD, NT, SK, PART)                                                                           \
+  do {                                                                                                    \
+    if (rope) hipLaunchKernelGGL((k_attn_global_bf16<HD, NT, true>), grid, dim3(NT), 0, s, p, SK, PART);  \
+    else hipLaunchKernelGGL((k_attn_global_bf16<HD, NT, false>), grid, dim3(NT), 0, s, p, SK, PART);      \
+  } while (0)
   if (splits == 1) {
     const dim3 grid(a.H, a.n_tiles, 1);
-    if (a.hd == 64) hipLaunchKernelGGL((k_attn_global_bf16<64, 1024>), grid, dim3(1024), 0, s, p, a.n + 1, nullptr);
-    else hipLaunchKernelGGL((k_attn_global_bf16<128, 1024>), grid, dim3(1024), 0, s, p, a.n + 1, nullptr);
+    if (a.hd == 64) TS_GL(64, 1024, a.n + 1, nullptr);
+    else TS_GL(128, 1024, a.n + 1, nullptr);
     return hipGetLastError();
   }
   int split_keys = (a.n + 1 + splits - 1) / splits;
@@ -665,12 +706,13 @@ hipError_t attention_global(hipStream_t s, const AttnArgs& a, float* scratch, in
   const int used = (a.n + 1 + split_keys - 1) / split_keys;   // every split holds >= 1 key
   const dim3 grid(a.H, a.n_tiles, used);
   if (a.hd == 64) {
-    hipLaunchKernelGGL((k_attn_global_bf16<64, 256>), grid, dim3(256), 0, s, p, split_keys, scratch);
+    TS_GL(64, 256, split_keys, scratch);
     hipLaunchKernelGGL(k_attn_global_merge<64>, dim3(a.H, a.n_tiles), dim3(64), 0, s, p, used, scratch);
   } else {
-    hipLaunchKernelGGL((k_attn_global_bf16<128, 256>), grid, dim3(256), 0, s, p, split_keys, scratch);
+    TS_GL(128, 256, split_keys, scratch);
     hipLaunchKernelGGL(k_attn_global_merge<128>, dim3(a.H, a.n_tiles), dim3(128), 0, s, p, used, scratch);
   }
+#undef TS_GL
   return hipGetLastError();
 }
 

@@ -74,13 +74,18 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, int M
   }
 }
 
-// ---- per-head QK-RMSNorm (Table S1: once per token) ----------------------
+// ---- per-head QK-RMSNorm (Table S1: once per token) and RoPE --------------
 // HD/8 lanes per (row, head slice); slices 0..H-1 are q heads, H..2H-1 k heads,
 // and slice s starts at column s*HD of the [q | k | v] row in both cases.
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void k_qknorm(T* __restrict__ qkv, int M, int d, int H,
+// NORM: RMS-normalise each head and scale by its gain first.  Then every q
+// and k head is rotated by the row's grid coordinates (RopeRows): the angle
+// of pair i of axis a is coord_a * base^(-i / pairs_a), so the score of two
+// window tokens depends only on their coordinate difference, as with
+// tile-local positions, and the attention kernels stage keys unchanged.
+template <typename T, int HD, bool NORM>
+__global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int d, int H,
                                                 const float* __restrict__ qg,
-                                                const float* __restrict__ kg, float eps) {
+                                                const float* __restrict__ kg, float eps, tsk::RopeRows rr) {
   constexpr int LPS = HD / 8;
   const int64_t gid = (int64_t(blockIdx.x) * 256 + threadIdx.x) / LPS;
   const int sub = threadIdx.x % LPS;
@@ -91,20 +96,49 @@ __global__ __launch_bounds__(256) void k_qknorm(T* __restrict__ qkv, int M, int 
   T* p = qkv + row * 3 * int64_t(d) + int64_t(sl) * HD + sub * 8;
   f32x4 a = ok ? load4(p) : f32x4{0, 0, 0, 0};
   f32x4 c = ok ? load4(p + 4) : f32x4{0, 0, 0, 0};
-  float ss = a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3] + c[0] * c[0] + c[1] * c[1] +
-             c[2] * c[2] + c[3] * c[3];
-  ss = group_sum(ss, LPS);
+  if constexpr (NORM) {
+    float ss = a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3] + c[0] * c[0] + c[1] * c[1] +
+               c[2] * c[2] + c[3] * c[3];
+    ss = group_sum(ss, LPS);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / HD) + eps);
+    const float* gg = (sl < H ? qg : kg) + sub * 8;
+    const f32x4 g0 = ok ? load4(gg) : f32x4{0, 0, 0, 0}, g1 = ok ? load4(gg + 4) : f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = a[e] * inv * g0[e];
+      c[e] = c[e] * inv * g1[e];
+    }
+  }
   if (!ok) return;
-  const float inv = 1.0f / sqrtf(ss * (1.0f / HD) + eps);
-  const float* gg = (sl < H ? qg : kg) + sub * 8;
-  const f32x4 g0 = load4(gg), g1 = load4(gg + 4);
+  // grid coordinates of the row
+  int co[3];
+  const int r = int(row);
+  if (rr.shared && r < rr.n_union) {
+    co[2] = r % rr.grid[2];
+    co[1] = (r / rr.grid[2]) % rr.grid[1];
+    co[0] = r / (rr.grid[2] * rr.grid[1]);
+  } else {
+    const int t = rr.shared ? r - rr.n_union : r / (rr.n + 1), i = rr.shared ? rr.n : r % (rr.n + 1);
+    const int lp = i < rr.n ? rr.local_pos[i] : 0;
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) co[ax] = rr.tile_start[3 * t + ax] + ((lp >> (10 * ax)) & 1023);
+  }
+  float v[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    a[e] = a[e] * inv * g0[e];
-    c[e] = c[e] * inv * g1[e];
+    const int k = 4 * sub + e;
+    const int ax = k < rr.pairs[0] ? 0 : (k < rr.pairs[0] + rr.pairs[1] ? 1 : 2);
+    const int i = ax == 0 ? k : (ax == 1 ? k - rr.pairs[0] : k - rr.pairs[0] - rr.pairs[1]);
+    const int np = ax == 0 ? rr.pairs[0] : (ax == 1 ? rr.pairs[1] : rr.pairs[2]);
+    const int off = ax == 0 ? rr.off[0] : (ax == 1 ? rr.off[1] : rr.off[2]);
+    const int cc = ax == 0 ? co[0] : (ax == 1 ? co[1] : co[2]);
+    const float2 cs = *reinterpret_cast<const float2*>(rr.tab + off + 2 * (cc * np + i));
+    const float x = v[2 * e], y = v[2 * e + 1];
+    v[2 * e] = x * cs.x - y * cs.y;
+    v[2 * e + 1] = x * cs.y + y * cs.x;
   }
-  store4(p, a);
-  store4(p + 4, c);
+  store4(p, f32x4{v[0], v[1], v[2], v[3]});
+  store4(p + 4, f32x4{v[4], v[5], v[6], v[7]});
 }
 
 // ---- w-bar blend / state merge (Figure 2 caption: the only approximate step)
@@ -268,13 +302,17 @@ hipError_t norm(hipStream_t s, int act, bool rms, const float* x, int M, int d, 
   return hipGetLastError();
 }
 
-hipError_t qk_norm(hipStream_t s, int act, void* qkv, int M, int d, int H, int hd, const float* qg,
-                   const float* kg, float eps) {
+hipError_t qk_prep(hipStream_t s, int act, void* qkv, int M, int d, int H, int hd, const float* qg,
+                   const float* kg, float eps, const RopeRows& rr) {
   if (M <= 0) return hipSuccess;
   const int64_t threads = int64_t(M) * 2 * H * (hd / 8);
   const dim3 grid(unsigned((threads + 255) / 256)), block(256);
-#define TS_QK(T, HD)                                                                              \
-  hipLaunchKernelGGL((k_qknorm<T, HD>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps)
+  const bool norm = qg != nullptr;
+#define TS_QK(T, HD)                                                                                         \
+  do {                                                                                                       \
+    if (norm) hipLaunchKernelGGL((k_qkprep<T, HD, true>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps, rr); \
+    else hipLaunchKernelGGL((k_qkprep<T, HD, false>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps, rr);    \
+  } while (0)
   if (act == ACT_F32) {
     if (hd == 32) TS_QK(float, 32); else if (hd == 64) TS_QK(float, 64); else TS_QK(float, 128);
   } else {

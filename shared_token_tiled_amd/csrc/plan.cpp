@@ -180,4 +180,27 @@ void rope_table(const ts_plan& p, int32_t head_dim, float base, std::vector<floa
   }
 }
 
+// RoPE table over the whole grid: axis a's block holds, for every grid
+// coordinate pos in [0, grid[a]) and every pair i of the axis, (cos, sin) of
+// pos * base^(-i / pairs[a]) at tab[off[a] + 2*(pos*pairs[a] + i) + {0, 1}].
+void rope_table_global(const ts_plan& p, int32_t head_dim, float base, std::vector<float>& tab, int32_t off[3]) {
+  int32_t pairs[3];
+  rope_pairs(p.desc.ndim, head_dim, pairs);
+  int32_t total = 0;
+  for (int a = 0; a < 3; ++a) {
+    off[a] = total;
+    total += 2 * pairs[a] * p.desc.grid[a];
+  }
+  tab.assign(size_t(total), 0.f);
+  for (int a = 0; a < 3; ++a)
+    for (int32_t i = 0; i < pairs[a]; ++i) {
+      const double inv = std::pow(double(base), double(-i) / double(pairs[a]));
+      for (int32_t pos = 0; pos < p.desc.grid[a]; ++pos) {
+        const double ang = double(pos) * inv;
+        tab[off[a] + 2 * (size_t(pos) * pairs[a] + i)] = float(std::cos(ang));
+        tab[off[a] + 2 * (size_t(pos) * pairs[a] + i) + 1] = float(std::sin(ang));
+      }
+    }
+}
+
 }  // namespace tsplan

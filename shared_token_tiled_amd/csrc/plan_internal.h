@@ -27,6 +27,9 @@ struct ts_plan {
   void* d_cover_w = nullptr;     // fp32 [n_entries]
   void* d_local_pos = nullptr;   // int32 [n]
   void* d_rope = nullptr;        // compact per-axis (cos, sin) table, see rope_table
+  void* d_rope_glob = nullptr;   // grid-coordinate (cos, sin) table, see rope_table_global
+  void* d_tile_start = nullptr;  // int32 [n_tiles*3]
+  int32_t rope_glob_off[3] = {0, 0, 0};
   int32_t rope_hd = 0;
   float rope_base = 0.f;
   int32_t rope_floats = 0;       // floats in the compact table
@@ -51,4 +54,10 @@ void rope_pairs(int32_t ndim, int32_t head_dim, int32_t out[3]);
 // pairs that belong to another axis hold the identity (1, 0).
 void rope_table(const ts_plan& p, int32_t head_dim, float base, std::vector<float>& tab, int32_t pairs[3],
                 int32_t off[3], int32_t wbase[3], int32_t wpairs[3]);
+// RoPE table over grid coordinates: pair i of axis a at coordinate pos is
+// (cos, sin) at tab[off[a] + 2*(pos*pairs[a] + i) + {0, 1}].  Rotating every
+// row by its grid coordinate gives the same token-token scores as rotating by
+// tile-local positions (the angle of a pair depends only on the coordinate
+// difference); the global token of tile t is rotated by the tile's start.
+void rope_table_global(const ts_plan& p, int32_t head_dim, float base, std::vector<float>& tab, int32_t off[3]);
 }  // namespace tsplan

@@ -22,8 +22,25 @@ enum Epi {
 hipError_t norm(hipStream_t s, int act, bool rms, const float* x, int M, int d, const float* g,
                 const float* b, float eps, void* y);
 // In place per-head RMSNorm of the q and k sections of qkv [M, 3d] (act).
-hipError_t qk_norm(hipStream_t s, int act, void* qkv, int M, int d, int H, int hd, const float* qg,
-                   const float* kg, float eps);
+// RoPE coordinates of the rows of a qkv array for qk_prep.  Shared layout
+// (shared = true): row r < n_union is grid row r (coordinates (r / (gh*gw),
+// (r / gw) % gh, r % gw) for grid = {gt, gh, gw}), row n_union + t is tile
+// t's global token at the tile's start.  Per-tile layout: row t*(n+1) + i is
+// tile t's start plus the local position of window token i (i = n: the
+// global token, the start itself).
+struct RopeRows {
+  bool shared;
+  int n_union, n, n_tiles;
+  int grid[3];
+  const int* tile_start;   // [n_tiles*3] (t, h, w)
+  const int* local_pos;    // [n] packed tau | y<<10 | x<<20
+  const float* tab;        // (cos, sin) of pair i of axis a at coordinate c: tab[off[a] + 2*(c*pairs[a] + i)]
+  int off[3], pairs[3];
+};
+// In place on the q and k heads of qkv [M, 3d]: QK-RMSNorm with gains qg, kg
+// (skipped when qg is null), then RoPE by the rows' coordinates.
+hipError_t qk_prep(hipStream_t s, int act, void* qkv, int M, int d, int H, int hd, const float* qg,
+                   const float* kg, float eps, const RopeRows& rr);
 // out_union[p] = sum_e w[e] * in[entry_row[e]] over cover_ptr[p]..cover_ptr[p+1];
 // out_global[t] = in[t*(n+1)+n] (skipped when out_global is null).
 hipError_t blend(hipStream_t s, int tin, int tout, const void* in, int d, int n_union, int n_tiles,
@@ -67,11 +84,13 @@ struct AttnArgs {
 };
 // fp32: every window row.  bf16: the n tile-token query rows of every window;
 // the global-token row (window row n) is attention_global's.
-hipError_t attention(hipStream_t s, int act, const AttnArgs& a);
+// rope: rotate q and k by tile-local positions while staging (the global
+// token unrotated); otherwise they are used as stored (rotated by qk_prep).
+hipError_t attention(hipStream_t s, int act, const AttnArgs& a, bool rope);
 // bf16 only: the global-token query row of every (tile, head).  With
 // scratch (fp32, scratch_floats long) the keys are split over several
 // workgroups per row and merged by a second kernel; without, one workgroup
 // per row.
-hipError_t attention_global(hipStream_t s, const AttnArgs& a, float* scratch, int64_t scratch_floats);
+hipError_t attention_global(hipStream_t s, const AttnArgs& a, bool rope, float* scratch, int64_t scratch_floats);
 
 }  // namespace tsk
