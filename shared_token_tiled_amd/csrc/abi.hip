@@ -144,6 +144,7 @@ struct WS {
   uint8_t* q8 = nullptr;     // e4m3 [M_s, max(d, mlp)] quantised GEMM operand
   float* gpart = nullptr;    // fp32 split states of the global-token attention rows
   int64_t gpart_floats = 0;
+  void* vt = nullptr;        // bf16 [n_tiles, d, n_pad] window values transposed per head
   size_t bytes = 0;
 };
 
@@ -176,6 +177,7 @@ WS layout(const ts_model_desc* m, const ts_plan* p, bool states, bool per_tile, 
   if (m->act_dtype == TS_BF16) {  // up to 64 splits of each global row's keys
     w.gpart_floats = int64_t(p->n_tiles) * m->n_heads * 64 * (m->head_dim + 2);
     w.gpart = (float*)take(size_t(w.gpart_floats * 4));
+    w.vt = take(size_t(p->n_tiles) * d * ((int64_t(p->n) + 63) / 64 * 64) * 2);
   }
   w.bytes = off;
   return w;
@@ -244,7 +246,8 @@ tsk::RopeRows rope_rows(const ts_plan* p, bool shared) {
 // as the QKV projection (and QK-norm) left them and the kernels rotate them
 // by tile-local positions; otherwise qk_prep has rotated them already.
 ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared, bool rope, const void* qkv,
-                           void* out, hipStream_t s, float* gscratch = nullptr, int64_t gscratch_floats = 0) {
+                           void* out, hipStream_t s, float* gscratch = nullptr, int64_t gscratch_floats = 0,
+                           void* vt = nullptr) {
   tsk::AttnArgs a;
   a.qkv = qkv;
   a.out = out;
@@ -279,6 +282,12 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared
     Scope sc(s, "attn_f32", 4.0 * nn * nn * m->d * p->n_tiles, double(p->n_tiles) * nn * m->d * 4 * ab);
     TS_HIP(tsk::attention(s, m->act_dtype, a, rope), "attention");
     return TS_OK;
+  }
+  if (!rope) {
+    if (!vt) return fail(TS_EINVAL, "internal: unrotated attention needs the V^T workspace");
+    Scope sc(s, "v_transpose", 0.0, double(p->n_tiles) * double(p->n) * m->d * 2 * ab);
+    TS_HIP(tsk::v_transpose(s, a, vt), "v_transpose");
+    a.vt = vt;
   }
   {
     Scope sc(s, "attn_bf16", 4.0 * double(p->n) * nn * m->d * p->n_tiles,
@@ -322,7 +331,7 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
                         rope_rows(p, shared)),
            "qk_prep");
   }
-  if ((st = window_attention(m, p, shared, false, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats)) != TS_OK)
+  if ((st = window_attention(m, p, shared, false, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats, ws.vt)) != TS_OK)
     return st;
   const void* aout = ws.o;
   if (shared) {
@@ -397,7 +406,8 @@ ts_status run_layer_partial(const Ctx& c, const ts_layer_weights& w, float* X, i
                         rope_rows(p, sq)),
            "qk_prep");
   }
-  if ((st = window_attention(m, p, sq, false, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats)) != TS_OK) return st;
+  if ((st = window_attention(m, p, sq, false, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats, ws.vt)) != TS_OK)
+    return st;
   // out-projection
   if (so) {
     {

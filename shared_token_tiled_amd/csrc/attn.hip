@@ -42,6 +42,7 @@ struct AttnP {
   int rope_wbase[3];
   int rope_wpairs[3];
   float scale_log2;  // log2(e) / sqrt(hd)
+  const bf16* vt;    // [n_tiles][H][HD][n_pad] transposed window values (unrotated path)
 };
 
 __device__ __forceinline__ int window_row(const AttnP& p, int t, int i) {
@@ -294,8 +295,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // stage, i.e. row b / KROWB, slot (b % KROWB) / 16 for lane byte b, and the
   // lane loads the logical chunk the swizzle puts in that slot
   constexpr int KDI = KB * KROWB / 1024 / NW;  // K DMA instructions per wavefront
+  constexpr int VDI = HD * KB * 2 / 1024 / NW;  // V^T DMA instructions per wavefront
+  static_assert(KDI >= 1 && VDI >= 1, "whole 1 KB DMA rows per wavefront");
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  auto gload = [&](int slot) {
+  const int64_t n_pad = int64_t(nkb) * KB;
+  const bf16* vtbase = ROPE ? nullptr : p.vt + (int64_t(t) * p.H + h) * HD * n_pad;
+  auto gload = [&](int slot, int blk) {
     if constexpr (!ROPE) {
 #pragma unroll
       for (int i = 0; i < KDI; ++i) {
@@ -305,19 +310,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         __builtin_amdgcn_global_load_lds((const void*)(kbase + r * ld + c * 8),
                                          (TS_LDS void*)(&Ks[slot][(wv * KDI + i) * 1024]), 16, 0, 0);
       }
+      // V^T rows hd = 8*(wv*VDI + i) + lane/8, LDS slot lane%8 of the 128-byte
+      // row holds logical key chunk slot ^ vswz(hd) of block kb
+#pragma unroll
+      for (int i = 0; i < VDI; ++i) {
+        const int hdr = 8 * (wv * VDI + i) + (lane >> 3), c = (lane & 7) ^ vswz(hdr);
+        __builtin_amdgcn_global_load_lds((const void*)(vtbase + int64_t(hdr) * n_pad + blk * KB + c * 8),
+                                         (TS_LDS void*)(&Vt[slot][(wv * VDI + i) * 1024]), 16, 0, 0);
+      }
     } else {
       const int r = idx_s[slot][0][kr_row];
 #pragma unroll
       for (int i = 0; i < KCPT; ++i)
         kreg[i] = *reinterpret_cast<const i32x4*>(kbase + r * ld + (kpart + 8 * i) * 8);
     }
-    if (v_on) {
+    if (ROPE && v_on) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int rv = idx_s[slot][0][2 * v_k2 + e];
         vreg[e] = *reinterpret_cast<const i32x4*>(vbase + rv * ld + v_hc * 8);
       }
     }
+    (void)blk;
   };
   auto lstore = [&](int slot, int st) {
     if constexpr (ROPE) {
@@ -329,7 +343,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         *reinterpret_cast<bf16x8*>(&Ks[st][kr_row * KROWB + ((c ^ kswz<HD>(kr_row)) * 16)]) = o;
       }
     }
-    if (v_on) {
+    if (ROPE && v_on) {
       const bf16x8 v0 = __builtin_bit_cast(bf16x8, vreg[0]), v1 = __builtin_bit_cast(bf16x8, vreg[1]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -343,7 +357,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
 
   __syncthreads();  // rope_s, idx_s ready
-  gload(0);
+  gload(0, 0);
 
   // ---- this wavefront's 32 queries: B operand of S^T = K Q^T (hd 16s + 8g + e)
   const int qi = qblk * QB + wave * 32 + l32;
@@ -385,7 +399,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int krow_a = swap23(l32);  // key row this lane feeds as MFMA A row
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1;
-    if (kb + 1 < nkb) gload((kb + 1) & 1);
+    if (kb + 1 < nkb) gload((kb + 1) & 1, kb + 1);
     int pre_r = 0, pre_p = 0;
     const bool pre = tid < KB && kb + 2 < nkb;
     if (pre) key_meta((kb + 2) * KB + tid, pre_r, pre_p);
@@ -633,6 +647,39 @@ __global__ __launch_bounds__(HD) void k_attn_global_merge(AttnP p, int splits, c
   out[tid] = bf16(o / lt);
 }
 
+// Window values of one (64-key block, head, tile) transposed into vt: the
+// block's 64 V rows (gathered through the tile's row map) are read as 16-byte
+// chunks into an LDS tile [key][hd], then each thread assembles 16-byte
+// chunks of 8 consecutive keys of one hd row (2-byte LDS reads, consecutive
+// lanes on consecutive hd rows) and stores them; keys past the window end
+// are zero.
+template <int HD>
+__global__ __launch_bounds__(256) void k_vtrans(AttnP p) {
+  constexpr int CPR = HD / 8;   // 16-byte chunks per key row
+  constexpr int LD = HD + 8;    // LDS row stride (elements)
+  __shared__ __attribute__((aligned(16))) bf16 tile[64 * LD];
+  const int jb = blockIdx.x, h = blockIdx.y, t = blockIdx.z, tid = threadIdx.x;
+  const int n = p.n;
+  const int64_t ld = 3 * int64_t(p.d);
+  const bf16* qkv = (const bf16*)p.qkv;
+  for (int c = tid; c < 64 * CPR; c += 256) {
+    const int key = c / CPR, part = c % CPR, j = jb * 64 + key;
+    i32x4 v = {0, 0, 0, 0};
+    if (j < n) v = *reinterpret_cast<const i32x4*>(qkv + int64_t(window_row(p, t, j)) * ld + 2 * p.d + h * HD + part * 8);
+    *reinterpret_cast<i32x4*>(&tile[key * LD + part * 8]) = v;
+  }
+  __syncthreads();
+  const int64_t n_pad = int64_t((n + 63) / 64) * 64;
+  bf16* dst = const_cast<bf16*>(p.vt) + (int64_t(t) * p.H + h) * HD * n_pad + jb * 64;
+  for (int c = tid; c < HD * 8; c += 256) {
+    const int row = c % HD, kc = c / HD;
+    bf16x8 w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = tile[(kc * 8 + e) * LD + row];
+    *reinterpret_cast<bf16x8*>(dst + int64_t(row) * n_pad + kc * 8) = w;
+  }
+}
+
 }  // namespace
 
 namespace tsk {
@@ -642,7 +689,7 @@ static AttnP make_params(const AttnArgs& a) {
                {a.pairs[0], a.pairs[1], a.pairs[2]}, {a.rope_off[0], a.rope_off[1], a.rope_off[2]},
                {a.rope_wbase[0], a.rope_wbase[1], a.rope_wbase[2]},
                {a.rope_wpairs[0], a.rope_wpairs[1], a.rope_wpairs[2]},
-               1.4426950408889634f / sqrtf(float(a.hd))};
+               1.4426950408889634f / sqrtf(float(a.hd)), (const bf16*)a.vt};
 }
 
 hipError_t attention(hipStream_t s, int act, const AttnArgs& a, bool rope) {
@@ -671,6 +718,18 @@ hipError_t attention(hipStream_t s, int act, const AttnArgs& a, bool rope) {
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t v_transpose(hipStream_t s, const AttnArgs& a, void* vt) {
+  AttnArgs b = a;
+  b.vt = vt;
+  const AttnP p = make_params(b);
+  if (a.n < 1) return hipErrorInvalidValue;
+  const dim3 grid((a.n + 63) / 64, a.H, a.n_tiles), block(256);
+  if (a.hd == 64) hipLaunchKernelGGL(k_vtrans<64>, grid, block, 0, s, p);
+  else if (a.hd == 128) hipLaunchKernelGGL(k_vtrans<128>, grid, block, 0, s, p);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

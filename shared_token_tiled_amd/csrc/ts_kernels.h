@@ -81,7 +81,12 @@ struct AttnArgs {
   int rope_off[3];      // float offset of each axis' block; global pair k at position pos
   int rope_wbase[3];    // of axis a is (cos, sin) at
   int rope_wpairs[3];   // rope_off[a] + 2*(pos*rope_wpairs[a] + k - rope_wbase[a])
+  const void* vt = nullptr;  // bf16 [n_tiles][H][hd][n_pad]: each window's V transposed
+                             // (v_transpose), n_pad = n rounded up to 64; read when !rope
 };
+// Window values transposed per (tile, head) for the bf16 kernel: vt[t][h][e][j]
+// = V of window token j, dim e of head h (zero for j >= n, up to n_pad).
+hipError_t v_transpose(hipStream_t s, const AttnArgs& a, void* vt);
 // fp32: every window row.  bf16: the n tile-token query rows of every window;
 // the global-token row (window row n) is attention_global's.
 // rope: rotate q and k by tile-local positions while staging (the global
