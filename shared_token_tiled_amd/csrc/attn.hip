@@ -228,10 +228,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int NHB = HD / 32;        // 32-row hd blocks of O^T
   constexpr int KSTEPS = HD / 16;     // MFMA k-steps of S^T
   static_assert(VSB <= NT, "one V unit per thread");
-  __shared__ __attribute__((aligned(16))) char Ks[2][KB * KROWB];
-  __shared__ __attribute__((aligned(16))) char Vt[2][HD * KB * 2];
+  // LDS stages of K and V^T: two with in-kernel RoPE (registers carry the
+  // next block), three when both are DMA-staged (block kb+2 is in flight
+  // while kb is computed, so a block's loads have two blocks of time to land)
+  constexpr int NST = ROPE ? 2 : 3;
+  constexpr int AHEAD = ROPE ? 2 : 3;   // blocks ahead the key rows are fetched
+  constexpr int NSL = ROPE ? 2 : 4;     // slots of the key-row ring
+  __shared__ __attribute__((aligned(16))) char Ks[NST][KB * KROWB];
+  __shared__ __attribute__((aligned(16))) char Vt[NST][HD * KB * 2];
   __shared__ __attribute__((aligned(16))) float rope_s[ROPE ? ROPE_LDS_FLOATS : 4];
-  __shared__ int idx_s[2][2][KB];     // [slot][row | pos][key]
+  __shared__ int idx_s[NSL][2][KB];   // [slot][row | pos][key]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -265,13 +271,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     pos = ROPE ? p.local_pos[j] : 0;
   };
   if (tid < KB) {
-    int r0, p0, r1, p1;
-    key_meta(tid, r0, p0);
-    key_meta(KB + tid, r1, p1);
-    idx_s[0][0][tid] = r0;
-    idx_s[0][1][tid] = p0;
-    idx_s[1][0][tid] = r1;
-    idx_s[1][1][tid] = p1;
+#pragma unroll
+    for (int b = 0; b < AHEAD; ++b) {
+      int r0, p0;
+      key_meta(b * KB + tid, r0, p0);
+      idx_s[b][0][tid] = r0;
+      idx_s[b][1][tid] = p0;
+    }
   }
 
   // staging roles.  K: row kr_row, chunks kpart + 8*i, 8 threads per row; a
@@ -300,24 +306,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int64_t n_pad = int64_t(nkb) * KB;
   const bf16* vtbase = ROPE ? nullptr : p.vt + (int64_t(t) * p.H + h) * HD * n_pad;
-  auto gload = [&](int slot, int blk) {
+  // DMA staging in two steps: the key rows this lane's K loads need (from
+  // the ring), then the loads, so that the ring can be refilled in between
+  auto dma_rows = [&](int blk, int (&rr)[KDI]) {
+#pragma unroll
+    for (int i = 0; i < KDI; ++i) {
+      const int row = ((wv * KDI + i) * 1024 + 16 * lane) / KROWB;
+      rr[i] = p.rows ? idx_s[blk % NSL][0][row] : t * (n + 1) + min(blk * KB + row, n - 1);
+    }
+  };
+  auto dma = [&](int blk, const int (&rr)[KDI]) {
+    const int st = blk % NST;
+#pragma unroll
+    for (int i = 0; i < KDI; ++i) {
+      const int b = (wv * KDI + i) * 1024 + 16 * lane;
+      const int row = b / KROWB, c = ((b % KROWB) / 16) ^ kswz<HD>(row);
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + rr[i] * ld + c * 8),
+                                       (TS_LDS void*)(&Ks[st][(wv * KDI + i) * 1024]), 16, 0, 0);
+    }
+    // V^T rows hd = 8*(wv*VDI + i) + lane/8, LDS slot lane%8 of the 128-byte
+    // row holds logical key chunk slot ^ vswz(hd) of block blk
+#pragma unroll
+    for (int i = 0; i < VDI; ++i) {
+      const int hdr = 8 * (wv * VDI + i) + (lane >> 3), c = (lane & 7) ^ vswz(hdr);
+      __builtin_amdgcn_global_load_lds((const void*)(vtbase + int64_t(hdr) * n_pad + blk * KB + c * 8),
+                                       (TS_LDS void*)(&Vt[st][(wv * VDI + i) * 1024]), 16, 0, 0);
+    }
+  };
+  auto gload = [&](int blk) {
+    const int slot = blk % NSL;
     if constexpr (!ROPE) {
-#pragma unroll
-      for (int i = 0; i < KDI; ++i) {
-        const int b = (wv * KDI + i) * 1024 + 16 * lane;
-        const int row = b / KROWB, c = ((b % KROWB) / 16) ^ kswz<HD>(row);
-        const int r = idx_s[slot][0][row];
-        __builtin_amdgcn_global_load_lds((const void*)(kbase + r * ld + c * 8),
-                                         (TS_LDS void*)(&Ks[slot][(wv * KDI + i) * 1024]), 16, 0, 0);
-      }
-      // V^T rows hd = 8*(wv*VDI + i) + lane/8, LDS slot lane%8 of the 128-byte
-      // row holds logical key chunk slot ^ vswz(hd) of block kb
-#pragma unroll
-      for (int i = 0; i < VDI; ++i) {
-        const int hdr = 8 * (wv * VDI + i) + (lane >> 3), c = (lane & 7) ^ vswz(hdr);
-        __builtin_amdgcn_global_load_lds((const void*)(vtbase + int64_t(hdr) * n_pad + blk * KB + c * 8),
-                                         (TS_LDS void*)(&Vt[slot][(wv * VDI + i) * 1024]), 16, 0, 0);
-      }
+      int rr[KDI];
+      dma_rows(blk, rr);
+      dma(blk, rr);
     } else {
       const int r = idx_s[slot][0][kr_row];
 #pragma unroll
@@ -331,9 +352,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         vreg[e] = *reinterpret_cast<const i32x4*>(vbase + rv * ld + v_hc * 8);
       }
     }
-    (void)blk;
   };
-  auto lstore = [&](int slot, int st) {
+  auto lstore = [&](int blk, int st) {
+    const int slot = blk % NSL;
     if constexpr (ROPE) {
       const int pos = idx_s[slot][1][kr_row];
 #pragma unroll
@@ -357,7 +378,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
 
   __syncthreads();  // rope_s, idx_s ready
-  gload(0, 0);
+  gload(0);
+  if (!ROPE && nkb > 1) gload(1);
 
   // ---- this wavefront's 32 queries: B operand of S^T = K Q^T (hd 16s + 8g + e)
   const int qi = qblk * QB + wave * 32 + l32;
@@ -398,11 +420,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __syncthreads();
   const int krow_a = swap23(l32);  // key row this lane feeds as MFMA A row
   for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < nkb) gload((kb + 1) & 1, kb + 1);
+    const int cur = kb % NST;
+    // key rows of block kb+AHEAD.  DMA-staged: wavefront 0 copies them from
+    // the row map straight into the ring (no registers, so nothing waits on
+    // them before the block-end wait), ahead of this block's K / V^T loads so
+    // that wait covers them; per-tile rows need no map.  In-kernel RoPE: row
+    // and position through registers, stored at the block end.
     int pre_r = 0, pre_p = 0;
-    const bool pre = tid < KB && kb + 2 < nkb;
-    if (pre) key_meta((kb + 2) * KB + tid, pre_r, pre_p);
+    const bool pre = ROPE && tid < KB && kb + AHEAD < nkb;
+    if (pre) key_meta((kb + AHEAD) * KB + tid, pre_r, pre_p);
+    if constexpr (ROPE) {
+      if (kb + 1 < nkb) gload(kb + 1);
+    } else {
+      int rr[KDI];
+      if (kb + 2 < nkb) dma_rows(kb + 2, rr);
+      if (p.rows && wave == 0 && kb + AHEAD < nkb) {
+        const int j = min((kb + AHEAD) * KB + lane, n - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(p.rows + int64_t(t) * n + j),
+                                         (TS_LDS void*)(&idx_s[(kb + AHEAD) % NSL][0][0]), 4, 0, 0);
+      }
+      if (kb + 2 < nkb) dma(kb + 2, rr);
+    }
     const char* ks = Ks[cur];
     const char* vt = Vt[cur];
     const int j0 = kb * KB;
@@ -490,13 +528,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
-    if (kb + 1 < nkb) lstore((kb + 1) & 1, cur ^ 1);
+    if (ROPE && kb + 1 < nkb) lstore(kb + 1, cur ^ 1);
     if (pre) {
-      idx_s[cur][0][tid] = pre_r;
-      idx_s[cur][1][tid] = pre_p;
+      idx_s[(kb + AHEAD) % NSL][0][tid] = pre_r;
+      idx_s[(kb + AHEAD) % NSL][1][tid] = pre_p;
     }
-    if (!ROPE) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    if constexpr (ROPE) {
+      __syncthreads();
+    } else {
+      // this wavefront's loads of block kb+1 have landed (kb+2's may still be
+      // in flight) and its LDS traffic is done; then a barrier without the
+      // fence of __syncthreads, which would also wait for block kb+2
+      if (kb + 2 < nkb) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(KDI + VDI) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
