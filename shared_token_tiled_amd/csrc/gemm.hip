@@ -338,10 +338,40 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
   // kt+1 are read.  The barrier therefore only has to follow this wavefront's
   // reads of stage kt and its loads into stage kt+1; right after it, stage kt
   // is free for the loads of block kt+2.
+  //
+  // fp8 keeps the plain loop (next block's loads at the top, one barrier at
+  // the end): its 32-byte fragments, double buffered across the barrier,
+  // would not fit the register budget next to the accumulators.
   const int KT = p.K * ESZ / ROWB;
   gload(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if constexpr (FP8) {
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      // the other stage was last read in the previous iteration, before its barrier
+      if (kt + 1 < KT) gload(kt + 1, cur ^ 1);
+      const char* sA = smem + cur * STAGE;
+      const char* sB = sA + BM * ROWB;
+      Frags<FP8, NB> fr[2];
+      load_frags<FP8, NB>(fr[0], sA, sB, 0, arow, brow, lane);
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+        if (s + 1 < STEPS) load_frags<FP8, NB>(fr[(s + 1) & 1], sA, sB, s + 1, arow, brow, lane);
+        mfma_frags<FP8, NB>(fr[s & 1], acc);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+#pragma unroll
+      for (int s = 0; s + 1 < STEPS; ++s) sched_interleave<MFMAS, READS>();
+      __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);
+      // this iteration's loads of the next stage must have landed before anyone reads it
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    store_tile<EPI, FP8, NB>(p, acc, reinterpret_cast<float*>(smem) + wave * (32 * (WCOLS + 8)), m0 + arow,
+                             n0 + brow, lane);
+    return;
+  }
   if (KT > 1) gload(1, 1);
   Frags<FP8, NB> fr[2];
   load_frags<FP8, NB>(fr[0], smem, smem + BM * ROWB, 0, arow, brow, lane);
