@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define TS_ABI_VERSION 2
+#define TS_ABI_VERSION 3
 
 typedef int32_t ts_status;
 #define TS_OK 0
@@ -255,6 +255,17 @@ ts_status ts_fp8_quantize(const void* src, int32_t src_dtype, int64_t n, uint8_t
 ts_status ts_op_gemm(int32_t dtype, int32_t epilogue, const void* a, const void* b, int32_t m,
                      int32_t n, int32_t k, const float* bias, void* c, const float* scale_a,
                      const float* scale_b, void* stream);
+/* The same GEMM with a device workspace (ws, ws_bytes; 256-byte aligned, may
+ * be NULL / 0): the 256x256 output tiles of a partial last round over the
+ * compute units are split along k into up to 8 parts run side by side, their
+ * fp32 partial sums kept in ws and added in part order (the result does not
+ * vary from run to run).  Uses at most ws_bytes; with less than two parts'
+ * room for that round it runs unsplit.  8 x 256 KB per compute unit (64 MiB
+ * on MI355X) allows every split.  The forward calls pass their workspace. */
+#define TS_GEMM_SPLIT_WS_BYTES (64u << 20)
+ts_status ts_op_gemm_ws(int32_t dtype, int32_t epilogue, const void* a, const void* b, int32_t m,
+                        int32_t n, int32_t k, const float* bias, void* c, const float* scale_a,
+                        const float* scale_b, void* ws, size_t ws_bytes, void* stream);
 
 /* Window attention of one layer (Figure 2 caption; Table S1 "Attention
  * (dense, per tile)"): for every tile t and head, dense softmax attention

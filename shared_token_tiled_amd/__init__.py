@@ -90,6 +90,9 @@ def lib():
                                                  ctypes.c_size_t, _VP]),
             "ts_op_gemm": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _VP, _VP, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP]),
+            "ts_op_gemm_ws": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _VP, _VP, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,
+                                               ctypes.c_size_t, _VP]),
             "ts_op_window_attention": (ctypes.c_int32, [P(ModelDesc), _VP, ctypes.c_int32, _VP, _VP, _VP]),
             "ts_profile_begin": (ctypes.c_int32, []),
             "ts_profile_end": (ctypes.c_int32, [P(KernelStat), ctypes.c_int32, P(ctypes.c_int32)]),
@@ -223,14 +226,21 @@ def ts_fp8_quantize(src, dst, scale, ws, stream=None):
 
 
 TS_EPI_BIAS, TS_EPI_BIAS_GELU, TS_EPI_RESIDUAL, TS_EPI_F32 = 0, 1, 2, 3
+TS_GEMM_SPLIT_WS_BYTES = 64 << 20   # workspace that allows every K-split (8 x 256 KB per CU)
 
 
-def ts_op_gemm(dtype, epilogue, a, b, bias, c, scale_a=None, scale_b=None, stream=None):
-    """c = epilogue(a b^T + bias); a [m, k], b [n, k] device tensors."""
+def ts_op_gemm(dtype, epilogue, a, b, bias, c, scale_a=None, scale_b=None, stream=None, ws=None):
+    """c = epilogue(a b^T + bias); a [m, k], b [n, k] device tensors.  ws: an
+    optional device workspace (uint8 tensor) for the K-split last round."""
     m, k = a.shape[0], a.shape[1]
     n = b.shape[0]
-    _check(lib().ts_op_gemm(dtype, epilogue, _ptr(a), _ptr(b), m, n, k, _ptr(bias), _ptr(c), _ptr(scale_a),
-                            _ptr(scale_b), _stream(stream)), "ts_op_gemm")
+    if ws is None:
+        _check(lib().ts_op_gemm(dtype, epilogue, _ptr(a), _ptr(b), m, n, k, _ptr(bias), _ptr(c), _ptr(scale_a),
+                                _ptr(scale_b), _stream(stream)), "ts_op_gemm")
+    else:
+        _check(lib().ts_op_gemm_ws(dtype, epilogue, _ptr(a), _ptr(b), m, n, k, _ptr(bias), _ptr(c),
+                                   _ptr(scale_a), _ptr(scale_b), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)), "ts_op_gemm_ws")
 
 
 def ts_op_window_attention(model, plan, shared, qkv, out, stream=None):

@@ -145,6 +145,7 @@ struct WS {
   float* gpart = nullptr;    // fp32 split states of the global-token attention rows
   int64_t gpart_floats = 0;
   void* vt = nullptr;        // bf16 [n_tiles, d, n_pad] window values transposed per head
+  float* gsplit = nullptr;   // fp32 K-split parts of a GEMM's partial last round of tiles
   size_t bytes = 0;
 };
 
@@ -179,6 +180,7 @@ WS layout(const ts_model_desc* m, const ts_plan* p, bool states, bool per_tile, 
     w.gpart = (float*)take(size_t(w.gpart_floats * 4));
     w.vt = take(size_t(p->n_tiles) * d * ((int64_t(p->n) + 63) / 64 * 64) * 2);
   }
+  if (m->act_dtype != TS_F32) w.gsplit = (float*)take(TS_GEMM_SPLIT_WS_BYTES);
   w.bytes = off;
   return w;
 }
@@ -215,11 +217,14 @@ ts_status proj(const Ctx& c, const WS& ws, bool f8, const char* role, int epi, c
       TS_HIP(tsk::fp8_quantize(c.s, act, A, M * K, ws.q8, ws.sa, ws.amax), "fp8 quantize");
     }
     Scope sc(c.s, name.c_str(), 2.0 * M * N * K, gemm_bytes(M, N, K, 1, ob, epi == tsk::EPI_RESID));
-    TS_HIP(tsk::gemm(c.s, tsk::ACT_FP8, epi, ws.q8, W8, int(M), N, K, bias, C, ws.sa, w8scale), "fp8 gemm");
+    TS_HIP(tsk::gemm(c.s, tsk::ACT_FP8, epi, ws.q8, W8, int(M), N, K, bias, C, ws.sa, w8scale, ws.gsplit,
+                   TS_GEMM_SPLIT_WS_BYTES),
+         "fp8 gemm");
     return TS_OK;
   }
   Scope sc(c.s, name.c_str(), 2.0 * M * N * K, gemm_bytes(M, N, K, act_bytes(act), ob, epi == tsk::EPI_RESID));
-  TS_HIP(tsk::gemm(c.s, act, epi, A, Wt, int(M), N, K, bias, C, nullptr, nullptr), "gemm");
+  TS_HIP(tsk::gemm(c.s, act, epi, A, Wt, int(M), N, K, bias, C, nullptr, nullptr, ws.gsplit, TS_GEMM_SPLIT_WS_BYTES),
+         "gemm");
   return TS_OK;
 }
 
@@ -800,6 +805,13 @@ ts_status ts_fp8_quantize(const void* src, int32_t src_dtype, int64_t n, uint8_t
 ts_status ts_op_gemm(int32_t dtype, int32_t epilogue, const void* a, const void* b, int32_t m, int32_t n,
                      int32_t k, const float* bias, void* c, const float* scale_a, const float* scale_b,
                      void* stream) {
+  return ts_op_gemm_ws(dtype, epilogue, a, b, m, n, k, bias, c, scale_a, scale_b, nullptr, 0, stream);
+}
+
+ts_status ts_op_gemm_ws(int32_t dtype, int32_t epilogue, const void* a, const void* b, int32_t m, int32_t n,
+                        int32_t k, const float* bias, void* c, const float* scale_a, const float* scale_b,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (ws && reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(TS_EWORKSPACE, "workspace must be 256-byte aligned");
   if (!a || !b || !c) return fail(TS_EINVAL, "a, b and c must be non-null");
   if (m < 0 || n <= 0 || k <= 0) return fail(TS_EINVAL, "bad GEMM sizes");
   if (epilogue < 0 || epilogue > 3) return fail(TS_EINVAL, "bad epilogue");
@@ -815,7 +827,7 @@ ts_status ts_op_gemm(int32_t dtype, int32_t epilogue, const void* a, const void*
   Scope sc(s, dtype == TS_F32 ? "gemm_f32" : (dtype == TS_BF16 ? "gemm_bf16" : "gemm_fp8"), 2.0 * m * n * k,
            gemm_bytes(m, n, k, ab, ob, epilogue == TS_EPI_RESIDUAL));
   TS_HIP(tsk::gemm(s, dtype == TS_F32 ? tsk::ACT_F32 : (dtype == TS_BF16 ? tsk::ACT_BF16 : tsk::ACT_FP8), epilogue,
-                   a, b, m, n, k, bias, c, scale_a, scale_b),
+                   a, b, m, n, k, bias, c, scale_a, scale_b, (float*)ws, ws ? ws_bytes : 0),
          "gemm");
   return TS_OK;
 }

@@ -17,6 +17,7 @@
 // epilogue goes through LDS so every lane writes 16 contiguous output bytes.
 //
 // fp32: a plain LDS-tiled FMA kernel, used by the fp32 configuration.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -38,7 +39,16 @@ struct GemmP {
   const float* sa;
   const float* sb;
   int M, N, K;
+  // tile kernels: this launch covers tile ids [0, ntiles) of the XCD-aware
+  // order (ksplit = 1), or the tiles tile0 + b / ksplit with K split
+  // ksplit ways (workgroup b takes part b % ksplit and writes its raw 256x256
+  // fp32 partial product to part + b * 65536)
+  int ntiles, tile0, ksplit;
+  float* part;
 };
+
+// Epilogue code of a split part: the raw accumulator, no scale, no bias.
+constexpr int EPI_RAW = 100;
 
 // GELU x Phi(x) = x (1 + erf(x / sqrt 2)) / 2 with erf from Abramowitz and
 // Stegun, Handbook of Mathematical Functions, eq. 7.1.28: for z >= 0,
@@ -67,6 +77,7 @@ __device__ __forceinline__ float gelu_as(float x) {
 // (the fp32 kernel).
 template <int EPI, bool FAST = false>
 __device__ __forceinline__ float epi_value(float acc, float alpha, float bias) {
+  if (EPI == EPI_RAW) return acc;
   float v = fmaf(acc, alpha, bias);
   if (EPI == EPI_BIAS_GELU) v = FAST ? gelu_as(v) : gelu_erf(v);
   return v;
@@ -130,11 +141,8 @@ constexpr int BM = 256, BN = 256;
 constexpr int ROWB = 128;  // bytes per staged row: 64 bf16 or 128 fp8
 constexpr int STAGE = (BM + BN) * ROWB;
 
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int nblk = tiles_m * tiles_n;
-  const int xcd = bid & 7, loc = bid >> 3;
-  const int q = nblk >> 3, r = nblk & 7;
-  const int id = xcd < r ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
+// Tile id -> (tm, tn): groups of GROUP tile rows, column-major inside a group.
+__device__ __forceinline__ void group_tile(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int GROUP = 8;
   const int per_group = GROUP * tiles_n;
   const int grp = id / per_group;
@@ -143,6 +151,14 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   const int in_grp = id - grp * per_group;
   tm = first_m + in_grp % gsize;
   tn = in_grp / gsize;
+}
+
+// Workgroup b of a launch of nblk tiles -> its tile: the hardware deals
+// workgroup b to XCD b % 8, so each XCD gets a contiguous run of tile ids.
+__device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int xcd = bid & 7, loc = bid >> 3;
+  const int q = nblk >> 3, r = nblk & 7;
+  group_tile(xcd < r ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc, tiles_m, tiles_n, tm, tn);
 }
 
 // LDS swizzle: 16-byte chunk c of staged row r sits at chunk c ^ swz(r).  The
@@ -226,21 +242,23 @@ __device__ __forceinline__ void sched_interleave() {
 // each 32-row block goes through the wavefront's own LDS staging area (32
 // rows of 32*NB + 8 floats) so that every lane then writes 16 contiguous
 // output bytes (4 columns) with the bias / GELU / residual applied.
+// The destination is C with row pitch ldc, rows < mlim and columns < nlim
+// stored (a split part: its own 256x256 block, raw sums).
 template <int EPI, bool FP8, int NB>
-__device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4][NB], float* stg, int row0,
-                                           int col0, int lane) {
+__device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4][NB], float* stg, void* Cd,
+                                           int64_t ldc, int mlim, int nlim, int row0, int col0, int lane) {
   constexpr int WCOLS = 32 * NB, EPI_LD = WCOLS + 8;
   float alpha = 1.0f;
-  if (FP8) alpha = (*p.sa) * (*p.sb);
+  if (FP8 && EPI != EPI_RAW) alpha = (*p.sa) * (*p.sb);
   const int l32 = lane & 31, g = lane >> 5;
   // read-back mapping: LPR lanes cover one row (4 columns each), RPP rows per pass
   constexpr int LPR = WCOLS / 4, RPP = 64 / LPR;
   const int c4 = lane % LPR, rsub = lane / LPR;
   const int colb = col0 + c4 * 4;
   f32x4 bias4 = {0.f, 0.f, 0.f, 0.f};
-  if (p.bias) {
+  if (EPI != EPI_RAW && p.bias) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bias4[e] = colb + e < p.N ? p.bias[colb + e] : 0.f;
+    for (int e = 0; e < 4; ++e) bias4[e] = colb + e < nlim ? p.bias[colb + e] : 0.f;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -254,19 +272,19 @@ __device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4
       const int rl = RPP * it + rsub;
       const int row = row0 + i * 32 + rl;
       const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * EPI_LD + c4 * 4);
-      if (row < p.M && colb < p.N) {
+      if (row < mlim && colb < nlim) {
         f32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, bias4[e]);
-        const int64_t off = int64_t(row) * p.N + colb;
+        const int64_t off = int64_t(row) * ldc + colb;
         if (EPI == EPI_RESID) {
-          float* C = (float*)p.C;
+          float* C = (float*)Cd;
           const f32x4 old = load4(C + off);
           store4(C + off, old + o);
-        } else if (EPI == EPI_F32) {
-          store4((float*)p.C + off, o);
+        } else if (EPI == EPI_F32 || EPI == EPI_RAW) {
+          store4((float*)Cd + off, o);
         } else {
-          store4((bf16*)p.C + off, o);
+          store4((bf16*)Cd + off, o);
         }
       }
     }
@@ -289,7 +307,16 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
   const int arow = wm * 128, brow = wn * WCOLS;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int KTT = p.K * (FP8 ? 1 : 2) / ROWB;  // K blocks of the whole product
+  int kb0 = 0, kb1 = KTT;                      // this workgroup's K blocks
+  if (p.ksplit > 1) {
+    const int part = blockIdx.x % p.ksplit;
+    group_tile(p.tile0 + blockIdx.x / p.ksplit, tiles_m, tiles_n, tm, tn);
+    kb0 = int(int64_t(KTT) * part / p.ksplit);
+    kb1 = int(int64_t(KTT) * (part + 1) / p.ksplit);
+  } else {
+    tile_coords(blockIdx.x, p.ntiles, tiles_m, tiles_n, tm, tn);
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int ESZ = FP8 ? 1 : 2;               // element bytes
   const uint32_t ldab = uint32_t(p.K) * ESZ; // row pitch of A and B in bytes
@@ -310,8 +337,8 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
     offA[i] = uint32_t(min(m0 + lrow + 8 * NW * i, p.M - 1)) * ldab + lchunk * 16;
     offB[i] = uint32_t(min(n0 + lrow + 8 * NW * i, p.N - 1)) * ldab + lchunk * 16;
   }
-  auto gload = [&](int kt, int st) {
-    const uint32_t kb = uint32_t(kt) * ROWB;
+  auto gload = [&](int kt, int st) {   // K block kb0 + kt into stage st
+    const uint32_t kb = uint32_t(kb0 + kt) * ROWB;
     char* sA = smem + st * STAGE;
     char* sB = sA + BM * ROWB;
 #pragma unroll
@@ -323,6 +350,14 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
     }
   };
 
+  // epilogue: the C tile, or this part's raw sums for a split launch
+  auto store = [&](const f32x16 (&ac)[4][NB]) {
+    float* stg = reinterpret_cast<float*>(smem) + wave * (32 * (WCOLS + 8));
+    if constexpr (EPI == EPI_RAW)
+      store_tile<EPI, FP8, NB>(p, ac, stg, p.part + int64_t(blockIdx.x) * (BM * BN), BN, BM, BN, arow, brow, lane);
+    else
+      store_tile<EPI, FP8, NB>(p, ac, stg, p.C, p.N, p.M, p.N, m0 + arow, n0 + brow, lane);
+  };
   f32x16 acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -342,7 +377,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
   // fp8 keeps the plain loop (next block's loads at the top, one barrier at
   // the end): its 32-byte fragments, double buffered across the barrier,
   // would not fit the register budget next to the accumulators.
-  const int KT = p.K * ESZ / ROWB;
+  const int KT = kb1 - kb0;
   gload(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -368,8 +403,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
-    store_tile<EPI, FP8, NB>(p, acc, reinterpret_cast<float*>(smem) + wave * (32 * (WCOLS + 8)), m0 + arow,
-                             n0 + brow, lane);
+    store(acc);
     return;
   }
   if (KT > 1) gload(1, 1);
@@ -403,8 +437,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
   }
 
   // ---- epilogue: per 32-row block, stage 32 x WCOLS fp32 through LDS ----
-  store_tile<EPI, FP8, NB>(p, acc, reinterpret_cast<float*>(smem) + wave * (32 * (WCOLS + 8)), m0 + arow,
-                           n0 + brow, lane);
+  store(acc);
 }
 
 // Rows of C past the last full 256-row tile when there are at most 32 of
@@ -495,6 +528,31 @@ __global__ __launch_bounds__(512) void k_gemm_rows(GemmP p) {
   }
 }
 
+// Sum of the ksplit parts of each tile of a K-split launch, in part order
+// (the same result on every run), then the epilogue.  One workgroup per 4 rows
+// of a tile, 4 columns per thread.
+template <int EPI, bool FP8>
+__global__ __launch_bounds__(256) void k_gemm_reduce(GemmP p) {
+  const int tl = blockIdx.x / (BM / 4), rb = blockIdx.x % (BM / 4);
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn;
+  group_tile(p.tile0 + tl, tiles_m, tiles_n, tm, tn);
+  const int r = rb * 4 + int(threadIdx.x) / 64, c = (int(threadIdx.x) % 64) * 4;
+  const int row = tm * BM + r, col = tn * BN + c;
+  if (row >= p.M || col >= p.N) return;
+  const float* src = p.part + int64_t(tl) * p.ksplit * (BM * BN) + r * BN + c;
+  f32x4 v = load4(src);
+  for (int k = 1; k < p.ksplit; ++k) v += load4(src + int64_t(k) * (BM * BN));
+  const float alpha = FP8 ? (*p.sa) * (*p.sb) : 1.0f;
+  f32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, p.bias ? p.bias[col + e] : 0.f);
+  const int64_t off = int64_t(row) * p.N + col;
+  if (EPI == EPI_RESID) store4((float*)p.C + off, load4((const float*)p.C + off) + o);
+  else if (EPI == EPI_F32) store4((float*)p.C + off, o);
+  else store4((bf16*)p.C + off, o);
+}
+
 // Compute units of the current device (for the tile-round count).
 int device_cus() {
   static int v = [] {
@@ -521,10 +579,10 @@ int gemm_waves_n() {
 namespace tsk {
 
 hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, int M, int N, int K,
-                const float* bias, void* C, const float* sa, const float* sb) {
+                const float* bias, void* C, const float* sa, const float* sb, float* ws, size_t ws_bytes) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (act == ACT_F32) {
-    GemmP p{A, B, C, bias, sa, sb, M, N, K};
+    GemmP p{A, B, C, bias, sa, sb, M, N, K, 0, 0, 1, nullptr};
     const dim3 grid((N + FT - 1) / FT, (M + FT - 1) / FT), block(256);
     switch (epi) {
       case EPI_BIAS: hipLaunchKernelGGL(k_gemm_f32<EPI_BIAS>, grid, block, 0, s, p); break;
@@ -547,16 +605,43 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
     const int64_t all = int64_t((M + BM - 1) / BM) * tiles_n, full = int64_t(M / BM) * tiles_n;
     if ((e && strcmp(e, "always") == 0) || (full > 0 && (full + ncu - 1) / ncu < (all + ncu - 1) / ncu)) Mm = M - R;
   }
-  GemmP pm{A, B, C, bias, sa, sb, Mm, N, K};
-  GemmP pt{(const char*)A + int64_t(Mm) * K * esz, B, (char*)C + int64_t(Mm) * N * osz, bias, sa, sb, M - Mm, N, K};
+  // The tiles of a partial last round over the CUs (when a workspace is
+  // given) run K-split: ks parts per tile, as many workgroups as fit one
+  // round, their raw sums reduced in part order by k_gemm_reduce.  At least 4
+  // K blocks per part, at most 8 parts, and what the workspace holds.  Only
+  // for long K (>= 64 K blocks, e.g. fc2): a short tile's last round runs at
+  // a raised clock and gains less than the reduction costs (measured).
+  const int64_t T = int64_t((Mm + BM - 1) / BM) * tiles_n;
+  const int KTT = K * esz / ROWB;
+  int64_t Tm = T;
+  int ks = 1;
+  if (ws && T > 0 && KTT >= 64) {
+    const int64_t ncu = device_cus(), rem = T % ncu;
+    if (rem > 0) {
+      int64_t k = std::min<int64_t>({ncu / rem, KTT / 4, 8, int64_t(ws_bytes / (size_t(rem) * BM * BN * 4))});
+      if (k >= 2) {
+        ks = int(k);
+        Tm = T - rem;
+      }
+    }
+  }
+  GemmP pm{A, B, C, bias, sa, sb, Mm, N, K, int(Tm), 0, 1, nullptr};
+  GemmP ps{A, B, C, bias, sa, sb, Mm, N, K, 0, int(Tm), ks, ws};
+  GemmP pt{(const char*)A + int64_t(Mm) * K * esz, B, (char*)C + int64_t(Mm) * N * osz, bias, sa, sb, M - Mm, N, K,
+           0, 0, 1, nullptr};
   const int wn = gemm_waves_n();
-  const dim3 grid(((Mm + BM - 1) / BM) * tiles_n), block(128 * wn), tgrid((N + 31) / 32);
-#define TS_G(E, F8)                                                                      \
-  do {                                                                                   \
-    if (Mm == 0) {                                                                       \
-    } else if (wn == 2) hipLaunchKernelGGL((k_gemm_mfma<E, F8, 2>), grid, block, 0, s, pm); \
-    else hipLaunchKernelGGL((k_gemm_mfma<E, F8, 4>), grid, block, 0, s, pm);              \
-    if (Mm < M) hipLaunchKernelGGL((k_gemm_rows<E, F8>), tgrid, dim3(512), 0, s, pt);     \
+  const dim3 grid(static_cast<unsigned>(Tm)), block(128 * wn), tgrid((N + 31) / 32);
+  const dim3 sgrid(static_cast<unsigned>((T - Tm) * ks)), rgrid(static_cast<unsigned>((T - Tm) * (BM / 4)));
+#define TS_G(E, F8)                                                                          \
+  do {                                                                                       \
+    if (Tm == 0) {                                                                           \
+    } else if (wn == 2) hipLaunchKernelGGL((k_gemm_mfma<E, F8, 2>), grid, block, 0, s, pm);   \
+    else hipLaunchKernelGGL((k_gemm_mfma<E, F8, 4>), grid, block, 0, s, pm);                  \
+    if (Tm < T) {                                                                            \
+      hipLaunchKernelGGL((k_gemm_mfma<EPI_RAW, F8, 4>), sgrid, dim3(512), 0, s, ps);          \
+      hipLaunchKernelGGL((k_gemm_reduce<E, F8>), rgrid, dim3(256), 0, s, ps);                 \
+    }                                                                                        \
+    if (Mm < M) hipLaunchKernelGGL((k_gemm_rows<E, F8>), tgrid, dim3(512), 0, s, pt);         \
   } while (0)
   switch (epi) {
     case EPI_BIAS: if (f8) TS_G(EPI_BIAS, true); else TS_G(EPI_BIAS, false); break;

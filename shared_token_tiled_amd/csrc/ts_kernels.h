@@ -64,8 +64,11 @@ hipError_t fp8_quantize(hipStream_t s, int tin, const void* src, int64_t n, uint
 
 // ---- gemm_*.hip ----
 // act: ACT_F32 (fp32 operands), ACT_BF16, ACT_FP8 (e4m3 operands, alpha = *sa * *sb).
+// ws (fp32, ws_bytes; may be null): scratch for the K-split parts of a
+// partial last round of tiles (up to 8 x 256 KB per tile of that round).
 hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, int M, int N, int K,
-                const float* bias, void* C, const float* sa, const float* sb);
+                const float* bias, void* C, const float* sa, const float* sb, float* ws = nullptr,
+                size_t ws_bytes = 0);
 
 // ---- attn_*.hip ----
 struct AttnArgs {

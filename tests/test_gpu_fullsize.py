@@ -71,7 +71,10 @@ def test_full_size_gemm_bf16(name, M_, N, K, epi):
     c0 = c[rows].cpu().numpy().astype(np.float64) if resid else 0.0
     a = torch.from_numpy(A).to(DEV, torch.bfloat16)
     b = torch.from_numpy(B).to(DEV, torch.bfloat16)
-    ts.ts_op_gemm(ts.TS_BF16, epi, a, b, torch.from_numpy(bias).to(DEV), c)
+    # with the layers' workspace, as the forward calls run it (fc1, fc2 and out
+    # split their partial last round of tiles along K)
+    ws = torch.empty(ts.TS_GEMM_SPLIT_WS_BYTES, dtype=torch.uint8, device=DEV)
+    ts.ts_op_gemm(ts.TS_BF16, epi, a, b, torch.from_numpy(bias).to(DEV), c, ws=ws)
     torch.cuda.synchronize()
     got = c[rows].float().cpu().numpy().astype(np.float64)
     ref = A[rows].astype(np.float64) @ B.astype(np.float64).T + bias
@@ -113,7 +116,8 @@ def test_full_size_gemm_fp8(name, N, K, epi):
     ts.ts_fp8_quantize(a, a8, sc[0:1], ws)
     ts.ts_fp8_quantize(b, b8, sc[1:2], ws)
     c = torch.empty(M_, N, dtype=torch.float32 if epi == ts.TS_EPI_F32 else torch.bfloat16, device=DEV)
-    ts.ts_op_gemm(ts.TS_FP8E4M3, epi, a8, b8, torch.from_numpy(bias).to(DEV), c, sc[0:1], sc[1:2])
+    ts.ts_op_gemm(ts.TS_FP8E4M3, epi, a8, b8, torch.from_numpy(bias).to(DEV), c, sc[0:1], sc[1:2],
+                  ws=torch.empty(ts.TS_GEMM_SPLIT_WS_BYTES, dtype=torch.uint8, device=DEV))
     torch.cuda.synchronize()
     sa, sb = ofp8.tensor_scale(A), ofp8.tensor_scale(B)
     s_got = sc.cpu().numpy()
