@@ -112,3 +112,11 @@ def test_model_and_workspace_validation_on_host():
         assert st == -1
     finally:
         ts.ts_plan_destroy(h)
+
+
+def test_gemm_workspace_alignment_is_checked_before_any_gpu_work():
+    L = ts.lib()
+    p = ctypes.c_void_p(4096)
+    st = L.ts_op_gemm_ws(ts.TS_BF16, ts.TS_EPI_BIAS, p, p, 256, 256, 256, None, p, None, None,
+                         ctypes.c_void_p(4096 + 3), 1 << 20, None)
+    assert st == -7   # TS_EWORKSPACE
