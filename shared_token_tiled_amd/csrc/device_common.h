@@ -31,6 +31,25 @@ __device__ __forceinline__ void store4(bf16* p, f32x4 v) {
   *reinterpret_cast<bf16x4*>(p) = o;
 }
 
+// Load / store 8 consecutive elements (16-byte aligned) as two fp32 quads.
+__device__ __forceinline__ void load8(const float* p, f32x4& a, f32x4& b) {
+  a = load4(p);
+  b = load4(p + 4);
+}
+__device__ __forceinline__ void load8(const bf16* p, f32x4& a, f32x4& b) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+  a = f32x4{float(v[0]), float(v[1]), float(v[2]), float(v[3])};
+  b = f32x4{float(v[4]), float(v[5]), float(v[6]), float(v[7])};
+}
+__device__ __forceinline__ void store8(float* p, f32x4 a, f32x4 b) {
+  store4(p, a);
+  store4(p + 4, b);
+}
+__device__ __forceinline__ void store8(bf16* p, f32x4 a, f32x4 b) {
+  const bf16x8 o = {bf16(a[0]), bf16(a[1]), bf16(a[2]), bf16(a[3]), bf16(b[0]), bf16(b[1]), bf16(b[2]), bf16(b[3])};
+  *reinterpret_cast<bf16x8*>(p) = o;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);

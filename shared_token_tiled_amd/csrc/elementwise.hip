@@ -87,15 +87,16 @@ __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int 
                                                 const float* __restrict__ qg,
                                                 const float* __restrict__ kg, float eps, tsk::RopeRows rr) {
   constexpr int LPS = HD / 8;
-  const int64_t gid = (int64_t(blockIdx.x) * 256 + threadIdx.x) / LPS;
+  // 32-bit index arithmetic (the host checks M * 2H * HD/8 < 2^31)
+  const uint32_t gid = (blockIdx.x * 256u + threadIdx.x) / LPS;
   const int sub = threadIdx.x % LPS;
-  const int64_t total = int64_t(M) * 2 * H;
+  const uint32_t total = uint32_t(M) * 2u * uint32_t(H);
   const bool ok = gid < total;
-  const int64_t row = ok ? gid / (2 * H) : 0;
-  const int sl = ok ? int(gid % (2 * H)) : 0;
-  T* p = qkv + row * 3 * int64_t(d) + int64_t(sl) * HD + sub * 8;
-  f32x4 a = ok ? load4(p) : f32x4{0, 0, 0, 0};
-  f32x4 c = ok ? load4(p + 4) : f32x4{0, 0, 0, 0};
+  const uint32_t row = ok ? gid / (2u * H) : 0u;
+  const int sl = ok ? int(gid - row * (2u * H)) : 0;
+  T* p = qkv + int64_t(row) * 3 * d + sl * HD + sub * 8;
+  f32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
+  if (ok) load8(p, a, c);
   if constexpr (NORM) {
     float ss = a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3] + c[0] * c[0] + c[1] * c[1] +
                c[2] * c[2] + c[3] * c[3];
@@ -137,8 +138,7 @@ __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int 
     v[2 * e] = x * cs.x - y * cs.y;
     v[2 * e + 1] = x * cs.y + y * cs.x;
   }
-  store4(p, f32x4{v[0], v[1], v[2], v[3]});
-  store4(p + 4, f32x4{v[4], v[5], v[6], v[7]});
+  store8(p, f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]});
 }
 
 // ---- w-bar blend / state merge (Figure 2 caption: the only approximate step)
@@ -306,6 +306,7 @@ hipError_t qk_prep(hipStream_t s, int act, void* qkv, int M, int d, int H, int h
                    const float* kg, float eps, const RopeRows& rr) {
   if (M <= 0) return hipSuccess;
   const int64_t threads = int64_t(M) * 2 * H * (hd / 8);
+  if (threads >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const dim3 grid(unsigned((threads + 255) / 256)), block(256);
   const bool norm = qg != nullptr;
 #define TS_QK(T, HD)                                                                                         \
