@@ -260,8 +260,24 @@ __device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4
 #pragma unroll
     for (int e = 0; e < 4; ++e) bias4[e] = colb + e < nlim ? p.bias[colb + e] : 0.f;
   }
+  // residual: the old C values of 32-row block i+1 are loaded while block i
+  // is written, so no pass waits on a load issued just before it
+  constexpr int NP = 32 / RPP;
+  f32x4 oldv[2][EPI == EPI_RESID ? NP : 1];
+  auto load_old = [&](int i, f32x4 (&dst)[EPI == EPI_RESID ? NP : 1]) {
+    if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+      for (int it = 0; it < NP; ++it) {
+        const int row = row0 + i * 32 + RPP * it + rsub;
+        dst[it] = (row < mlim && colb < nlim) ? load4((const float*)Cd + int64_t(row) * ldc + colb)
+                                              : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  load_old(0, oldv[0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    if (i + 1 < 4) load_old(i + 1, oldv[(i + 1) & 1]);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -277,10 +293,8 @@ __device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, bias4[e]);
         const int64_t off = int64_t(row) * ldc + colb;
-        if (EPI == EPI_RESID) {
-          float* C = (float*)Cd;
-          const f32x4 old = load4(C + off);
-          store4(C + off, old + o);
+        if constexpr (EPI == EPI_RESID) {
+          store4((float*)Cd + off, oldv[i & 1][it] + o);
         } else if (EPI == EPI_F32 || EPI == EPI_RAW) {
           store4((float*)Cd + off, o);
         } else {
