@@ -138,6 +138,17 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmP p) {
 
 // ------------------------------------------------------------ MFMA ------
 constexpr int BM = 256, BN = 256;
+
+// s_setprio with a priority known after unrolling (the instruction takes an
+// immediate)
+__device__ __forceinline__ void set_prio(int v) {
+  switch (v) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
 constexpr int ROWB = 128;  // bytes per staged row: 64 bf16 or 128 fp8
 constexpr int STAGE = (BM + BN) * ROWB;
 
@@ -428,13 +439,18 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
     const int cur = kt & 1;
     const char* sA = smem + cur * STAGE;
     const char* sB = sA + BM * ROWB;
+    // k-step s runs at issue priority STEPS-1-s, so that of the two
+    // wavefronts of a SIMD the one that is behind is preferred (with equal
+    // priorities the older one takes the MFMA slots first, reaches the
+    // barrier early and the other finishes alone)
 #pragma unroll
     for (int s = 0; s + 1 < STEPS; ++s) {
+      set_prio(STEPS - 1 - s);
       load_frags<FP8, NB>(fr[(s + 1) & 1], sA, sB, s + 1, arow, brow, lane);
       mfma_frags<FP8, NB>(fr[s & 1], acc);
+      sched_interleave<MFMAS, READS>();
     }
-#pragma unroll
-    for (int s = 0; s + 1 < STEPS; ++s) sched_interleave<MFMAS, READS>();
+    __builtin_amdgcn_s_setprio(0);
     // this wavefront's loads of stage kt+1 have landed and its reads of stage
     // kt are done; after the barrier the same holds for every wavefront
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
