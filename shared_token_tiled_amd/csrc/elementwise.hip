@@ -11,7 +11,11 @@ constexpr int kMaxChunks = 16;  // d <= 64 lanes * 4 elements * 16 = 4096
 
 // ---- Norm1 / Norm2 (Table S1: once per token in shared layers) ---------
 // One wavefront per row; the row stays in registers between the passes.
-template <typename TOUT, bool RMS>
+// NCH: 4-element chunks per lane (d <= 256 NCH), so the register arrays are
+// sized for the model width.  The gain (and LayerNorm bias) chunks are loaded
+// together with the row, not after the reduction, so a row costs one memory
+// round trip.
+template <typename TOUT, bool RMS, int NCH>
 __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, int M, int d,
                                               const float* __restrict__ g,
                                               const float* __restrict__ b, float eps,
@@ -21,16 +25,23 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, int M
   if (row >= M) return;
   const float* xr = x + size_t(row) * d;
   const int nc = d >> 2;
-  f32x4 v[kMaxChunks];
-  float s = 0.f;
+  f32x4 v[NCH], gv[NCH], bv[RMS ? 1 : NCH];
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = lane + 64 * i;
     if (c < nc) {
       v[i] = load4(xr + 4 * c);
+      gv[i] = load4(g + 4 * c);
+      if (!RMS) bv[i] = load4(b + 4 * c);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nc)
       s += RMS ? (v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3])
                : (v[i][0] + v[i][1] + v[i][2] + v[i][3]);
-    }
   }
   s = wave_sum(s);
   const float inv_d = 1.0f / float(d);
@@ -41,7 +52,7 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, int M
     mean = s * inv_d;
     float q = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int c = lane + 64 * i;
       if (c < nc) {
 #pragma unroll
@@ -56,16 +67,16 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, int M
   }
   TOUT* yr = y + size_t(row) * d;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = lane + 64 * i;
     if (c < nc) {
-      const f32x4 gg = load4(g + 4 * c);
+      const f32x4 gg = gv[i];
       f32x4 o;
       if (RMS) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = v[i][e] * inv * gg[e];
       } else {
-        const f32x4 bb = load4(b + 4 * c);
+        const f32x4 bb = bv[RMS ? 0 : i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = (v[i][e] - mean) * inv * gg[e] + bb[e];
       }
@@ -75,8 +86,11 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, int M
 }
 
 // ---- per-head QK-RMSNorm (Table S1: once per token) and RoPE --------------
-// HD/8 lanes per (row, head slice); slices 0..H-1 are q heads, H..2H-1 k heads,
-// and slice s starts at column s*HD of the [q | k | v] row in both cases.
+// HD/8 lanes share a row, each owning 8 values (4 rotation pairs) of every
+// head slice: slices 0..H-1 are the q heads, H..2H-1 the k heads, slice s
+// starting at column s*HD of the [q | k | v] row.  A lane loads its gains
+// and the (cos, sin) of its four pairs at the row's grid coordinates once and
+// then streams the 2H slices of the row, U at a time.
 // NORM: RMS-normalise each head and scale by its gain first.  Then every q
 // and k head is rotated by the row's grid coordinates (RopeRows): the angle
 // of pair i of axis a is coord_a * base^(-i / pairs_a), so the score of two
@@ -86,34 +100,15 @@ template <typename T, int HD, bool NORM>
 __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int d, int H,
                                                 const float* __restrict__ qg,
                                                 const float* __restrict__ kg, float eps, tsk::RopeRows rr) {
-  constexpr int LPS = HD / 8;
-  // 32-bit index arithmetic (the host checks M * 2H * HD/8 < 2^31)
-  const uint32_t gid = (blockIdx.x * 256u + threadIdx.x) / LPS;
-  const int sub = threadIdx.x % LPS;
-  const uint32_t total = uint32_t(M) * 2u * uint32_t(H);
-  const bool ok = gid < total;
-  const uint32_t row = ok ? gid / (2u * H) : 0u;
-  const int sl = ok ? int(gid - row * (2u * H)) : 0;
-  T* p = qkv + int64_t(row) * 3 * d + sl * HD + sub * 8;
-  f32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
-  if (ok) load8(p, a, c);
-  if constexpr (NORM) {
-    float ss = a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3] + c[0] * c[0] + c[1] * c[1] +
-               c[2] * c[2] + c[3] * c[3];
-    ss = group_sum(ss, LPS);
-    const float inv = 1.0f / sqrtf(ss * (1.0f / HD) + eps);
-    const float* gg = (sl < H ? qg : kg) + sub * 8;
-    const f32x4 g0 = ok ? load4(gg) : f32x4{0, 0, 0, 0}, g1 = ok ? load4(gg + 4) : f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = a[e] * inv * g0[e];
-      c[e] = c[e] * inv * g1[e];
-    }
-  }
-  if (!ok) return;
+  constexpr int LPS = HD / 8;    // lanes per row
+  constexpr int RPW = 64 / LPS;  // rows per wavefront
+  constexpr int U = 4;           // head slices in flight per lane
+  const int lane = threadIdx.x & 63, sub = lane % LPS;
+  const int64_t row64 = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW + lane / LPS;
+  const bool ok = row64 < M;
+  const int r = ok ? int(row64) : 0;
   // grid coordinates of the row
   int co[3];
-  const int r = int(row);
   if (rr.shared && r < rr.n_union) {
     co[2] = r % rr.grid[2];
     co[1] = (r / rr.grid[2]) % rr.grid[1];
@@ -124,7 +119,7 @@ __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int 
 #pragma unroll
     for (int ax = 0; ax < 3; ++ax) co[ax] = rr.tile_start[3 * t + ax] + ((lp >> (10 * ax)) & 1023);
   }
-  float v[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+  float2 cs[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int k = 4 * sub + e;
@@ -133,17 +128,56 @@ __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int 
     const int np = ax == 0 ? rr.pairs[0] : (ax == 1 ? rr.pairs[1] : rr.pairs[2]);
     const int off = ax == 0 ? rr.off[0] : (ax == 1 ? rr.off[1] : rr.off[2]);
     const int cc = ax == 0 ? co[0] : (ax == 1 ? co[1] : co[2]);
-    const float2 cs = *reinterpret_cast<const float2*>(rr.tab + off + 2 * (cc * np + i));
-    const float x = v[2 * e], y = v[2 * e + 1];
-    v[2 * e] = x * cs.x - y * cs.y;
-    v[2 * e + 1] = x * cs.y + y * cs.x;
+    cs[e] = *reinterpret_cast<const float2*>(rr.tab + off + 2 * (cc * np + i));
   }
-  store8(p, f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]});
+  f32x4 gq0 = {1, 1, 1, 1}, gq1 = gq0, gk0 = gq0, gk1 = gq0;
+  if constexpr (NORM) {
+    gq0 = load4(qg + sub * 8);
+    gq1 = load4(qg + sub * 8 + 4);
+    gk0 = load4(kg + sub * 8);
+    gk1 = load4(kg + sub * 8 + 4);
+  }
+  T* base = qkv + int64_t(r) * 3 * d + sub * 8;
+  const int ns = 2 * H;
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    f32x4 a[U], c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      a[u] = c[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (ok && s0 + u < ns) load8(base + (s0 + u) * HD, a[u], c[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sl = s0 + u;
+      if constexpr (NORM) {
+        float ss = a[u][0] * a[u][0] + a[u][1] * a[u][1] + a[u][2] * a[u][2] + a[u][3] * a[u][3] +
+                   c[u][0] * c[u][0] + c[u][1] * c[u][1] + c[u][2] * c[u][2] + c[u][3] * c[u][3];
+        ss = group_sum(ss, LPS);
+        const float inv = 1.0f / sqrtf(ss * (1.0f / HD) + eps);
+        const bool isq = sl < H;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[u][e] = a[u][e] * inv * (isq ? gq0[e] : gk0[e]);
+          c[u][e] = c[u][e] * inv * (isq ? gq1[e] : gk1[e]);
+        }
+      }
+      float v[8] = {a[u][0], a[u][1], a[u][2], a[u][3], c[u][0], c[u][1], c[u][2], c[u][3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = v[2 * e], y = v[2 * e + 1];
+        v[2 * e] = x * cs[e].x - y * cs[e].y;
+        v[2 * e + 1] = x * cs[e].y + y * cs[e].x;
+      }
+      if (ok && sl < ns) store8(base + sl * HD, f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]});
+    }
+  }
 }
 
 // ---- w-bar blend / state merge (Figure 2 caption: the only approximate step)
 // One wavefront per output row; entries summed in ascending tile order.
-template <typename TIN, typename TOUT>
+// NCH: 8-element chunks per lane (d <= 512 NCH).  Entries are taken two at a
+// time, both rows loaded before either is added, and added in entry order.
+template <typename TIN, typename TOUT, int NCH>
 __global__ __launch_bounds__(256) void k_blend(const TIN* __restrict__ in, int d, int n_union,
                                                int n_tiles, int n, const int* __restrict__ cover_ptr,
                                                const int* __restrict__ entry_row,
@@ -152,36 +186,52 @@ __global__ __launch_bounds__(256) void k_blend(const TIN* __restrict__ in, int d
                                                TOUT* __restrict__ out_global) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nc = d >> 2;
+  const int nc = d >> 3;
   if (r < n_union) {
     const int e0 = cover_ptr[r], e1 = cover_ptr[r + 1];
-    f32x4 acc[kMaxChunks];
+    f32x4 acc[NCH][2];
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i) acc[i] = f32x4{0, 0, 0, 0};
-    for (int e = e0; e < e1; ++e) {
-      const TIN* src = in + size_t(entry_row[e]) * d;
-      const float we = w[e];
+    for (int i = 0; i < NCH; ++i) acc[i][0] = acc[i][1] = f32x4{0, 0, 0, 0};
+    for (int e = e0; e < e1; e += 2) {
+      const bool two = e + 1 < e1;
+      const TIN* s0 = in + size_t(entry_row[e]) * d;
+      const TIN* s1 = two ? in + size_t(entry_row[e + 1]) * d : s0;
+      const float w0 = w[e], w1 = two ? w[e + 1] : 0.f;
+      f32x4 v0[NCH][2], v1[NCH][2];
 #pragma unroll
-      for (int i = 0; i < kMaxChunks; ++i) {
+      for (int i = 0; i < NCH; ++i) {
         const int c = lane + 64 * i;
         if (c < nc) {
-          const f32x4 v = load4(src + 4 * c);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) acc[i][k] = fmaf(we, v[k], acc[i][k]);
+          load8(s0 + 8 * c, v0[i][0], v0[i][1]);
+          if (two) load8(s1 + 8 * c, v1[i][0], v1[i][1]);
         }
+      }
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[i][h][k] = fmaf(w0, v0[i][h][k], acc[i][h][k]);
+      if (two) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[i][h][k] = fmaf(w1, v1[i][h][k], acc[i][h][k]);
       }
     }
     TOUT* dst = out_union + size_t(r) * d;
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int c = lane + 64 * i;
-      if (c < nc) store4(dst + 4 * c, acc[i]);
+      if (c < nc) store8(dst + 8 * c, acc[i][0], acc[i][1]);
     }
   } else if (r < n_union + n_tiles && out_global != nullptr) {
     const int t = r - n_union;
     const TIN* src = in + (size_t(t) * (n + 1) + n) * d;
     TOUT* dst = out_global + size_t(t) * d;
-    for (int c = lane; c < nc; c += 64) store4(dst + 4 * c, load4(src + 4 * c));
+    for (int c = lane; c < (d >> 2); c += 64) store4(dst + 4 * c, load4(src + 4 * c));
   }
 }
 
@@ -292,22 +342,29 @@ hipError_t norm(hipStream_t s, int act, bool rms, const float* x, int M, int d, 
                 const float* b, float eps, void* y) {
   if (M <= 0) return hipSuccess;
   const dim3 grid(blocks_for_rows(M)), block(256);
-  if (act == ACT_F32) {
-    if (rms) hipLaunchKernelGGL((k_norm<float, true>), grid, block, 0, s, x, M, d, g, b, eps, (float*)y);
-    else hipLaunchKernelGGL((k_norm<float, false>), grid, block, 0, s, x, M, d, g, b, eps, (float*)y);
-  } else {
-    if (rms) hipLaunchKernelGGL((k_norm<bf16, true>), grid, block, 0, s, x, M, d, g, b, eps, (bf16*)y);
-    else hipLaunchKernelGGL((k_norm<bf16, false>), grid, block, 0, s, x, M, d, g, b, eps, (bf16*)y);
-  }
+#define TS_NORM(NCH)                                                                                       \
+  do {                                                                                                     \
+    if (act == ACT_F32) {                                                                                  \
+      if (rms) hipLaunchKernelGGL((k_norm<float, true, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (float*)y);  \
+      else hipLaunchKernelGGL((k_norm<float, false, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (float*)y);     \
+    } else {                                                                                               \
+      if (rms) hipLaunchKernelGGL((k_norm<bf16, true, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (bf16*)y);    \
+      else hipLaunchKernelGGL((k_norm<bf16, false, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (bf16*)y);       \
+    }                                                                                                      \
+  } while (0)
+  if (d <= 256 * 4) TS_NORM(4);
+  else if (d <= 256 * 10) TS_NORM(10);
+  else TS_NORM(kMaxChunks);
+#undef TS_NORM
   return hipGetLastError();
 }
 
 hipError_t qk_prep(hipStream_t s, int act, void* qkv, int M, int d, int H, int hd, const float* qg,
                    const float* kg, float eps, const RopeRows& rr) {
   if (M <= 0) return hipSuccess;
-  const int64_t threads = int64_t(M) * 2 * H * (hd / 8);
-  if (threads >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  const dim3 grid(unsigned((threads + 255) / 256)), block(256);
+  // four wavefronts per block, 512 / hd rows per wavefront
+  const int64_t rows_per_block = 4 * (512 / hd);
+  const dim3 grid(unsigned((M + rows_per_block - 1) / rows_per_block)), block(256);
   const bool norm = qg != nullptr;
 #define TS_QK(T, HD)                                                                                         \
   do {                                                                                                       \
@@ -327,14 +384,21 @@ hipError_t blend(hipStream_t s, int tin, int tout, const void* in, int d, int n_
                  int n, const int* cover_ptr, const int* entry_row, const float* w, void* out_union,
                  void* out_global) {
   const dim3 grid(blocks_for_rows(n_union + n_tiles)), block(256);
-#define TS_BL(TI, TO)                                                                             \
-  hipLaunchKernelGGL((k_blend<TI, TO>), grid, block, 0, s, (const TI*)in, d, n_union, n_tiles, n, \
+#define TS_BLN(TI, TO, NCH)                                                                             \
+  hipLaunchKernelGGL((k_blend<TI, TO, NCH>), grid, block, 0, s, (const TI*)in, d, n_union, n_tiles, n, \
                      cover_ptr, entry_row, w, (TO*)out_union, (TO*)out_global)
+#define TS_BL(TI, TO)                        \
+  do {                                       \
+    if (d <= 512 * 2) TS_BLN(TI, TO, 2);     \
+    else if (d <= 512 * 5) TS_BLN(TI, TO, 5); \
+    else TS_BLN(TI, TO, 8);                  \
+  } while (0)
   if (tin == ACT_F32 && tout == ACT_F32) TS_BL(float, float);
   else if (tin == ACT_BF16 && tout == ACT_BF16) TS_BL(bf16, bf16);
   else if (tin == ACT_F32 && tout == ACT_BF16) TS_BL(float, bf16);
   else TS_BL(bf16, float);
 #undef TS_BL
+#undef TS_BLN
   return hipGetLastError();
 }
 
