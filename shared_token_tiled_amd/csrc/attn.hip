@@ -695,15 +695,16 @@ __global__ __launch_bounds__(HD) void k_attn_global_merge(AttnP p, int splits, c
 }
 
 // Window values of one (64-key block, head, tile) transposed into vt: the
-// block's 64 V rows (gathered through the tile's row map) are read as 16-byte
-// chunks into an LDS tile [key][hd], then each thread assembles 16-byte
-// chunks of 8 consecutive keys of one hd row (2-byte LDS reads, consecutive
-// lanes on consecutive hd rows) and stores them; keys past the window end
-// are zero.
+// block's 64 V rows (gathered through the tile's row map, 16-byte loads) go
+// into an LDS tile [key][hd] whose row stride is an odd number of 4-byte
+// words, written as 4-byte words; then 8 consecutive lanes assemble one hd
+// row's 64 keys (8 keys each, 2-byte LDS reads that are free of bank
+// conflicts with that stride) and store its 128 contiguous bytes.  Keys past
+// the window end are zero.
 template <int HD>
 __global__ __launch_bounds__(256) void k_vtrans(AttnP p) {
   constexpr int CPR = HD / 8;   // 16-byte chunks per key row
-  constexpr int LD = HD + 8;    // LDS row stride (elements)
+  constexpr int LD = HD + 2;    // LDS row stride (elements): HD/2 + 1 words, odd
   __shared__ __attribute__((aligned(16))) bf16 tile[64 * LD];
   const int jb = blockIdx.x, h = blockIdx.y, t = blockIdx.z, tid = threadIdx.x;
   const int n = p.n;
@@ -713,13 +714,15 @@ __global__ __launch_bounds__(256) void k_vtrans(AttnP p) {
     const int key = c / CPR, part = c % CPR, j = jb * 64 + key;
     i32x4 v = {0, 0, 0, 0};
     if (j < n) v = *reinterpret_cast<const i32x4*>(qkv + int64_t(window_row(p, t, j)) * ld + 2 * p.d + h * HD + part * 8);
-    *reinterpret_cast<i32x4*>(&tile[key * LD + part * 8]) = v;
+    uint32_t* w = reinterpret_cast<uint32_t*>(&tile[key * LD + part * 8]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = uint32_t(v[e]);
   }
   __syncthreads();
   const int64_t n_pad = int64_t((n + 63) / 64) * 64;
   bf16* dst = const_cast<bf16*>(p.vt) + (int64_t(t) * p.H + h) * HD * n_pad + jb * 64;
   for (int c = tid; c < HD * 8; c += 256) {
-    const int row = c % HD, kc = c / HD;
+    const int row = c >> 3, kc = c & 7;
     bf16x8 w;
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = tile[(kc * 8 + e) * LD + row];
