@@ -50,6 +50,10 @@ struct GemmP {
 // Epilogue code of a split part: the raw accumulator, no scale, no bias.
 constexpr int EPI_RAW = 100;
 
+// Store target of the epilogue lanes that fall outside a partial tile (16
+// bytes per lane; the values written there are never read).
+__device__ __attribute__((aligned(16))) float g_store_sink[64 * 4];
+
 // GELU x Phi(x) = x (1 + erf(x / sqrt 2)) / 2 with erf from Abramowitz and
 // Stegun, Handbook of Mathematical Functions, eq. 7.1.28: for z >= 0,
 // erf(z) = 1 - (1 + a1 z + ... + a6 z^6)^-16, absolute error <= 3e-7 (about
@@ -266,10 +270,20 @@ __device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4
   constexpr int LPR = WCOLS / 4, RPP = 64 / LPR;
   const int c4 = lane % LPR, rsub = lane / LPR;
   const int colb = col0 + c4 * 4;
+  // No memory operation of the epilogue sits behind a branch: loads use
+  // clamped indices and lanes past the tile's valid rows or columns store
+  // into g_store_sink.  With branches around them the compiler loses count
+  // of the outstanding loads and stores at every join and waits for all of
+  // them (every earlier store included) before each store.
+  const bool col_ok = colb < nlim;
+  const int colc = col_ok ? colb : 0;
   f32x4 bias4 = {0.f, 0.f, 0.f, 0.f};
   if (EPI != EPI_RAW && p.bias) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bias4[e] = colb + e < nlim ? p.bias[colb + e] : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      const float bv = p.bias[min(colb + e, nlim - 1)];
+      bias4[e] = colb + e < nlim ? bv : 0.f;
+    }
   }
   // residual: the old C values of 32-row block i+1 are loaded while block i
   // is written, so no pass waits on a load issued just before it
@@ -280,8 +294,8 @@ __device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4
 #pragma unroll
       for (int it = 0; it < NP; ++it) {
         const int row = row0 + i * 32 + RPP * it + rsub;
-        dst[it] = (row < mlim && colb < nlim) ? load4((const float*)Cd + int64_t(row) * ldc + colb)
-                                              : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 ov = load4((const float*)Cd + int64_t(min(row, mlim - 1)) * ldc + colc);
+        dst[it] = (row < mlim && col_ok) ? ov : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
   };
@@ -299,18 +313,18 @@ __device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4
       const int rl = RPP * it + rsub;
       const int row = row0 + i * 32 + rl;
       const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * EPI_LD + c4 * 4);
-      if (row < mlim && colb < nlim) {
-        f32x4 o;
+      const bool ok = row < mlim && col_ok;
+      f32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, bias4[e]);
-        const int64_t off = int64_t(row) * ldc + colb;
-        if constexpr (EPI == EPI_RESID) {
-          store4((float*)Cd + off, oldv[i & 1][it] + o);
-        } else if (EPI == EPI_F32 || EPI == EPI_RAW) {
-          store4((float*)Cd + off, o);
-        } else {
-          store4((bf16*)Cd + off, o);
-        }
+      for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, bias4[e]);
+      const int64_t off = int64_t(row) * ldc + colb;
+      float* sink = g_store_sink + lane * 4;
+      if constexpr (EPI == EPI_RESID) {
+        store4(ok ? (float*)Cd + off : sink, oldv[i & 1][it] + o);
+      } else if (EPI == EPI_F32 || EPI == EPI_RAW) {
+        store4(ok ? (float*)Cd + off : sink, o);
+      } else {
+        store4(ok ? (bf16*)Cd + off : reinterpret_cast<bf16*>(sink), o);
       }
     }
     __builtin_amdgcn_wave_barrier();

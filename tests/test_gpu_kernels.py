@@ -63,6 +63,15 @@ def test_gemm_against_oracle(M_, N, K, epi, dtype, ws):
         assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * rms)
 
 
+@pytest.mark.parametrize("M_,N,K", [(40 * 256 + 100, 2048, 256), (40 * 256, 2048, 192)])
+@pytest.mark.parametrize("epi", [0, 1, 2, 3])
+def test_gemm_many_tiles(M_, N, K, epi):
+    """More 256x256 tiles than compute units (several rounds), an even and an
+    odd K block count, and (first shape) a partial last row tile, whose lanes
+    past the last row store into the epilogue's sink instead of C."""
+    test_gemm_against_oracle(M_, N, K, epi, "bf16", False)
+
+
 @pytest.mark.parametrize("M_", [5, 512 + 7, 256 + 32])
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
