@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -165,9 +166,10 @@ WS layout(const ts_model_desc* m, const ts_plan* p, bool states, bool per_tile, 
     off += align256(bytes);
     return r;
   };
-  char* scratch = take(256);
+  // fp8 scratch: the max slots (tsk::AMAX_SLOTS, 256 bytes apart), then the scale
+  char* scratch = take(size_t(tsk::AMAX_SLOTS) * tsk::AMAX_STRIDE * 4 + 256);
   w.amax = (unsigned*)scratch;
-  w.sa = (float*)(scratch + 64);
+  w.sa = (float*)(scratch + size_t(tsk::AMAX_SLOTS) * tsk::AMAX_STRIDE * 4);
   if (states && per_tile) w.X = (float*)take(size_t(Mt * d * 4));
   if (shared_xs) w.xs = (float*)take(size_t(Ms * d * 4));
   w.h = take(size_t(Mmax * d * ab));
@@ -201,10 +203,21 @@ bool gemm_offsets_fit(int64_t M, int64_t N, int64_t K, int esz) {
   return M * K * esz < (int64_t(1) << 32) && N * K * esz < (int64_t(1) << 32);
 }
 
+// The producer of an fp8 GEMM operand (a norm, the blend, a bf16-output
+// GEMM epilogue) takes the operand's max |value| itself, so its fp8
+// quantisation only encodes; TS_FP8_SEPARATE_AMAX=1 selects the separate max
+// pass instead (the two give bit-identical results).
+bool fused_amax() {
+  const char* e = getenv("TS_FP8_SEPARATE_AMAX");
+  return !(e && atoi(e) == 1);
+}
+
 // y = A W^T (+ epilogue) for one projection; fp8 quantises A first.
+// amax_ready: ws.amax already holds max |A| (see fused_amax).  out_amax: the
+// epilogue takes max |C| into it (for the next projection's quantisation).
 ts_status proj(const Ctx& c, const WS& ws, bool f8, const char* role, int epi, const void* A, int64_t M,
                int N, int K, const void* Wt, const uint8_t* W8, const float* w8scale, const float* bias,
-               void* C) {
+               void* C, bool amax_ready = false, unsigned* out_amax = nullptr) {
   const int act = c.m->act_dtype;
   if (act != TS_F32 && !gemm_offsets_fit(M, N, K, f8 ? 1 : 2))
     return fail(TS_ESHAPE, std::string("GEMM operand larger than 4 GiB (") + role + ")");
@@ -214,16 +227,20 @@ ts_status proj(const Ctx& c, const WS& ws, bool f8, const char* role, int epi, c
     {
       Scope sc(c.s, (std::string("fp8_quantize[") + role + "]").c_str(), 0.0,
                double(M * K) * (2.0 * act_bytes(act) + 1.0));
-      TS_HIP(tsk::fp8_quantize(c.s, act, A, M * K, ws.q8, ws.sa, ws.amax), "fp8 quantize");
+      TS_HIP(tsk::fp8_quantize(c.s, act, A, M * K, ws.q8, ws.sa, ws.amax, amax_ready, tsk::AMAX_SLOTS),
+             "fp8 quantize");
     }
+    if (out_amax) TS_HIP(tsk::zero_amax(c.s, out_amax), "amax reset");  // after the quantisation read it
     Scope sc(c.s, name.c_str(), 2.0 * M * N * K, gemm_bytes(M, N, K, 1, ob, epi == tsk::EPI_RESID));
     TS_HIP(tsk::gemm(c.s, tsk::ACT_FP8, epi, ws.q8, W8, int(M), N, K, bias, C, ws.sa, w8scale, ws.gsplit,
-                   TS_GEMM_SPLIT_WS_BYTES),
+                   TS_GEMM_SPLIT_WS_BYTES, out_amax),
          "fp8 gemm");
     return TS_OK;
   }
+  if (out_amax) TS_HIP(tsk::zero_amax(c.s, out_amax), "amax reset");
   Scope sc(c.s, name.c_str(), 2.0 * M * N * K, gemm_bytes(M, N, K, act_bytes(act), ob, epi == tsk::EPI_RESID));
-  TS_HIP(tsk::gemm(c.s, act, epi, A, Wt, int(M), N, K, bias, C, nullptr, nullptr, ws.gsplit, TS_GEMM_SPLIT_WS_BYTES),
+  TS_HIP(tsk::gemm(c.s, act, epi, A, Wt, int(M), N, K, bias, C, nullptr, nullptr, ws.gsplit, TS_GEMM_SPLIT_WS_BYTES,
+                   out_amax),
          "gemm");
   return TS_OK;
 }
@@ -322,13 +339,20 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
   const int f8 = fp8_mask(m, shared);
   const bool rms = m->norm == 1;
   ts_status st;
+  // producers that take the max of an fp8 operand (see fused_amax)
+  const bool fa = f8 != 0 && fused_amax();
+  unsigned* am_qkv = fa && (f8 & TS_FP8_QKV) ? ws.amax : nullptr;
+  unsigned* am_out = fa && shared && (f8 & TS_FP8_OUT) ? ws.amax : nullptr;
+  unsigned* am_fc1 = fa && (f8 & TS_FP8_FC1) ? ws.amax : nullptr;
+  unsigned* am_fc2 = fa && (f8 & TS_FP8_FC2) ? ws.amax : nullptr;
 
   {
+    if (am_qkv) TS_HIP(tsk::zero_amax(c.s, am_qkv), "amax reset");
     Scope sc(c.s, "norm", 0.0, double(M * d) * (4 + ab));
-    TS_HIP(tsk::norm(c.s, act, rms, x, int(M), d, w.norm1_g, w.norm1_b, m->eps, ws.h), "norm1");
+    TS_HIP(tsk::norm(c.s, act, rms, x, int(M), d, w.norm1_g, w.norm1_b, m->eps, ws.h, am_qkv), "norm1");
   }
   if ((st = proj(c, ws, (f8 & TS_FP8_QKV) != 0, "qkv", tsk::EPI_BIAS, ws.h, M, 3 * d, d, w.w_qkv, w.w_qkv_f8,
-                 w.w_scale_f8 ? w.w_scale_f8 + 0 : nullptr, w.b_qkv, ws.big)) != TS_OK)
+                 w.w_scale_f8 ? w.w_scale_f8 + 0 : nullptr, w.b_qkv, ws.big, am_qkv != nullptr)) != TS_OK)
     return st;
   {
     Scope sc(c.s, "qk_prep", 0.0, double(M * 2 * d) * 2 * ab);
@@ -340,25 +364,27 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
     return st;
   const void* aout = ws.o;
   if (shared) {
+    if (am_out) TS_HIP(tsk::zero_amax(c.s, am_out), "amax reset");
     Scope sc(c.s, "blend", 0.0, (double(p->n_entries + p->n_tiles) + double(Ms)) * d * ab);
     TS_HIP(tsk::blend(c.s, act, act, ws.o, d, p->n_union, p->n_tiles, p->n, (const int*)p->d_cover_ptr,
                       (const int*)p->d_entry_row, (const float*)p->d_cover_w, ws.h,
-                      (char*)ws.h + size_t(p->n_union) * d * ab),
+                      (char*)ws.h + size_t(p->n_union) * d * ab, am_out),
            "blend");
     aout = ws.h;
   }
   if ((st = proj(c, ws, (f8 & TS_FP8_OUT) != 0, "out", tsk::EPI_RESID, aout, M, d, d, w.w_o, w.w_o_f8,
-                 w.w_scale_f8 ? w.w_scale_f8 + 1 : nullptr, w.b_o, x)) != TS_OK)
+                 w.w_scale_f8 ? w.w_scale_f8 + 1 : nullptr, w.b_o, x, am_out != nullptr)) != TS_OK)
     return st;
   {
+    if (am_fc1) TS_HIP(tsk::zero_amax(c.s, am_fc1), "amax reset");
     Scope sc(c.s, "norm", 0.0, double(M * d) * (4 + ab));
-    TS_HIP(tsk::norm(c.s, act, rms, x, int(M), d, w.norm2_g, w.norm2_b, m->eps, ws.h), "norm2");
+    TS_HIP(tsk::norm(c.s, act, rms, x, int(M), d, w.norm2_g, w.norm2_b, m->eps, ws.h, am_fc1), "norm2");
   }
   if ((st = proj(c, ws, (f8 & TS_FP8_FC1) != 0, "fc1", tsk::EPI_BIAS_GELU, ws.h, M, dm, d, w.w_1, w.w_1_f8,
-                 w.w_scale_f8 ? w.w_scale_f8 + 2 : nullptr, w.b_1, ws.big)) != TS_OK)
+                 w.w_scale_f8 ? w.w_scale_f8 + 2 : nullptr, w.b_1, ws.big, am_fc1 != nullptr, am_fc2)) != TS_OK)
     return st;
   if ((st = proj(c, ws, (f8 & TS_FP8_FC2) != 0, "fc2", tsk::EPI_RESID, ws.big, M, d, dm, w.w_2, w.w_2_f8,
-                 w.w_scale_f8 ? w.w_scale_f8 + 3 : nullptr, w.b_2, x)) != TS_OK)
+                 w.w_scale_f8 ? w.w_scale_f8 + 3 : nullptr, w.b_2, x, am_fc2 != nullptr)) != TS_OK)
     return st;
   return TS_OK;
 }

@@ -9,17 +9,37 @@ namespace {
 
 constexpr int kMaxChunks = 16;  // d <= 64 lanes * 4 elements * 16 = 4096
 
+// Maximum of |v| over the four values of a chunk as stored in T.
+template <typename T> __device__ __forceinline__ float stored_amax4(f32x4 v) {
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(to_f32(from_f32<T>(v[e]))));
+  return m;
+}
+// Wavefront maximum (all 64 lanes active), then one atomic max in float bits
+// (values >= 0, so integer order is float order) into one of the
+// tsk::AMAX_SLOTS slots, chosen by workgroup and wavefront: atomics on one
+// address serialise, so the producers spread them and the quantisation takes
+// the max over the slots.
+__device__ __forceinline__ void wave_amax(unsigned* amax, float m) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const int slot = int(blockIdx.x * 4u + (threadIdx.x >> 6)) & (tsk::AMAX_SLOTS - 1);
+  if ((threadIdx.x & 63) == 0) atomicMax(amax + slot * tsk::AMAX_STRIDE, __float_as_uint(m));
+}
+
 // ---- Norm1 / Norm2 (Table S1: once per token in shared layers) ---------
 // One wavefront per row; the row stays in registers between the passes.
 // NCH: 4-element chunks per lane (d <= 256 NCH), so the register arrays are
 // sized for the model width.  The gain (and LayerNorm bias) chunks are loaded
 // together with the row, not after the reduction, so a row costs one memory
 // round trip.
+// amax (optional): max |y| as stored (for the fp8 quantisation of y).
 template <typename TOUT, bool RMS, int NCH>
 __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, int M, int d,
                                               const float* __restrict__ g,
                                               const float* __restrict__ b, float eps,
-                                              TOUT* __restrict__ y) {
+                                              TOUT* __restrict__ y, unsigned* __restrict__ amax) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
@@ -66,6 +86,7 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, int M
     inv = 1.0f / sqrtf(q * inv_d + eps);
   }
   TOUT* yr = y + size_t(row) * d;
+  float am = 0.f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + 64 * i;
@@ -81,8 +102,10 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, int M
         for (int e = 0; e < 4; ++e) o[e] = (v[i][e] - mean) * inv * gg[e] + bb[e];
       }
       store4(yr + 4 * c, o);
+      if (amax) am = fmaxf(am, stored_amax4<TOUT>(o));
     }
   }
+  if (amax) wave_amax(amax, am);  // one row per wavefront: all lanes here
 }
 
 // ---- per-head QK-RMSNorm (Table S1: once per token) and RoPE --------------
@@ -183,10 +206,11 @@ __global__ __launch_bounds__(256) void k_blend(const TIN* __restrict__ in, int d
                                                const int* __restrict__ entry_row,
                                                const float* __restrict__ w,
                                                TOUT* __restrict__ out_union,
-                                               TOUT* __restrict__ out_global) {
+                                               TOUT* __restrict__ out_global, unsigned* __restrict__ amax) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nc = d >> 3;
+  float am = 0.f;  // max |output| as stored (one row per wavefront)
   if (r < n_union) {
     const int e0 = cover_ptr[r], e1 = cover_ptr[r + 1];
     f32x4 acc[NCH][2];
@@ -225,14 +249,22 @@ __global__ __launch_bounds__(256) void k_blend(const TIN* __restrict__ in, int d
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = lane + 64 * i;
-      if (c < nc) store8(dst + 8 * c, acc[i][0], acc[i][1]);
+      if (c < nc) {
+        store8(dst + 8 * c, acc[i][0], acc[i][1]);
+        if (amax) am = fmaxf(am, fmaxf(stored_amax4<TOUT>(acc[i][0]), stored_amax4<TOUT>(acc[i][1])));
+      }
     }
   } else if (r < n_union + n_tiles && out_global != nullptr) {
     const int t = r - n_union;
     const TIN* src = in + (size_t(t) * (n + 1) + n) * d;
     TOUT* dst = out_global + size_t(t) * d;
-    for (int c = lane; c < (d >> 2); c += 64) store4(dst + 4 * c, load4(src + 4 * c));
+    for (int c = lane; c < (d >> 2); c += 64) {
+      const f32x4 v = load4(src + 4 * c);
+      store4(dst + 4 * c, v);
+      if (amax) am = fmaxf(am, stored_amax4<TOUT>(v));
+    }
   }
+  if (amax) wave_amax(amax, am);  // r is uniform over the wavefront
 }
 
 // ---- per-tile gather at stack entry (tile states = tile rows + global token)
@@ -282,6 +314,9 @@ __global__ __launch_bounds__(256) void k_copy4(const float* __restrict__ src, fl
 
 // ---- e4m3 quantisation (Table S5 "V0 + FP8"; OCP e4m3, RNE, +-448) ------
 __global__ void k_zero_u32(unsigned* p) { *p = 0u; }
+__global__ void k_zero_slots(unsigned* p, int nslots) {
+  if (int(threadIdx.x) < nslots) p[threadIdx.x * tsk::AMAX_STRIDE] = 0u;
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_amax(const T* __restrict__ x, int64_t n,
@@ -309,9 +344,11 @@ __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ x, int64_t n,
-                                               const unsigned* __restrict__ amax_bits,
+                                               const unsigned* __restrict__ amax_bits, int nslots,
                                                uint8_t* __restrict__ q, float* __restrict__ scale_out) {
-  const float amax = __uint_as_float(*amax_bits);
+  unsigned mb = 0u;  // max over the slots (float bits of values >= 0)
+  for (int i = 0; i < nslots; ++i) mb = max(mb, amax_bits[i * tsk::AMAX_STRIDE]);
+  const float amax = __uint_as_float(mb);
   const float s = amax > 0.f ? amax / 448.0f : 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) *scale_out = s;
   const int64_t n4 = n >> 2;
@@ -339,17 +376,17 @@ inline int grid_stride_blocks(int64_t items) {
 namespace tsk {
 
 hipError_t norm(hipStream_t s, int act, bool rms, const float* x, int M, int d, const float* g,
-                const float* b, float eps, void* y) {
+                const float* b, float eps, void* y, unsigned* amax) {
   if (M <= 0) return hipSuccess;
   const dim3 grid(blocks_for_rows(M)), block(256);
 #define TS_NORM(NCH)                                                                                       \
   do {                                                                                                     \
     if (act == ACT_F32) {                                                                                  \
-      if (rms) hipLaunchKernelGGL((k_norm<float, true, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (float*)y);  \
-      else hipLaunchKernelGGL((k_norm<float, false, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (float*)y);     \
+      if (rms) hipLaunchKernelGGL((k_norm<float, true, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (float*)y, amax);  \
+      else hipLaunchKernelGGL((k_norm<float, false, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (float*)y, amax);     \
     } else {                                                                                               \
-      if (rms) hipLaunchKernelGGL((k_norm<bf16, true, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (bf16*)y);    \
-      else hipLaunchKernelGGL((k_norm<bf16, false, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (bf16*)y);       \
+      if (rms) hipLaunchKernelGGL((k_norm<bf16, true, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (bf16*)y, amax);    \
+      else hipLaunchKernelGGL((k_norm<bf16, false, NCH>), grid, block, 0, s, x, M, d, g, b, eps, (bf16*)y, amax);       \
     }                                                                                                      \
   } while (0)
   if (d <= 256 * 4) TS_NORM(4);
@@ -382,11 +419,11 @@ hipError_t qk_prep(hipStream_t s, int act, void* qkv, int M, int d, int H, int h
 
 hipError_t blend(hipStream_t s, int tin, int tout, const void* in, int d, int n_union, int n_tiles,
                  int n, const int* cover_ptr, const int* entry_row, const float* w, void* out_union,
-                 void* out_global) {
+                 void* out_global, unsigned* amax) {
   const dim3 grid(blocks_for_rows(n_union + n_tiles)), block(256);
 #define TS_BLN(TI, TO, NCH)                                                                             \
   hipLaunchKernelGGL((k_blend<TI, TO, NCH>), grid, block, 0, s, (const TI*)in, d, n_union, n_tiles, n, \
-                     cover_ptr, entry_row, w, (TO*)out_union, (TO*)out_global)
+                     cover_ptr, entry_row, w, (TO*)out_union, (TO*)out_global, amax)
 #define TS_BL(TI, TO)                        \
   do {                                       \
     if (d <= 512 * 2) TS_BLN(TI, TO, 2);     \
@@ -430,18 +467,24 @@ hipError_t copy_f32(hipStream_t s, const float* src, float* dst, int64_t n) {
 }
 
 hipError_t fp8_quantize(hipStream_t s, int tin, const void* src, int64_t n, uint8_t* dst,
-                        float* scale_out, unsigned* amax_slot) {
-  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, amax_slot);
+                        float* scale_out, unsigned* amax_slot, bool amax_ready, int nslots) {
   const int nb = grid_stride_blocks((n + 3) / 4);
+  if (nslots < 1 || nslots > AMAX_SLOTS) return hipErrorInvalidValue;
+  if (!amax_ready) hipLaunchKernelGGL(k_zero_slots, dim3(1), dim3(64), 0, s, amax_slot, nslots);
   if (tin == ACT_F32) {
-    hipLaunchKernelGGL(k_amax<float>, dim3(nb), dim3(256), 0, s, (const float*)src, n, amax_slot);
-    hipLaunchKernelGGL(k_quant<float>, dim3(nb), dim3(256), 0, s, (const float*)src, n, amax_slot, dst,
+    if (!amax_ready) hipLaunchKernelGGL(k_amax<float>, dim3(nb), dim3(256), 0, s, (const float*)src, n, amax_slot);
+    hipLaunchKernelGGL(k_quant<float>, dim3(nb), dim3(256), 0, s, (const float*)src, n, amax_slot, nslots, dst,
                        scale_out);
   } else {
-    hipLaunchKernelGGL(k_amax<bf16>, dim3(nb), dim3(256), 0, s, (const bf16*)src, n, amax_slot);
-    hipLaunchKernelGGL(k_quant<bf16>, dim3(nb), dim3(256), 0, s, (const bf16*)src, n, amax_slot, dst,
+    if (!amax_ready) hipLaunchKernelGGL(k_amax<bf16>, dim3(nb), dim3(256), 0, s, (const bf16*)src, n, amax_slot);
+    hipLaunchKernelGGL(k_quant<bf16>, dim3(nb), dim3(256), 0, s, (const bf16*)src, n, amax_slot, nslots, dst,
                        scale_out);
   }
+  return hipGetLastError();
+}
+
+hipError_t zero_amax(hipStream_t s, unsigned* p) {
+  hipLaunchKernelGGL(k_zero_slots, dim3(1), dim3(64), 0, s, p, AMAX_SLOTS);
   return hipGetLastError();
 }
 

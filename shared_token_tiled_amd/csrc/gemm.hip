@@ -45,7 +45,25 @@ struct GemmP {
   // fp32 partial product to part + b * 65536)
   int ntiles, tile0, ksplit;
   float* part;
+  // when set (bf16 output epilogues): atomic max of |output| as stored, in
+  // float bits (all values are >= 0, so integer order is float order); the
+  // fp8 quantisation of this output then needs no separate max pass
+  unsigned* amax;
 };
+
+// |v| of a value as stored in bf16 (for the output max)
+__device__ __forceinline__ float stored_abs(float v) { return fabsf(float(bf16(v))); }
+
+// Maximum over a wavefront (all 64 lanes active), then one atomic max into
+// one of the tsk::AMAX_SLOTS slots, chosen by workgroup and wavefront
+// (atomics on one address serialise; the quantisation takes the max over the
+// slots).
+__device__ __forceinline__ void wave_amax(unsigned* amax, float m, int lane) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const int slot = int(blockIdx.x * 8u + (threadIdx.x >> 6)) & (tsk::AMAX_SLOTS - 1);
+  if (lane == 0) atomicMax(amax + slot * tsk::AMAX_STRIDE, __float_as_uint(m));
+}
 
 // Epilogue code of a split part: the raw accumulator, no scale, no bias.
 constexpr int EPI_RAW = 100;
@@ -300,6 +318,7 @@ __device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4
     }
   };
   load_old(0, oldv[0]);
+  float am = 0.f;  // max |output| of this lane (bf16 outputs)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i + 1 < 4) load_old(i + 1, oldv[(i + 1) & 1]);
@@ -319,6 +338,11 @@ __device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4
       for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, bias4[e]);
       const int64_t off = int64_t(row) * ldc + colb;
       float* sink = g_store_sink + lane * 4;
+      if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
+        if (ok)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) am = fmaxf(am, stored_abs(o[e]));
+      }
       if constexpr (EPI == EPI_RESID) {
         store4(ok ? (float*)Cd + off : sink, oldv[i & 1][it] + o);
       } else if (EPI == EPI_F32 || EPI == EPI_RAW) {
@@ -329,6 +353,8 @@ __device__ __forceinline__ void store_tile(const GemmP& p, const f32x16 (&acc)[4
     }
     __builtin_amdgcn_wave_barrier();
   }
+  if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU)
+    if (p.amax) wave_amax(p.amax, am, lane);
 }
 
 template <int EPI, bool FP8, int WN>
@@ -549,6 +575,7 @@ __global__ __launch_bounds__(512) void k_gemm_rows(GemmP p) {
   __syncthreads();
   if (tid < 256) {
     const int row = tid >> 3, c = (tid & 7) * 4, col = n0 + c;
+    float am = 0.f;
     if (row < p.M && col < p.N) {
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -567,8 +594,11 @@ __global__ __launch_bounds__(512) void k_gemm_rows(GemmP p) {
         store4((float*)p.C + off, o);
       } else {
         store4((bf16*)p.C + off, o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) am = fmaxf(am, stored_abs(o[e]));
       }
     }
+    if (EPI != EPI_RESID && EPI != EPI_F32 && p.amax) wave_amax(p.amax, am, lane);  // waves 0-3, all lanes
   }
 }
 
@@ -583,18 +613,27 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmP p) {
   group_tile(p.tile0 + tl, tiles_m, tiles_n, tm, tn);
   const int r = rb * 4 + int(threadIdx.x) / 64, c = (int(threadIdx.x) % 64) * 4;
   const int row = tm * BM + r, col = tn * BN + c;
-  if (row >= p.M || col >= p.N) return;
-  const float* src = p.part + int64_t(tl) * p.ksplit * (BM * BN) + r * BN + c;
-  f32x4 v = load4(src);
-  for (int k = 1; k < p.ksplit; ++k) v += load4(src + int64_t(k) * (BM * BN));
-  const float alpha = FP8 ? (*p.sa) * (*p.sb) : 1.0f;
-  f32x4 o;
+  float am = 0.f;
+  if (row < p.M && col < p.N) {
+    const float* src = p.part + int64_t(tl) * p.ksplit * (BM * BN) + r * BN + c;
+    f32x4 v = load4(src);
+    for (int k = 1; k < p.ksplit; ++k) v += load4(src + int64_t(k) * (BM * BN));
+    const float alpha = FP8 ? (*p.sa) * (*p.sb) : 1.0f;
+    f32x4 o;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, p.bias ? p.bias[col + e] : 0.f);
-  const int64_t off = int64_t(row) * p.N + col;
-  if (EPI == EPI_RESID) store4((float*)p.C + off, load4((const float*)p.C + off) + o);
-  else if (EPI == EPI_F32) store4((float*)p.C + off, o);
-  else store4((bf16*)p.C + off, o);
+    for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, p.bias ? p.bias[col + e] : 0.f);
+    const int64_t off = int64_t(row) * p.N + col;
+    if (EPI == EPI_RESID) {
+      store4((float*)p.C + off, load4((const float*)p.C + off) + o);
+    } else if (EPI == EPI_F32) {
+      store4((float*)p.C + off, o);
+    } else {
+      store4((bf16*)p.C + off, o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) am = fmaxf(am, stored_abs(o[e]));
+    }
+  }
+  if (EPI != EPI_RESID && EPI != EPI_F32 && p.amax) wave_amax(p.amax, am, int(threadIdx.x) & 63);
 }
 
 // Compute units of the current device (for the tile-round count).
@@ -623,7 +662,8 @@ int gemm_waves_n() {
 namespace tsk {
 
 hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, int M, int N, int K,
-                const float* bias, void* C, const float* sa, const float* sb, float* ws, size_t ws_bytes) {
+                const float* bias, void* C, const float* sa, const float* sb, float* ws, size_t ws_bytes,
+                unsigned* amax) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (act == ACT_F32) {
     GemmP p{A, B, C, bias, sa, sb, M, N, K, 0, 0, 1, nullptr};
@@ -669,10 +709,10 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
       }
     }
   }
-  GemmP pm{A, B, C, bias, sa, sb, Mm, N, K, int(Tm), 0, 1, nullptr};
-  GemmP ps{A, B, C, bias, sa, sb, Mm, N, K, 0, int(Tm), ks, ws};
+  GemmP pm{A, B, C, bias, sa, sb, Mm, N, K, int(Tm), 0, 1, nullptr, amax};
+  GemmP ps{A, B, C, bias, sa, sb, Mm, N, K, 0, int(Tm), ks, ws, amax};
   GemmP pt{(const char*)A + int64_t(Mm) * K * esz, B, (char*)C + int64_t(Mm) * N * osz, bias, sa, sb, M - Mm, N, K,
-           0, 0, 1, nullptr};
+           0, 0, 1, nullptr, amax};
   const int wn = gemm_waves_n();
   const dim3 grid(static_cast<unsigned>(Tm)), block(128 * wn), tgrid((N + 31) / 32);
   const dim3 sgrid(static_cast<unsigned>((T - Tm) * ks)), rgrid(static_cast<unsigned>((T - Tm) * (BM / 4)));

@@ -19,8 +19,9 @@ enum Epi {
 
 // ---- elementwise.hip ----
 // y[M,d] (act) = Norm(x[M,d] fp32); rms: RMSNorm(g) else LayerNorm(g, b).
+// amax (optional): atomic max of |y| as stored, in float bits (see fp8_quantize).
 hipError_t norm(hipStream_t s, int act, bool rms, const float* x, int M, int d, const float* g,
-                const float* b, float eps, void* y);
+                const float* b, float eps, void* y, unsigned* amax = nullptr);
 // In place per-head RMSNorm of the q and k sections of qkv [M, 3d] (act).
 // RoPE coordinates of the rows of a qkv array for qk_prep.  Shared layout
 // (shared = true): row r < n_union is grid row r (coordinates (r / (gh*gw),
@@ -43,9 +44,10 @@ hipError_t qk_prep(hipStream_t s, int act, void* qkv, int M, int d, int H, int h
                    const float* kg, float eps, const RopeRows& rr);
 // out_union[p] = sum_e w[e] * in[entry_row[e]] over cover_ptr[p]..cover_ptr[p+1];
 // out_global[t] = in[t*(n+1)+n] (skipped when out_global is null).
+// amax (optional): atomic max of |output| as stored, over both outputs.
 hipError_t blend(hipStream_t s, int tin, int tout, const void* in, int d, int n_union, int n_tiles,
                  int n, const int* cover_ptr, const int* entry_row, const float* w, void* out_union,
-                 void* out_global);
+                 void* out_global, unsigned* amax = nullptr);
 // X[t*(n+1)+j] += delta[tile_rows[t*n+j]], X[t*(n+1)+n] += delta[n_union+t]  (fp32)
 hipError_t add_to_tiles(hipStream_t s, float* X, const float* delta, const int* tile_rows, int n_union,
                         int n_tiles, int n, int d);
@@ -58,17 +60,29 @@ hipError_t init_shared(hipStream_t s, const float* x_in, const float* g, int n_u
                        int d, float* xs);
 // dst[i] = src[i], n multiple of 4 (fp32)
 hipError_t copy_f32(hipStream_t s, const float* src, float* dst, int64_t n);
-// e4m3 per-tensor quantisation; amax_slot: 4 bytes of scratch device memory.
+// Max |value| slots of an fp8 operand: producers (norm, blend, GEMM
+// epilogues) take atomic maxima in float bits into AMAX_SLOTS slots of 4
+// bytes, AMAX_STRIDE unsigned apart (256 bytes), spread over their
+// wavefronts; the quantisation takes the max over the slots.
+constexpr int AMAX_SLOTS = 64, AMAX_STRIDE = 64;
+// e4m3 per-tensor quantisation; amax_slot: nslots (1..AMAX_SLOTS) slots of
+// scratch device memory, AMAX_STRIDE unsigned apart.  amax_ready: the slots
+// already hold max |src| (its producer took it), so only the codes and the
+// scale are written; otherwise a separate pass takes it (into slot 0).
 hipError_t fp8_quantize(hipStream_t s, int tin, const void* src, int64_t n, uint8_t* dst,
-                        float* scale_out, unsigned* amax_slot);
+                        float* scale_out, unsigned* amax_slot, bool amax_ready = false, int nslots = 1);
+// All AMAX_SLOTS slots at p set to 0 (a kernel, so that it can sit in a
+// captured graph)
+hipError_t zero_amax(hipStream_t s, unsigned* p);
 
 // ---- gemm_*.hip ----
 // act: ACT_F32 (fp32 operands), ACT_BF16, ACT_FP8 (e4m3 operands, alpha = *sa * *sb).
 // ws (fp32, ws_bytes; may be null): scratch for the K-split parts of a
 // partial last round of tiles (up to 8 x 256 KB per tile of that round).
+// amax (optional, bf16-output epilogues): atomic max of |C| as stored.
 hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, int M, int N, int K,
                 const float* bias, void* C, const float* sa, const float* sb, float* ws = nullptr,
-                size_t ws_bytes = 0);
+                size_t ws_bytes = 0, unsigned* amax = nullptr);
 
 // ---- attn_*.hip ----
 struct AttnArgs {

@@ -208,6 +208,33 @@ def test_fp8_scope_against_oracle(k, gemms, per_tile):
     assert e < TOL["fp8"] and eg < TOL["fp8"]
 
 
+@pytest.mark.parametrize("k,gemms,per_tile", [(1, ("qkv", "out", "fc1", "fc2"), False),
+                                              (1, ("fc1", "fc2"), True), (0, ("out", "fc2"), False)])
+@pytest.mark.parametrize("rows_kernel", [False, True])
+def test_fp8_fused_amax_bit_identical(k, gemms, per_tile, rows_kernel, monkeypatch):
+    """The fp8 operand's max |value| taken by its producer (norm, blend, the
+    fc1 epilogue, and the ragged-row GEMM kernel when rows_kernel) gives the
+    same outputs, bit for bit, as the separate max pass (TS_FP8_SEPARATE_AMAX=1):
+    the max of the same stored values does not depend on the order."""
+    cfg = dict(reduced("minimax_h3_fp8"), fp8_gemms=gemms, fp8_per_tile=per_tile)
+    say(f"fp8 fused amax k={k} gemms={gemms} per_tile={per_tile} rows_kernel={rows_kernel}")
+    if rows_kernel:
+        monkeypatch.setenv("TS_GEMM_ROWS", "always")
+    x, g, layers = make_inputs(cfg)
+    outs = []
+    for separate in (False, True):
+        if separate:
+            monkeypatch.setenv("TS_FP8_SEPARATE_AMAX", "1")
+        else:
+            monkeypatch.delenv("TS_FP8_SEPARATE_AMAX", raising=False)
+        run = Run(cfg, layers)
+        try:
+            outs.append(run.stack(x, g, k))
+        finally:
+            run.close()
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
 PARTIAL = [("tiny2d", None, 0, "o"), ("tiny2d", None, 0, "qm"),
            ("minimax_h3", "r", 1, "q"), ("minimax_h3", "r", 1, "o"), ("minimax_h3", "r", 1, "m"),
            ("minimax_h3", "r", 0, "qo"), ("minimax_h3", "r", 1, "qom"), ("minimax_h3", "r", 2, ""),
