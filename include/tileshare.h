@@ -231,8 +231,9 @@ ts_status ts_partial_share_forward(const ts_model_desc* model, const ts_layer_we
 /* Per-tensor e4m3 quantisation (Table S5 "V0 + FP8"; OCP e4m3, round to
  * nearest even, saturation at +-448): scale = max|src| / 448 (1 if all zero),
  * dst[i] = e4m3(clamp(src[i] / scale, -448, 448)).  src: device, n elements of
- * src_dtype (TS_F32 or TS_BF16); dst: device uint8 [n]; scale: device fp32
- * [1].  ws: device workspace of at least 256 bytes.  Asynchronous. */
+ * src_dtype (TS_F32 or TS_BF16), 16-byte aligned; dst: device uint8 [n],
+ * 8-byte aligned (TS_EINVAL otherwise); scale: device fp32 [1].  ws: device
+ * workspace of at least 256 bytes.  Asynchronous. */
 ts_status ts_fp8_quantize(const void* src, int32_t src_dtype, int64_t n, uint8_t* dst,
                           float* scale, void* ws, size_t ws_bytes, void* stream);
 

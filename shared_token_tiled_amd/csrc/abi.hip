@@ -820,6 +820,8 @@ ts_status ts_fp8_quantize(const void* src, int32_t src_dtype, int64_t n, uint8_t
   if (!src || !dst || !scale) return fail(TS_EINVAL, "null argument");
   if (src_dtype != TS_F32 && src_dtype != TS_BF16) return fail(TS_EDTYPE, "src_dtype must be TS_F32 or TS_BF16");
   if (n <= 0) return fail(TS_EINVAL, "n must be positive");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 8 != 0)
+    return fail(TS_EINVAL, "src must be 16-byte and dst 8-byte aligned");
   ts_status st;
   if ((st = check_ws(ws, ws_bytes, 256)) != TS_OK) return st;
   hipStream_t s = (hipStream_t)stream;

@@ -351,14 +351,19 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ x, int64_t 
   const float amax = __uint_as_float(mb);
   const float s = amax > 0.f ? amax / 448.0f : 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) *scale_out = s;
-  const int64_t n4 = n >> 2;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += int64_t(gridDim.x) * 256) {
-    const f32x4 v = load4(x + 4 * i);
-    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v[0] / s), clamp448(v[1] / s), 0, false);
-    pk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v[2] / s), clamp448(v[3] / s), pk, true);
-    reinterpret_cast<int*>(q)[i] = pk;
+  // eight values per lane and step: one 16-byte (bf16) or two 16-byte (fp32)
+  // loads, one 8-byte store of codes
+  const int64_t n8 = n >> 3;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n8; i += int64_t(gridDim.x) * 256) {
+    f32x4 a, b;
+    load8(x + 8 * i, a, b);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a[0] / s), clamp448(a[1] / s), 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a[2] / s), clamp448(a[3] / s), lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(b[0] / s), clamp448(b[1] / s), 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(b[2] / s), clamp448(b[3] / s), hi, true);
+    reinterpret_cast<int2*>(q)[i] = make_int2(lo, hi);
   }
-  for (int64_t i = 4 * n4 + int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+  for (int64_t i = 8 * n8 + int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
     const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(to_f32(x[i]) / s), 0.f, 0, false);
     q[i] = uint8_t(pk & 0xff);
   }
@@ -468,16 +473,17 @@ hipError_t copy_f32(hipStream_t s, const float* src, float* dst, int64_t n) {
 
 hipError_t fp8_quantize(hipStream_t s, int tin, const void* src, int64_t n, uint8_t* dst,
                         float* scale_out, unsigned* amax_slot, bool amax_ready, int nslots) {
-  const int nb = grid_stride_blocks((n + 3) / 4);
+  const int nb = grid_stride_blocks((n + 3) / 4);   // max pass: four values per lane and step
+  const int nq = grid_stride_blocks((n + 7) / 8);   // codes: eight
   if (nslots < 1 || nslots > AMAX_SLOTS) return hipErrorInvalidValue;
   if (!amax_ready) hipLaunchKernelGGL(k_zero_slots, dim3(1), dim3(64), 0, s, amax_slot, nslots);
   if (tin == ACT_F32) {
     if (!amax_ready) hipLaunchKernelGGL(k_amax<float>, dim3(nb), dim3(256), 0, s, (const float*)src, n, amax_slot);
-    hipLaunchKernelGGL(k_quant<float>, dim3(nb), dim3(256), 0, s, (const float*)src, n, amax_slot, nslots, dst,
+    hipLaunchKernelGGL(k_quant<float>, dim3(nq), dim3(256), 0, s, (const float*)src, n, amax_slot, nslots, dst,
                        scale_out);
   } else {
     if (!amax_ready) hipLaunchKernelGGL(k_amax<bf16>, dim3(nb), dim3(256), 0, s, (const bf16*)src, n, amax_slot);
-    hipLaunchKernelGGL(k_quant<bf16>, dim3(nb), dim3(256), 0, s, (const bf16*)src, n, amax_slot, nslots, dst,
+    hipLaunchKernelGGL(k_quant<bf16>, dim3(nq), dim3(256), 0, s, (const bf16*)src, n, amax_slot, nslots, dst,
                        scale_out);
   }
   return hipGetLastError();

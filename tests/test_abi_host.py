@@ -120,3 +120,14 @@ def test_gemm_workspace_alignment_is_checked_before_any_gpu_work():
     st = L.ts_op_gemm_ws(ts.TS_BF16, ts.TS_EPI_BIAS, p, p, 256, 256, 256, None, p, None, None,
                          ctypes.c_void_p(4096 + 3), 1 << 20, None)
     assert st == -7   # TS_EWORKSPACE
+
+
+def test_fp8_quantize_alignment_is_checked_before_any_gpu_work():
+    """The quantiser reads 16 bytes and writes 8 bytes per lane."""
+    L = ts.lib()
+    ws = ctypes.c_void_p(4096)
+    for src, dst in ((4096 + 8, 4096), (4096, 4096 + 4)):
+        st = L.ts_fp8_quantize(ctypes.c_void_p(src), ts.TS_BF16, 1024, ctypes.c_void_p(dst), ctypes.c_void_p(8192),
+                               ws, 256, None)
+        assert st == -1   # TS_EINVAL
+        assert b"aligned" in L.ts_last_error()
