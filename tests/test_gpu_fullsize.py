@@ -205,6 +205,37 @@ def test_full_size_shared_layer(name):
     assert ex < tol and eg < tol and ed < tol
 
 
+@pytest.mark.parametrize("name,per_tile", [("minimax_h3", False), ("minimax_h3", True), ("small_video", False),
+                                           ("vitok4k", False)])
+def test_full_size_global_rows_attention(name, per_tile):
+    """The global-token rows' attention at full size, on its own: with the MLP
+    and the out-projection bias zero, a global row's layer delta is its
+    attention output (over the n window keys and the global key) times W_o.
+    Checked per row against the oracle, to the attention bound."""
+    cfg, x, g, layers, pl = _full_inputs(name)
+    for k in ("w_1", "b_1", "w_2", "b_2", "b_o"):
+        layers[0][k] = np.zeros_like(layers[0][k])
+    say(f"full-size global rows {name} per_tile={per_tile} tiles={pl.n_tiles} n={pl.tile_tokens}")
+    run = Run(cfg, layers)
+    try:
+        if per_tile:
+            G = np.tile(g[None], (pl.n_tiles, 1)).astype(np.float32)
+            _, got = run.stack(x, g, 1)
+            _, ref = M.tiled_layer_rows(cfg, pl, x, g, layers[0], [0])
+        else:
+            rng = np.random.default_rng(6)
+            G = (np.tile(g[None], (pl.n_tiles, 1)) + 0.1 * _randn(rng, (pl.n_tiles, cfg["d"]))).astype(np.float32)
+            got = run.shared_layer(np.vstack([x, G]))[pl.n_union:]
+            _, ref = M.shared_layer_rows(x.astype(np.float64), G.astype(np.float64), layers[0], cfg, pl,
+                                         M.Rope(pl, cfg), [0])
+    finally:
+        run.close()
+    dg, dr = got - G, ref - G
+    err = np.linalg.norm(dg - dr, axis=1) / np.linalg.norm(dr, axis=1)
+    print("  per-row rel-L2 of the global deltas: " + " ".join(f"{v:.1e}" for v in err))
+    assert np.all(err < 2e-2)
+
+
 def test_full_size_tiled_layer_and_merge():
     cfg, x, g, layers, pl = _full_inputs("minimax_h3")
     say(f"full-size per-tile layer + merge minimax_h3 tiles={pl.n_tiles} n={pl.tile_tokens}")
