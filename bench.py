@@ -120,11 +120,12 @@ def measured_traffic(name, workload, k):
     return ent["hbm_bytes_per_launch"]
 
 
-def decode_flops(cfg, pl, k, share="qom"):
+def decode_flops(cfg, pl, k, share="qom", dedup0=False):
     """Algorithmic FLOPs of a TileShare-k decode: 2*(3d^2 + d^2 + 2 d dm) per row
     per layer for the projections, 4 (n+1)^2 d per tile per layer for attention.
     ``share``: the operations that run once per token from layer k on (q: QKV,
-    o: out-projection, m: MLP); the others run on every tile's rows."""
+    o: out-projection, m: MLP); the others run on every tile's rows.
+    ``dedup0``: a per-tile layer 0 runs its QKV once per token."""
     d, dm, L = cfg["d"], cfg["mlp_hidden"], cfg["n_layers"]
     mt = pl.n_tiles * (pl.tile_tokens + 1)
     ms = pl.n_union + pl.n_tiles
@@ -133,7 +134,8 @@ def decode_flops(cfg, pl, k, share="qom"):
     later = attn
     for op, fl in (("q", 2.0 * 3 * d * d), ("o", 2.0 * d * d), ("m", 2.0 * 2 * d * dm)):
         later += fl * (ms if op in share else mt)
-    return k * per_tile + (L - k) * later
+    saved = 2.0 * 3 * d * d * (mt - ms) if dedup0 and k > 0 else 0.0
+    return k * per_tile + (L - k) * later - saved
 
 
 def main():
@@ -152,6 +154,9 @@ def main():
     ap.add_argument("--fp8-gemms", default=None,
                     help="comma list of the fp8 GEMMs (qkv,out,fc1,fc2) for fp8 configurations")
     ap.add_argument("--fp8-per-tile", action="store_true", help="fp8 GEMMs in per-tile layers too")
+    ap.add_argument("--layer0-dedup", action="store_true",
+                    help="TileShare-k with k >= 1: layer 0's Norm1, QKV and QK-norm once per token "
+                         "(the tiled baseline stays as released)")
     ap.add_argument("--partial-share", default=None, metavar="OPS",
                     help="time partial sharing from layer k with per-tile streams; OPS from q, o, m (e.g. qo)")
     args = ap.parse_args()
@@ -168,6 +173,7 @@ def main():
     if args.fp8_gemms:
         cfg["fp8_gemms"] = tuple(args.fp8_gemms.split(","))
     cfg["fp8_per_tile"] = args.fp8_per_tile
+    cfg["layer0_dedup"] = args.layer0_dedup
     k = cfg["k_values"][0] if args.k is None else args.k
     L = cfg["n_layers"]
     dev = "cuda"
@@ -179,6 +185,7 @@ def main():
     ts.ts_plan_upload(plan, cfg["head_dim"], cfg.get("rope_base", 10000.0))
     info = ts.ts_plan_get_info(plan)
     model = ts.model_desc(cfg)
+    model_base = ts.model_desc(dict(cfg, layer0_dedup=False))
     x, g, tens, structs = device_inputs(cfg, cfg.get("seed", 0), dev)
     ws_bytes = max(ts.ts_workspace_size(model, plan, kk) for kk in (k, L, -1))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -198,7 +205,7 @@ def main():
             ts.ts_stack_forward(model, structs, plan, k, x, g, xo, go, ws)
 
     def step_base():
-        ts.ts_tiled_forward(model, structs, plan, x, g, xo, go, ws)
+        ts.ts_tiled_forward(model_base, structs, plan, x, g, xo, go, ws)
 
     def timed(fn, steps, warmup, profile):
         for _ in range(warmup):
@@ -259,14 +266,18 @@ def main():
     pl_flops = None
     from oracle.plan import Plan  # FLOP count needs only the tile counts
     pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
-    pl_flops = (decode_flops(cfg, pl, L) if args.merge_once is not None else
-                decode_flops(cfg, pl, k, args.partial_share if args.partial_share is not None else "qom"))
+    pl_flops = (decode_flops(cfg, pl, L, dedup0=args.layer0_dedup)
+                if args.merge_once is not None else
+                decode_flops(cfg, pl, k, args.partial_share if args.partial_share is not None else "qom",
+                             dedup0=args.layer0_dedup))
     mode = (f"merge once at layer {args.merge_once}, then per tile" if args.merge_once is not None
             else (f"per-tile streams from layer {k} sharing {args.partial_share or 'nothing'}"
                   if args.partial_share is not None else f"TileShare-{k}"))
     extras = []
     if args.blend == "hard":
         extras.append("hard stitching")
+    if args.layer0_dedup:
+        extras.append("layer 0 Norm1/QKV/QK-norm once per token")
     if cfg["gemm_shared"] == "fp8":
         extras.append(f"fp8 GEMMs {','.join(cfg.get('fp8_gemms') or ('qkv', 'out', 'fc1', 'fc2'))} in shared"
                       + (" and per-tile" if args.fp8_per_tile else "") + " layers")

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define TS_ABI_VERSION 3
+#define TS_ABI_VERSION 4
 
 typedef int32_t ts_status;
 #define TS_OK 0
@@ -134,6 +134,13 @@ typedef struct {
                            TS_FP8_FC1 | TS_FP8_FC2; 0 = all four */
   int32_t fp8_per_tile; /* 1: per-tile layers (and the tiled decoder) use the
                            same fp8 GEMMs; 0: only shared layers */
+  int32_t layer0_dedup; /* 1: when layer 0 runs per tile (stack with k >= 1,
+                           tiled decoder, merge-once, partial sharing with
+                           k >= 1), its Norm1, QKV and QK-norm run once per
+                           token on the rows every tile copied its states
+                           from, and attention reads each window through the
+                           tile map (Table S1, layer 0 column: exact); 0
+                           (default): once per per-tile row */
 } ts_model_desc;
 #define TS_FP8_QKV 1
 #define TS_FP8_OUT 2

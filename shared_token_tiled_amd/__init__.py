@@ -33,7 +33,8 @@ class ModelDesc(ctypes.Structure):
                 ("mlp_hidden", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("norm", ctypes.c_int32),
                 ("qk_norm", ctypes.c_int32), ("eps", ctypes.c_float), ("rope_base", ctypes.c_float),
                 ("act_dtype", ctypes.c_int32), ("gemm_dtype_shared", ctypes.c_int32),
-                ("fp8_gemms", ctypes.c_int32), ("fp8_per_tile", ctypes.c_int32)]
+                ("fp8_gemms", ctypes.c_int32), ("fp8_per_tile", ctypes.c_int32),
+                ("layer0_dedup", ctypes.c_int32)]
 
 
 _VP = ctypes.c_void_p
@@ -55,6 +56,7 @@ class TileShareError(RuntimeError):
 
 
 _lib = None
+ABI_VERSION = 4   # the layout of the structs below; a library of another version is refused
 
 
 def lib():
@@ -101,6 +103,9 @@ def lib():
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args
+        if ABI_VERSION is not None and L.ts_abi_version() != ABI_VERSION:
+            raise TileShareError(f"{LIB_PATH} has ABI version {L.ts_abi_version()}, this binding {ABI_VERSION}; "
+                                 "rebuild with __graft_entry__.build()")
         _lib = L
     return _lib
 
@@ -268,14 +273,15 @@ FP8_BITS = {"qkv": TS_FP8_QKV, "out": TS_FP8_OUT, "fc1": TS_FP8_FC1, "fc2": TS_F
 
 def model_desc(cfg):
     """ts_model_desc from a configuration dict (synth.configs keys; optional
-    "fp8_gemms": names of the fp8 GEMMs, default all four; "fp8_per_tile")."""
+    "fp8_gemms": names of the fp8 GEMMs, default all four; "fp8_per_tile";
+    "layer0_dedup")."""
     act = TS_F32 if cfg["dtype"] == "f32" else TS_BF16
     gs = {"f32": TS_F32, "bf16": TS_BF16, "fp8": TS_FP8E4M3}[cfg.get("gemm_shared", cfg["dtype"])]
     mask = sum(FP8_BITS[n] for n in cfg.get("fp8_gemms", ()))
     return ModelDesc(cfg["d"], cfg["n_heads"], cfg["head_dim"], cfg["mlp_hidden"], cfg["n_layers"],
                      1 if cfg["norm"] == "rms" else 0, 1 if cfg["qk_norm"] else 0,
                      cfg.get("eps", 1e-6), cfg.get("rope_base", 10000.0), act, gs, mask,
-                     1 if cfg.get("fp8_per_tile", False) else 0)
+                     1 if cfg.get("fp8_per_tile", False) else 0, 1 if cfg.get("layer0_dedup", False) else 0)
 
 
 def layer_weights(p):

@@ -86,6 +86,7 @@ ts_status check_model(const ts_model_desc* m) {
   if (m->mlp_hidden % 64 != 0) return fail(TS_ESHAPE, "mlp_hidden must be a multiple of 64");
   if (m->norm != 0 && m->norm != 1) return fail(TS_EINVAL, "norm must be 0 (LayerNorm) or 1 (RMSNorm)");
   if (!(m->eps > 0.f)) return fail(TS_EINVAL, "eps must be > 0");
+  if (m->layer0_dedup != 0 && m->layer0_dedup != 1) return fail(TS_EINVAL, "layer0_dedup must be 0 or 1");
   if (m->act_dtype == TS_F32) {
     if (m->head_dim != 32 && m->head_dim != 64)
       return fail(TS_ESHAPE, "fp32 attention supports head_dim 32 or 64");
@@ -171,7 +172,8 @@ WS layout(const ts_model_desc* m, const ts_plan* p, bool states, bool per_tile, 
   w.amax = (unsigned*)scratch;
   w.sa = (float*)(scratch + size_t(tsk::AMAX_SLOTS) * tsk::AMAX_STRIDE * 4);
   if (states && per_tile) w.X = (float*)take(size_t(Mt * d * 4));
-  if (shared_xs) w.xs = (float*)take(size_t(Ms * d * 4));
+  // shared states; with layer-0 dedup also the shared-layout input rows of per-tile layer 0
+  if (shared_xs || (per_tile && m->layer0_dedup)) w.xs = (float*)take(size_t(Ms * d * 4));
   w.h = take(size_t(Mmax * d * ab));
   w.big = take(size_t(Mmax * wide * ab));
   w.o = take(size_t(Mt * d * ab));
@@ -327,7 +329,13 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared
 // One pre-norm block on rows x [M, d] fp32.  shared: M = n_union + n_tiles and
 // attention reads each tile through the plan's row map, then the w-bar blend
 // forms one row per token; otherwise M = n_tiles*(n+1) per-tile rows.
-ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shared, const WS& ws) {
+// xq (per-tile layer only): shared-layout rows [n_union + n_tiles, d] of which
+// every per-tile row of x is a copy (layer 0 of a stack); Norm1, QKV and
+// QK-norm then run once per token on xq and attention reads each window
+// through the row map (Table S1, layer 0: exact), while the out-projection,
+// Norm2 and MLP run on the per-tile rows.
+ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shared, const WS& ws,
+                    const float* xq = nullptr) {
   const ts_model_desc* m = c.m;
   const ts_plan* p = c.p;
   const int act = m->act_dtype;
@@ -335,6 +343,9 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
   const int64_t Mt = int64_t(p->n_tiles) * (p->n + 1);
   const int64_t Ms = int64_t(p->n_union) + p->n_tiles;
   const int64_t M = shared ? Ms : Mt;
+  const bool qsh = shared || xq;        // Norm1 .. attention on shared-layout rows
+  const int64_t Mq = qsh ? Ms : Mt;
+  const float* xn = xq ? xq : x;
   const int d = m->d, H = m->n_heads, hd = m->head_dim, dm = m->mlp_hidden;
   const int f8 = fp8_mask(m, shared);
   const bool rms = m->norm == 1;
@@ -348,19 +359,19 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
 
   {
     if (am_qkv) TS_HIP(tsk::zero_amax(c.s, am_qkv), "amax reset");
-    Scope sc(c.s, "norm", 0.0, double(M * d) * (4 + ab));
-    TS_HIP(tsk::norm(c.s, act, rms, x, int(M), d, w.norm1_g, w.norm1_b, m->eps, ws.h, am_qkv), "norm1");
+    Scope sc(c.s, "norm", 0.0, double(Mq * d) * (4 + ab));
+    TS_HIP(tsk::norm(c.s, act, rms, xn, int(Mq), d, w.norm1_g, w.norm1_b, m->eps, ws.h, am_qkv), "norm1");
   }
-  if ((st = proj(c, ws, (f8 & TS_FP8_QKV) != 0, "qkv", tsk::EPI_BIAS, ws.h, M, 3 * d, d, w.w_qkv, w.w_qkv_f8,
+  if ((st = proj(c, ws, (f8 & TS_FP8_QKV) != 0, "qkv", tsk::EPI_BIAS, ws.h, Mq, 3 * d, d, w.w_qkv, w.w_qkv_f8,
                  w.w_scale_f8 ? w.w_scale_f8 + 0 : nullptr, w.b_qkv, ws.big, am_qkv != nullptr)) != TS_OK)
     return st;
   {
-    Scope sc(c.s, "qk_prep", 0.0, double(M * 2 * d) * 2 * ab);
-    TS_HIP(tsk::qk_prep(c.s, act, ws.big, int(M), d, H, hd, m->qk_norm ? w.q_g : nullptr, w.k_g, m->eps,
-                        rope_rows(p, shared)),
+    Scope sc(c.s, "qk_prep", 0.0, double(Mq * 2 * d) * 2 * ab);
+    TS_HIP(tsk::qk_prep(c.s, act, ws.big, int(Mq), d, H, hd, m->qk_norm ? w.q_g : nullptr, w.k_g, m->eps,
+                        rope_rows(p, qsh)),
            "qk_prep");
   }
-  if ((st = window_attention(m, p, shared, false, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats, ws.vt)) != TS_OK)
+  if ((st = window_attention(m, p, qsh, false, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats, ws.vt)) != TS_OK)
     return st;
   const void* aout = ws.o;
   if (shared) {
@@ -510,8 +521,15 @@ ts_status stack_impl(const ts_model_desc* m, const ts_layer_weights* layers, con
       Scope sc(c.s, "gather", 0.0, double(Mt) * d * 8);
       TS_HIP(tsk::gather(c.s, x_in, g, 0, (const int*)p->d_tile_rows, p->n_tiles, p->n, d, w.X), "gather");
     }
+    // layer-0 dedup: the shared-layout input rows (the tokens, then g once per tile)
+    const float* x0 = nullptr;
+    if (m->layer0_dedup) {
+      Scope sc(c.s, "init_shared", 0.0, double(Ms) * d * 8);
+      TS_HIP(tsk::init_shared(c.s, x_in, g, p->n_union, p->n_tiles, d, w.xs), "init");
+      x0 = w.xs;
+    }
     for (int l = 0; l < k; ++l)
-      if ((st = run_layer(c, layers[l], w.X, false, w)) != TS_OK) return st;
+      if ((st = run_layer(c, layers[l], w.X, false, w, l == 0 ? x0 : nullptr)) != TS_OK) return st;
     // merge into one shared state (or the output, for the tiled baseline)
     float* mu = shared_xs ? w.xs : x_out;
     float* mg = shared_xs ? w.xs + size_t(p->n_union) * d : g_out;
@@ -567,8 +585,16 @@ ts_status merge_once_impl(const ts_model_desc* m, const ts_layer_weights* layers
     Scope sc(c.s, "gather", 0.0, double(Mt) * d * 8);
     TS_HIP(tsk::gather(c.s, x_in, g, 0, (const int*)p->d_tile_rows, p->n_tiles, p->n, d, w.X), "gather");
   }
+  // layer-0 dedup: layer 0's per-tile rows are copies of the input rows (l >= 1)
+  // or, after a merge at l = 0, of the merged rows
+  const float* x0 = nullptr;
+  if (m->layer0_dedup && l > 0) {
+    Scope sc(c.s, "init_shared", 0.0, double(Ms) * d * 8);
+    TS_HIP(tsk::init_shared(c.s, x_in, g, p->n_union, p->n_tiles, d, w.xs), "init");
+    x0 = w.xs;
+  }
   for (int i = 0; i < l; ++i)
-    if ((st = run_layer(c, layers[i], w.X, false, w)) != TS_OK) return st;
+    if ((st = run_layer(c, layers[i], w.X, false, w, i == 0 ? x0 : nullptr)) != TS_OK) return st;
   if ((st = merge(w.xs, w.xs + size_t(p->n_union) * d)) != TS_OK) return st;
   {
     Scope sc(c.s, "gather", 0.0, double(Mt) * d * 8);
@@ -577,7 +603,8 @@ ts_status merge_once_impl(const ts_model_desc* m, const ts_layer_weights* layers
            "re-gather");
   }
   for (int i = l; i < m->n_layers; ++i)
-    if ((st = run_layer(c, layers[i], w.X, false, w)) != TS_OK) return st;
+    if ((st = run_layer(c, layers[i], w.X, false, w, i == 0 && m->layer0_dedup ? w.xs : nullptr)) != TS_OK)
+      return st;
   return merge(x_out, g_out);
 }
 
@@ -608,8 +635,14 @@ ts_status partial_share_impl(const ts_model_desc* m, const ts_layer_weights* lay
     Scope sc(c.s, "gather", 0.0, double(Mt) * d * 8);
     TS_HIP(tsk::gather(c.s, x_in, g, 0, (const int*)p->d_tile_rows, p->n_tiles, p->n, d, w.X), "gather");
   }
+  const float* x0 = nullptr;   // layer-0 dedup (per-tile layer 0 only)
+  if (m->layer0_dedup && k > 0) {
+    Scope sc(c.s, "init_shared", 0.0, double(Ms) * d * 8);
+    TS_HIP(tsk::init_shared(c.s, x_in, g, p->n_union, p->n_tiles, d, w.xs), "init");
+    x0 = w.xs;
+  }
   for (int i = 0; i < k; ++i)
-    if ((st = run_layer(c, layers[i], w.X, false, w)) != TS_OK) return st;
+    if ((st = run_layer(c, layers[i], w.X, false, w, i == 0 ? x0 : nullptr)) != TS_OK) return st;
   for (int i = k; i < m->n_layers; ++i)
     if ((st = run_layer_partial(c, layers[i], w.X, share, w)) != TS_OK) return st;
   Scope sc(c.s, "merge", 0.0, (double(p->n_entries + p->n_tiles) + double(Ms)) * d * 4);

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
-    assert ts.ts_abi_version() == 3
+    assert ts.ts_abi_version() == 4
 
 
 PLAN_CASES = [(configs.get(n)["ndim"], configs.get(n)["grid"], configs.get(n)["tile"], configs.get(n)["stride"])
@@ -131,3 +131,23 @@ def test_fp8_quantize_alignment_is_checked_before_any_gpu_work():
                                ws, 256, None)
         assert st == -1   # TS_EINVAL
         assert b"aligned" in L.ts_last_error()
+
+
+def test_layer0_dedup_field_is_validated_and_sized():
+    """layer0_dedup must be 0 or 1; with it, the tiled decoder (k = n_layers)
+    also holds the shared-layout rows of layer 0 in its workspace."""
+    h = ts.ts_plan_create(3, (4, 12, 20), (4, 12, 12), (4, 8, 8))
+    try:
+        m = _model()
+        m.layer0_dedup = 2
+        with pytest.raises(ts.TileShareError, match="TS_EINVAL.*layer0_dedup"):
+            ts.ts_workspace_size(m, h, 0)
+        L = m.n_layers
+        plain = ts.ts_workspace_size(_model(), h, L)
+        dedup = ts.ts_workspace_size(_model(layer0_dedup=True), h, L)
+        info = ts.ts_plan_get_info(h)
+        assert dedup - plain >= (info.n_union + info.n_tiles) * m.d * 4
+        # stacks with shared layers hold those rows already
+        assert ts.ts_workspace_size(_model(layer0_dedup=True), h, 1) == ts.ts_workspace_size(_model(), h, 1)
+    finally:
+        ts.ts_plan_destroy(h)

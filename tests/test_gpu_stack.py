@@ -260,3 +260,49 @@ def test_partial_sharing_against_oracle(name, size, k, share):
     e, eg = max_rel(got, ref), max_rel(ggot, gref)
     print(f"  max|err|/rms = {e:.3e} (globals {eg:.3e}), tolerance {tol}")
     assert e < tol and eg < tol
+
+
+DEDUP = [("stack", "tiny2d", None, 1), ("stack", "minimax_h3", "r", 1), ("stack", "minimax_h3", "r", 3),
+         ("stack", "small_video", "r", 2), ("stack", "vitok4k", "r", 1), ("stack", "minimax_h3_fp8", "r", 1),
+         ("merge_once", "minimax_h3", "r", 0), ("merge_once", "minimax_h3", "r", 2),
+         ("partial", "minimax_h3", "r", 1)]
+
+
+@pytest.mark.parametrize("entry,name,size,k", DEDUP)
+def test_layer0_dedup_against_oracle_and_per_tile_rows(entry, name, size, k):
+    """Table S1, layer 0: Norm1, QKV and QK-norm once per token (every tile
+    holds copies of the same rows) and attention through the tile map give
+    the per-tile layer 0's result: against the oracle (which runs layer 0 per
+    tile) to the usual bound, and against the same GPU entry point without the
+    dedup to rounding."""
+    cfg = configs.get(name) if size is None else reduced(name)
+    say(f"layer-0 dedup {entry} {name} k={k}")
+    x, g, layers = make_inputs(cfg, qk_scale=2.0)
+    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    if entry == "stack":
+        ref, gref = _oracle(cfg, x, g, layers, k)
+    elif entry == "merge_once":
+        ref, gref = M.merge_once_forward(cfg, pl, x, g, layers, k)
+    else:
+        ref, gref = M.partial_share_forward(cfg, pl, x, g, layers, k, {"q"})
+    outs = {}
+    for dd in (False, True):
+        run = Run(dict(cfg, layer0_dedup=dd), layers)
+        try:
+            if entry == "stack":
+                outs[dd] = run.stack(x, g, k)
+            elif entry == "merge_once":
+                outs[dd] = run.merge_once(x, g, k)
+            else:
+                outs[dd] = run.partial_share(x, g, k, {"q"})
+        finally:
+            run.close()
+    (got, ggot), (plain, gplain) = outs[True], outs[False]
+    tol = TOL["fp8" if cfg["gemm_shared"] == "fp8" and k < cfg["n_layers"] else cfg["dtype"]]
+    e, eg = max_rel(got, ref), max_rel(ggot, gref)
+    ep = max(max_rel(got, plain), max_rel(ggot, gplain))
+    print(f"  max|err|/rms = {e:.3e} (globals {eg:.3e}), tolerance {tol}; against per-tile rows {ep:.3e}")
+    assert e < tol and eg < tol
+    # the same kernels on the same values: equal up to the summation order of
+    # rows that fall into the ragged-row GEMM in one layout and not the other
+    assert ep < 1e-3
