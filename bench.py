@@ -69,7 +69,6 @@ def cpu_baseline(cfg, k):
     the workload: one per-tile block on one tile window (tile_tokens + 1 rows),
     then scale to decoded tokens/s of the whole TileShare-k decode by the
     ratio of algorithmic FLOPs."""
-    import numpy as np
     from oracle import model as M
     from oracle.plan import Plan
     from synth import make_inputs

@@ -3,7 +3,6 @@ import json
 import math
 import os
 from collections import Counter
-from fractions import Fraction
 
 import numpy as np
 import pytest
