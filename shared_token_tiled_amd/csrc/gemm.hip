@@ -682,15 +682,16 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
   const bool f8 = act == ACT_FP8;
   const int esz = f8 ? 1 : 2, osz = (epi == EPI_RESID || epi == EPI_F32) ? 4 : 2;
   // Ragged rows (M % 256 <= 32) go to k_gemm_rows when that saves a round of
-  // 256x256 tiles over the device's compute units (TS_GEMM_ROWS=always: in
-  // every such case, for tests).
+  // 256x256 tiles over the device's compute units (for tests, TS_GEMM_ROWS=
+  // always: in every such case; never: not at all).
   const int tiles_n = (N + BN - 1) / BN, R = M % BM;
   int Mm = M;
-  if (R != 0 && R <= 32) {
-    const char* e = getenv("TS_GEMM_ROWS");
+  const char* rows_env = getenv("TS_GEMM_ROWS");
+  if (R != 0 && R <= 32 && !(rows_env && strcmp(rows_env, "never") == 0)) {
     const int64_t ncu = device_cus();
     const int64_t all = int64_t((M + BM - 1) / BM) * tiles_n, full = int64_t(M / BM) * tiles_n;
-    if ((e && strcmp(e, "always") == 0) || (full > 0 && (full + ncu - 1) / ncu < (all + ncu - 1) / ncu)) Mm = M - R;
+    if ((rows_env && strcmp(rows_env, "always") == 0) || (full > 0 && (full + ncu - 1) / ncu < (all + ncu - 1) / ncu))
+      Mm = M - R;
   }
   // The tiles of a partial last round over the CUs (when a workspace is
   // given) run K-split: ks parts per tile, as many workgroups as fit one

@@ -267,3 +267,33 @@ def test_full_size_stack_is_deterministic_and_finite():
         run.close()
     assert np.all(np.isfinite(a)) and np.all(np.isfinite(ga))
     assert np.array_equal(a, b) and np.array_equal(ga, gb)
+
+
+@pytest.mark.parametrize("name", ["minimax_h3", "small_video"])
+@pytest.mark.parametrize("rows_kernel", [True, False])
+def test_full_size_layer0_dedup_matches_per_tile_rows(name, rows_kernel, monkeypatch):
+    """Table S1, layer 0 at full size: a one-layer tiled decoder with layer 0's
+    Norm1, QKV and QK-norm once per token and attention through the tile map
+    equals the per-tile layer 0.  Without the ragged-row GEMM the two are
+    bit-identical (the same kernels on the same values); with it, the few rows
+    it takes differ between the layouts in summation order, so a bf16 q, k or
+    v value there can round one unit apart (2^-8 relative), which moves the
+    layer output by less than that."""
+    if not rows_kernel:
+        monkeypatch.setenv("TS_GEMM_ROWS", "never")
+    cfg, x, g, layers, pl = _full_inputs(name)
+    say(f"full-size layer-0 dedup {name} rows_kernel={rows_kernel} n_union={pl.n_union} tiles={pl.n_tiles}")
+    outs = {}
+    for dd in (False, True):
+        run = Run(dict(cfg, layer0_dedup=dd), layers)
+        try:
+            outs[dd] = run.stack(x, g, 1)
+        finally:
+            run.close()
+    e = max(max_rel(outs[True][0], outs[False][0]), max_rel(outs[True][1], outs[False][1]))
+    print(f"  max|diff|/rms against the per-tile layer 0: {e:.3e}")
+    assert np.all(np.isfinite(outs[True][0]))
+    if rows_kernel:
+        assert e < 2.0 ** -8
+    else:
+        assert np.array_equal(outs[True][0], outs[False][0]) and np.array_equal(outs[True][1], outs[False][1])
