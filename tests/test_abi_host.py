@@ -151,3 +151,13 @@ def test_layer0_dedup_field_is_validated_and_sized():
         assert ts.ts_workspace_size(_model(layer0_dedup=True), h, 1) == ts.ts_workspace_size(_model(), h, 1)
     finally:
         ts.ts_plan_destroy(h)
+
+
+def test_graft_entry_build_accepts_the_built_library(monkeypatch):
+    """__graft_entry__.build() checks the library it built against the
+    binding's ABI version (the compile step itself is stubbed here, so the
+    library the other tests loaded is not rewritten under them)."""
+    import __graft_entry__ as entry
+    from shared_token_tiled_amd import build as b
+    monkeypatch.setattr(b, "build", lambda *a, **k: None)
+    entry.build()
