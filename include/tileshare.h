@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define TS_ABI_VERSION 4
+#define TS_ABI_VERSION 5
 
 typedef int32_t ts_status;
 #define TS_OK 0
@@ -107,10 +107,23 @@ ts_status ts_plan_export(const ts_plan* plan, int32_t* tile_start, int32_t* tile
  * pos * base^(-i/m), evaluated in float64 and rounded to fp32. */
 ts_status ts_plan_export_rope(const ts_plan* plan, int32_t head_dim, float rope_base,
                               float* cos_out, float* sin_out);
-/* Upload the maps and the RoPE table for (head_dim, rope_base) to device
- * memory owned by the plan (the only device allocation the library makes).
- * Must be called before any forward call that uses the plan; calling it
- * again with another head size replaces the table.  Synchronous. */
+/* The query blocks of the shared layers' attention (Figure 2 caption: the
+ * blend of an overlap token's per-tile outputs): grid rows grouped by the set
+ * of tiles holding them with a nonzero w-bar, groups ordered by decreasing set
+ * size then by their ascending tile lists, rows ascending, cut into blocks of
+ * 256 rows.  *nblk and *maxc receive the block count and the largest set;
+ * the arrays (caller-owned host buffers, any may be NULL) receive blk_nt
+ * [nblk] (tiles of each block), blk_tiles [nblk*maxc] (ascending, -1 padded),
+ * blk_rows [nblk*256] (grid rows, -1 in empty slots) and blk_w
+ * [nblk*maxc*256] (w-bar of (block, tile, slot), 0 in empty slots). */
+ts_status ts_plan_export_blocks(const ts_plan* plan, int32_t* nblk, int32_t* maxc, int32_t* blk_nt,
+                                int32_t* blk_tiles, int32_t* blk_rows, float* blk_w);
+/* Upload the maps, the attention's query blocks (grid rows grouped by the
+ * tiles that hold them with a nonzero w-bar) and the grid-coordinate RoPE
+ * table for (head_dim, rope_base) to device memory owned by the plan (the
+ * only device allocation the library makes).  Must be called before any
+ * forward call that uses the plan; calling it again with another head size
+ * replaces the table.  Synchronous. */
 ts_status ts_plan_upload(ts_plan* plan, int32_t head_dim, float rope_base, void* stream);
 void ts_plan_destroy(ts_plan* plan);
 
@@ -275,18 +288,28 @@ ts_status ts_op_gemm_ws(int32_t dtype, int32_t epilogue, const void* a, const vo
                         int32_t n, int32_t k, const float* bias, void* c, const float* scale_a,
                         const float* scale_b, void* ws, size_t ws_bytes, void* stream);
 
-/* Window attention of one layer (Figure 2 caption; Table S1 "Attention
- * (dense, per tile)"): for every tile t and head, dense softmax attention
- * with scale 1/sqrt(head_dim) over the tile's window (its tile_tokens rows
- * plus its global token), RoPE at tile-local coordinates on q and k (none
- * on the global token).  qkv: device [rows, 3d] act_dtype, q | k | v.
- * shared = 1: rows = n_union + n_tiles, window rows read through the plan's
- * tile_rows, global row of tile t = n_union + t; shared = 0: rows =
- * n_tiles*(tile_tokens+1) in per-tile layout (tile t at t*(tile_tokens+1),
- * its global token last).  out: device [n_tiles*(tile_tokens+1), d]
- * act_dtype in per-tile layout. */
-ts_status ts_op_window_attention(const ts_model_desc* model, const ts_plan* plan, int32_t shared,
-                                 const void* qkv, void* out, void* stream);
+/* The attention step of one layer exactly as the forward calls run it
+ * (Figure 2 caption; Table S1 "Attention (dense, per tile)" and "Blend of
+ * attention outputs"): the q and k sections of qkv are normalised per head
+ * (QK-RMSNorm with gains q_g, k_g [head_dim] fp32 when model->qk_norm) and
+ * rotated, IN PLACE -- every row by its grid coordinate (a tile's global row
+ * by the tile's start), which gives every window the scores of tile-local
+ * RoPE -- then, for every tile t and head, dense softmax attention with scale
+ * 1/sqrt(head_dim) over the tile's window (its tile_tokens rows plus its
+ * global row).  qkv: device [rows, 3d] act_dtype, q | k | v as the QKV
+ * projection writes them.
+ *  shared = 1: rows = n_union + n_tiles (grid rows, then the global row of
+ *    tile t at n_union + t); out: device [n_union + n_tiles, d] act_dtype,
+ *    row p < n_union the w-bar blend of the outputs of every window holding p
+ *    (ascending tile order), row n_union + t tile t's global-token output --
+ *    the out-projection's input of a shared layer;
+ *  shared = 0: per-tile layout, rows = n_tiles*(tile_tokens+1) (tile t at
+ *    t*(tile_tokens+1), its global token last); out in the same layout.
+ * ws: device workspace of at least ts_workspace_size(model, plan, n_layers)
+ * bytes, 256-byte aligned.  Asynchronous. */
+ts_status ts_op_attention(const ts_model_desc* model, const ts_plan* plan, int32_t shared, void* qkv,
+                          const float* q_g, const float* k_g, void* out, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* ---- diagnostics ------------------------------------------------------- */
 /* Per-kernel timing of the calling thread's forward calls.  Between

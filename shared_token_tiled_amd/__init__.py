@@ -56,7 +56,7 @@ class TileShareError(RuntimeError):
 
 
 _lib = None
-ABI_VERSION = 4   # the layout of the structs below; a library of another version is refused
+ABI_VERSION = 5   # the layout of the structs below; a library of another version is refused
 
 
 def lib():
@@ -74,6 +74,7 @@ def lib():
             "ts_plan_get_info": (ctypes.c_int32, [_VP, P(PlanInfo)]),
             "ts_plan_export": (ctypes.c_int32, [_VP] + [_VP] * 6),
             "ts_plan_export_rope": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_float, _VP, _VP]),
+            "ts_plan_export_blocks": (ctypes.c_int32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP]),
             "ts_plan_upload": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_float, _VP]),
             "ts_plan_destroy": (None, [_VP]),
             "ts_workspace_size": (ctypes.c_int32, [P(ModelDesc), _VP, ctypes.c_int32, P(ctypes.c_size_t)]),
@@ -95,7 +96,8 @@ def lib():
             "ts_op_gemm_ws": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _VP, _VP, ctypes.c_int32,
                                                ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,
                                                ctypes.c_size_t, _VP]),
-            "ts_op_window_attention": (ctypes.c_int32, [P(ModelDesc), _VP, ctypes.c_int32, _VP, _VP, _VP]),
+            "ts_op_attention": (ctypes.c_int32, [P(ModelDesc), _VP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,
+                                                 ctypes.c_size_t, _VP]),
             "ts_profile_begin": (ctypes.c_int32, []),
             "ts_profile_end": (ctypes.c_int32, [P(KernelStat), ctypes.c_int32, P(ctypes.c_int32)]),
         }
@@ -169,6 +171,21 @@ def ts_plan_export_rope(plan, head_dim, rope_base=10000.0):
     _check(lib().ts_plan_export_rope(plan, head_dim, rope_base, c.ctypes.data_as(_VP), s.ctypes.data_as(_VP)),
            "ts_plan_export_rope")
     return c, s
+
+
+def ts_plan_export_blocks(plan):
+    """Return numpy arrays (blk_nt [nblk], blk_tiles [nblk, maxc], blk_rows [nblk, 256], blk_w [nblk, maxc, 256])."""
+    import numpy as np
+    nb, mc = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().ts_plan_export_blocks(plan, ctypes.byref(nb), ctypes.byref(mc), None, None, None, None),
+           "ts_plan_export_blocks")
+    nt = np.empty(nb.value, np.int32)
+    tl = np.empty((nb.value, mc.value), np.int32)
+    rw = np.empty((nb.value, 256), np.int32)
+    w = np.empty((nb.value, mc.value, 256), np.float32)
+    _check(lib().ts_plan_export_blocks(plan, None, None, *(a.ctypes.data_as(_VP) for a in (nt, tl, rw, w))),
+           "ts_plan_export_blocks")
+    return nt, tl, rw, w
 
 
 def ts_plan_upload(plan, head_dim, rope_base=10000.0, stream=None):
@@ -248,9 +265,13 @@ def ts_op_gemm(dtype, epilogue, a, b, bias, c, scale_a=None, scale_b=None, strea
                                    _stream(stream)), "ts_op_gemm_ws")
 
 
-def ts_op_window_attention(model, plan, shared, qkv, out, stream=None):
-    _check(lib().ts_op_window_attention(ctypes.byref(model), plan, 1 if shared else 0, _ptr(qkv), _ptr(out),
-                                        _stream(stream)), "ts_op_window_attention")
+def ts_op_attention(model, plan, shared, qkv, q_g, k_g, out, ws, stream=None):
+    """The layer's attention step: qkv (device, modified in place: q and k
+    normalised and rotated), q_g / k_g (device fp32 [head_dim] or None), out
+    (device, blended rows when shared), ws (device uint8 workspace)."""
+    _check(lib().ts_op_attention(ctypes.byref(model), plan, 1 if shared else 0, _ptr(qkv), _ptr(q_g), _ptr(k_g),
+                                 _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "ts_op_attention")
 
 
 def ts_profile_begin():

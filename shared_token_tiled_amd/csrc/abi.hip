@@ -142,11 +142,11 @@ struct WS {
   float* xs = nullptr;       // fp32 [M_s, d] shared states
   void* h = nullptr;         // act [M_max, d] norm / blend output
   void* big = nullptr;       // act [M_max, max(3d, mlp)] qkv, then MLP hidden
-  void* o = nullptr;         // act [M_t, d] attention output, per-tile layout
+  void* o = nullptr;         // act [M_t, d] attention output, per-tile layout; in shared
+                             // layers fp32 [n_union, d] partial blends of the attention
   uint8_t* q8 = nullptr;     // e4m3 [M_s, max(d, mlp)] quantised GEMM operand
   float* gpart = nullptr;    // fp32 split states of the global-token attention rows
   int64_t gpart_floats = 0;
-  void* vt = nullptr;        // bf16 [n_tiles, d, n_pad] window values transposed per head
   float* gsplit = nullptr;   // fp32 K-split parts of a GEMM's partial last round of tiles
   size_t bytes = 0;
 };
@@ -176,13 +176,13 @@ WS layout(const ts_model_desc* m, const ts_plan* p, bool states, bool per_tile, 
   if (shared_xs || (per_tile && m->layer0_dedup)) w.xs = (float*)take(size_t(Ms * d * 4));
   w.h = take(size_t(Mmax * d * ab));
   w.big = take(size_t(Mmax * wide * ab));
-  w.o = take(size_t(Mt * d * ab));
+  // per-tile attention outputs, or (shared layers) the fp32 partial blends
+  w.o = take(std::max(size_t(Mt * d * ab), size_t(p->n_union) * d * 4));
   if (m->gemm_dtype_shared == TS_FP8E4M3)
     w.q8 = (uint8_t*)take(size_t((m->fp8_per_tile ? Mmax : Ms) * std::max<int64_t>(d, m->mlp_hidden)));
   if (m->act_dtype == TS_BF16) {  // up to 64 splits of each global row's keys
     w.gpart_floats = int64_t(p->n_tiles) * m->n_heads * 64 * (m->head_dim + 2);
     w.gpart = (float*)take(size_t(w.gpart_floats * 4));
-    w.vt = take(size_t(p->n_tiles) * d * ((int64_t(p->n) + 63) / 64 * 64) * 2);
   }
   if (m->act_dtype != TS_F32) w.gsplit = (float*)take(TS_GEMM_SPLIT_WS_BYTES);
   w.bytes = off;
@@ -266,62 +266,57 @@ tsk::RopeRows rope_rows(const ts_plan* p, bool shared) {
   return r;
 }
 
-// Window attention of every (tile, head) for one layer.  rope: q and k are
-// as the QKV projection (and QK-norm) left them and the kernels rotate them
-// by tile-local positions; otherwise qk_prep has rotated them already.
-ts_status window_attention(const ts_model_desc* m, const ts_plan* p, bool shared, bool rope, const void* qkv,
-                           void* out, hipStream_t s, float* gscratch = nullptr, int64_t gscratch_floats = 0,
-                           void* vt = nullptr) {
+// Window attention of every (tile, head) for one layer; q and k as qk_prep
+// left them.  Layouts: ATT_TILED (per-tile qkv rows and outputs),
+// ATT_SHARED_ROWS (shared qkv rows read through the tile map, per-tile
+// outputs: layer 0 once per token), ATT_BLENDED (shared qkv rows, outputs
+// blended with w-bar into [n_union + n_tiles] rows; `part` holds the fp32
+// partial blends).  amax (optional, bf16): max |output| as stored.
+enum AttnLayout { ATT_TILED, ATT_SHARED_ROWS, ATT_BLENDED };
+ts_status window_attention(const ts_model_desc* m, const ts_plan* p, AttnLayout lay, const void* qkv, void* out,
+                           float* part, unsigned* amax, hipStream_t s, float* gscratch = nullptr,
+                           int64_t gscratch_floats = 0) {
   tsk::AttnArgs a;
   a.qkv = qkv;
   a.out = out;
-  a.rows = shared ? (const int*)p->d_tile_rows : nullptr;
+  a.part = part;
+  a.rows = lay != ATT_TILED ? (const int*)p->d_tile_rows : nullptr;
+  if (lay == ATT_BLENDED) {
+    a.blk_nt = (const int*)p->d_blk_nt;
+    a.blk_tiles = (const int*)p->d_blk_tiles;
+    a.blk_rows = (const int*)p->d_blk_rows;
+    a.blk_w = (const float*)p->d_blk_w;
+    a.nblk = p->nblk;
+    a.maxc = p->blk_maxc;
+  }
   a.n_union = p->n_union;
   a.d = m->d;
   a.H = m->n_heads;
   a.hd = m->head_dim;
   a.n_tiles = p->n_tiles;
   a.n = p->n;
-  a.local_pos = (const int*)p->d_local_pos;
-  a.rope = (const float*)p->d_rope;
-  a.rope_floats = p->rope_floats;
-  for (int ax = 0; ax < 3; ++ax) {
-    a.pairs[ax] = p->rope_pairs[ax];
-    a.rope_off[ax] = p->rope_off[ax];
-    a.rope_wbase[ax] = p->rope_wbase[ax];
-    a.rope_wpairs[ax] = p->rope_wpairs[ax];
-  }
-  if (rope && m->act_dtype == TS_BF16) {
-    // the bf16 kernels rotate 8 dims (4 pairs) at a time and allow a group to
-    // straddle one axis boundary, not two
-    const int b0 = p->rope_pairs[0], b1 = p->rope_pairs[0] + p->rope_pairs[1];
-    for (int g = 0; 4 * g < m->head_dim / 2; ++g)
-      if (b0 > 4 * g && b1 < 4 * g + 4 && p->rope_pairs[1] > 0)
-        return fail(TS_ESHAPE, "bf16 attention: a group of 4 RoPE pairs spans three axes (head_dim too small)");
-  }
-  // algorithmic work: 4 (n+1) d FLOPs per query row (QK^T and PV over the
-  // n+1 keys); bytes: the window's q, k, v rows read once, o written once
+  a.amax = m->act_dtype == TS_BF16 ? amax : nullptr;
+  // algorithmic work: 4 (n+1) d FLOPs per query row and window (QK^T and PV
+  // over the n+1 keys); bytes: the windows' q, k, v rows read once, each
+  // output row written once
   const double nn = double(p->n + 1), ab = act_bytes(m->act_dtype);
+  const double qrows = lay == ATT_BLENDED ? double(p->n_entries) : double(p->n_tiles) * p->n;
+  const double orows = lay == ATT_BLENDED ? double(p->n_union) : double(p->n_tiles) * p->n;
   if (m->act_dtype == TS_F32) {
-    Scope sc(s, "attn_f32", 4.0 * nn * nn * m->d * p->n_tiles, double(p->n_tiles) * nn * m->d * 4 * ab);
-    TS_HIP(tsk::attention(s, m->act_dtype, a, rope), "attention");
+    Scope sc(s, "attn_f32", 4.0 * nn * (qrows + p->n_tiles) * m->d,
+             (double(p->n_tiles) * nn * 3 * m->d + orows * m->d + double(p->n_tiles) * m->d) * ab);
+    TS_HIP(tsk::attention(s, m->act_dtype, a), "attention");
     return TS_OK;
   }
-  if (!rope) {
-    if (!vt) return fail(TS_EINVAL, "internal: unrotated attention needs the V^T workspace");
-    Scope sc(s, "v_transpose", 0.0, double(p->n_tiles) * double(p->n) * m->d * 2 * ab);
-    TS_HIP(tsk::v_transpose(s, a, vt), "v_transpose");
-    a.vt = vt;
-  }
   {
-    Scope sc(s, "attn_bf16", 4.0 * double(p->n) * nn * m->d * p->n_tiles,
-             double(p->n_tiles) * (nn * 3 * m->d + double(p->n) * m->d) * ab);
-    TS_HIP(tsk::attention(s, m->act_dtype, a, rope), "attention");
+    Scope sc(s, lay == ATT_BLENDED ? "attn_blend_bf16" : "attn_bf16", 4.0 * nn * qrows * m->d,
+             (double(p->n_tiles) * nn * 3 * m->d + orows * m->d) * ab);
+    TS_HIP(tsk::attention(s, m->act_dtype, a), "attention");
   }
   {
     Scope sc(s, "attn_global_bf16", 4.0 * nn * m->d * p->n_tiles,
              double(p->n_tiles) * (nn * 2 * m->d + 2 * m->d) * ab);
-    TS_HIP(tsk::attention_global(s, a, rope, gscratch, gscratch_floats), "attention (global rows)");
+    TS_HIP(tsk::attention_global(s, a, gscratch, gscratch_floats), "attention (global rows)");
   }
   return TS_OK;
 }
@@ -353,7 +348,7 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
   // producers that take the max of an fp8 operand (see fused_amax)
   const bool fa = f8 != 0 && fused_amax();
   unsigned* am_qkv = fa && (f8 & TS_FP8_QKV) ? ws.amax : nullptr;
-  unsigned* am_out = fa && shared && (f8 & TS_FP8_OUT) ? ws.amax : nullptr;
+  unsigned* am_out = fa && (f8 & TS_FP8_OUT) ? ws.amax : nullptr;
   unsigned* am_fc1 = fa && (f8 & TS_FP8_FC1) ? ws.amax : nullptr;
   unsigned* am_fc2 = fa && (f8 & TS_FP8_FC2) ? ws.amax : nullptr;
 
@@ -371,18 +366,13 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
                         rope_rows(p, qsh)),
            "qk_prep");
   }
-  if ((st = window_attention(m, p, qsh, false, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats, ws.vt)) != TS_OK)
+  // shared layers: the w-bar blend of the windows' outputs is formed by the
+  // attention itself, straight into the out-projection's operand rows
+  if (am_out) TS_HIP(tsk::zero_amax(c.s, am_out), "amax reset");
+  const void* aout = shared ? ws.h : ws.o;
+  if ((st = window_attention(m, p, shared ? ATT_BLENDED : (qsh ? ATT_SHARED_ROWS : ATT_TILED), ws.big,
+                             const_cast<void*>(aout), (float*)ws.o, am_out, c.s, ws.gpart, ws.gpart_floats)) != TS_OK)
     return st;
-  const void* aout = ws.o;
-  if (shared) {
-    if (am_out) TS_HIP(tsk::zero_amax(c.s, am_out), "amax reset");
-    Scope sc(c.s, "blend", 0.0, (double(p->n_entries + p->n_tiles) + double(Ms)) * d * ab);
-    TS_HIP(tsk::blend(c.s, act, act, ws.o, d, p->n_union, p->n_tiles, p->n, (const int*)p->d_cover_ptr,
-                      (const int*)p->d_entry_row, (const float*)p->d_cover_w, ws.h,
-                      (char*)ws.h + size_t(p->n_union) * d * ab, am_out),
-           "blend");
-    aout = ws.h;
-  }
   if ((st = proj(c, ws, (f8 & TS_FP8_OUT) != 0, "out", tsk::EPI_RESID, aout, M, d, d, w.w_o, w.w_o_f8,
                  w.w_scale_f8 ? w.w_scale_f8 + 1 : nullptr, w.b_o, x, am_out != nullptr)) != TS_OK)
     return st;
@@ -448,7 +438,8 @@ ts_status run_layer_partial(const Ctx& c, const ts_layer_weights& w, float* X, i
                         rope_rows(p, sq)),
            "qk_prep");
   }
-  if ((st = window_attention(m, p, sq, false, ws.big, ws.o, c.s, ws.gpart, ws.gpart_floats, ws.vt)) != TS_OK)
+  if ((st = window_attention(m, p, sq ? ATT_SHARED_ROWS : ATT_TILED, ws.big, ws.o, nullptr, nullptr, c.s, ws.gpart,
+                             ws.gpart_floats)) != TS_OK)
     return st;
   // out-projection
   if (so) {
@@ -706,25 +697,27 @@ ts_status ts_plan_export_rope(const ts_plan* p, int32_t head_dim, float rope_bas
                               float* sin_out) {
   if (!p || !cos_out || !sin_out) return fail(TS_EINVAL, "null argument");
   if (head_dim <= 0 || head_dim % 2 != 0) return fail(TS_EINVAL, "head_dim must be even and positive");
-  std::vector<float> tab;
-  int32_t pairs[3], off[3], wbase[3], wpairs[3];
-  tsplan::rope_table(*p, head_dim, rope_base, tab, pairs, off, wbase, wpairs);
-  const int32_t P = head_dim / 2;
-  for (int32_t j = 0; j < p->n; ++j) {
-    for (int32_t k = 0; k < P; ++k) {
-      const int ax = k < pairs[0] ? 0 : (k < pairs[0] + pairs[1] ? 1 : 2);
-      const int pos = (p->local_pos[j] >> (10 * ax)) & 1023;
-      const size_t at = off[ax] + 2 * (size_t(pos) * wpairs[ax] + k - wbase[ax]);
-      cos_out[size_t(j) * P + k] = tab[at];
-      sin_out[size_t(j) * P + k] = tab[at + 1];
-    }
-  }
+  tsplan::rope_local(*p, head_dim, rope_base, cos_out, sin_out);
+  return TS_OK;
+}
+
+ts_status ts_plan_export_blocks(const ts_plan* p, int32_t* nblk, int32_t* maxc, int32_t* blk_nt, int32_t* blk_tiles,
+                                int32_t* blk_rows, float* blk_w) {
+  if (!p) return fail(TS_EINVAL, "plan is null");
+  static_assert(TS_QBLOCK == tsk::QBLOCK, "plan and kernel query blocks");
+  if (nblk) *nblk = p->nblk;
+  if (maxc) *maxc = p->blk_maxc;
+  if (blk_nt) std::memcpy(blk_nt, p->blk_nt.data(), p->blk_nt.size() * 4);
+  if (blk_tiles) std::memcpy(blk_tiles, p->blk_tiles.data(), p->blk_tiles.size() * 4);
+  if (blk_rows) std::memcpy(blk_rows, p->blk_rows.data(), p->blk_rows.size() * 4);
+  if (blk_w) std::memcpy(blk_w, p->blk_w.data(), p->blk_w.size() * 4);
   return TS_OK;
 }
 
 static void free_device(ts_plan* p) {
-  void** ptrs[] = {&p->d_tile_rows, &p->d_cover_ptr, &p->d_entry_row, &p->d_cover_w,
-                   &p->d_local_pos, &p->d_rope,      &p->d_rope_glob, &p->d_tile_start};
+  void** ptrs[] = {&p->d_tile_rows, &p->d_cover_ptr,  &p->d_entry_row, &p->d_cover_w, &p->d_local_pos,
+                   &p->d_rope_glob, &p->d_tile_start, &p->d_blk_nt,    &p->d_blk_tiles, &p->d_blk_rows,
+                   &p->d_blk_w};
   for (void** q : ptrs) {
     if (*q) (void)hipFree(*q);
     *q = nullptr;
@@ -735,10 +728,8 @@ static void free_device(ts_plan* p) {
 ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* stream) {
   if (!p) return fail(TS_EINVAL, "plan is null");
   if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > 256) return fail(TS_EINVAL, "bad head_dim");
-  std::vector<float> tab;
-  int32_t pairs[3], off[3], wbase[3], wpairs[3];
-  tsplan::rope_table(*p, head_dim, rope_base, tab, pairs, off, wbase, wpairs);
-  if (tab.size() > 4096) return fail(TS_ESHAPE, "RoPE table exceeds 16 KB (head_dim/2 * tile extent too large)");
+  int32_t pairs[3];
+  tsplan::rope_pairs(p->desc.ndim, head_dim, pairs);
   std::vector<float> gtab;
   int32_t goff[3];
   tsplan::rope_table_global(*p, head_dim, rope_base, gtab, goff);
@@ -756,9 +747,12 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
       {&p->d_entry_row, entry_row.data(), entry_row.size() * 4},
       {&p->d_cover_w, p->cover_w.data(), p->cover_w.size() * 4},
       {&p->d_local_pos, p->local_pos.data(), p->local_pos.size() * 4},
-      {&p->d_rope, tab.data(), tab.size() * 4},
       {&p->d_rope_glob, gtab.data(), gtab.size() * 4},
       {&p->d_tile_start, p->tile_start.data(), p->tile_start.size() * 4},
+      {&p->d_blk_nt, p->blk_nt.data(), p->blk_nt.size() * 4},
+      {&p->d_blk_tiles, p->blk_tiles.data(), p->blk_tiles.size() * 4},
+      {&p->d_blk_rows, p->blk_rows.data(), p->blk_rows.size() * 4},
+      {&p->d_blk_w, p->blk_w.data(), p->blk_w.size() * 4},
   };
   for (auto& it : items) {
     if (hipMalloc(it.dst, std::max<size_t>(it.bytes, 4)) != hipSuccess) {
@@ -778,14 +772,10 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
   }
   for (int a = 0; a < 3; ++a) {
     p->rope_pairs[a] = pairs[a];
-    p->rope_off[a] = off[a];
-    p->rope_wbase[a] = wbase[a];
-    p->rope_wpairs[a] = wpairs[a];
     p->rope_glob_off[a] = goff[a];
   }
   p->rope_hd = head_dim;
   p->rope_base = rope_base;
-  p->rope_floats = int32_t(tab.size());
   p->uploaded = true;
   return TS_OK;
 }
@@ -893,13 +883,26 @@ ts_status ts_op_gemm_ws(int32_t dtype, int32_t epilogue, const void* a, const vo
   return TS_OK;
 }
 
-ts_status ts_op_window_attention(const ts_model_desc* m, const ts_plan* p, int32_t shared, const void* qkv,
-                                 void* out, void* stream) {
+ts_status ts_op_attention(const ts_model_desc* m, const ts_plan* p, int32_t shared, void* qkv, const float* q_g,
+                          const float* k_g, void* out, void* ws, size_t ws_bytes, void* stream) {
   ts_status st;
   if ((st = check_model(m)) != TS_OK) return st;
   if ((st = check_plan(p, m)) != TS_OK) return st;
   if (!qkv || !out) return fail(TS_EINVAL, "qkv and out must be non-null");
-  return window_attention(m, p, shared != 0, true, qkv, out, (hipStream_t)stream);
+  if (m->qk_norm && (!q_g || !k_g)) return fail(TS_EINVAL, "QK-norm needs q_g and k_g");
+  WS w0 = layout(m, p, false, false, false, nullptr);
+  if ((st = check_ws(ws, ws_bytes, w0.bytes)) != TS_OK) return st;
+  WS w = layout(m, p, false, false, false, (char*)ws);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t M = shared ? int64_t(p->n_union) + p->n_tiles : int64_t(p->n_tiles) * (p->n + 1);
+  {
+    Scope sc(s, "qk_prep", 0.0, double(M * 2 * m->d) * 2 * act_bytes(m->act_dtype));
+    TS_HIP(tsk::qk_prep(s, m->act_dtype, qkv, int(M), m->d, m->n_heads, m->head_dim, m->qk_norm ? q_g : nullptr, k_g,
+                        m->eps, rope_rows(p, shared != 0)),
+           "qk_prep");
+  }
+  return window_attention(m, p, shared ? ATT_BLENDED : ATT_TILED, qkv, out, (float*)w.o, nullptr, s, w.gpart,
+                          w.gpart_floats);
 }
 
 ts_status ts_profile_begin(void) {

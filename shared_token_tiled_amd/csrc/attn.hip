@@ -1,26 +1,40 @@
-// Per-tile window attention of the TileShare layer (Figure 2 caption and
-// Table S1: attention still runs per released tile, with the tile's own
-// global token and tile-local coordinates; in shared layers keys and values
-// come from the shared states).  One launch covers every (tile, head):
-// query / key / value rows of tile t are read in place from the row-major
-// qkv array through the tile's row map (shared layers) or from the tile's own
-// rows (per-tile layers), RoPE is applied while staging, and the global token
-// enters the online softmax as its initial state (score, weight 1, value).
-// Output rows are written in per-tile layout: row t*(n+1)+i for window token
-// i (i = n is the global token).
+// Window attention of the TileShare layer (Figure 2 caption and Table S1:
+// attention still runs per released tile, with the tile's own global token
+// and coordinates; in shared layers keys and values come from the shared
+// states, and an overlap token's per-tile outputs are blended with w-bar).
+//
+// q and k arrive normalised and rotated by qk_prep, which rotates every row
+// once by its grid coordinate (a tile's global row by the tile's start): a
+// score depends only on the two coordinates' difference, the same in every
+// tile, so rows are read in place and no per-tile copies are made.
+//
+// Three layouts of the query rows and outputs:
+//  - per tile: qkv rows and outputs t*(n+1)+i (tile t's window token i, its
+//    global token i = n);
+//  - shared, per-tile outputs: keys and queries read from the shared
+//    [n_union + n_tiles] rows through the tile map, outputs per tile (layer 0
+//    of a stack run once per token);
+//  - shared, blended (shared layers): the plan's query blocks group rows by
+//    the tiles that hold them; a block is attended in each of its windows in
+//    turn and the per-window outputs are added with their w-bar weights in
+//    ascending tile order, so the blended row a[p] = sum_t w_t o_t is written
+//    once (global rows: their tile's output, weight 1).
 //
 // bf16 kernel (gfx950 MFMA 32x32x16): a workgroup of eight wavefronts owns
-// 256 query rows of one (tile, head), 32 per wavefront, and stages each block
-// of 64 keys once for all of them.  Scores are formed transposed, S^T = K Q^T,
-// so each lane holds one query's scores and the softmax max/sum stay in-lane
-// (plus one exchange with the lane 32 apart); the output is accumulated
-// transposed, O^T = V^T P^T, so the per-query rescale is in-lane too.  K rows
-// are fed to the MFMA in an order that swaps bits 2 and 3 of the row index,
-// which makes the score accumulator layout equal the P^T operand layout of
-// the second MFMA (no shuffles).  K is staged as [key][hd] (rotated) and V
-// transposed as [hd][key], both with XOR-swizzled 16-byte chunks, double
-// buffered; row indices and positions of the keys are prefetched two blocks
-// ahead into an LDS ring, and the RoPE table sits in LDS.
+// 256 query rows of one head, 32 per wavefront, and streams every window it
+// attends in blocks of 64 keys, each block staged once for all of them.
+// Scores are formed transposed, S^T = K Q^T, so each lane holds one query's
+// scores and the softmax max/sum stay in-lane (plus one exchange with the
+// lane 32 apart); the output is accumulated transposed, O^T = V^T P^T, so the
+// per-query rescale is in-lane too.  K rows are fed to the MFMA in an order
+// that swaps bits 2 and 3 of the row index, which makes the score accumulator
+// layout equal the P^T operand layout of the second MFMA (no shuffles).  K
+// and V blocks go from the qkv rows straight into LDS ([key][hd], 16-byte
+// chunks XOR-swizzled by key) with global_load_lds, three blocks in flight;
+// V^T fragments are read with the transposing LDS load ds_read_b64_tr_b16,
+// so V is never copied transposed.  The key rows of a window come through a
+// four-slot LDS ring filled three blocks ahead.  The windows of a query block
+// form one stream of key blocks, so the staging runs on across windows.
 #include <algorithm>
 #include <cstdlib>
 
@@ -32,417 +46,379 @@ namespace {
 struct AttnP {
   const void* qkv;
   void* out;
+  float* part;
   const int* rows;
+  const int* blk_nt;
+  const int* blk_tiles;
+  const int* blk_rows;
+  const float* blk_w;
+  int nblk, maxc;
   int n_union, d, H, n_tiles, n;
-  const int* local_pos;
-  const float* rope;   // compact per-axis (cos, sin) table (see rope_cs)
-  int rope_floats;
-  int pairs[3];
-  int rope_off[3];
-  int rope_wbase[3];
-  int rope_wpairs[3];
   float scale_log2;  // log2(e) / sqrt(hd)
-  const bf16* vt;    // [n_tiles][H][HD][n_pad] transposed window values (unrotated path)
+  unsigned* amax;
 };
 
-__device__ __forceinline__ int window_row(const AttnP& p, int t, int i) {
-  if (p.rows) return i < p.n ? p.rows[int64_t(t) * p.n + i] : p.n_union + t;
-  return t * (p.n + 1) + i;
-}
+constexpr int QB = 256;  // query rows per workgroup (both kernels)
 
-// Axis of rotation pair k (pairs are split over t, h, w in contiguous chunks).
-__device__ __forceinline__ int pair_axis(const AttnP& p, int k) {
-  return k < p.pairs[0] ? 0 : (k < p.pairs[0] + p.pairs[1] ? 1 : 2);
+// qkv row of window token j < n of tile t, and of tile t's global token
+__device__ __forceinline__ int key_row(const AttnP& p, int t, int j) {
+  return p.rows ? p.rows[int64_t(t) * p.n + j] : t * (p.n + 1) + j;
 }
-__device__ __forceinline__ int pick3(const int (&v)[3], int a) { return a == 0 ? v[0] : (a == 1 ? v[1] : v[2]); }
+__device__ __forceinline__ int gkey_row(const AttnP& p, int t) { return p.rows ? p.n_union + t : t * (p.n + 1) + p.n; }
+// output row of tile t's global query
+__device__ __forceinline__ int gout_row(const AttnP& p, int t) { return p.blk_nt ? p.n_union + t : t * (p.n + 1) + p.n; }
 
-// (cos, sin) of rotation pair k of a head at the packed tile-local position
-// pos (tau | y<<10 | x<<20).  Axis a's block of the compact table spans the
-// pairs [rope_wbase[a], rope_wbase[a] + rope_wpairs[a]) per position.
-__device__ __forceinline__ float2 rope_cs(const AttnP& p, const float* tab, int k, int pos) {
-  const int ax = pair_axis(p, k);
-  const int ps = (pos >> (10 * ax)) & 1023;
-  return *reinterpret_cast<const float2*>(tab + pick3(p.rope_off, ax) +
-                                          2 * (ps * pick3(p.rope_wpairs, ax) + k - pick3(p.rope_wbase, ax)));
+// Wavefront max of m (all 64 lanes), then one atomic max in float bits
+// (values >= 0) into one of the tsk::AMAX_SLOTS slots.
+__device__ __forceinline__ void wave_amax(unsigned* amax, float m, int slot_seed) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0)
+    atomicMax(amax + (slot_seed & (tsk::AMAX_SLOTS - 1)) * tsk::AMAX_STRIDE, __float_as_uint(m));
 }
 
 // ------------------------------------------------------------- fp32 -----
-// One thread per query row, keys staged through LDS 64 at a time.
-template <int HD, bool ROPE>
-__global__ __launch_bounds__(64) void k_attn_f32(AttnP p) {
+// One thread per query row, 256 per workgroup, keys staged through LDS 64 at
+// a time.  Workgroups [0, njob) take query blocks, the next n_tiles the
+// global query rows (thread 0).  blockIdx.y is the head.
+template <int HD, bool BLEND>
+__global__ __launch_bounds__(QB) void k_attn_f32(AttnP p) {
   __shared__ float Ks[64][HD + 1];
   __shared__ float Vs[64][HD + 1];
-  const int t = blockIdx.z, h = blockIdx.y;
-  const int i = blockIdx.x * 64 + threadIdx.x;
-  const int n = p.n;
+  const int h = blockIdx.y, tid = threadIdx.x, n = p.n, b = blockIdx.x;
+  const int nqb = (n + QB - 1) / QB;
+  const int njob = BLEND ? p.nblk : p.n_tiles * nqb;
   const float* qkv = (const float*)p.qkv;
   const int64_t ld = 3 * int64_t(p.d);
-  const bool valid = i <= n;
-  const int qrow = window_row(p, t, valid ? i : n);
-  float q[HD];
-  const float* qp = qkv + qrow * ld + h * HD;
-  const int pos = (valid && i < n) ? p.local_pos[i] : -1;
+  const bool tok = b < njob;
+  int npass = 1, t0 = 0, qrow, orow;
+  bool valid;
+  if (!tok) {
+    t0 = b - njob;
+    valid = tid == 0;
+    qrow = gkey_row(p, t0);
+    orow = gout_row(p, t0);
+  } else if (BLEND) {
+    npass = p.blk_nt[b];
+    const int r = p.blk_rows[b * QB + tid];
+    valid = r >= 0;
+    qrow = valid ? r : p.blk_rows[b * QB];
+    orow = qrow;
+  } else {
+    t0 = b / nqb;
+    const int qi = (b % nqb) * QB + tid;
+    valid = qi < n;
+    qrow = key_row(p, t0, min(qi, n - 1));
+    orow = t0 * (n + 1) + qi;
+  }
+  float q[HD], o[HD], acc[HD];
 #pragma unroll
-  for (int k = 0; k < HD / 2; ++k) {
-    float c = 1.f, s = 0.f;
-    if (ROPE && pos >= 0) {
-      const float2 cs = rope_cs(p, p.rope, k, pos);
-      c = cs.x;
-      s = cs.y;
-    }
-    const float a = qp[2 * k], b = qp[2 * k + 1];
-    q[2 * k] = a * c - b * s;
-    q[2 * k + 1] = a * s + b * c;
+  for (int e = 0; e < HD; ++e) {
+    q[e] = qkv[qrow * ld + h * HD + e];
+    acc[e] = 0.f;
   }
   const float scale = 1.0f / sqrtf(float(HD));
-  // global key: initial state
-  const int grow = window_row(p, t, n);
-  const float* kg = qkv + grow * ld + p.d + h * HD;
-  const float* vg = qkv + grow * ld + 2 * p.d + h * HD;
-  float sg = 0.f;
+  for (int ps = 0; ps < npass; ++ps) {
+    const int t = (BLEND && tok) ? p.blk_tiles[b * p.maxc + ps] : t0;
+    // the global key is the initial state: score, weight 1, value
+    const int64_t gr = gkey_row(p, t);
+    float sg = 0.f;
 #pragma unroll
-  for (int e = 0; e < HD; ++e) sg += q[e] * kg[e];
-  float m = sg * scale, l = 1.f;
-  float o[HD];
+    for (int e = 0; e < HD; ++e) sg += q[e] * qkv[gr * ld + p.d + h * HD + e];
+    float m = sg * scale, l = 1.f;
 #pragma unroll
-  for (int e = 0; e < HD; ++e) o[e] = vg[e];
-  for (int j0 = 0; j0 < n; j0 += 64) {
-    __syncthreads();
-    {  // stage keys j0..j0+63 (this thread: key j0 + tid), RoPE applied
-      const int j = j0 + threadIdx.x;
-      if (j < n) {
-        const int r = window_row(p, t, j);
-        const float* kp = qkv + r * ld + p.d + h * HD;
-        const float* vp = qkv + r * ld + 2 * p.d + h * HD;
-        const int kpos = p.local_pos[j];
-        for (int k = 0; k < HD / 2; ++k) {
-          const float2 cs = ROPE ? rope_cs(p, p.rope, k, kpos) : make_float2(1.f, 0.f);
-          const float a = kp[2 * k], b = kp[2 * k + 1];
-          Ks[threadIdx.x][2 * k] = a * cs.x - b * cs.y;
-          Ks[threadIdx.x][2 * k + 1] = a * cs.y + b * cs.x;
+    for (int e = 0; e < HD; ++e) o[e] = qkv[gr * ld + 2 * p.d + h * HD + e];
+    for (int j0 = 0; j0 < n; j0 += 64) {
+      __syncthreads();
+      {  // stage keys j0 .. j0+63, four threads per key
+        const int kk = tid >> 2, part = tid & 3, j = j0 + kk;
+        if (j < n) {
+          const int64_t r = key_row(p, t, j);
+          for (int e = part; e < HD; e += 4) {
+            Ks[kk][e] = qkv[r * ld + p.d + h * HD + e];
+            Vs[kk][e] = qkv[r * ld + 2 * p.d + h * HD + e];
+          }
         }
-        for (int e = 0; e < HD; ++e) Vs[threadIdx.x][e] = vp[e];
+      }
+      __syncthreads();
+      const int jn = min(64, n - j0);
+      for (int jj = 0; jj < jn; ++jj) {
+        float sc = 0.f;
+#pragma unroll
+        for (int e = 0; e < HD; ++e) sc += q[e] * Ks[jj][e];
+        sc *= scale;
+        const float mn = fmaxf(m, sc);
+        const float al = expf(m - mn), pj = expf(sc - mn);
+        l = l * al + pj;
+#pragma unroll
+        for (int e = 0; e < HD; ++e) o[e] = o[e] * al + pj * Vs[jj][e];
+        m = mn;
       }
     }
-    __syncthreads();
-    const int jn = min(64, n - j0);
-    for (int jj = 0; jj < jn; ++jj) {
-      float sc = 0.f;
+    // blend: acc += w-bar(t) * o / l, tiles in ascending order
+    const float coef = ((BLEND && tok) ? p.blk_w[(b * p.maxc + ps) * QB + tid] : 1.0f) / l;
 #pragma unroll
-      for (int e = 0; e < HD; ++e) sc += q[e] * Ks[jj][e];
-      sc *= scale;
-      const float mn = fmaxf(m, sc);
-      const float al = expf(m - mn), pj = expf(sc - mn);
-      l = l * al + pj;
-#pragma unroll
-      for (int e = 0; e < HD; ++e) o[e] = o[e] * al + pj * Vs[jj][e];
-      m = mn;
-    }
+    for (int e = 0; e < HD; ++e) acc[e] = fmaf(coef, o[e], acc[e]);
   }
   if (!valid) return;
-  float* out = (float*)p.out + (int64_t(t) * (n + 1) + i) * p.d + h * HD;
-  const float inv = 1.0f / l;
+  float* out = (float*)p.out + int64_t(orow) * p.d + h * HD;
 #pragma unroll
-  for (int e = 0; e < HD; ++e) out[e] = o[e] * inv;
+  for (int e = 0; e < HD; ++e) out[e] = acc[e];
 }
 
 // ------------------------------------------------------------- bf16 -----
-constexpr int NW = 8;              // wavefronts per workgroup
-constexpr int QB = 32 * NW;        // query rows per workgroup
-constexpr int KB = 64;             // keys per staged block
-constexpr int ROPE_LDS_FLOATS = 4096;  // 16 KB
+constexpr int NW = 8;                  // wavefronts per workgroup
+constexpr int KB = 64;                 // keys per staged block
+constexpr int NST = 3;                 // LDS stages of K and V
+constexpr int AHEAD = 3;               // blocks ahead the key rows are fetched
+constexpr int NSL = 4;                 // slots of the key-row ring
 constexpr float RESCALE_LOG2 = 8.0f;   // keep a stale running max until a block exceeds it by 2^8
+static_assert(QB == 32 * NW, "32 query rows per wavefront");
+static_assert(QB == tsk::QBLOCK, "query blocks of the plan");
 
 // Swap bits 2 and 3 of a row index in 0..31.
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// LDS swizzles (16-byte chunk c of row r is stored at chunk c ^ key(r)).  The
-// LDS has 64 banks of 4 bytes; a 16-byte access is served 16 lanes at a time,
-// so the 16 lanes of one phase must hit 16 different 16-byte bank groups.
-// K rows (HD*2 bytes): the 16 rows one MFMA read phase touches (swap23(0..15)
-// = 0..15) get 16 different keys (head size 128: row & 15; head size 64,
-// 128-byte rows where row parity already selects the half: (row >> 1) & 7).
-// V^T rows (128 bytes): hd ^ (hd >> 3), distinct over the even and over the
-// odd rows of 16 consecutive hd rows (fragment reads) and over hd rows 8 apart
-// (transposing writes).
+// LDS swizzles: 16-byte chunk c of key row r is stored at chunk c ^ key(r).
+// The LDS has 64 banks of 4 bytes.  K fragment reads (16 bytes per lane,
+// served 16 lanes at a time) touch 16 rows at one chunk: head size 128 takes
+// row & 15; head size 64 (128-byte rows, row parity already picks the half of
+// the bank range) (row >> 1) & 7.  V^T fragment reads are transposing 8-byte
+// reads; a half wavefront touches 4 consecutive rows x 4 consecutive chunks:
+// 4 (row & 3) at head size 128, 4 ((row >> 1) & 1) at 64, so the 16 pieces
+// fall in 16 different 16-byte bank groups.
 template <int HD> __device__ __forceinline__ int kswz(int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); }
-__device__ __forceinline__ int vswz(int hd) { return (hd ^ (hd >> 3)) & 7; }
+template <int HD> __device__ __forceinline__ int vswz(int r) { return HD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-// Table lookup of one 8-dim group, rotation pairs 4c .. 4c+3.  Segment 0 is
-// the table block of the axis of pair 4c, segment 1 that of pair 4c+3; the
-// first `split` pairs take segment 0 (split = 4 when the group lies in one
-// axis).  In each block the group's four (cos, sin) pairs are 32 contiguous,
-// 32-byte aligned bytes, so a segment is two 16-byte reads.
-struct GroupRope {
-  int off0, step0, shift0;
-  int off1, step1, shift1;
-  int split;
-};
-__device__ __forceinline__ GroupRope group_rope(const AttnP& p, int c) {
-  const int k = 4 * c;
-  const int a0 = pair_axis(p, k), a1 = pair_axis(p, k + 3);
-  GroupRope g;
-  g.off0 = pick3(p.rope_off, a0) + 2 * (k - pick3(p.rope_wbase, a0));
-  g.step0 = 2 * pick3(p.rope_wpairs, a0);
-  g.shift0 = 10 * a0;
-  g.off1 = pick3(p.rope_off, a1) + 2 * (k - pick3(p.rope_wbase, a1));
-  g.step1 = 2 * pick3(p.rope_wpairs, a1);
-  g.shift1 = 10 * a1;
-  g.split = a0 == a1 ? 4 : (a0 == 0 ? p.pairs[0] : p.pairs[0] + p.pairs[1]) - k;
-  return g;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// One V^T operand fragment (32 hd rows x 16 keys) of the MFMA from two
+// transposing reads.  In each group of 16 lanes, ds_read_b64_tr_b16 gives lane
+// j element j % 4 of the 8-byte pieces addressed by lanes j/4, j/4 + 4,
+// j/4 + 8 and j/4 + 12.  Lane 16G + j addresses key row (4 keys apart per
+// j/4 step) and hd dims dbase + 4 (j % 4) .. +3, so it receives hd dim
+// dbase + j of four consecutive keys: the A-operand layout (row = lane % 32,
+// k = 8 (lane / 32) + 0..7) after the two reads, keys 0-3 then 4-7.
+__device__ __forceinline__ bf16x8 v_fragment(const char* lo, const char* hi) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TS_LDS s16x4*)lo);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TS_LDS s16x4*)hi);
+  const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
 }
 
-// Rotate one 8-dim group (4 pairs, bf16) by position `pos`; each rotated
-// value is rounded to bf16.
-__device__ __forceinline__ bf16x8 rope_group(const float* tab, const GroupRope& gr, int pos, bf16x8 v) {
-  const float* cs = tab + gr.off0 + ((pos >> gr.shift0) & 1023) * gr.step0;
-  f32x4 c01 = *reinterpret_cast<const f32x4*>(cs);      // (cos, sin) of pairs 0, 1
-  f32x4 c23 = *reinterpret_cast<const f32x4*>(cs + 4);  // pairs 2, 3
-  if (gr.split < 4) {  // pairs split .. 3 belong to the next axis
-    const float* cs1 = tab + gr.off1 + ((pos >> gr.shift1) & 1023) * gr.step1;
-    const f32x4 d01 = *reinterpret_cast<const f32x4*>(cs1);
-    const f32x4 d23 = *reinterpret_cast<const f32x4*>(cs1 + 4);
-    if (gr.split == 1) c01 = f32x4{c01[0], c01[1], d01[2], d01[3]};
-    if (gr.split <= 2) c23 = d23;
-    else c23 = f32x4{c23[0], c23[1], d23[2], d23[3]};
-  }
-  bf16x8 o;
-#pragma unroll
-  for (int q2 = 0; q2 < 4; ++q2) {
-    const float c = q2 < 2 ? c01[2 * q2] : c23[2 * q2 - 4];
-    const float s = q2 < 2 ? c01[2 * q2 + 1] : c23[2 * q2 - 3];
-    const float a = float(v[2 * q2]), b = float(v[2 * q2 + 1]);
-    o[2 * q2] = bf16(a * c - b * s);
-    o[2 * q2 + 1] = bf16(a * s + b * c);
-  }
-  return o;
-}
-
-template <int HD, bool ROPE>
+template <int HD, bool BLEND>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(AttnP p) {
-  constexpr int NT = NW * 64;         // threads
-  constexpr int HC = HD / 8;          // 16-byte chunks per head row
   constexpr int KROWB = HD * 2;       // bytes per staged key row
-  constexpr int KCPT = HC / 8;        // key chunks per thread (8 threads per key row)
-  constexpr int VSB = KB / 2 * HC;    // V transpose units (2 keys x 8 hd)
   constexpr int NHB = HD / 32;        // 32-row hd blocks of O^T
   constexpr int KSTEPS = HD / 16;     // MFMA k-steps of S^T
-  static_assert(VSB <= NT, "one V unit per thread");
-  // LDS stages of K and V^T: two with in-kernel RoPE (registers carry the
-  // next block), three when both are DMA-staged (block kb+2 is in flight
-  // while kb is computed, so a block's loads have two blocks of time to land)
-  constexpr int NST = ROPE ? 2 : 3;
-  constexpr int AHEAD = ROPE ? 2 : 3;   // blocks ahead the key rows are fetched
-  constexpr int NSL = ROPE ? 2 : 4;     // slots of the key-row ring
+  // global_load_lds: lane l of a wavefront instruction writes 16 bytes at LDS
+  // base + 16*l; instruction i of wavefront w fills bytes [(w*KDI + i) KB,
+  // +1 KB) of a stage, i.e. key row b / KROWB, slot (b % KROWB) / 16 for lane
+  // byte b, and the lane loads the logical chunk the swizzle puts in that slot
+  constexpr int KDI = KB * KROWB / 1024 / NW;  // DMA instructions per wavefront, each of K and V
+  static_assert(KDI >= 1, "whole 1 KB DMA rows per wavefront");
   __shared__ __attribute__((aligned(16))) char Ks[NST][KB * KROWB];
-  __shared__ __attribute__((aligned(16))) char Vt[NST][HD * KB * 2];
-  __shared__ __attribute__((aligned(16))) float rope_s[ROPE ? ROPE_LDS_FLOATS : 4];
-  __shared__ int idx_s[NSL][2][KB];   // [slot][row | pos][key]
+  __shared__ __attribute__((aligned(16))) char Vs[NST][KB * KROWB];
+  __shared__ int idx_s[NSL][KB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int n = p.n;
-  // XCD-aware order: the hardware deals workgroup b to XCD b % 8; give each
-  // XCD a contiguous run of (tile, head, query-block) jobs so the query blocks
-  // that stream the same keys and values share one L2.
+  const int nkb = (n + KB - 1) / KB;
   const int nqb = (n + QB - 1) / QB;
-  int qblk, h, t;
+  // XCD-aware order: the hardware deals workgroup b to XCD b % 8; give each
+  // XCD a contiguous run of jobs so the query blocks that stream the same keys
+  // and values share one L2 (blended: blocks of one head in plan order;
+  // otherwise the query blocks of one (tile, head)).
+  int h, t0 = 0, qblk = 0, blk = 0, npass = 1;
   {
-    const int total = nqb * p.H * p.n_tiles;
+    const int total = (BLEND ? p.nblk : nqb * p.n_tiles) * p.H;
     const int b = blockIdx.x, xcd = b & 7, loc = b >> 3;
     const int q8 = total >> 3, r8 = total & 7;
     const int id = xcd < r8 ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
-    qblk = id % nqb;
-    h = (id / nqb) % p.H;
-    t = id / (nqb * p.H);
+    if constexpr (BLEND) {
+      blk = id % p.nblk;
+      h = id / p.nblk;
+      npass = p.blk_nt[blk];
+    } else {
+      qblk = id % nqb;
+      h = (id / nqb) % p.H;
+      t0 = id / (nqb * p.H);
+    }
   }
   const bf16* qkv = (const bf16*)p.qkv;
   const int64_t ld = 3 * int64_t(p.d);
   const bf16* kbase = qkv + p.d + h * HD;
   const bf16* vbase = qkv + 2 * p.d + h * HD;
-  const int nkb = (n + KB - 1) / KB;
-
-  if (ROPE)
-    for (int e = tid; e < p.rope_floats; e += NT) rope_s[e] = p.rope[e];
-  // row index and position of key j (clamped into the window)
-  auto key_meta = [&](int j, int& row, int& pos) {
-    j = min(j, n - 1);
-    row = window_row(p, t, j);
-    pos = ROPE ? p.local_pos[j] : 0;
+  const int nblocks = npass * nkb;  // key blocks streamed over all windows
+  auto tile_of = [&](int ps) -> int {
+    if constexpr (BLEND) return p.blk_tiles[blk * p.maxc + ps];
+    else return t0;
   };
-  if (tid < KB) {
-#pragma unroll
-    for (int b = 0; b < AHEAD; ++b) {
-      int r0, p0;
-      key_meta(b * KB + tid, r0, p0);
-      idx_s[b][0][tid] = r0;
-      idx_s[b][1][tid] = p0;
-    }
-  }
 
-  // staging roles.  K: row kr_row, chunks kpart + 8*i, 8 threads per row; a
-  // 16-lane write phase covers two rows, chosen 8 apart at head size 128 (so
-  // their keys differ in bit 3) and adjacent at 64 (so their parity differs).
-  // V: keys 2*v_k2, 2*v_k2+1 of hd chunk v_hc (one 4-byte write phase hits
-  // 32 banks twice: a 2-way conflict on 8 small writes per block, cheaper than
-  // the per-lane row reordering that would avoid it).
-  const int lg = lane >> 3;
-  const int kr_row = HD == 128 ? (wave >> 1) * 16 + (wave & 1) * 4 + (lg >> 1) + (lg & 1) * 8 : tid >> 3;
-  const int kpart = tid & 7;
-  GroupRope kgr[KCPT];
+  // key rows of the first AHEAD blocks (row-map layouts)
+  if (p.rows && tid < KB) {
 #pragma unroll
-  for (int i = 0; i < KCPT; ++i) kgr[i] = group_rope(p, kpart + 8 * i);
-  const bool v_on = tid < VSB;
-  const int v_hc = (tid & 7) + 8 * (tid / 256), v_k2 = (tid >> 3) & 31;
-  i32x4 kreg[KCPT], vreg[2];
-  // without RoPE, K goes straight from global memory to LDS (global_load_lds:
-  // lane l of a wavefront instruction writes 16 bytes at LDS base + 16*l):
-  // instruction i of wavefront w fills bytes [(w*KDI + i) KB, +1 KB) of the
-  // stage, i.e. row b / KROWB, slot (b % KROWB) / 16 for lane byte b, and the
-  // lane loads the logical chunk the swizzle puts in that slot
-  constexpr int KDI = KB * KROWB / 1024 / NW;  // K DMA instructions per wavefront
-  constexpr int VDI = HD * KB * 2 / 1024 / NW;  // V^T DMA instructions per wavefront
-  static_assert(KDI >= 1 && VDI >= 1, "whole 1 KB DMA rows per wavefront");
+    for (int b = 0; b < AHEAD; ++b)
+      if (b < nblocks) {
+        const int ps = b / nkb, kb = b - ps * nkb;
+        idx_s[b][tid] = p.rows[int64_t(tile_of(ps)) * n + min(kb * KB + tid, n - 1)];
+      }
+  }
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int64_t n_pad = int64_t(nkb) * KB;
-  const bf16* vtbase = ROPE ? nullptr : p.vt + (int64_t(t) * p.H + h) * HD * n_pad;
-  // DMA staging in two steps: the key rows this lane's K loads need (from
-  // the ring), then the loads, so that the ring can be refilled in between
-  auto dma_rows = [&](int blk, int (&rr)[KDI]) {
+  // DMA staging in two steps: the key rows this lane's loads need (from the
+  // ring), then the loads, so that the ring can be refilled in between
+  auto dma_rows = [&](int gb, int (&rr)[KDI]) {
 #pragma unroll
     for (int i = 0; i < KDI; ++i) {
       const int row = ((wv * KDI + i) * 1024 + 16 * lane) / KROWB;
-      rr[i] = p.rows ? idx_s[blk % NSL][0][row] : t * (n + 1) + min(blk * KB + row, n - 1);
+      rr[i] = p.rows ? idx_s[gb % NSL][row] : t0 * (n + 1) + min(gb * KB + row, n - 1);
     }
   };
-  auto dma = [&](int blk, const int (&rr)[KDI]) {
-    const int st = blk % NST;
+  auto dma = [&](int gb, const int (&rr)[KDI]) {
+    const int st = gb % NST;
 #pragma unroll
     for (int i = 0; i < KDI; ++i) {
       const int b = (wv * KDI + i) * 1024 + 16 * lane;
-      const int row = b / KROWB, c = ((b % KROWB) / 16) ^ kswz<HD>(row);
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + rr[i] * ld + c * 8),
+      const int row = b / KROWB, slot = (b % KROWB) / 16;
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + int64_t(rr[i]) * ld + (slot ^ kswz<HD>(row)) * 8),
                                        (TS_LDS void*)(&Ks[st][(wv * KDI + i) * 1024]), 16, 0, 0);
-    }
-    // V^T rows hd = 8*(wv*VDI + i) + lane/8, LDS slot lane%8 of the 128-byte
-    // row holds logical key chunk slot ^ vswz(hd) of block blk
-#pragma unroll
-    for (int i = 0; i < VDI; ++i) {
-      const int hdr = 8 * (wv * VDI + i) + (lane >> 3), c = (lane & 7) ^ vswz(hdr);
-      __builtin_amdgcn_global_load_lds((const void*)(vtbase + int64_t(hdr) * n_pad + blk * KB + c * 8),
-                                       (TS_LDS void*)(&Vt[st][(wv * VDI + i) * 1024]), 16, 0, 0);
-    }
-  };
-  auto gload = [&](int blk) {
-    const int slot = blk % NSL;
-    if constexpr (!ROPE) {
-      int rr[KDI];
-      dma_rows(blk, rr);
-      dma(blk, rr);
-    } else {
-      const int r = idx_s[slot][0][kr_row];
-#pragma unroll
-      for (int i = 0; i < KCPT; ++i)
-        kreg[i] = *reinterpret_cast<const i32x4*>(kbase + r * ld + (kpart + 8 * i) * 8);
-    }
-    if (ROPE && v_on) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int rv = idx_s[slot][0][2 * v_k2 + e];
-        vreg[e] = *reinterpret_cast<const i32x4*>(vbase + rv * ld + v_hc * 8);
-      }
-    }
-  };
-  auto lstore = [&](int blk, int st) {
-    const int slot = blk % NSL;
-    if constexpr (ROPE) {
-      const int pos = idx_s[slot][1][kr_row];
-#pragma unroll
-      for (int i = 0; i < KCPT; ++i) {
-        const int c = kpart + 8 * i;
-        const bf16x8 o = rope_group(rope_s, kgr[i], pos, __builtin_bit_cast(bf16x8, kreg[i]));
-        *reinterpret_cast<bf16x8*>(&Ks[st][kr_row * KROWB + ((c ^ kswz<HD>(kr_row)) * 16)]) = o;
-      }
-    }
-    if (ROPE && v_on) {
-      const bf16x8 v0 = __builtin_bit_cast(bf16x8, vreg[0]), v1 = __builtin_bit_cast(bf16x8, vreg[1]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int hdr = v_hc * 8 + e;
-        const bf16 w2[2] = {v0[e], v1[e]};
-        const int chunk = (v_k2 >> 2) ^ vswz(hdr);
-        *reinterpret_cast<uint32_t*>(&Vt[st][hdr * (KB * 2) + chunk * 16 + (v_k2 & 3) * 4]) =
-            __builtin_bit_cast(uint32_t, w2);
-      }
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + int64_t(rr[i]) * ld + (slot ^ vswz<HD>(row)) * 8),
+                                       (TS_LDS void*)(&Vs[st][(wv * KDI + i) * 1024]), 16, 0, 0);
     }
   };
 
-  __syncthreads();  // rope_s, idx_s ready
-  gload(0);
-  if (!ROPE && nkb > 1) gload(1);
+  __syncthreads();  // ring slots ready
+  {
+    int rr[KDI];
+    dma_rows(0, rr);
+    dma(0, rr);
+    if (nblocks > 1) {
+      dma_rows(1, rr);
+      dma(1, rr);
+    }
+  }
 
   // ---- this wavefront's 32 queries: B operand of S^T = K Q^T (hd 16s + 8g + e)
-  const int qi = qblk * QB + wave * 32 + l32;
-  const int grow = window_row(p, t, n);
-  const bf16* kgp = kbase + grow * ld;
-  const bf16* vgp = vbase + grow * ld;
-  const float C = p.scale_log2;
+  const int slot = wave * 32 + l32;
+  int qrow, orow;
+  bool qvalid;
+  if constexpr (BLEND) {
+    const int r = p.blk_rows[blk * QB + slot];
+    qvalid = r >= 0;
+    qrow = qvalid ? r : p.blk_rows[blk * QB];
+    orow = qrow;
+  } else {
+    const int qi = qblk * QB + slot;
+    qvalid = qi < n;
+    qrow = key_row(p, t0, min(qi, n - 1));
+    orow = t0 * (n + 1) + qi;
+  }
   bf16x8 qf[KSTEPS];
-  float m_run, l_run;
-  f32x16 oacc[NHB];
   {
-    const int qc = min(qi, n - 1);
-    const bf16* qp = qkv + window_row(p, t, qc) * ld + h * HD;
-    const int qpos = p.local_pos[qc];
+    const bf16* qp = qkv + int64_t(qrow) * ld + h * HD;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * g);
+  }
+  const float C = p.scale_log2;
+  float m_run = 0.f, l_run = 0.f;
+  f32x16 oacc[NHB];
+  // the window's global key is the softmax's initial state: score, weight 1, value
+  auto window_init = [&](int t) {
+    const int64_t gr = gkey_row(p, t);
+    const bf16* kgp = kbase + gr * ld;
+    const bf16* vgp = vbase + gr * ld;
     float sg = 0.f;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      const int hd0 = 16 * s + 8 * g;
-      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qp + hd0);
-      const bf16x8 r = ROPE ? rope_group(rope_s, group_rope(p, hd0 / 8), qpos, qv) : qv;
-      const bf16x8 kg = *reinterpret_cast<const bf16x8*>(kgp + hd0);
-      qf[s] = r;
+      const bf16x8 kg = *reinterpret_cast<const bf16x8*>(kgp + 16 * s + 8 * g);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sg += float(r[e]) * float(kg[e]);
+      for (int e = 0; e < 8; ++e) sg += float(qf[s][e]) * float(kg[e]);
     }
     sg += __shfl_xor(sg, 32, 64);
-    // online softmax state starts from the global key: score sg, weight 1, value v_g
     m_run = sg * C;
     l_run = g == 0 ? 1.f : 0.f;
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[hb][r] = float(vgp[hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)]);
-  }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const bf16x4 v = *reinterpret_cast<const bf16x4*>(vgp + hb * 32 + 8 * r4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[hb][4 * r4 + e] = float(v[e]);
+      }
+  };
+  // the window's output o = O / l: written (per-tile layouts), or weighted by
+  // w-bar and added to the row's blend, the partial sum kept in fp32 between
+  // windows and the blend written after the last one
+  auto window_finish = [&](int ps) {
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    float coef;
+    if constexpr (BLEND) coef = p.blk_w[(int64_t(blk) * p.maxc + ps) * QB + slot] / l_tot;
+    else coef = 1.0f / l_tot;
+    const bool last = !BLEND || ps + 1 == npass;
+    float* prow = p.part + int64_t(orow) * p.d + h * HD;
+    bf16* op = (bf16*)p.out + int64_t(orow) * p.d + h * HD;
+    float am = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int col = hb * 32 + 8 * r4 + 4 * g;
+        f32x4 v = {oacc[hb][4 * r4] * coef, oacc[hb][4 * r4 + 1] * coef, oacc[hb][4 * r4 + 2] * coef,
+                   oacc[hb][4 * r4 + 3] * coef};
+        if (!qvalid) continue;
+        if (BLEND && ps > 0) v += load4(prow + col);
+        if (!last) {
+          store4(prow + col, v);
+        } else {
+          const bf16x4 w = {bf16(v[0]), bf16(v[1]), bf16(v[2]), bf16(v[3])};
+          *reinterpret_cast<bf16x4*>(op + col) = w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(float(w[e])));
+        }
+      }
+    if (last && p.amax) wave_amax(p.amax, am, int(blockIdx.x) * NW + wave);
+  };
 
-  lstore(0, 0);
-  if (!ROPE) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's K DMA landed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's DMA of the first blocks landed
   __syncthreads();
   const int krow_a = swap23(l32);  // key row this lane feeds as MFMA A row
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb % NST;
-    // key rows of block kb+AHEAD.  DMA-staged: wavefront 0 copies them from
-    // the row map straight into the ring (no registers, so nothing waits on
-    // them before the block-end wait), ahead of this block's K / V^T loads so
-    // that wait covers them; per-tile rows need no map.  In-kernel RoPE: row
-    // and position through registers, stored at the block end.
-    int pre_r = 0, pre_p = 0;
-    const bool pre = ROPE && tid < KB && kb + AHEAD < nkb;
-    if (pre) key_meta((kb + AHEAD) * KB + tid, pre_r, pre_p);
-    if constexpr (ROPE) {
-      if (kb + 1 < nkb) gload(kb + 1);
-    } else {
+  // V^T fragment addresses: lane 16G + j reads key row 8 (G / 2) + j / 4 (+16
+  // per 16-key chunk, +4 for the second read) at hd dims hb*32 + 16 (G % 2) +
+  // 4 (j % 4) .. +3; the swizzle depends only on the row's low bits, which
+  // the chunk and read offsets keep
+  int vaddr[NHB];
+  {
+    const int G = lane >> 4, j = lane & 15;
+    const int row0 = 8 * (G >> 1) + (j >> 2);
+    const int clow = 2 * (G & 1) + ((j & 3) >> 1);
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) vaddr[hb] = row0 * KROWB + (((hb * 4 + clow) ^ vswz<HD>(row0)) * 16) + 8 * (j & 1);
+  }
+
+  for (int ps = 0; ps < npass; ++ps) {
+   window_init(tile_of(ps));
+   for (int kb = 0; kb < nkb; ++kb) {
+    const int gb = ps * nkb + kb;  // position in the stream of key blocks
+    const int cur = gb % NST;
+    {
+      // key rows of block gb+AHEAD: wavefront 0 copies them from the row map
+      // straight into the ring (no registers, so nothing waits on them before
+      // the block-end wait), ahead of this block's K / V loads so that wait
+      // covers them; per-tile rows need no map
       int rr[KDI];
-      if (kb + 2 < nkb) dma_rows(kb + 2, rr);
-      if (p.rows && wave == 0 && kb + AHEAD < nkb) {
-        const int j = min((kb + AHEAD) * KB + lane, n - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(p.rows + int64_t(t) * n + j),
-                                         (TS_LDS void*)(&idx_s[(kb + AHEAD) % NSL][0][0]), 4, 0, 0);
+      if (gb + 2 < nblocks) dma_rows(gb + 2, rr);
+      if (p.rows && wave == 0 && gb + AHEAD < nblocks) {
+        const int b3 = gb + AHEAD, ps3 = b3 / nkb, kb3 = b3 - ps3 * nkb;
+        const int j = min(kb3 * KB + lane, n - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(p.rows + int64_t(tile_of(ps3)) * n + j),
+                                         (TS_LDS void*)(&idx_s[b3 % NSL][0]), 4, 0, 0);
       }
-      if (kb + 2 < nkb) dma(kb + 2, rr);
+      if (gb + 2 < nblocks) dma(gb + 2, rr);
     }
     const char* ks = Ks[cur];
-    const char* vt = Vt[cur];
+    const char* vs = Vs[cur];
     const int j0 = kb * KB;
 
     // ---- S^T = K Q^T for the 64 keys: two 32-key chains, K fragments read
@@ -469,7 +445,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next LDS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    if (j0 + KB > n) {  // keys past the window end (last block only)
+    if (j0 + KB > n) {  // keys past the window end (last block of a window only)
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -514,66 +490,46 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) {
-        const int hdr = hb * 32 + l32;
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-            vt + hdr * (KB * 2) + (((2 * cc + g) ^ vswz(hdr)) * 16));
+        const char* a = vs + vaddr[hb] + 16 * cc * KROWB;
+        const bf16x8 vf = v_fragment(a, a + 4 * KROWB);
         oacc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], oacc[hb], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 4 fragments (8 reads) ahead
 #pragma unroll
     for (int i = 0; i < 4 * NHB - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
-    if (ROPE && kb + 1 < nkb) lstore(kb + 1, cur ^ 1);
-    if (pre) {
-      idx_s[(kb + AHEAD) % NSL][0][tid] = pre_r;
-      idx_s[(kb + AHEAD) % NSL][1][tid] = pre_p;
-    }
-    if constexpr (ROPE) {
-      __syncthreads();
-    } else {
-      // this wavefront's loads of block kb+1 have landed (kb+2's may still be
-      // in flight) and its LDS traffic is done; then a barrier without the
-      // fence of __syncthreads, which would also wait for block kb+2
-      if (kb + 2 < nkb) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(KDI + VDI) : "memory");
-      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    }
+    // this wavefront's loads of block gb+1 have landed (gb+2's may still be
+    // in flight) and its LDS traffic is done; then a barrier without the
+    // fence of __syncthreads, which would also wait for block gb+2.  Vector
+    // memory operations complete in issue order, so the count also covers
+    // the previous window's output loads and stores, issued before gb+2's.
+    if (gb + 2 < nblocks) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * KDI) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+   }
+   window_finish(ps);
   }
-
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (qi >= n) return;
-  const float inv = 1.0f / l_tot;
-  bf16* out = (bf16*)p.out + (int64_t(t) * (n + 1) + qi) * p.d + h * HD;
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const bf16x4 w = {bf16(oacc[hb][4 * r4] * inv), bf16(oacc[hb][4 * r4 + 1] * inv),
-                        bf16(oacc[hb][4 * r4 + 2] * inv), bf16(oacc[hb][4 * r4 + 3] * inv)};
-      *reinterpret_cast<bf16x4*>(out + hb * 32 + 8 * r4 + 4 * g) = w;
-    }
 }
 
 // Global-token query row of one (head, tile), over the window keys
-// [j_begin, j_end) of split blockIdx.z (key n is the global key itself, not
-// rotated).  Keys are taken in chunks of GCH.  Score pass: HD/16 threads per
-// key, 16 dims each (two 8-dim RoPE groups, the rotated key rounded to bf16 as
-// the MFMA kernel stages it), summed across those lanes; scores and row
-// indices go to LDS.  Value pass: each thread owns one 8-dim group of the
-// output and a strided subset of the chunk's keys and keeps a running
-// (max-shifted) weighted sum; the chunk max is shared by the workgroup, so
-// every thread rescales by the same factor.  The partial sums are added in
-// LDS at the end.  With one split the row is written; with several, each
-// split leaves its state (max m, weight sum l, unnormalised output o[HD], in
-// the exp2 domain) in `part` for k_attn_global_merge.
+// [j_begin, j_end) of split blockIdx.z (key n is the global key itself).
+// Keys are taken in chunks of GCH.  Score pass: HD/16 threads per key, 16
+// dims each, summed across those lanes; scores and row indices go to LDS.
+// Value pass: each thread owns one 8-dim group of the output and a strided
+// subset of the chunk's keys and keeps a running (max-shifted) weighted sum;
+// the chunk max is shared by the workgroup, so every thread rescales by the
+// same factor.  The partial sums are added in LDS at the end.  With one split
+// the row is written; with several, each split leaves its state (max m,
+// weight sum l, unnormalised output o[HD], in the exp2 domain) in `part` for
+// k_attn_global_merge.
 constexpr int GCH = 1024;
-template <int HD, int NT, bool ROPE>
+template <int HD, int NT>
 __global__ __launch_bounds__(NT) void k_attn_global_bf16(AttnP p, int split_keys, float* part) {
   constexpr int TPK = HD / 16;    // threads per key, score pass
   constexpr int KPP = NT / TPK;   // keys per score pass
@@ -589,13 +545,12 @@ __global__ __launch_bounds__(NT) void k_attn_global_bf16(AttnP p, int split_keys
   const int j_begin = blockIdx.z * split_keys, j_end = min(j_begin + split_keys, n + 1);
   const bf16* qkv = (const bf16*)p.qkv;
   const int64_t ld = 3 * int64_t(p.d);
-  const int64_t grow = window_row(p, t, n);
+  const int64_t grow = gkey_row(p, t);
 
   // score-pass role: dims [16*sub, 16*sub + 16) of key slot kk
   const int sub = tid % TPK, kk = tid / TPK;
   const bf16* qp = qkv + grow * ld + h * HD + 16 * sub;
   const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(qp), q1 = *reinterpret_cast<const bf16x8*>(qp + 8);
-  const GroupRope gr0 = group_rope(p, 2 * sub), gr1 = group_rope(p, 2 * sub + 1);
   // value-pass role: dims [8*dg, 8*dg + 8), keys kg, kg + KG, ...
   const int dg = tid % DG, kg = tid / DG;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -606,14 +561,9 @@ __global__ __launch_bounds__(NT) void k_attn_global_bf16(AttnP p, int split_keys
 #pragma unroll 4
     for (int jj = kk; jj < cnt; jj += KPP) {
       const int j = c0 + jj;
-      const int64_t r = window_row(p, t, j);
+      const int64_t r = j < n ? key_row(p, t, j) : grow;
       const bf16* kp = qkv + r * ld + p.d + h * HD + 16 * sub;
-      bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kp), k1 = *reinterpret_cast<const bf16x8*>(kp + 8);
-      if (ROPE && j < n) {
-        const int pos = p.local_pos[j];
-        k0 = rope_group(p.rope, gr0, pos, k0);
-        k1 = rope_group(p.rope, gr1, pos, k1);
-      }
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kp), k1 = *reinterpret_cast<const bf16x8*>(kp + 8);
       float sc = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) sc += float(q0[e]) * float(k0[e]);
@@ -670,8 +620,10 @@ __global__ __launch_bounds__(NT) void k_attn_global_bf16(AttnP p, int split_keys
       }
       st[2 + tid] = o;
     } else {
-      bf16* out = (bf16*)p.out + (int64_t(t) * (n + 1) + n) * p.d + h * HD;
-      out[tid] = bf16(o / lt);
+      bf16* out = (bf16*)p.out + int64_t(gout_row(p, t)) * p.d + h * HD;
+      const bf16 w = bf16(o / lt);
+      out[tid] = w;
+      if (p.amax) wave_amax(p.amax, fabsf(float(w)), t * p.H + h + wave);  // tid < HD: whole wavefronts
     }
   }
 }
@@ -690,44 +642,10 @@ __global__ __launch_bounds__(HD) void k_attn_global_merge(AttnP p, int splits, c
     lt += st[s * (HD + 2) + 1] * w;
     o += st[s * (HD + 2) + 2 + tid] * w;
   }
-  bf16* out = (bf16*)p.out + (int64_t(t) * (p.n + 1) + p.n) * p.d + h * HD;
-  out[tid] = bf16(o / lt);
-}
-
-// Window values of one (64-key block, head, tile) transposed into vt: the
-// block's 64 V rows (gathered through the tile's row map, 16-byte loads) go
-// into an LDS tile [key][hd] whose row stride is an odd number of 4-byte
-// words, written as 4-byte words; then 8 consecutive lanes assemble one hd
-// row's 64 keys (8 keys each, 2-byte LDS reads that are free of bank
-// conflicts with that stride) and store its 128 contiguous bytes.  Keys past
-// the window end are zero.
-template <int HD>
-__global__ __launch_bounds__(256) void k_vtrans(AttnP p) {
-  constexpr int CPR = HD / 8;   // 16-byte chunks per key row
-  constexpr int LD = HD + 2;    // LDS row stride (elements): HD/2 + 1 words, odd
-  __shared__ __attribute__((aligned(16))) bf16 tile[64 * LD];
-  const int jb = blockIdx.x, h = blockIdx.y, t = blockIdx.z, tid = threadIdx.x;
-  const int n = p.n;
-  const int64_t ld = 3 * int64_t(p.d);
-  const bf16* qkv = (const bf16*)p.qkv;
-  for (int c = tid; c < 64 * CPR; c += 256) {
-    const int key = c / CPR, part = c % CPR, j = jb * 64 + key;
-    i32x4 v = {0, 0, 0, 0};
-    if (j < n) v = *reinterpret_cast<const i32x4*>(qkv + int64_t(window_row(p, t, j)) * ld + 2 * p.d + h * HD + part * 8);
-    uint32_t* w = reinterpret_cast<uint32_t*>(&tile[key * LD + part * 8]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = uint32_t(v[e]);
-  }
-  __syncthreads();
-  const int64_t n_pad = int64_t((n + 63) / 64) * 64;
-  bf16* dst = const_cast<bf16*>(p.vt) + (int64_t(t) * p.H + h) * HD * n_pad + jb * 64;
-  for (int c = tid; c < HD * 8; c += 256) {
-    const int row = c >> 3, kc = c & 7;
-    bf16x8 w;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = tile[(kc * 8 + e) * LD + row];
-    *reinterpret_cast<bf16x8*>(dst + int64_t(row) * n_pad + kc * 8) = w;
-  }
+  bf16* out = (bf16*)p.out + int64_t(gout_row(p, t)) * p.d + h * HD;
+  const bf16 w = bf16(o / lt);
+  out[tid] = w;
+  if (p.amax) wave_amax(p.amax, fabsf(float(w)), t * p.H + h + (tid >> 6));
 }
 
 }  // namespace
@@ -735,51 +653,40 @@ __global__ __launch_bounds__(256) void k_vtrans(AttnP p) {
 namespace tsk {
 
 static AttnP make_params(const AttnArgs& a) {
-  return AttnP{a.qkv, a.out, a.rows, a.n_union, a.d, a.H, a.n_tiles, a.n, a.local_pos, a.rope, a.rope_floats,
-               {a.pairs[0], a.pairs[1], a.pairs[2]}, {a.rope_off[0], a.rope_off[1], a.rope_off[2]},
-               {a.rope_wbase[0], a.rope_wbase[1], a.rope_wbase[2]},
-               {a.rope_wpairs[0], a.rope_wpairs[1], a.rope_wpairs[2]},
-               1.4426950408889634f / sqrtf(float(a.hd)), (const bf16*)a.vt};
+  return AttnP{a.qkv,       a.out,       a.part, a.rows, a.blk_nt, a.blk_tiles, a.blk_rows, a.blk_w, a.nblk, a.maxc,
+               a.n_union,   a.d,         a.H,    a.n_tiles,        a.n,
+               1.4426950408889634f / sqrtf(float(a.hd)),           a.amax};
 }
 
-hipError_t attention(hipStream_t s, int act, const AttnArgs& a, bool rope) {
+hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
   const AttnP p = make_params(a);
+  const bool blend = a.blk_nt != nullptr;
+  if (a.n < 1 || (blend && (!a.rows || a.nblk < 1))) return hipErrorInvalidValue;
+  const int nqb = (a.n + QB - 1) / QB;
+  const int njob = blend ? a.nblk : nqb * a.n_tiles;
   if (act == ACT_F32) {
-    const dim3 grid((a.n + 1 + 63) / 64, a.H, a.n_tiles), block(64);
-    if (a.hd == 32) {
-      if (rope) hipLaunchKernelGGL((k_attn_f32<32, true>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((k_attn_f32<32, false>), grid, block, 0, s, p);
-    } else if (a.hd == 64) {
-      if (rope) hipLaunchKernelGGL((k_attn_f32<64, true>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((k_attn_f32<64, false>), grid, block, 0, s, p);
-    } else {
-      return hipErrorInvalidValue;
-    }
+    const dim3 grid(njob + a.n_tiles, a.H), block(QB);
+#define TS_F32A(HD)                                                                  \
+  do {                                                                               \
+    if (blend) hipLaunchKernelGGL((k_attn_f32<HD, true>), grid, block, 0, s, p);   \
+    else hipLaunchKernelGGL((k_attn_f32<HD, false>), grid, block, 0, s, p);        \
+  } while (0)
+    if (a.hd == 32) TS_F32A(32);
+    else if (a.hd == 64) TS_F32A(64);
+    else return hipErrorInvalidValue;
+#undef TS_F32A
     return hipGetLastError();
   }
-  if (a.n < 1) return hipErrorInvalidValue;
-  const dim3 grid(((a.n + QB - 1) / QB) * a.H * a.n_tiles), block(NW * 64);
-  if (a.hd == 64) {
-    if (rope) hipLaunchKernelGGL((k_attn_bf16<64, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_attn_bf16<64, false>), grid, block, 0, s, p);
-  } else if (a.hd == 128) {
-    if (rope) hipLaunchKernelGGL((k_attn_bf16<128, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_attn_bf16<128, false>), grid, block, 0, s, p);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t v_transpose(hipStream_t s, const AttnArgs& a, void* vt) {
-  AttnArgs b = a;
-  b.vt = vt;
-  const AttnP p = make_params(b);
-  if (a.n < 1) return hipErrorInvalidValue;
-  const dim3 grid((a.n + 63) / 64, a.H, a.n_tiles), block(256);
-  if (a.hd == 64) hipLaunchKernelGGL(k_vtrans<64>, grid, block, 0, s, p);
-  else if (a.hd == 128) hipLaunchKernelGGL(k_vtrans<128>, grid, block, 0, s, p);
+  const dim3 grid(njob * a.H), block(NW * 64);
+#define TS_BFA(HD)                                                                 \
+  do {                                                                             \
+    if (blend) hipLaunchKernelGGL((k_attn_bf16<HD, true>), grid, block, 0, s, p); \
+    else hipLaunchKernelGGL((k_attn_bf16<HD, false>), grid, block, 0, s, p);      \
+  } while (0)
+  if (a.hd == 64) TS_BFA(64);
+  else if (a.hd == 128) TS_BFA(128);
   else return hipErrorInvalidValue;
+#undef TS_BFA
   return hipGetLastError();
 }
 
@@ -795,19 +702,14 @@ int attention_global_splits(const AttnArgs& a, int64_t scratch_floats) {
   return std::max(1, std::min(splits, 64));
 }
 
-hipError_t attention_global(hipStream_t s, const AttnArgs& a, bool rope, float* scratch, int64_t scratch_floats) {
+hipError_t attention_global(hipStream_t s, const AttnArgs& a, float* scratch, int64_t scratch_floats) {
   const AttnP p = make_params(a);
   if (a.n < 1 || (a.hd != 64 && a.hd != 128)) return hipErrorInvalidValue;
   const int splits = scratch ? attention_global_splits(a, scratch_floats) : 1;
-#define TS_GL(HD, NT, SK, PART)                                                                           \
-  do {                                                                                                    \
-    if (rope) hipLaunchKernelGGL((k_attn_global_bf16<HD, NT, true>), grid, dim3(NT), 0, s, p, SK, PART);  \
-    else hipLaunchKernelGGL((k_attn_global_bf16<HD, NT, false>), grid, dim3(NT), 0, s, p, SK, PART);      \
-  } while (0)
   if (splits == 1) {
     const dim3 grid(a.H, a.n_tiles, 1);
-    if (a.hd == 64) TS_GL(64, 1024, a.n + 1, nullptr);
-    else TS_GL(128, 1024, a.n + 1, nullptr);
+    if (a.hd == 64) hipLaunchKernelGGL((k_attn_global_bf16<64, 1024>), grid, dim3(1024), 0, s, p, a.n + 1, nullptr);
+    else hipLaunchKernelGGL((k_attn_global_bf16<128, 1024>), grid, dim3(1024), 0, s, p, a.n + 1, nullptr);
     return hipGetLastError();
   }
   int split_keys = (a.n + 1 + splits - 1) / splits;
@@ -815,13 +717,12 @@ hipError_t attention_global(hipStream_t s, const AttnArgs& a, bool rope, float* 
   const int used = (a.n + 1 + split_keys - 1) / split_keys;   // every split holds >= 1 key
   const dim3 grid(a.H, a.n_tiles, used);
   if (a.hd == 64) {
-    TS_GL(64, 256, split_keys, scratch);
+    hipLaunchKernelGGL((k_attn_global_bf16<64, 256>), grid, dim3(256), 0, s, p, split_keys, scratch);
     hipLaunchKernelGGL(k_attn_global_merge<64>, dim3(a.H, a.n_tiles), dim3(64), 0, s, p, used, scratch);
   } else {
-    TS_GL(128, 256, split_keys, scratch);
+    hipLaunchKernelGGL((k_attn_global_bf16<128, 256>), grid, dim3(256), 0, s, p, split_keys, scratch);
     hipLaunchKernelGGL(k_attn_global_merge<128>, dim3(a.H, a.n_tiles), dim3(128), 0, s, p, used, scratch);
   }
-#undef TS_GL
   return hipGetLastError();
 }
 

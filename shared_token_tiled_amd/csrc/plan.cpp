@@ -8,8 +8,10 @@
 // Built with the host compiler and -ffp-contract=off: w-bar and the RoPE
 // angles are float64 expressions evaluated in a fixed order and rounded once
 // to fp32, so the maps are reproducible bit for bit.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <map>
 
 #include "plan_internal.h"
 
@@ -38,6 +40,53 @@ static double axis_ramp(const std::vector<int32_t>& st, int32_t L, size_t i, int
   const double lead = u < o_prev ? double(u + 1) / double(o_prev + 1) : 1.0;
   const double trail = u >= L - o_next ? double(L - u) / double(o_next + 1) : 1.0;
   return lead * trail;
+}
+
+// Query blocks of the blended attention.  Rows with the same set of tiles
+// of nonzero weight form a group (a ramp weight is never zero, so the set is
+// the row's cover; hard stitching keeps one tile); groups are ordered by
+// decreasing set size (longest work first), then by their tile lists, and
+// their rows ascending, cut into blocks of TS_QBLOCK slots.
+static void build_blocks(ts_plan& p) {
+  std::map<std::vector<int32_t>, std::vector<int32_t>> groups;
+  std::vector<int32_t> key;
+  for (int32_t q = 0; q < p.n_union; ++q) {
+    key.clear();
+    for (int32_t e = p.cover_ptr[q]; e < p.cover_ptr[q + 1]; ++e)
+      if (p.cover_w[e] != 0.f) key.push_back(p.cover_tile[e]);
+    groups[key].push_back(q);
+  }
+  std::vector<const std::pair<const std::vector<int32_t>, std::vector<int32_t>>*> order;
+  p.blk_maxc = 0;
+  for (const auto& g : groups) {
+    order.push_back(&g);
+    p.blk_maxc = std::max<int32_t>(p.blk_maxc, int32_t(g.first.size()));
+  }
+  std::stable_sort(order.begin(), order.end(),
+                   [](const auto* a, const auto* b) { return a->first.size() > b->first.size(); });
+  p.nblk = 0;
+  for (const auto* g : order) p.nblk += int32_t((g->second.size() + TS_QBLOCK - 1) / TS_QBLOCK);
+  p.blk_nt.assign(p.nblk, 0);
+  p.blk_tiles.assign(size_t(p.nblk) * p.blk_maxc, -1);
+  p.blk_rows.assign(size_t(p.nblk) * TS_QBLOCK, -1);
+  p.blk_w.assign(size_t(p.nblk) * p.blk_maxc * TS_QBLOCK, 0.f);
+  int32_t b = 0;
+  for (const auto* g : order) {
+    const std::vector<int32_t>& tiles = g->first;
+    const std::vector<int32_t>& rows = g->second;
+    for (size_t r0 = 0; r0 < rows.size(); r0 += TS_QBLOCK, ++b) {
+      p.blk_nt[b] = int32_t(tiles.size());
+      for (size_t i = 0; i < tiles.size(); ++i) p.blk_tiles[size_t(b) * p.blk_maxc + i] = tiles[i];
+      for (int32_t s = 0; s < TS_QBLOCK && r0 + s < rows.size(); ++s) {
+        const int32_t q = rows[r0 + s];
+        p.blk_rows[size_t(b) * TS_QBLOCK + s] = q;
+        for (int32_t e = p.cover_ptr[q]; e < p.cover_ptr[q + 1]; ++e)
+          for (size_t i = 0; i < tiles.size(); ++i)
+            if (p.cover_tile[e] == tiles[i])
+              p.blk_w[(size_t(b) * p.blk_maxc + i) * TS_QBLOCK + s] = p.cover_w[e];
+      }
+    }
+  }
 }
 
 std::string build(const ts_tiling_desc& d, ts_plan& p) {
@@ -130,6 +179,7 @@ std::string build(const ts_tiling_desc& d, ts_plan& p) {
     for (int32_t e = e0; e < e1; ++e) total = total + r_of(e);
     for (int32_t e = e0; e < e1; ++e) p.cover_w[e] = float(r_of(e) / total);
   }
+  build_blocks(p);
   return "";
 }
 
@@ -148,36 +198,18 @@ void rope_pairs(int32_t ndim, int32_t head_dim, int32_t out[3]) {
   }
 }
 
-void rope_table(const ts_plan& p, int32_t head_dim, float base, std::vector<float>& tab, int32_t pairs[3],
-                int32_t off[3], int32_t wbase[3], int32_t wpairs[3]) {
+void rope_local(const ts_plan& p, int32_t head_dim, float base, float* cos_out, float* sin_out) {
+  int32_t pairs[3];
   rope_pairs(p.desc.ndim, head_dim, pairs);
-  int32_t total = 0, k0 = 0;
-  for (int a = 0; a < 3; ++a) {
-    const int32_t k1 = k0 + pairs[a];
-    wbase[a] = pairs[a] ? (k0 / 4) * 4 : 0;
-    wpairs[a] = pairs[a] ? ((k1 + 3) / 4) * 4 - wbase[a] : 0;
-    off[a] = total;
-    total += 2 * wpairs[a] * p.ext[a];
-    k0 = k1;
-  }
-  // identity (cos 1, sin 0) in the window slots of pairs of other axes
-  tab.assign(size_t(total), 0.f);
-  for (int a = 0; a < 3; ++a)
-    for (int32_t pos = 0; pos < p.ext[a]; ++pos)
-      for (int32_t w = 0; w < wpairs[a]; ++w) tab[off[a] + 2 * (size_t(pos) * wpairs[a] + w)] = 1.f;
-  k0 = 0;
-  for (int a = 0; a < 3; ++a) {
-    for (int32_t i = 0; i < pairs[a]; ++i) {
-      const double inv = std::pow(double(base), double(-i) / double(pairs[a]));
-      const int32_t w = k0 + i - wbase[a];
-      for (int32_t pos = 0; pos < p.ext[a]; ++pos) {
-        const double ang = double(pos) * inv;
-        tab[off[a] + 2 * (size_t(pos) * wpairs[a] + w)] = float(std::cos(ang));
-        tab[off[a] + 2 * (size_t(pos) * wpairs[a] + w) + 1] = float(std::sin(ang));
-      }
+  const int32_t P = head_dim / 2;
+  for (int32_t j = 0; j < p.n; ++j)
+    for (int32_t k = 0, a = 0, k0 = 0; k < P; ++k) {
+      while (k >= k0 + pairs[a]) k0 += pairs[a++];
+      const int32_t pos = (p.local_pos[j] >> (10 * a)) & 1023;
+      const double ang = double(pos) * std::pow(double(base), double(-(k - k0)) / double(pairs[a]));
+      cos_out[size_t(j) * P + k] = float(std::cos(ang));
+      sin_out[size_t(j) * P + k] = float(std::sin(ang));
     }
-    k0 += pairs[a];
-  }
 }
 
 // RoPE table over the whole grid: axis a's block holds, for every grid

@@ -84,35 +84,37 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
                 const float* bias, void* C, const float* sa, const float* sb, float* ws = nullptr,
                 size_t ws_bytes = 0, unsigned* amax = nullptr);
 
-// ---- attn_*.hip ----
+// ---- attn.hip ----
+// Query rows per attention workgroup, and per query block of the plan.
+constexpr int QBLOCK = 256;
+// q and k of qkv are as qk_prep left them (normalised, rotated by grid
+// coordinates).  Layouts (see attn.hip):
+//  - rows == null: per-tile qkv rows t*(n+1)+i; outputs in the same rows;
+//  - rows != null, blk_nt == null: shared qkv rows [n_union + n_tiles] read
+//    through the tile map; outputs per tile, t*(n+1)+i;
+//  - rows and blk_nt != null: shared qkv rows; every grid row's outputs of
+//    the windows of its query block blended with the block's weights, written
+//    to out row p (global rows: out row n_union + t).
 struct AttnArgs {
-  const void* qkv;      // [rows, 3d] act
-  void* out;            // [n_tiles*(n+1), d] act, per-tile layout
-  const int* rows;      // [n_tiles*n] grid rows (shared layer) or null (per-tile rows)
-  int n_union;          // global row of tile t = n_union + t when rows != null
-  int d, H, hd, n_tiles, n;
-  const int* local_pos; // [n] packed tau | y<<10 | x<<20
-  const float* rope;    // compact per-axis (cos, sin) table
-  int rope_floats;      // its length in floats
-  int pairs[3];         // rotation pairs per axis (t, h, w), contiguous chunks in that order
-  int rope_off[3];      // float offset of each axis' block; global pair k at position pos
-  int rope_wbase[3];    // of axis a is (cos, sin) at
-  int rope_wpairs[3];   // rope_off[a] + 2*(pos*rope_wpairs[a] + k - rope_wbase[a])
-  const void* vt = nullptr;  // bf16 [n_tiles][H][hd][n_pad]: each window's V transposed
-                             // (v_transpose), n_pad = n rounded up to 64; read when !rope
+  const void* qkv;          // [rows, 3d] act
+  void* out;                // act, rows as above
+  float* part = nullptr;    // blended: fp32 [n_union, d] partial sums between windows
+  const int* rows = nullptr;       // [n_tiles*n] grid rows of each tile's tokens
+  const int* blk_nt = nullptr;     // [nblk] windows of each query block
+  const int* blk_tiles = nullptr;  // [nblk*maxc] their tiles, ascending
+  const int* blk_rows = nullptr;   // [nblk*QBLOCK] grid row of each query slot (-1: empty)
+  const float* blk_w = nullptr;    // [nblk*maxc*QBLOCK] w-bar of (block, window, slot)
+  int nblk = 0, maxc = 0;
+  int n_union, d, H, hd, n_tiles, n;
+  unsigned* amax = nullptr;        // optional (bf16): max |out| as stored
 };
-// Window values transposed per (tile, head) for the bf16 kernel: vt[t][h][e][j]
-// = V of window token j, dim e of head h (zero for j >= n, up to n_pad).
-hipError_t v_transpose(hipStream_t s, const AttnArgs& a, void* vt);
-// fp32: every window row.  bf16: the n tile-token query rows of every window;
-// the global-token row (window row n) is attention_global's.
-// rope: rotate q and k by tile-local positions while staging (the global
-// token unrotated); otherwise they are used as stored (rotated by qk_prep).
-hipError_t attention(hipStream_t s, int act, const AttnArgs& a, bool rope);
+// fp32: every query row, the global rows included.  bf16: the tile-token
+// query rows; the global-token rows are attention_global's.
+hipError_t attention(hipStream_t s, int act, const AttnArgs& a);
 // bf16 only: the global-token query row of every (tile, head).  With
 // scratch (fp32, scratch_floats long) the keys are split over several
 // workgroups per row and merged by a second kernel; without, one workgroup
 // per row.
-hipError_t attention_global(hipStream_t s, const AttnArgs& a, bool rope, float* scratch, int64_t scratch_floats);
+hipError_t attention_global(hipStream_t s, const AttnArgs& a, float* scratch, int64_t scratch_floats);
 
 }  // namespace tsk

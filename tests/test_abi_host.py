@@ -12,6 +12,8 @@ import shared_token_tiled_amd as ts
 from oracle.plan import Plan, rope_tables
 from synth import configs
 
+import attn_rounding as AR
+
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tileshare.h")
 
 
@@ -27,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
-    assert ts.ts_abi_version() == 4
+    assert ts.ts_abi_version() == 5
 
 
 PLAN_CASES = [(configs.get(n)["ndim"], configs.get(n)["grid"], configs.get(n)["tile"], configs.get(n)["stride"])
@@ -161,3 +163,43 @@ def test_graft_entry_build_accepts_the_built_library(monkeypatch):
     from shared_token_tiled_amd import build as b
     monkeypatch.setattr(b, "build", lambda *a, **k: None)
     entry.build()
+
+
+@pytest.mark.parametrize("blend", [0, 1])
+@pytest.mark.parametrize("ndim,grid,tile,stride", PLAN_CASES)
+def test_query_blocks_bit_exact_against_the_rule(ndim, grid, tile, stride, blend):
+    """The attention's query blocks (grid rows grouped by the tiles holding
+    them with a nonzero w-bar) equal the ones the rule builds from the
+    oracle's plan: same order, rows, tiles and w-bar bits."""
+    h = ts.ts_plan_create(ndim, grid, tile, stride, blend=blend)
+    try:
+        nt, tl, rw, w = ts.ts_plan_export_blocks(h)
+    finally:
+        ts.ts_plan_destroy(h)
+    ref = Plan(grid, tile, stride, blend=("ramp", "hard")[blend])
+    blocks = AR.query_blocks(ref)
+    assert len(nt) == len(blocks)
+    for b, (tiles, rows) in enumerate(blocks):
+        assert nt[b] == len(tiles)
+        assert list(tl[b, :len(tiles)]) == list(tiles) and np.all(tl[b, len(tiles):] == -1)
+        assert np.array_equal(rw[b, :len(rows)], rows) and np.all(rw[b, len(rows):] == -1)
+        for i, t in enumerate(tiles):
+            want = np.array([dict((tt, ww) for tt, _, ww in ref.cover_of(int(r)))[t] for r in rows], np.float32)
+            assert np.array_equal(w[b, i, :len(rows)].view(np.uint32), want.view(np.uint32))
+            assert np.all(w[b, i, len(rows):] == 0)
+
+
+def test_large_tiles_plan_and_rope_export():
+    """64 x 64 tiles with head size 128 (8192 tile-local RoPE values per pair
+    set): the plan builds and exports its tile-local table; nothing in the
+    layer path limits the table size (the layers rotate by grid coordinate)."""
+    h = ts.ts_plan_create(2, (1, 160, 208), (1, 64, 64), (1, 48, 48))
+    try:
+        c, s = ts.ts_plan_export_rope(h, 128, 10000.0)
+        ref = Plan((1, 160, 208), (1, 64, 64), (1, 48, 48))
+        rc, rs = rope_tables(ref, 2, 128, 10000.0)
+        assert c.shape == (4096, 64)
+        assert np.array_equal(c.view(np.uint32), rc.view(np.uint32))
+        assert np.array_equal(s.view(np.uint32), rs.view(np.uint32))
+    finally:
+        ts.ts_plan_destroy(h)

@@ -17,6 +17,8 @@ from oracle import model as M
 from oracle.plan import Plan
 from synth import configs, make_inputs, round_bf16
 
+import attn_cases as AC
+import attn_rounding as AR
 from gpu_helpers import DEV, TOL, Run, max_rel, say
 
 pytestmark = pytest.mark.gpu
@@ -135,41 +137,36 @@ def test_full_size_gemm_fp8(name, N, K, epi):
     assert np.all(err <= bound)
 
 
-@pytest.mark.parametrize("shared", [True, False])
-def test_full_size_window_attention(shared):
-    cfg = MINIMAX
-    pl = _PL
-    n, d = pl.tile_tokens, cfg["d"]
-    rows = pl.n_union + pl.n_tiles if shared else pl.n_tiles * (n + 1)
-    say(f"full-size attention bf16 shared={shared} rows={rows} tiles={pl.n_tiles} n={n}")
-    r = np.random.default_rng(21)
-    qkv = round_bf16(_randn(r, (rows, 3 * d)))
-    h = ts.ts_plan_create(cfg["ndim"], cfg["grid"], cfg["tile"], cfg["stride"])
-    try:
-        ts.ts_plan_upload(h, cfg["head_dim"])
-        out = torch.zeros(pl.n_tiles * (n + 1), d, dtype=torch.bfloat16, device=DEV)
-        ts.ts_op_window_attention(ts.model_desc(cfg), h, shared, torch.from_numpy(qkv).to(DEV, torch.bfloat16), out)
-        torch.cuda.synchronize()
-        got = out.float().cpu().numpy()
-    finally:
-        ts.ts_plan_destroy(h)
-    rope = M.Rope(pl, cfg)
-    q64 = qkv.astype(np.float64)
-    worst = 0.0
-    for t in range(pl.n_tiles):
-        if shared:
-            win = np.concatenate([pl.tile_rows[t].astype(np.int64), [pl.n_union + t]])
-        else:
-            win = np.arange(t * (n + 1), (t + 1) * (n + 1))
-        local = _sample_rows(n + 1, 30 + t, extra=(n,))
-        ref = M.attention_rows(q64[win[local], :d], q64[win, d:2 * d], q64[win, 2 * d:], local,
-                               rope.cos, rope.sin, cfg)
-        o = got[t * (n + 1) + local]
-        err = np.linalg.norm(o - ref, axis=1) / np.linalg.norm(ref, axis=1)
-        worst = max(worst, float(err.max()))
-    print(f"  worst sampled row rel-L2 {worst:.3e}")
-    # the same per-row bound as the small cases (bf16 q, k, weights and output)
-    assert worst < 2e-2
+@pytest.mark.parametrize("name", ["minimax_h3", "vitok4k"])
+def test_full_size_attention_step(name):
+    """The shared layers' attention step at the full workload size, in the
+    launch configuration of a shared layer (qk_prep, the blended window kernel
+    over every query block, the split global-row kernels), checked as the
+    small cases are (test_gpu_kernels.check_attention) on whole query blocks:
+    the first and last block of every window count and the last block."""
+    from test_gpu_kernels import check_attention, run_attention_op
+    base = configs.get(name)
+    cfg = AC.case_cfg(base["ndim"], base["grid"], base["tile"], base["stride"], base["n_heads"],
+                      base["head_dim"], base["qk_norm"], "bf16")
+    say(f"full-size attention step {name} grid={cfg['grid']} tiles={cfg['tile']}")
+    pl, qkv, q_g, k_g = AC.case_inputs(cfg, True, 1.0, seed=21)
+    got, qkv_gpu = run_attention_op(cfg, pl, qkv, q_g, k_g, True)
+    blocks = AR.query_blocks(pl)
+    pick = set()
+    for nt in sorted({len(t) for t, _ in blocks}):
+        idx = [i for i, (t, _) in enumerate(blocks) if len(t) == nt]
+        pick.update((idx[0], idx[-1]))
+    pick.add(len(blocks) - 1)
+    pick = sorted(pick)
+    rows = np.concatenate([blocks[i][1] for i in pick])
+    ref_rows = AC.oracle_attention_rows(qkv, cfg, pl, rows, q_g, k_g)
+    ref = np.full_like(got, np.nan)
+    ref[rows] = ref_rows[:len(rows)]
+    ref[pl.n_union:] = ref_rows[len(rows):]
+    sel = np.concatenate([rows, pl.n_union + np.arange(pl.n_tiles)])
+    e = check_attention(cfg, pl, qkv, q_g, k_g, True, got, qkv_gpu, ref, emu_blocks=pick, rows=sel)
+    print(f"  {len(pick)} blocks ({len(rows)} rows) + {pl.n_tiles} global rows: max|gpu-oracle|/rms {e:.3e}")
+    assert e < AC.CAP[1.0]
 
 
 FULL_LAYER = ["minimax_h3", "small_video", "vitok4k"]

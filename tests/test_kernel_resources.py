@@ -24,7 +24,7 @@ def resources():
 def test_every_kernel_reported(resources):
     names = " ".join(resources)
     for k in ("k_gemm_mfma", "k_gemm_rows", "k_gemm_f32", "k_attn_bf16", "k_attn_global_bf16", "k_attn_f32",
-              "k_vtrans", "k_qkprep", "k_norm", "k_blend", "k_gather", "k_quant", "k_amax"):
+              "k_qkprep", "k_norm", "k_blend", "k_gather", "k_quant", "k_amax"):
         assert k in names, k
 
 
