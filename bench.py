@@ -69,14 +69,17 @@ def cpu_baseline(cfg, k):
     the workload: one per-tile block on one tile window (tile_tokens + 1 rows),
     then scale to decoded tokens/s of the whole TileShare-k decode by the
     ratio of algorithmic FLOPs."""
+    from threadpoolctl import threadpool_limits
+
     from oracle import model as M
     from oracle.plan import Plan
     from synth import make_inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
+    threads = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=threads):
+        return _cpu_baseline(cfg, k, threads, M, Plan, make_inputs)
+
+
+def _cpu_baseline(cfg, k, threads, M, Plan, make_inputs):
     pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
     x, g, layers = make_inputs(cfg, n_layers=1)
     rope = M.Rope(pl, cfg)
@@ -122,6 +125,8 @@ def measured_traffic(name, workload, k):
 def decode_flops(cfg, pl, k, share="qom", dedup0=False):
     """Algorithmic FLOPs of a TileShare-k decode: 2*(3d^2 + d^2 + 2 d dm) per row
     per layer for the projections, 4 (n+1)^2 d per tile per layer for attention.
+    ``pl``: anything with n_tiles, tile_tokens and n_union (the library's
+    ts_plan_info).
     ``share``: the operations that run once per token from layer k on (q: QKV,
     o: out-projection, m: MLP); the others run on every tile's rows.
     ``dedup0``: a per-tile layer 0 runs its QKV once per token."""
@@ -262,9 +267,7 @@ def main():
         kernels[r["name"]] = {"ms_per_step": round(r["total_ms"] / args.steps, 3),
                               "tflops": round(r["flops"] / sec / 1e12, 1) if r["flops"] else None,
                               "gbps": round(r["bytes"] / sec / 1e9, 1)}
-    pl_flops = None
-    from oracle.plan import Plan  # FLOP count needs only the tile counts
-    pl = Plan(cfg["grid"], cfg["tile"], cfg["stride"])
+    pl = info   # FLOP count needs only the tile counts, from the library's plan
     pl_flops = (decode_flops(cfg, pl, L, dedup0=args.layer0_dedup)
                 if args.merge_once is not None else
                 decode_flops(cfg, pl, k, args.partial_share if args.partial_share is not None else "qom",
@@ -295,6 +298,8 @@ def main():
         "speedup_vs_tiled": None if ms_base is None else round(ms_base / ms_ts, 4),
         "decode_tflops": round(pl_flops / (ms_ts / 1e3) / 1e12, 1),
         "frac_of_bf16_peak": round(pl_flops / (ms_ts / 1e3) / PEAK["bf16"], 4),
+        "frac_of_fp8_peak": (round(pl_flops / (ms_ts / 1e3) / PEAK["fp8"], 4)
+                             if cfg["gemm_shared"] == "fp8" else None),
         "roofline": roof,
         "kernels": kernels,
         "profiled_ms_per_step": round(ms_prof, 3),

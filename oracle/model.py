@@ -21,6 +21,8 @@ the per-tile states are merged with w-bar (global rows stay per tile); the
 tiled baseline is k = L followed by the same merge; no final norm.
 """
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 from scipy.special import erf
@@ -121,6 +123,23 @@ def qkv_heads(h, p, cfg, fp8=False):
     return q, k, v
 
 
+def per_head(fn, n_heads):
+    """fn(h) for every head, heads evaluated concurrently when that pays.
+
+    The heads are independent, so this changes only when each is computed,
+    not what: every head runs exactly the numpy expressions of fn.  BLAS is
+    held to one thread per head meanwhile, so the threads do not compete for
+    cores inside the products."""
+    workers = min(n_heads, len(os.sched_getaffinity(0)))
+    if workers <= 1:
+        for h in range(n_heads):
+            fn(h)
+        return
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fn, range(n_heads)))
+
+
 def tile_attention(q, k, v, cos_t, sin_t, cfg):
     """Dense attention of one tile window.
 
@@ -131,11 +150,14 @@ def tile_attention(q, k, v, cos_t, sin_t, cfg):
     hd = cfg["head_dim"]
     out = np.empty_like(q)
     scale = 1.0 / math.sqrt(hd)
-    for hh in range(cfg["n_heads"]):
+
+    def head(hh):
         cs = slice(hh * hd, (hh + 1) * hd)
         qh = rope_rotate(q[:, cs], cos_t, sin_t)
         kh = rope_rotate(k[:, cs], cos_t, sin_t)
         out[:, cs] = softmax_attention(qh, kh, v[:, cs], scale)
+
+    per_head(head, cfg["n_heads"])
     return out
 
 
@@ -293,11 +315,14 @@ def attention_rows(q_sel, k, v, local, cos_t, sin_t, cfg):
     local = np.asarray(local, dtype=np.int64)
     out = np.empty_like(q_sel)
     scale = 1.0 / math.sqrt(hd)
-    for hh in range(cfg["n_heads"]):
+
+    def head(hh):
         cs = slice(hh * hd, (hh + 1) * hd)
         qh = rope_rotate(q_sel[:, cs], cos_t[local], sin_t[local])
         kh = rope_rotate(k[:, cs], cos_t, sin_t)
         out[:, cs] = softmax_attention(qh, kh, v[:, cs], scale)
+
+    per_head(head, cfg["n_heads"])
     return out
 
 

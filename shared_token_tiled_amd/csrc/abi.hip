@@ -280,7 +280,11 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, AttnLayout 
   a.qkv = qkv;
   a.out = out;
   a.part = part;
-  a.rows = lay != ATT_TILED ? (const int*)p->d_tile_rows : nullptr;
+  // window rows through a map in every layout: the tile map into shared
+  // rows, or t*(n+1)+j into per-tile rows; the global key row is g0 + gstep*t
+  a.rows = lay != ATT_TILED ? (const int*)p->d_tile_rows : (const int*)p->d_tile_rows_local;
+  a.g0 = lay != ATT_TILED ? p->n_union : p->n;
+  a.gstep = lay != ATT_TILED ? 1 : p->n + 1;
   if (lay == ATT_BLENDED) {
     a.blk_nt = (const int*)p->d_blk_nt;
     a.blk_tiles = (const int*)p->d_blk_tiles;
@@ -715,7 +719,7 @@ ts_status ts_plan_export_blocks(const ts_plan* p, int32_t* nblk, int32_t* maxc, 
 }
 
 static void free_device(ts_plan* p) {
-  void** ptrs[] = {&p->d_tile_rows, &p->d_cover_ptr,  &p->d_entry_row, &p->d_cover_w, &p->d_local_pos,
+  void** ptrs[] = {&p->d_tile_rows, &p->d_tile_rows_local, &p->d_cover_ptr, &p->d_entry_row, &p->d_cover_w, &p->d_local_pos,
                    &p->d_rope_glob, &p->d_tile_start, &p->d_blk_nt,    &p->d_blk_tiles, &p->d_blk_rows,
                    &p->d_blk_w};
   for (void** q : ptrs) {
@@ -735,6 +739,9 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
   tsplan::rope_table_global(*p, head_dim, rope_base, gtab, goff);
   std::vector<int32_t> entry_row(p->n_entries);
   for (int32_t e = 0; e < p->n_entries; ++e) entry_row[e] = p->cover_tile[e] * (p->n + 1) + p->cover_local[e];
+  std::vector<int32_t> rows_local(size_t(p->n_tiles) * p->n);
+  for (int32_t t = 0; t < p->n_tiles; ++t)
+    for (int32_t j = 0; j < p->n; ++j) rows_local[size_t(t) * p->n + j] = t * (p->n + 1) + j;
   free_device(p);
   hipStream_t s = (hipStream_t)stream;
   struct Item {
@@ -743,6 +750,7 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
     size_t bytes;
   } items[] = {
       {&p->d_tile_rows, p->tile_rows.data(), p->tile_rows.size() * 4},
+      {&p->d_tile_rows_local, rows_local.data(), rows_local.size() * 4},
       {&p->d_cover_ptr, p->cover_ptr.data(), p->cover_ptr.size() * 4},
       {&p->d_entry_row, entry_row.data(), entry_row.size() * 4},
       {&p->d_cover_w, p->cover_w.data(), p->cover_w.size() * 4},

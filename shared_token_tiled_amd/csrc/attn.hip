@@ -48,6 +48,7 @@ struct AttnP {
   void* out;
   float* part;
   const int* rows;
+  int g0, gstep;
   const int* blk_nt;
   const int* blk_tiles;
   const int* blk_rows;
@@ -61,10 +62,8 @@ struct AttnP {
 constexpr int QB = 256;  // query rows per workgroup (both kernels)
 
 // qkv row of window token j < n of tile t, and of tile t's global token
-__device__ __forceinline__ int key_row(const AttnP& p, int t, int j) {
-  return p.rows ? p.rows[int64_t(t) * p.n + j] : t * (p.n + 1) + j;
-}
-__device__ __forceinline__ int gkey_row(const AttnP& p, int t) { return p.rows ? p.n_union + t : t * (p.n + 1) + p.n; }
+__device__ __forceinline__ int key_row(const AttnP& p, int t, int j) { return p.rows[int64_t(t) * p.n + j]; }
+__device__ __forceinline__ int gkey_row(const AttnP& p, int t) { return p.g0 + p.gstep * t; }
 // output row of tile t's global query
 __device__ __forceinline__ int gout_row(const AttnP& p, int t) { return p.blk_nt ? p.n_union + t : t * (p.n + 1) + p.n; }
 
@@ -169,9 +168,18 @@ __global__ __launch_bounds__(QB) void k_attn_f32(AttnP p) {
 // ------------------------------------------------------------- bf16 -----
 constexpr int NW = 8;                  // wavefronts per workgroup
 constexpr int KB = 64;                 // keys per staged block
-constexpr int NST = 3;                 // LDS stages of K and V
-constexpr int AHEAD = 3;               // blocks ahead the key rows are fetched
-constexpr int NSL = 4;                 // slots of the key-row ring
+// Staging pipeline.  NST LDS stages of K and V: at key block gb the DMA of
+// block gb + NST - 1 is issued, and a block's end waits only for block gb+1
+// (the NST - 2 newer blocks stay in flight).  A wavefront's vector memory
+// operations complete in issue order, so a key-row ring load issued at block
+// j has landed by the end of block j + NST - 3 and is read (for the DMA of its
+// block) NST - 1 blocks before that block: the ring runs AHEAD = 2 NST - 3
+// blocks ahead, in NSL slots.
+constexpr int NST = 4;                 // LDS stages of K and V
+constexpr int DEPTH = NST - 1;         // blocks whose DMA is in flight ahead of the current one
+constexpr int AHEAD = 2 * DEPTH - 1;   // blocks ahead the key rows are fetched
+constexpr int NSL = 8;                 // slots of the key-row ring (>= AHEAD + 1)
+static_assert(NSL >= AHEAD + 1 && DEPTH >= 2 && DEPTH <= 3, "staging pipeline");
 constexpr float RESCALE_LOG2 = 8.0f;   // keep a stale running max until a block exceeds it by 2^8
 static_assert(QB == 32 * NW, "32 query rows per wavefront");
 static_assert(QB == tsk::QBLOCK, "query blocks of the plan");
@@ -227,21 +235,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int n = p.n;
   const int nkb = (n + KB - 1) / KB;
   const int nqb = (n + QB - 1) / QB;
-  // XCD-aware order: the hardware deals workgroup b to XCD b % 8; give each
-  // XCD a contiguous run of jobs so the query blocks that stream the same keys
-  // and values share one L2 (blended: blocks of one head in plan order;
-  // otherwise the query blocks of one (tile, head)).
+  // Job order.  The hardware deals workgroup b to XCD b % 8.  Per tile: give
+  // each XCD a contiguous run of jobs, the query blocks of one (tile, head),
+  // which stream the same keys and values through that XCD's L2.  Blended:
+  // jobs run from the plan's longest blocks (most windows) to its shortest,
+  // (block, head) with the head fastest, dealt round-robin: every XCD gets the
+  // same mix of lengths, longest first, and the heads it holds of consecutive
+  // blocks of one tile group share their windows in L2.
   int h, t0 = 0, qblk = 0, blk = 0, npass = 1;
-  {
-    const int total = (BLEND ? p.nblk : nqb * p.n_tiles) * p.H;
+  if constexpr (BLEND) {
+    blk = blockIdx.x / p.H;
+    h = blockIdx.x % p.H;
+    npass = p.blk_nt[blk];
+  } else {
+    const int total = nqb * p.n_tiles * p.H;
     const int b = blockIdx.x, xcd = b & 7, loc = b >> 3;
     const int q8 = total >> 3, r8 = total & 7;
     const int id = xcd < r8 ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
-    if constexpr (BLEND) {
-      blk = id % p.nblk;
-      h = id / p.nblk;
-      npass = p.blk_nt[blk];
-    } else {
+    {
       qblk = id % nqb;
       h = (id / nqb) % p.H;
       t0 = id / (nqb * p.H);
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
 
   // key rows of the first AHEAD blocks (row-map layouts)
-  if (p.rows && tid < KB) {
+  if (tid < KB) {
 #pragma unroll
     for (int b = 0; b < AHEAD; ++b)
       if (b < nblocks) {
@@ -273,7 +284,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int i = 0; i < KDI; ++i) {
       const int row = ((wv * KDI + i) * 1024 + 16 * lane) / KROWB;
-      rr[i] = p.rows ? idx_s[gb % NSL][row] : t0 * (n + 1) + min(gb * KB + row, n - 1);
+      rr[i] = idx_s[gb % NSL][row];
     }
   };
   auto dma = [&](int gb, const int (&rr)[KDI]) {
@@ -292,28 +303,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __syncthreads();  // ring slots ready
   {
     int rr[KDI];
-    dma_rows(0, rr);
-    dma(0, rr);
-    if (nblocks > 1) {
-      dma_rows(1, rr);
-      dma(1, rr);
-    }
+#pragma unroll
+    for (int b = 0; b < DEPTH; ++b)
+      if (b < nblocks) {
+        dma_rows(b, rr);
+        dma(b, rr);
+      }
   }
 
   // ---- this wavefront's 32 queries: B operand of S^T = K Q^T (hd 16s + 8g + e)
   const int slot = wave * 32 + l32;
-  int qrow, orow;
-  bool qvalid;
+  int qrow;
   if constexpr (BLEND) {
     const int r = p.blk_rows[blk * QB + slot];
-    qvalid = r >= 0;
-    qrow = qvalid ? r : p.blk_rows[blk * QB];
-    orow = qrow;
+    qrow = r >= 0 ? r : p.blk_rows[blk * QB];   // an empty slot runs the block's first row
   } else {
-    const int qi = qblk * QB + slot;
-    qvalid = qi < n;
-    qrow = key_row(p, t0, min(qi, n - 1));
-    orow = t0 * (n + 1) + qi;
+    const int qc = min(qblk * QB + slot, n - 1);
+    qrow = p.rows[int64_t(t0) * n + qc];
   }
   bf16x8 qf[KSTEPS];
   {
@@ -353,31 +359,64 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // windows and the blend written after the last one
   auto window_finish = [&](int ps) {
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    // the output row is read again here rather than kept from the start:
+    // nothing but the softmax state stays in registers across the key loop
+    int orw;
+    bool valid;
     float coef;
-    if constexpr (BLEND) coef = p.blk_w[(int64_t(blk) * p.maxc + ps) * QB + slot] / l_tot;
-    else coef = 1.0f / l_tot;
+    if constexpr (BLEND) {
+      const int r = p.blk_rows[blk * QB + slot];
+      valid = r >= 0;
+      orw = valid ? r : p.blk_rows[blk * QB];
+      coef = p.blk_w[(int64_t(blk) * p.maxc + ps) * QB + slot] / l_tot;
+    } else {
+      const int qi = qblk * QB + slot;
+      valid = qi < n;
+      orw = t0 * (n + 1) + qi;
+      coef = 1.0f / l_tot;
+    }
     const bool last = !BLEND || ps + 1 == npass;
-    float* prow = p.part + int64_t(orow) * p.d + h * HD;
-    bf16* op = (bf16*)p.out + int64_t(orow) * p.d + h * HD;
-    float am = 0.f;
+    float* prow = p.part + int64_t(orw) * p.d + h * HD;
+    bf16* op = (bf16*)p.out + int64_t(orw) * p.d + h * HD;
+    // in place on the accumulators (the next window starts them afresh)
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
+    for (int hb = 0; hb < NHB; ++hb) oacc[hb] *= coef;
+    if (BLEND && ps > 0) {
+      // every lane reads (an empty slot's row is the block's first row); the
+      // reads of half the head go out together before they are added
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int col = hb * 32 + 8 * r4 + 4 * g;
-        f32x4 v = {oacc[hb][4 * r4] * coef, oacc[hb][4 * r4 + 1] * coef, oacc[hb][4 * r4 + 2] * coef,
-                   oacc[hb][4 * r4 + 3] * coef};
-        if (!qvalid) continue;
-        if (BLEND && ps > 0) v += load4(prow + col);
-        if (!last) {
-          store4(prow + col, v);
-        } else {
-          const bf16x4 w = {bf16(v[0]), bf16(v[1]), bf16(v[2]), bf16(v[3])};
-          *reinterpret_cast<bf16x4*>(op + col) = w;
+      for (int h0 = 0; h0 < NHB; h0 += (NHB + 1) / 2) {
+        f32x4 prev[(NHB + 1) / 2][4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(float(w[e])));
-        }
+        for (int hb = h0; hb < min(h0 + (NHB + 1) / 2, NHB); ++hb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) prev[hb - h0][r4] = load4(prow + hb * 32 + 8 * r4 + 4 * g);
+#pragma unroll
+        for (int hb = h0; hb < min(h0 + (NHB + 1) / 2, NHB); ++hb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[hb][4 * r4 + e] += prev[hb - h0][r4][e];
       }
+    }
+    float am = 0.f;
+    if (valid) {
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int col = hb * 32 + 8 * r4 + 4 * g;
+          const f32x4 v = {oacc[hb][4 * r4], oacc[hb][4 * r4 + 1], oacc[hb][4 * r4 + 2], oacc[hb][4 * r4 + 3]};
+          if (!last) {
+            store4(prow + col, v);
+          } else {
+            const bf16x4 w = {bf16(v[0]), bf16(v[1]), bf16(v[2]), bf16(v[3])};
+            *reinterpret_cast<bf16x4*>(op + col) = w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(float(w[e])));
+          }
+        }
+    }
     if (last && p.amax) wave_amax(p.amax, am, int(blockIdx.x) * NW + wave);
   };
 
@@ -397,6 +436,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int hb = 0; hb < NHB; ++hb) vaddr[hb] = row0 * KROWB + (((hb * 4 + clow) ^ vswz<HD>(row0)) * 16) + 8 * (j & 1);
   }
 
+  // window and block AHEAD blocks ahead in the stream, and that window's map
+  int ps3 = AHEAD / nkb, kb3 = AHEAD % nkb;
+  const int* map3 = p.rows + int64_t(tile_of(min(ps3, npass - 1))) * n;
   for (int ps = 0; ps < npass; ++ps) {
    window_init(tile_of(ps));
    for (int kb = 0; kb < nkb; ++kb) {
@@ -406,16 +448,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // key rows of block gb+AHEAD: wavefront 0 copies them from the row map
       // straight into the ring (no registers, so nothing waits on them before
       // the block-end wait), ahead of this block's K / V loads so that wait
-      // covers them; per-tile rows need no map
+      // covers them
       int rr[KDI];
-      if (gb + 2 < nblocks) dma_rows(gb + 2, rr);
-      if (p.rows && wave == 0 && gb + AHEAD < nblocks) {
-        const int b3 = gb + AHEAD, ps3 = b3 / nkb, kb3 = b3 - ps3 * nkb;
-        const int j = min(kb3 * KB + lane, n - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(p.rows + int64_t(tile_of(ps3)) * n + j),
-                                         (TS_LDS void*)(&idx_s[b3 % NSL][0]), 4, 0, 0);
+      if (gb + DEPTH < nblocks) dma_rows(gb + DEPTH, rr);
+      if (gb + AHEAD < nblocks) {
+        if (wv == 0) {
+          const int j = min(kb3 * KB + lane, n - 1);
+          __builtin_amdgcn_global_load_lds((const void*)(map3 + j), (TS_LDS void*)(&idx_s[(gb + AHEAD) % NSL][0]),
+                                           4, 0, 0);
+        }
+        // the stream position AHEAD blocks on: its window's map is read only
+        // when it enters a new window
+        if (++kb3 == nkb) {
+          kb3 = 0;
+          if (++ps3 < npass) map3 = p.rows + int64_t(tile_of(ps3)) * n;
+        }
       }
-      if (gb + 2 < nblocks) dma(gb + 2, rr);
+      if (gb + DEPTH < nblocks) dma(gb + DEPTH, rr);
     }
     const char* ks = Ks[cur];
     const char* vs = Vs[cur];
@@ -446,14 +495,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     if (j0 + KB > n) {  // keys past the window end (last block of a window only)
+      // accumulator row 8(r/4)+4g+(r%4) holds key swap23(that row) =
+      // 16(r/8) + 4((r/4)%2) + r%4 + 8g: one per-lane limit, constant offsets
+      const int lim = n - j0 - 8 * g;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // accumulator row 8(r/4)+4g+(r%4) holds key swap23(that row)
-          const int key = j0 + sb * 32 + swap23(8 * (r >> 2) + 4 * g + (r & 3));
-          if (key >= n) sacc[sb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (sb * 32 + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3) >= lim) sacc[sb][r] = -INFINITY;
     }
     // ---- online softmax over the block (one rescale check per block)
     bf16x8 pf[4];
@@ -485,12 +534,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
       l_run += lsum;
     }
-    // ---- O^T += V^T P^T over four 16-key chunks (NHB independent chains)
+    // ---- O^T += V^T P^T over four 16-key chunks (NHB independent chains).
+    // The transposing reads take no immediate offset, so their 8*NHB
+    // addresses would all be precomputed and held across the loop; the empty
+    // asm makes the NHB per-lane bases opaque here, so each address is one
+    // add from a base inside the block instead.
+    int vb[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      vb[hb] = vaddr[hb];
+      asm volatile("" : "+v"(vb[hb]));
+    }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) {
-        const char* a = vs + vaddr[hb] + 16 * cc * KROWB;
+        const char* a = vs + vb[hb] + 16 * cc * KROWB;
         const bf16x8 vf = v_fragment(a, a + 4 * KROWB);
         oacc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], oacc[hb], 0, 0, 0);
       }
@@ -503,12 +562,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
-    // this wavefront's loads of block gb+1 have landed (gb+2's may still be
-    // in flight) and its LDS traffic is done; then a barrier without the
-    // fence of __syncthreads, which would also wait for block gb+2.  Vector
-    // memory operations complete in issue order, so the count also covers
-    // the previous window's output loads and stores, issued before gb+2's.
-    if (gb + 2 < nblocks) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * KDI) : "memory");
+    // this wavefront's loads of block gb+1 have landed (the newer blocks'
+    // may still be in flight) and its LDS traffic is done; then a barrier
+    // without the fence of __syncthreads, which would also wait for those.
+    // Vector memory operations complete in issue order, so the count also
+    // covers the previous window's output loads and stores.
+    if (gb + DEPTH < nblocks) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((DEPTH - 1) * 2 * KDI) : "memory");
+    else if (DEPTH == 3 && gb + 2 < nblocks) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * KDI) : "memory");
     else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -653,7 +713,7 @@ __global__ __launch_bounds__(HD) void k_attn_global_merge(AttnP p, int splits, c
 namespace tsk {
 
 static AttnP make_params(const AttnArgs& a) {
-  return AttnP{a.qkv,       a.out,       a.part, a.rows, a.blk_nt, a.blk_tiles, a.blk_rows, a.blk_w, a.nblk, a.maxc,
+  return AttnP{a.qkv,       a.out,       a.part, a.rows, a.g0, a.gstep, a.blk_nt, a.blk_tiles, a.blk_rows, a.blk_w, a.nblk, a.maxc,
                a.n_union,   a.d,         a.H,    a.n_tiles,        a.n,
                1.4426950408889634f / sqrtf(float(a.hd)),           a.amax};
 }
@@ -661,7 +721,7 @@ static AttnP make_params(const AttnArgs& a) {
 hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
   const AttnP p = make_params(a);
   const bool blend = a.blk_nt != nullptr;
-  if (a.n < 1 || (blend && (!a.rows || a.nblk < 1))) return hipErrorInvalidValue;
+  if (a.n < 1 || !a.rows || (blend && a.nblk < 1)) return hipErrorInvalidValue;
   const int nqb = (a.n + QB - 1) / QB;
   const int njob = blend ? a.nblk : nqb * a.n_tiles;
   if (act == ACT_F32) {

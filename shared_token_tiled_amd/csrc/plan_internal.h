@@ -35,6 +35,7 @@ struct ts_plan {
 
   // device copies (owned; void* to keep HIP out of this header)
   void* d_tile_rows = nullptr;   // int32 [n_tiles*n]
+  void* d_tile_rows_local = nullptr;  // int32 [n_tiles*n]: t*(n+1)+j, the rows of per-tile layouts
   void* d_cover_ptr = nullptr;   // int32 [n_union+1]
   void* d_entry_row = nullptr;   // int32 [n_entries]: t*(n+1)+local of each entry
   void* d_cover_w = nullptr;     // fp32 [n_entries]

@@ -88,18 +88,21 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
 // Query rows per attention workgroup, and per query block of the plan.
 constexpr int QBLOCK = 256;
 // q and k of qkv are as qk_prep left them (normalised, rotated by grid
-// coordinates).  Layouts (see attn.hip):
-//  - rows == null: per-tile qkv rows t*(n+1)+i; outputs in the same rows;
-//  - rows != null, blk_nt == null: shared qkv rows [n_union + n_tiles] read
-//    through the tile map; outputs per tile, t*(n+1)+i;
-//  - rows and blk_nt != null: shared qkv rows; every grid row's outputs of
-//    the windows of its query block blended with the block's weights, written
-//    to out row p (global rows: out row n_union + t).
+// coordinates).  Window token j of tile t is qkv row rows[t*n + j], its global
+// token row g0 + gstep*t.  Layouts (see attn.hip):
+//  - per tile: rows[t*n + j] = t*(n+1)+j, g0 = n, gstep = n+1; outputs in
+//    the same rows;
+//  - shared rows (blk_nt == null): the tile map into [n_union + n_tiles]
+//    rows, g0 = n_union, gstep = 1; outputs per tile, t*(n+1)+i;
+//  - blended (blk_nt != null): shared rows; every grid row's outputs of the
+//    windows of its query block blended with the block's weights, written to
+//    out row p (global rows: out row n_union + t).
 struct AttnArgs {
   const void* qkv;          // [rows, 3d] act
   void* out;                // act, rows as above
   float* part = nullptr;    // blended: fp32 [n_union, d] partial sums between windows
-  const int* rows = nullptr;       // [n_tiles*n] grid rows of each tile's tokens
+  const int* rows = nullptr;       // [n_tiles*n] qkv row of each tile's tokens
+  int g0 = 0, gstep = 0;           // qkv row of tile t's global token: g0 + gstep*t
   const int* blk_nt = nullptr;     // [nblk] windows of each query block
   const int* blk_tiles = nullptr;  // [nblk*maxc] their tiles, ascending
   const int* blk_rows = nullptr;   // [nblk*QBLOCK] grid row of each query slot (-1: empty)
