@@ -311,6 +311,22 @@ ts_status ts_op_attention(const ts_model_desc* model, const ts_plan* plan, int32
                           const float* q_g, const float* k_g, void* out, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * serving loops, harnesses that forbid hipMalloc): ts_op_attention with no
+ * workspace argument.  Its scratch -- the fp32 partial blends of the shared
+ * layout (n_union * d * 4 bytes) and the global rows' split states -- lives
+ * in a file-scope device array of TS_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds until the process ends; the call allocates nothing.
+ * A request whose partial blends exceed the array returns TS_EWORKSPACE
+ * (the per-tile layout, shared = 0, needs none).  All calls on one GPU share
+ * its array: calls that overlap on one GPU (on different streams, or from
+ * different threads) race and must be serialised by the caller.  Nothing in
+ * the array needs to start at zero.  Arguments and results as
+ * ts_op_attention. */
+#define TS_NOALLOC_SCRATCH_BYTES (64u << 20)
+ts_status ts_op_attention_noalloc(const ts_model_desc* model, const ts_plan* plan, int32_t shared, void* qkv,
+                                  const float* q_g, const float* k_g, void* out, void* stream);
+
 /* ---- diagnostics ------------------------------------------------------- */
 /* Per-kernel timing of the calling thread's forward calls.  Between
  * ts_profile_begin and ts_profile_end every kernel the library launches is

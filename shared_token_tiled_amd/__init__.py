@@ -98,6 +98,8 @@ def lib():
                                                ctypes.c_size_t, _VP]),
             "ts_op_attention": (ctypes.c_int32, [P(ModelDesc), _VP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,
                                                  ctypes.c_size_t, _VP]),
+            "ts_op_attention_noalloc": (ctypes.c_int32, [P(ModelDesc), _VP, ctypes.c_int32, _VP, _VP, _VP, _VP,
+                                                         _VP]),
             "ts_profile_begin": (ctypes.c_int32, []),
             "ts_profile_end": (ctypes.c_int32, [P(KernelStat), ctypes.c_int32, P(ctypes.c_int32)]),
         }
@@ -272,6 +274,17 @@ def ts_op_attention(model, plan, shared, qkv, q_g, k_g, out, ws, stream=None):
     _check(lib().ts_op_attention(ctypes.byref(model), plan, 1 if shared else 0, _ptr(qkv), _ptr(q_g), _ptr(k_g),
                                  _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "ts_op_attention")
+
+
+TS_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def ts_op_attention_noalloc(model, plan, shared, qkv, q_g, k_g, out, stream=None):
+    """ts_op_attention without a workspace: its scratch is the library's own
+    device array (TS_NOALLOC_SCRATCH_BYTES per GPU); calls that overlap on one
+    GPU race."""
+    _check(lib().ts_op_attention_noalloc(ctypes.byref(model), plan, 1 if shared else 0, _ptr(qkv), _ptr(q_g),
+                                         _ptr(k_g), _ptr(out), _stream(stream)), "ts_op_attention_noalloc")
 
 
 def ts_profile_begin():

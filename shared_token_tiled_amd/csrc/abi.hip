@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -647,6 +648,55 @@ ts_status partial_share_impl(const ts_model_desc* m, const ts_layer_weights* lay
   return TS_OK;
 }
 
+ts_status check_op_attention(const ts_model_desc* m, const ts_plan* p, void* qkv, const float* q_g,
+                             const float* k_g, void* out) {
+  ts_status st;
+  if ((st = check_model(m)) != TS_OK) return st;
+  if ((st = check_plan(p, m)) != TS_OK) return st;
+  if (!qkv || !out) return fail(TS_EINVAL, "qkv and out must be non-null");
+  if (m->qk_norm && (!q_g || !k_g)) return fail(TS_EINVAL, "QK-norm needs q_g and k_g");
+  return TS_OK;
+}
+
+// The attention step on caller rows: qk_prep in place, then the window
+// attention (blended when shared), with the partial blends in `part` (fp32
+// [n_union, d], shared only) and the global rows' split states in gpart.
+ts_status op_attention_impl(const ts_model_desc* m, const ts_plan* p, bool shared, void* qkv, const float* q_g,
+                            const float* k_g, void* out, float* part, float* gpart, int64_t gpart_floats,
+                            hipStream_t s) {
+  const int64_t M = shared ? int64_t(p->n_union) + p->n_tiles : int64_t(p->n_tiles) * (p->n + 1);
+  {
+    Scope sc(s, "qk_prep", 0.0, double(M * 2 * m->d) * 2 * act_bytes(m->act_dtype));
+    TS_HIP(tsk::qk_prep(s, m->act_dtype, qkv, int(M), m->d, m->n_heads, m->head_dim, m->qk_norm ? q_g : nullptr, k_g,
+                        m->eps, rope_rows(p, shared)),
+           "qk_prep");
+  }
+  return window_attention(m, p, shared ? ATT_BLENDED : ATT_TILED, qkv, out, part, nullptr, s, gpart, gpart_floats);
+}
+
+// ---- scratch of the no-allocation entry point --------------------------
+// A file-scope device array: every GPU the library runs on holds its own
+// copy until the process ends.  In host code its name is not a device
+// address; the address is taken once per device with hipGetSymbolAddress
+// (with that device current) and kept.
+__device__ __align__(256) unsigned char scratch[TS_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+std::map<int, char*> g_scratch_ptr;
+
+ts_status noalloc_scratch(char** out) {
+  int dev = 0;
+  TS_HIP(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    TS_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    it = g_scratch_ptr.emplace(dev, (char*)ptr).first;
+  }
+  *out = it->second;
+  return TS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -894,23 +944,29 @@ ts_status ts_op_gemm_ws(int32_t dtype, int32_t epilogue, const void* a, const vo
 ts_status ts_op_attention(const ts_model_desc* m, const ts_plan* p, int32_t shared, void* qkv, const float* q_g,
                           const float* k_g, void* out, void* ws, size_t ws_bytes, void* stream) {
   ts_status st;
-  if ((st = check_model(m)) != TS_OK) return st;
-  if ((st = check_plan(p, m)) != TS_OK) return st;
-  if (!qkv || !out) return fail(TS_EINVAL, "qkv and out must be non-null");
-  if (m->qk_norm && (!q_g || !k_g)) return fail(TS_EINVAL, "QK-norm needs q_g and k_g");
+  if ((st = check_op_attention(m, p, qkv, q_g, k_g, out)) != TS_OK) return st;
   WS w0 = layout(m, p, false, false, false, nullptr);
   if ((st = check_ws(ws, ws_bytes, w0.bytes)) != TS_OK) return st;
   WS w = layout(m, p, false, false, false, (char*)ws);
-  hipStream_t s = (hipStream_t)stream;
-  const int64_t M = shared ? int64_t(p->n_union) + p->n_tiles : int64_t(p->n_tiles) * (p->n + 1);
-  {
-    Scope sc(s, "qk_prep", 0.0, double(M * 2 * m->d) * 2 * act_bytes(m->act_dtype));
-    TS_HIP(tsk::qk_prep(s, m->act_dtype, qkv, int(M), m->d, m->n_heads, m->head_dim, m->qk_norm ? q_g : nullptr, k_g,
-                        m->eps, rope_rows(p, shared != 0)),
-           "qk_prep");
-  }
-  return window_attention(m, p, shared ? ATT_BLENDED : ATT_TILED, qkv, out, (float*)w.o, nullptr, s, w.gpart,
-                          w.gpart_floats);
+  return op_attention_impl(m, p, shared != 0, qkv, q_g, k_g, out, (float*)w.o, w.gpart, w.gpart_floats,
+                           (hipStream_t)stream);
+}
+
+ts_status ts_op_attention_noalloc(const ts_model_desc* m, const ts_plan* p, int32_t shared, void* qkv,
+                                  const float* q_g, const float* k_g, void* out, void* stream) {
+  ts_status st;
+  if ((st = check_op_attention(m, p, qkv, q_g, k_g, out)) != TS_OK) return st;
+  // the fp32 partial blends of the shared layout first, the global rows'
+  // split states in the rest (the split count shrinks to what fits)
+  const size_t part_bytes = shared ? align256(size_t(p->n_union) * m->d * 4) : 0;
+  if (part_bytes > TS_NOALLOC_SCRATCH_BYTES)
+    return fail(TS_EWORKSPACE, "ts_op_attention_noalloc: the partial blends need " + std::to_string(part_bytes) +
+                                   " bytes; its scratch holds " + std::to_string(TS_NOALLOC_SCRATCH_BYTES));
+  char* base = nullptr;
+  if ((st = noalloc_scratch(&base)) != TS_OK) return st;
+  const int64_t gfloats = int64_t((TS_NOALLOC_SCRATCH_BYTES - part_bytes) / 4);
+  return op_attention_impl(m, p, shared != 0, qkv, q_g, k_g, out, (float*)base, (float*)(base + part_bytes),
+                           gfloats, (hipStream_t)stream);
 }
 
 ts_status ts_profile_begin(void) {
