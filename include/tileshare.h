@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define TS_ABI_VERSION 5
+#define TS_ABI_VERSION 6
 
 typedef int32_t ts_status;
 #define TS_OK 0
@@ -118,6 +118,16 @@ ts_status ts_plan_export_rope(const ts_plan* plan, int32_t head_dim, float rope_
  * [nblk*maxc*256] (w-bar of (block, tile, slot), 0 in empty slots). */
 ts_status ts_plan_export_blocks(const ts_plan* plan, int32_t* nblk, int32_t* maxc, int32_t* blk_nt,
                                 int32_t* blk_tiles, int32_t* blk_rows, float* blk_w);
+/* The order in which the bf16 blended attention takes its (block, head)
+ * jobs; it decides speed only, never a value.  Each head's blocks are split
+ * in two halves of equal work (windows): every class of blocks with the same
+ * number of windows is cut at its middle, an odd block going to the half
+ * with less work so far.  order [nblk] (caller-owned host buffer) lists half
+ * A then half B, each class by class from the most windows down, blocks
+ * ascending; cls [ncls*4] holds per class {count in A, offset of those in
+ * order, count in B, offset}.  *ncls receives the class count; the arrays
+ * may be NULL. */
+ts_status ts_plan_export_job_order(const ts_plan* plan, int32_t* ncls, int32_t* order, int32_t* cls);
 /* Upload the maps, the attention's query blocks (grid rows grouped by the
  * tiles that hold them with a nonzero w-bar) and the grid-coordinate RoPE
  * table for (head_dim, rope_base) to device memory owned by the plan (the

@@ -56,7 +56,7 @@ class TileShareError(RuntimeError):
 
 
 _lib = None
-ABI_VERSION = 5   # the layout of the structs below; a library of another version is refused
+ABI_VERSION = 6   # the layout of the structs below; a library of another version is refused
 
 
 def lib():
@@ -75,6 +75,7 @@ def lib():
             "ts_plan_export": (ctypes.c_int32, [_VP] + [_VP] * 6),
             "ts_plan_export_rope": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_float, _VP, _VP]),
             "ts_plan_export_blocks": (ctypes.c_int32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+            "ts_plan_export_job_order": (ctypes.c_int32, [_VP, _VP, _VP, _VP]),
             "ts_plan_upload": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_float, _VP]),
             "ts_plan_destroy": (None, [_VP]),
             "ts_workspace_size": (ctypes.c_int32, [P(ModelDesc), _VP, ctypes.c_int32, P(ctypes.c_size_t)]),
@@ -188,6 +189,20 @@ def ts_plan_export_blocks(plan):
     _check(lib().ts_plan_export_blocks(plan, None, None, *(a.ctypes.data_as(_VP) for a in (nt, tl, rw, w))),
            "ts_plan_export_blocks")
     return nt, tl, rw, w
+
+
+def ts_plan_export_job_order(plan):
+    """Return numpy arrays (order [nblk], cls [ncls, 4]) of the blended attention's job order."""
+    import numpy as np
+    nc = ctypes.c_int32()
+    _check(lib().ts_plan_export_job_order(plan, ctypes.byref(nc), None, None), "ts_plan_export_job_order")
+    nb = ctypes.c_int32()
+    _check(lib().ts_plan_export_blocks(plan, ctypes.byref(nb), None, None, None, None, None), "ts_plan_export_blocks")
+    order = np.empty(nb.value, np.int32)
+    cls = np.empty((nc.value, 4), np.int32)
+    _check(lib().ts_plan_export_job_order(plan, None, order.ctypes.data_as(_VP), cls.ctypes.data_as(_VP)),
+           "ts_plan_export_job_order")
+    return order, cls
 
 
 def ts_plan_upload(plan, head_dim, rope_base=10000.0, stream=None):

@@ -293,6 +293,10 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, AttnLayout 
     a.blk_w = (const float*)p->d_blk_w;
     a.nblk = p->nblk;
     a.maxc = p->blk_maxc;
+    a.blk_order = (const int*)p->d_blk_order;
+    a.blk_cls = (const int*)p->d_blk_cls;
+    a.ncls = p->blk_ncls;
+    a.half_a = p->blk_ncls ? p->blk_cls[4 * (p->blk_ncls - 1)] + p->blk_cls[4 * (p->blk_ncls - 1) + 1] : 0;
   }
   a.n_union = p->n_union;
   a.d = m->d;
@@ -768,10 +772,18 @@ ts_status ts_plan_export_blocks(const ts_plan* p, int32_t* nblk, int32_t* maxc, 
   return TS_OK;
 }
 
+ts_status ts_plan_export_job_order(const ts_plan* p, int32_t* ncls, int32_t* order, int32_t* cls) {
+  if (!p) return fail(TS_EINVAL, "plan is null");
+  if (ncls) *ncls = p->blk_ncls;
+  if (order) std::memcpy(order, p->blk_order.data(), p->blk_order.size() * 4);
+  if (cls) std::memcpy(cls, p->blk_cls.data(), p->blk_cls.size() * 4);
+  return TS_OK;
+}
+
 static void free_device(ts_plan* p) {
   void** ptrs[] = {&p->d_tile_rows, &p->d_tile_rows_local, &p->d_cover_ptr, &p->d_entry_row, &p->d_cover_w, &p->d_local_pos,
                    &p->d_rope_glob, &p->d_tile_start, &p->d_blk_nt,    &p->d_blk_tiles, &p->d_blk_rows,
-                   &p->d_blk_w};
+                   &p->d_blk_w,    &p->d_blk_order, &p->d_blk_cls};
   for (void** q : ptrs) {
     if (*q) (void)hipFree(*q);
     *q = nullptr;
@@ -811,6 +823,8 @@ ts_status ts_plan_upload(ts_plan* p, int32_t head_dim, float rope_base, void* st
       {&p->d_blk_tiles, p->blk_tiles.data(), p->blk_tiles.size() * 4},
       {&p->d_blk_rows, p->blk_rows.data(), p->blk_rows.size() * 4},
       {&p->d_blk_w, p->blk_w.data(), p->blk_w.size() * 4},
+      {&p->d_blk_order, p->blk_order.data(), p->blk_order.size() * 4},
+      {&p->d_blk_cls, p->blk_cls.data(), p->blk_cls.size() * 4},
   };
   for (auto& it : items) {
     if (hipMalloc(it.dst, std::max<size_t>(it.bytes, 4)) != hipSuccess) {

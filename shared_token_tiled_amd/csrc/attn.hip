@@ -54,6 +54,9 @@ struct AttnP {
   const int* blk_rows;
   const float* blk_w;
   int nblk, maxc;
+  const int* blk_order;
+  const int* blk_cls;
+  int ncls;
   int n_union, d, H, n_tiles, n;
   float scale_log2;  // log2(e) / sqrt(hd)
   unsigned* amax;
@@ -215,6 +218,51 @@ __device__ __forceinline__ bf16x8 v_fragment(const char* lo, const char* hi) {
   return __builtin_bit_cast(bf16x8, c);
 }
 
+// Halves of heads dealt to XCD x: the 2H halves (u = 2 head + {0: A, 1: B})
+// cut into 8 contiguous runs; na, nb count the A and B halves of the run.
+struct HalfRange {
+  int u0, nu, na, nb;
+};
+__host__ __device__ __forceinline__ HalfRange xcd_halves(int H, int x) {
+  const int U = 2 * H, q8 = U >> 3, r8 = U & 7;
+  HalfRange r;
+  r.u0 = x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8;
+  r.nu = q8 + (x < r8 ? 1 : 0);
+  r.na = (r.nu + ((r.u0 & 1) ? 0 : 1)) >> 1;
+  r.nb = r.nu - r.na;
+  return r;
+}
+
+// Blended job (block, head) of workgroup b, false for a spare workgroup.
+// XCD b % 8 holds a contiguous run of half-heads (two halves of equal work
+// per head, so the runs carry equal work), which keeps the keys and values it
+// streams to a few heads: together the XCDs touch each head's K and V about
+// once.  Within the run the jobs go class by class, most windows first, so
+// the XCD's CUs finish together; within a class, half by half, blocks
+// ascending (neighbouring rows, the same windows).  All values are uniform.
+__device__ __forceinline__ bool blend_job(const AttnP& p, int b, int& blk, int& h) {
+  const HalfRange r = xcd_halves(p.H, b & 7);
+  int rem = b >> 3;
+  for (int c = 0; c < p.ncls; ++c) {
+    const int ca = p.blk_cls[4 * c], oa = p.blk_cls[4 * c + 1];
+    const int cb = p.blk_cls[4 * c + 2], ob = p.blk_cls[4 * c + 3];
+    const int m = r.na * ca + r.nb * cb;
+    if (rem < m) {
+      for (int u = r.u0;; ++u) {  // ends: the counts of the run's halves sum to m > rem
+        const int cnt = (u & 1) ? cb : ca;
+        if (rem < cnt) {
+          blk = p.blk_order[((u & 1) ? ob : oa) + rem];
+          h = u >> 1;
+          return true;
+        }
+        rem -= cnt;
+      }
+    }
+    rem -= m;
+  }
+  return false;
+}
+
 template <int HD, bool BLEND>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(AttnP p) {
   constexpr int KROWB = HD * 2;       // bytes per staged key row
@@ -238,14 +286,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // Job order.  The hardware deals workgroup b to XCD b % 8.  Per tile: give
   // each XCD a contiguous run of jobs, the query blocks of one (tile, head),
   // which stream the same keys and values through that XCD's L2.  Blended:
-  // jobs run from the plan's longest blocks (most windows) to its shortest,
-  // (block, head) with the head fastest, dealt round-robin: every XCD gets the
-  // same mix of lengths, longest first, and the heads it holds of consecutive
-  // blocks of one tile group share their windows in L2.
-  int h, t0 = 0, qblk = 0, blk = 0, npass = 1;
+  // see blend_job.
+  int h = 0, t0 = 0, qblk = 0, blk = 0, npass = 1;
   if constexpr (BLEND) {
-    blk = blockIdx.x / p.H;
-    h = blockIdx.x % p.H;
+    if (!blend_job(p, blockIdx.x, blk, h)) return;  // a spare workgroup (whole workgroup)
     npass = p.blk_nt[blk];
   } else {
     const int total = nqb * p.n_tiles * p.H;
@@ -339,8 +383,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       const bf16x8 kg = *reinterpret_cast<const bf16x8*>(kgp + 16 * s + 8 * g);
+      // q opaque here: its fp32 copy (64 registers) would otherwise be made
+      // once and held across every window
+      bf16x8 q = qf[s];
+      asm volatile("" : "+v"(q));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sg += float(qf[s][e]) * float(kg[e]);
+      for (int e = 0; e < 8; ++e) sg += float(q[e]) * float(kg[e]);
     }
     sg += __shfl_xor(sg, 32, 64);
     m_run = sg * C;
@@ -714,6 +762,7 @@ namespace tsk {
 
 static AttnP make_params(const AttnArgs& a) {
   return AttnP{a.qkv,       a.out,       a.part, a.rows, a.g0, a.gstep, a.blk_nt, a.blk_tiles, a.blk_rows, a.blk_w, a.nblk, a.maxc,
+               a.blk_order, a.blk_cls,   a.ncls,
                a.n_union,   a.d,         a.H,    a.n_tiles,        a.n,
                1.4426950408889634f / sqrtf(float(a.hd)),           a.amax};
 }
@@ -737,7 +786,19 @@ hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
 #undef TS_F32A
     return hipGetLastError();
   }
-  const dim3 grid(njob * a.H), block(NW * 64);
+  int nwg = njob * a.H;
+  if (blend) {
+    // every XCD is dealt the same number of workgroups; the XCD with the
+    // most jobs sets it, the others' spare workgroups exit
+    if (!a.blk_order || !a.blk_cls || a.ncls < 1) return hipErrorInvalidValue;
+    int most = 0;
+    for (int x = 0; x < 8; ++x) {
+      const HalfRange r = xcd_halves(a.H, x);
+      most = std::max(most, r.na * a.half_a + r.nb * (a.nblk - a.half_a));
+    }
+    nwg = 8 * most;
+  }
+  const dim3 grid(nwg), block(NW * 64);
 #define TS_BFA(HD)                                                                 \
   do {                                                                             \
     if (blend) hipLaunchKernelGGL((k_attn_bf16<HD, true>), grid, block, 0, s, p); \

@@ -87,6 +87,26 @@ static void build_blocks(ts_plan& p) {
       }
     }
   }
+  // halves of equal work; blocks are already ordered by decreasing windows,
+  // so a class is a run of block indices
+  std::vector<int32_t> ha, hb, cls;
+  int64_t work_a = 0, work_b = 0;
+  for (int32_t b0 = 0; b0 < p.nblk;) {
+    int32_t b1 = b0;
+    while (b1 < p.nblk && p.blk_nt[b1] == p.blk_nt[b0]) ++b1;
+    const int32_t cnt = b1 - b0, w = p.blk_nt[b0];
+    const int32_t ka = cnt / 2 + ((cnt & 1) && work_a <= work_b ? 1 : 0);
+    cls.insert(cls.end(), {ka, int32_t(ha.size()), cnt - ka, int32_t(hb.size())});
+    for (int32_t b = b0; b < b1; ++b) (b < b0 + ka ? ha : hb).push_back(b);
+    work_a += int64_t(ka) * w;
+    work_b += int64_t(cnt - ka) * w;
+    b0 = b1;
+  }
+  p.blk_ncls = int32_t(cls.size() / 4);
+  for (int32_t c = 0; c < p.blk_ncls; ++c) cls[4 * c + 3] += int32_t(ha.size());
+  p.blk_order = ha;
+  p.blk_order.insert(p.blk_order.end(), hb.begin(), hb.end());
+  p.blk_cls = cls;
 }
 
 std::string build(const ts_tiling_desc& d, ts_plan& p) {

@@ -32,6 +32,15 @@ struct ts_plan {
   std::vector<int32_t> blk_tiles;    // [nblk*blk_maxc] those tiles, ascending (padding -1)
   std::vector<int32_t> blk_rows;     // [nblk*TS_QBLOCK] grid row of each slot (-1: empty)
   std::vector<float> blk_w;          // [nblk*blk_maxc*TS_QBLOCK] w-bar of (block, tile i, slot)
+  // Job order of the blended attention.  Each head's blocks are split in two
+  // halves of equal work (windows), A and B; every class of blocks with the
+  // same number of windows is cut at its middle, the odd block going to the
+  // half with less work.  blk_order lists half A then half B, each class by
+  // class from the most windows down, blocks ascending; blk_cls holds, per
+  // class, {count in A, offset in blk_order, count in B, offset}.
+  int32_t blk_ncls = 0;
+  std::vector<int32_t> blk_order;    // [nblk]
+  std::vector<int32_t> blk_cls;      // [blk_ncls*4]
 
   // device copies (owned; void* to keep HIP out of this header)
   void* d_tile_rows = nullptr;   // int32 [n_tiles*n]
@@ -46,6 +55,8 @@ struct ts_plan {
   void* d_blk_tiles = nullptr;
   void* d_blk_rows = nullptr;
   void* d_blk_w = nullptr;
+  void* d_blk_order = nullptr;
+  void* d_blk_cls = nullptr;
   int32_t rope_glob_off[3] = {0, 0, 0};
   int32_t rope_hd = 0;
   float rope_base = 0.f;

@@ -108,6 +108,9 @@ struct AttnArgs {
   const int* blk_rows = nullptr;   // [nblk*QBLOCK] grid row of each query slot (-1: empty)
   const float* blk_w = nullptr;    // [nblk*maxc*QBLOCK] w-bar of (block, window, slot)
   int nblk = 0, maxc = 0;
+  const int* blk_order = nullptr;  // [nblk] blocks of the halves A, B of a head (bf16 job order)
+  const int* blk_cls = nullptr;    // [ncls*4] per class of equal windows: count, offset in A; in B
+  int ncls = 0, half_a = 0;        // classes; blocks in half A (half B: nblk - half_a)
   int n_union, d, H, hd, n_tiles, n;
   unsigned* amax = nullptr;        // optional (bf16): max |out| as stored
 };

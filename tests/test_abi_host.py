@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
-    assert ts.ts_abi_version() == 5
+    assert ts.ts_abi_version() == 6
 
 
 PLAN_CASES = [(configs.get(n)["ndim"], configs.get(n)["grid"], configs.get(n)["tile"], configs.get(n)["stride"])
@@ -203,3 +203,58 @@ def test_large_tiles_plan_and_rope_export():
         assert np.array_equal(s.view(np.uint32), rs.view(np.uint32))
     finally:
         ts.ts_plan_destroy(h)
+
+
+def _xcd_jobs(order, cls, H, x):
+    """The (block, head) jobs XCD x takes, in order: its contiguous run of
+    the 2H half-heads (u = 2 head + half), class by class, half by half."""
+    U = 2 * H
+    q8, r8 = divmod(U, 8)
+    u0 = x * (q8 + 1) if x < r8 else r8 * (q8 + 1) + (x - r8) * q8
+    nu = q8 + (1 if x < r8 else 0)
+    jobs = []
+    for ca, oa, cb, ob in cls:
+        for u in range(u0, u0 + nu):
+            cnt, off = (cb, ob) if u & 1 else (ca, oa)
+            jobs += [(int(order[off + i]), u >> 1) for i in range(cnt)]
+    return jobs
+
+
+@pytest.mark.parametrize("ndim,grid,tile,stride", PLAN_CASES + [
+    (3, (8, 44, 80), (8, 32, 32), (8, 24, 24)), (2, (1, 135, 240), (1, 64, 64), (1, 48, 48)),
+    (3, (4, 44, 80), (4, 44, 44), (4, 36, 36))])
+def test_blended_job_order_covers_every_job_once(ndim, grid, tile, stride):
+    """The job order of the bf16 blended attention: the two halves of a head
+    are a partition of its blocks with work (windows) equal up to one block,
+    classes run from the most windows down, and the workgroups the launcher
+    starts (8 x the most jobs of an XCD, dealt round-robin to the XCDs) take
+    every (block, head) exactly once."""
+    h = ts.ts_plan_create(ndim, grid, tile, stride)
+    try:
+        nt = ts.ts_plan_export_blocks(h)[0]
+        order, cls = ts.ts_plan_export_job_order(h)
+    finally:
+        ts.ts_plan_destroy(h)
+    nblk = len(nt)
+    assert sorted(order.tolist()) == list(range(nblk))
+    na = int(cls[:, 0].sum())
+    assert np.all(cls[:, 1] == np.concatenate([[0], np.cumsum(cls[:-1, 0])]))
+    assert np.all(cls[:, 3] == na + np.concatenate([[0], np.cumsum(cls[:-1, 2])]))
+    works = []
+    for half, (ci, oi) in enumerate(((0, 1), (2, 3))):
+        prev_w, work = None, 0
+        for c in cls:
+            blocks = order[c[oi]:c[oi] + c[ci]]
+            if len(blocks):
+                w = set(nt[blocks].tolist())
+                assert len(w) == 1 and (prev_w is None or w.pop() < prev_w)
+                prev_w = int(nt[blocks[0]])
+                assert np.all(np.diff(blocks) > 0)
+                work += prev_w * len(blocks)
+        works.append(work)
+    assert abs(works[0] - works[1]) <= int(nt.max())
+    for H in (1, 2, 3, 12, 16, 20):
+        per_xcd = [_xcd_jobs(order, cls, H, x) for x in range(8)]
+        nwg = 8 * max(len(j) for j in per_xcd)
+        taken = [per_xcd[b % 8][b // 8] for b in range(nwg) if b // 8 < len(per_xcd[b % 8])]
+        assert sorted(taken) == sorted((b, hh) for b in range(nblk) for hh in range(H))
