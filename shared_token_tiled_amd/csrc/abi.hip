@@ -149,6 +149,7 @@ struct WS {
   float* gpart = nullptr;    // fp32 split states of the global-token attention rows
   int64_t gpart_floats = 0;
   float* gsplit = nullptr;   // fp32 K-split parts of a GEMM's partial last round of tiles
+  unsigned* jobs = nullptr;  // job counters of the blended attention
   size_t bytes = 0;
 };
 
@@ -186,6 +187,7 @@ WS layout(const ts_model_desc* m, const ts_plan* p, bool states, bool per_tile, 
     w.gpart = (float*)take(size_t(w.gpart_floats * 4));
   }
   if (m->act_dtype != TS_F32) w.gsplit = (float*)take(TS_GEMM_SPLIT_WS_BYTES);
+  if (m->act_dtype == TS_BF16) w.jobs = (unsigned*)take(tsk::JOB_COUNTERS_BYTES);
   w.bytes = off;
   return w;
 }
@@ -272,10 +274,11 @@ tsk::RopeRows rope_rows(const ts_plan* p, bool shared) {
 // ATT_SHARED_ROWS (shared qkv rows read through the tile map, per-tile
 // outputs: layer 0 once per token), ATT_BLENDED (shared qkv rows, outputs
 // blended with w-bar into [n_union + n_tiles] rows; `part` holds the fp32
-// partial blends).  amax (optional, bf16): max |output| as stored.
+// partial blends; `jobs`, bf16 only, the job counters).  amax (optional,
+// bf16): max |output| as stored.
 enum AttnLayout { ATT_TILED, ATT_SHARED_ROWS, ATT_BLENDED };
 ts_status window_attention(const ts_model_desc* m, const ts_plan* p, AttnLayout lay, const void* qkv, void* out,
-                           float* part, unsigned* amax, hipStream_t s, float* gscratch = nullptr,
+                           float* part, unsigned* jobs, unsigned* amax, hipStream_t s, float* gscratch = nullptr,
                            int64_t gscratch_floats = 0) {
   tsk::AttnArgs a;
   a.qkv = qkv;
@@ -296,6 +299,7 @@ ts_status window_attention(const ts_model_desc* m, const ts_plan* p, AttnLayout 
     a.blk_order = (const int*)p->d_blk_order;
     a.blk_cls = (const int*)p->d_blk_cls;
     a.ncls = p->blk_ncls;
+    a.jobs = jobs;
     a.half_a = p->blk_ncls ? p->blk_cls[4 * (p->blk_ncls - 1)] + p->blk_cls[4 * (p->blk_ncls - 1) + 1] : 0;
   }
   a.n_union = p->n_union;
@@ -380,7 +384,8 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
   if (am_out) TS_HIP(tsk::zero_amax(c.s, am_out), "amax reset");
   const void* aout = shared ? ws.h : ws.o;
   if ((st = window_attention(m, p, shared ? ATT_BLENDED : (qsh ? ATT_SHARED_ROWS : ATT_TILED), ws.big,
-                             const_cast<void*>(aout), (float*)ws.o, am_out, c.s, ws.gpart, ws.gpart_floats)) != TS_OK)
+                             const_cast<void*>(aout), (float*)ws.o, ws.jobs, am_out, c.s, ws.gpart,
+                             ws.gpart_floats)) != TS_OK)
     return st;
   if ((st = proj(c, ws, (f8 & TS_FP8_OUT) != 0, "out", tsk::EPI_RESID, aout, M, d, d, w.w_o, w.w_o_f8,
                  w.w_scale_f8 ? w.w_scale_f8 + 1 : nullptr, w.b_o, x, am_out != nullptr)) != TS_OK)
@@ -447,8 +452,8 @@ ts_status run_layer_partial(const Ctx& c, const ts_layer_weights& w, float* X, i
                         rope_rows(p, sq)),
            "qk_prep");
   }
-  if ((st = window_attention(m, p, sq ? ATT_SHARED_ROWS : ATT_TILED, ws.big, ws.o, nullptr, nullptr, c.s, ws.gpart,
-                             ws.gpart_floats)) != TS_OK)
+  if ((st = window_attention(m, p, sq ? ATT_SHARED_ROWS : ATT_TILED, ws.big, ws.o, nullptr, nullptr, nullptr, c.s,
+                             ws.gpart, ws.gpart_floats)) != TS_OK)
     return st;
   // out-projection
   if (so) {
@@ -666,8 +671,8 @@ ts_status check_op_attention(const ts_model_desc* m, const ts_plan* p, void* qkv
 // attention (blended when shared), with the partial blends in `part` (fp32
 // [n_union, d], shared only) and the global rows' split states in gpart.
 ts_status op_attention_impl(const ts_model_desc* m, const ts_plan* p, bool shared, void* qkv, const float* q_g,
-                            const float* k_g, void* out, float* part, float* gpart, int64_t gpart_floats,
-                            hipStream_t s) {
+                            const float* k_g, void* out, float* part, unsigned* jobs, float* gpart,
+                            int64_t gpart_floats, hipStream_t s) {
   const int64_t M = shared ? int64_t(p->n_union) + p->n_tiles : int64_t(p->n_tiles) * (p->n + 1);
   {
     Scope sc(s, "qk_prep", 0.0, double(M * 2 * m->d) * 2 * act_bytes(m->act_dtype));
@@ -675,7 +680,8 @@ ts_status op_attention_impl(const ts_model_desc* m, const ts_plan* p, bool share
                         m->eps, rope_rows(p, shared)),
            "qk_prep");
   }
-  return window_attention(m, p, shared ? ATT_BLENDED : ATT_TILED, qkv, out, part, nullptr, s, gpart, gpart_floats);
+  return window_attention(m, p, shared ? ATT_BLENDED : ATT_TILED, qkv, out, part, jobs, nullptr, s, gpart,
+                          gpart_floats);
 }
 
 // ---- scratch of the no-allocation entry point --------------------------
@@ -962,7 +968,7 @@ ts_status ts_op_attention(const ts_model_desc* m, const ts_plan* p, int32_t shar
   WS w0 = layout(m, p, false, false, false, nullptr);
   if ((st = check_ws(ws, ws_bytes, w0.bytes)) != TS_OK) return st;
   WS w = layout(m, p, false, false, false, (char*)ws);
-  return op_attention_impl(m, p, shared != 0, qkv, q_g, k_g, out, (float*)w.o, w.gpart, w.gpart_floats,
+  return op_attention_impl(m, p, shared != 0, qkv, q_g, k_g, out, (float*)w.o, w.jobs, w.gpart, w.gpart_floats,
                            (hipStream_t)stream);
 }
 
@@ -970,17 +976,20 @@ ts_status ts_op_attention_noalloc(const ts_model_desc* m, const ts_plan* p, int3
                                   const float* q_g, const float* k_g, void* out, void* stream) {
   ts_status st;
   if ((st = check_op_attention(m, p, qkv, q_g, k_g, out)) != TS_OK) return st;
-  // the fp32 partial blends of the shared layout first, the global rows'
-  // split states in the rest (the split count shrinks to what fits)
+  // the job counters, then the fp32 partial blends of the shared layout, the
+  // global rows' split states in the rest (the split count shrinks to what
+  // fits)
+  const size_t jobs_bytes = tsk::JOB_COUNTERS_BYTES;
   const size_t part_bytes = shared ? align256(size_t(p->n_union) * m->d * 4) : 0;
-  if (part_bytes > TS_NOALLOC_SCRATCH_BYTES)
+  if (jobs_bytes + part_bytes > TS_NOALLOC_SCRATCH_BYTES)
     return fail(TS_EWORKSPACE, "ts_op_attention_noalloc: the partial blends need " + std::to_string(part_bytes) +
-                                   " bytes; its scratch holds " + std::to_string(TS_NOALLOC_SCRATCH_BYTES));
+                                   " bytes; its scratch holds " +
+                                   std::to_string(TS_NOALLOC_SCRATCH_BYTES - jobs_bytes));
   char* base = nullptr;
   if ((st = noalloc_scratch(&base)) != TS_OK) return st;
-  const int64_t gfloats = int64_t((TS_NOALLOC_SCRATCH_BYTES - part_bytes) / 4);
-  return op_attention_impl(m, p, shared != 0, qkv, q_g, k_g, out, (float*)base, (float*)(base + part_bytes),
-                           gfloats, (hipStream_t)stream);
+  const int64_t gfloats = int64_t((TS_NOALLOC_SCRATCH_BYTES - jobs_bytes - part_bytes) / 4);
+  return op_attention_impl(m, p, shared != 0, qkv, q_g, k_g, out, (float*)(base + jobs_bytes), (unsigned*)base,
+                           (float*)(base + jobs_bytes + part_bytes), gfloats, (hipStream_t)stream);
 }
 
 ts_status ts_profile_begin(void) {

@@ -37,6 +37,8 @@
 // form one stream of key blocks, so the staging runs on across windows.
 #include <algorithm>
 #include <cstdlib>
+#include <map>
+#include <mutex>
 
 #include "device_common.h"
 #include "ts_kernels.h"
@@ -56,7 +58,8 @@ struct AttnP {
   int nblk, maxc;
   const int* blk_order;
   const int* blk_cls;
-  int ncls;
+  int ncls, half_a;
+  unsigned* jobs;
   int n_union, d, H, n_tiles, n;
   float scale_log2;  // log2(e) / sqrt(hd)
   unsigned* amax;
@@ -233,13 +236,14 @@ __host__ __device__ __forceinline__ HalfRange xcd_halves(int H, int x) {
   return r;
 }
 
-// Blended job (block, head) of workgroup b, false for a spare workgroup.
-// XCD b % 8 holds a contiguous run of half-heads (two halves of equal work
-// per head, so the runs carry equal work), which keeps the keys and values it
-// streams to a few heads: together the XCDs touch each head's K and V about
-// once.  Within the run the jobs go class by class, most windows first, so
-// the XCD's CUs finish together; within a class, half by half, blocks
-// ascending (neighbouring rows, the same windows).  All values are uniform.
+// Blended job (block, head) number b >> 3 of XCD b % 8 (false past the
+// XCD's last job).  The XCD holds a contiguous run of half-heads (two halves
+// of equal work per head, so the runs carry equal work), which keeps the keys
+// and values it streams to a few heads: together the XCDs touch each head's
+// K and V about once.  Within the run the jobs go class by class, most
+// windows first, so the XCD's CUs finish together; within a class, half by
+// half, blocks ascending (neighbouring rows, the same windows).  All values
+// are uniform.
 __device__ __forceinline__ bool blend_job(const AttnP& p, int b, int& blk, int& h) {
   const HalfRange r = xcd_halves(p.H, b & 7);
   int rem = b >> 3;
@@ -277,352 +281,373 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(16))) char Ks[NST][KB * KROWB];
   __shared__ __attribute__((aligned(16))) char Vs[NST][KB * KROWB];
   __shared__ int idx_s[NSL][KB];
+  __shared__ int job_s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int n = p.n;
   const int nkb = (n + KB - 1) / KB;
   const int nqb = (n + QB - 1) / QB;
-  // Job order.  The hardware deals workgroup b to XCD b % 8.  Per tile: give
-  // each XCD a contiguous run of jobs, the query blocks of one (tile, head),
-  // which stream the same keys and values through that XCD's L2.  Blended:
-  // see blend_job.
-  int h = 0, t0 = 0, qblk = 0, blk = 0, npass = 1;
+  // Job order.  The hardware deals workgroup b to XCD b % 8.  Per tile: one
+  // job per workgroup, each XCD a contiguous run of jobs, the query blocks of
+  // one (tile, head), which stream the same keys and values through that
+  // XCD's L2.  Blended: one workgroup per CU slot, each taking jobs from its
+  // XCD's counter in the order blend_job gives until they run out.  Jobs
+  // differ in length (one to maxc windows), and the hardware hands out
+  // workgroups in order, each to a fixed shader engine of its XCD: a long
+  // job on one engine would hold back the launch of every later workgroup.
+  // Pulled jobs keep every CU busy until its XCD's list is done.
+  const int xcd = blockIdx.x & 7;
+  int njx = 0;  // blended: the XCD's job count
   if constexpr (BLEND) {
-    if (!blend_job(p, blockIdx.x, blk, h)) return;  // a spare workgroup (whole workgroup)
-    npass = p.blk_nt[blk];
-  } else {
-    const int total = nqb * p.n_tiles * p.H;
-    const int b = blockIdx.x, xcd = b & 7, loc = b >> 3;
-    const int q8 = total >> 3, r8 = total & 7;
-    const int id = xcd < r8 ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
+    const HalfRange xr = xcd_halves(p.H, xcd);
+    njx = xr.na * p.half_a + xr.nb * (p.nblk - p.half_a);
+  }
+  for (int it = 0;; ++it) {
+    int h = 0, t0 = 0, qblk = 0, blk = 0, npass = 1;
+    if constexpr (BLEND) {
+      // take the XCD's next job; every thread has read job_s before the job's
+      // first barrier, after which thread 0 may write it again
+      if (tid == 0) job_s = int(atomicAdd(p.jobs + 8 * xcd, 1u));
+      __syncthreads();
+      const int i = __builtin_amdgcn_readfirstlane(job_s);
+      if (i >= njx) break;
+      blend_job(p, 8 * i + xcd, blk, h);
+      npass = p.blk_nt[blk];
+    } else {
+      if (it > 0) break;
+      const int total = nqb * p.n_tiles * p.H;
+      const int loc = blockIdx.x >> 3;
+      const int q8 = total >> 3, r8 = total & 7;
+      const int id = xcd < r8 ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
+      {
+        qblk = id % nqb;
+        h = (id / nqb) % p.H;
+        t0 = id / (nqb * p.H);
+      }
+    }
+    const bf16* qkv = (const bf16*)p.qkv;
+    const int64_t ld = 3 * int64_t(p.d);
+    const bf16* kbase = qkv + p.d + h * HD;
+    const bf16* vbase = qkv + 2 * p.d + h * HD;
+    const int nblocks = npass * nkb;  // key blocks streamed over all windows
+    auto tile_of = [&](int ps) -> int {
+      if constexpr (BLEND) return p.blk_tiles[blk * p.maxc + ps];
+      else return t0;
+    };
+
+    // key rows of the first AHEAD blocks (row-map layouts)
+    if (tid < KB) {
+#pragma unroll
+      for (int b = 0; b < AHEAD; ++b)
+        if (b < nblocks) {
+          const int ps = b / nkb, kb = b - ps * nkb;
+          idx_s[b][tid] = p.rows[int64_t(tile_of(ps)) * n + min(kb * KB + tid, n - 1)];
+        }
+    }
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    // DMA staging in two steps: the key rows this lane's loads need (from the
+    // ring), then the loads, so that the ring can be refilled in between
+    auto dma_rows = [&](int gb, int (&rr)[KDI]) {
+#pragma unroll
+      for (int i = 0; i < KDI; ++i) {
+        const int row = ((wv * KDI + i) * 1024 + 16 * lane) / KROWB;
+        rr[i] = idx_s[gb % NSL][row];
+      }
+    };
+    auto dma = [&](int gb, const int (&rr)[KDI]) {
+      const int st = gb % NST;
+#pragma unroll
+      for (int i = 0; i < KDI; ++i) {
+        const int b = (wv * KDI + i) * 1024 + 16 * lane;
+        const int row = b / KROWB, slot = (b % KROWB) / 16;
+        __builtin_amdgcn_global_load_lds((const void*)(kbase + int64_t(rr[i]) * ld + (slot ^ kswz<HD>(row)) * 8),
+                                         (TS_LDS void*)(&Ks[st][(wv * KDI + i) * 1024]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vbase + int64_t(rr[i]) * ld + (slot ^ vswz<HD>(row)) * 8),
+                                         (TS_LDS void*)(&Vs[st][(wv * KDI + i) * 1024]), 16, 0, 0);
+      }
+    };
+
+    __syncthreads();  // ring slots ready
     {
-      qblk = id % nqb;
-      h = (id / nqb) % p.H;
-      t0 = id / (nqb * p.H);
+      int rr[KDI];
+#pragma unroll
+      for (int b = 0; b < DEPTH; ++b)
+        if (b < nblocks) {
+          dma_rows(b, rr);
+          dma(b, rr);
+        }
     }
-  }
-  const bf16* qkv = (const bf16*)p.qkv;
-  const int64_t ld = 3 * int64_t(p.d);
-  const bf16* kbase = qkv + p.d + h * HD;
-  const bf16* vbase = qkv + 2 * p.d + h * HD;
-  const int nblocks = npass * nkb;  // key blocks streamed over all windows
-  auto tile_of = [&](int ps) -> int {
-    if constexpr (BLEND) return p.blk_tiles[blk * p.maxc + ps];
-    else return t0;
-  };
 
-  // key rows of the first AHEAD blocks (row-map layouts)
-  if (tid < KB) {
-#pragma unroll
-    for (int b = 0; b < AHEAD; ++b)
-      if (b < nblocks) {
-        const int ps = b / nkb, kb = b - ps * nkb;
-        idx_s[b][tid] = p.rows[int64_t(tile_of(ps)) * n + min(kb * KB + tid, n - 1)];
-      }
-  }
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  // DMA staging in two steps: the key rows this lane's loads need (from the
-  // ring), then the loads, so that the ring can be refilled in between
-  auto dma_rows = [&](int gb, int (&rr)[KDI]) {
-#pragma unroll
-    for (int i = 0; i < KDI; ++i) {
-      const int row = ((wv * KDI + i) * 1024 + 16 * lane) / KROWB;
-      rr[i] = idx_s[gb % NSL][row];
-    }
-  };
-  auto dma = [&](int gb, const int (&rr)[KDI]) {
-    const int st = gb % NST;
-#pragma unroll
-    for (int i = 0; i < KDI; ++i) {
-      const int b = (wv * KDI + i) * 1024 + 16 * lane;
-      const int row = b / KROWB, slot = (b % KROWB) / 16;
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + int64_t(rr[i]) * ld + (slot ^ kswz<HD>(row)) * 8),
-                                       (TS_LDS void*)(&Ks[st][(wv * KDI + i) * 1024]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + int64_t(rr[i]) * ld + (slot ^ vswz<HD>(row)) * 8),
-                                       (TS_LDS void*)(&Vs[st][(wv * KDI + i) * 1024]), 16, 0, 0);
-    }
-  };
-
-  __syncthreads();  // ring slots ready
-  {
-    int rr[KDI];
-#pragma unroll
-    for (int b = 0; b < DEPTH; ++b)
-      if (b < nblocks) {
-        dma_rows(b, rr);
-        dma(b, rr);
-      }
-  }
-
-  // ---- this wavefront's 32 queries: B operand of S^T = K Q^T (hd 16s + 8g + e)
-  const int slot = wave * 32 + l32;
-  int qrow;
-  if constexpr (BLEND) {
-    const int r = p.blk_rows[blk * QB + slot];
-    qrow = r >= 0 ? r : p.blk_rows[blk * QB];   // an empty slot runs the block's first row
-  } else {
-    const int qc = min(qblk * QB + slot, n - 1);
-    qrow = p.rows[int64_t(t0) * n + qc];
-  }
-  bf16x8 qf[KSTEPS];
-  {
-    const bf16* qp = qkv + int64_t(qrow) * ld + h * HD;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * g);
-  }
-  const float C = p.scale_log2;
-  float m_run = 0.f, l_run = 0.f;
-  f32x16 oacc[NHB];
-  // the window's global key is the softmax's initial state: score, weight 1, value
-  auto window_init = [&](int t) {
-    const int64_t gr = gkey_row(p, t);
-    const bf16* kgp = kbase + gr * ld;
-    const bf16* vgp = vbase + gr * ld;
-    float sg = 0.f;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const bf16x8 kg = *reinterpret_cast<const bf16x8*>(kgp + 16 * s + 8 * g);
-      // q opaque here: its fp32 copy (64 registers) would otherwise be made
-      // once and held across every window
-      bf16x8 q = qf[s];
-      asm volatile("" : "+v"(q));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sg += float(q[e]) * float(kg[e]);
-    }
-    sg += __shfl_xor(sg, 32, 64);
-    m_run = sg * C;
-    l_run = g == 0 ? 1.f : 0.f;
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const bf16x4 v = *reinterpret_cast<const bf16x4*>(vgp + hb * 32 + 8 * r4 + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) oacc[hb][4 * r4 + e] = float(v[e]);
-      }
-  };
-  // the window's output o = O / l: written (per-tile layouts), or weighted by
-  // w-bar and added to the row's blend, the partial sum kept in fp32 between
-  // windows and the blend written after the last one
-  auto window_finish = [&](int ps) {
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    // the output row is read again here rather than kept from the start:
-    // nothing but the softmax state stays in registers across the key loop
-    int orw;
-    bool valid;
-    float coef;
+    // ---- this wavefront's 32 queries: B operand of S^T = K Q^T (hd 16s + 8g + e)
+    const int slot = wave * 32 + l32;
+    int qrow;
     if constexpr (BLEND) {
       const int r = p.blk_rows[blk * QB + slot];
-      valid = r >= 0;
-      orw = valid ? r : p.blk_rows[blk * QB];
-      coef = p.blk_w[(int64_t(blk) * p.maxc + ps) * QB + slot] / l_tot;
+      qrow = r >= 0 ? r : p.blk_rows[blk * QB];   // an empty slot runs the block's first row
     } else {
-      const int qi = qblk * QB + slot;
-      valid = qi < n;
-      orw = t0 * (n + 1) + qi;
-      coef = 1.0f / l_tot;
+      const int qc = min(qblk * QB + slot, n - 1);
+      qrow = p.rows[int64_t(t0) * n + qc];
     }
-    const bool last = !BLEND || ps + 1 == npass;
-    float* prow = p.part + int64_t(orw) * p.d + h * HD;
-    bf16* op = (bf16*)p.out + int64_t(orw) * p.d + h * HD;
-    // in place on the accumulators (the next window starts them afresh)
+    bf16x8 qf[KSTEPS];
+    {
+      const bf16* qp = qkv + int64_t(qrow) * ld + h * HD;
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) oacc[hb] *= coef;
-    if (BLEND && ps > 0) {
-      // every lane reads (an empty slot's row is the block's first row); the
-      // reads of half the head go out together before they are added
+      for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * g);
+    }
+    const float C = p.scale_log2;
+    float m_run = 0.f, l_run = 0.f;
+    f32x16 oacc[NHB];
+    // the window's global key is the softmax's initial state: score, weight 1, value
+    auto window_init = [&](int t) {
+      const int64_t gr = gkey_row(p, t);
+      const bf16* kgp = kbase + gr * ld;
+      const bf16* vgp = vbase + gr * ld;
+      float sg = 0.f;
 #pragma unroll
-      for (int h0 = 0; h0 < NHB; h0 += (NHB + 1) / 2) {
-        f32x4 prev[(NHB + 1) / 2][4];
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8 kg = *reinterpret_cast<const bf16x8*>(kgp + 16 * s + 8 * g);
+        // q opaque here: its fp32 copy (64 registers) would otherwise be made
+        // once and held across every window
+        bf16x8 q = qf[s];
+        asm volatile("" : "+v"(q));
 #pragma unroll
-        for (int hb = h0; hb < min(h0 + (NHB + 1) / 2, NHB); ++hb)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) prev[hb - h0][r4] = load4(prow + hb * 32 + 8 * r4 + 4 * g);
-#pragma unroll
-        for (int hb = h0; hb < min(h0 + (NHB + 1) / 2, NHB); ++hb)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) oacc[hb][4 * r4 + e] += prev[hb - h0][r4][e];
+        for (int e = 0; e < 8; ++e) sg += float(q[e]) * float(kg[e]);
       }
-    }
-    float am = 0.f;
-    if (valid) {
+      sg += __shfl_xor(sg, 32, 64);
+      m_run = sg * C;
+      l_run = g == 0 ? 1.f : 0.f;
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int col = hb * 32 + 8 * r4 + 4 * g;
-          const f32x4 v = {oacc[hb][4 * r4], oacc[hb][4 * r4 + 1], oacc[hb][4 * r4 + 2], oacc[hb][4 * r4 + 3]};
-          if (!last) {
-            store4(prow + col, v);
-          } else {
-            const bf16x4 w = {bf16(v[0]), bf16(v[1]), bf16(v[2]), bf16(v[3])};
-            *reinterpret_cast<bf16x4*>(op + col) = w;
+          const bf16x4 v = *reinterpret_cast<const bf16x4*>(vgp + hb * 32 + 8 * r4 + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(float(w[e])));
+          for (int e = 0; e < 4; ++e) oacc[hb][4 * r4 + e] = float(v[e]);
+        }
+    };
+    // the window's output o = O / l: written (per-tile layouts), or weighted by
+    // w-bar and added to the row's blend, the partial sum kept in fp32 between
+    // windows and the blend written after the last one
+    auto window_finish = [&](int ps) {
+      const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+      // the output row is read again here rather than kept from the start:
+      // nothing but the softmax state stays in registers across the key loop
+      int orw;
+      bool valid;
+      float coef;
+      if constexpr (BLEND) {
+        const int r = p.blk_rows[blk * QB + slot];
+        valid = r >= 0;
+        orw = valid ? r : p.blk_rows[blk * QB];
+        coef = p.blk_w[(int64_t(blk) * p.maxc + ps) * QB + slot] / l_tot;
+      } else {
+        const int qi = qblk * QB + slot;
+        valid = qi < n;
+        orw = t0 * (n + 1) + qi;
+        coef = 1.0f / l_tot;
+      }
+      const bool last = !BLEND || ps + 1 == npass;
+      float* prow = p.part + int64_t(orw) * p.d + h * HD;
+      bf16* op = (bf16*)p.out + int64_t(orw) * p.d + h * HD;
+      // in place on the accumulators (the next window starts them afresh)
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) oacc[hb] *= coef;
+      if (BLEND && ps > 0) {
+        // every lane reads (an empty slot's row is the block's first row); the
+        // reads of half the head go out together before they are added
+#pragma unroll
+        for (int h0 = 0; h0 < NHB; h0 += (NHB + 1) / 2) {
+          f32x4 prev[(NHB + 1) / 2][4];
+#pragma unroll
+          for (int hb = h0; hb < min(h0 + (NHB + 1) / 2, NHB); ++hb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) prev[hb - h0][r4] = load4(prow + hb * 32 + 8 * r4 + 4 * g);
+#pragma unroll
+          for (int hb = h0; hb < min(h0 + (NHB + 1) / 2, NHB); ++hb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) oacc[hb][4 * r4 + e] += prev[hb - h0][r4][e];
+        }
+      }
+      float am = 0.f;
+      if (valid) {
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int col = hb * 32 + 8 * r4 + 4 * g;
+            const f32x4 v = {oacc[hb][4 * r4], oacc[hb][4 * r4 + 1], oacc[hb][4 * r4 + 2], oacc[hb][4 * r4 + 3]};
+            if (!last) {
+              store4(prow + col, v);
+            } else {
+              const bf16x4 w = {bf16(v[0]), bf16(v[1]), bf16(v[2]), bf16(v[3])};
+              *reinterpret_cast<bf16x4*>(op + col) = w;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(float(w[e])));
+            }
+          }
+      }
+      if (last && p.amax) wave_amax(p.amax, am, int(blockIdx.x) * NW + wave);
+    };
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's DMA of the first blocks landed
+    __syncthreads();
+    const int krow_a = swap23(l32);  // key row this lane feeds as MFMA A row
+    // V^T fragment addresses: lane 16G + j reads key row 8 (G / 2) + j / 4 (+16
+    // per 16-key chunk, +4 for the second read) at hd dims hb*32 + 16 (G % 2) +
+    // 4 (j % 4) .. +3; the swizzle depends only on the row's low bits, which
+    // the chunk and read offsets keep
+    int vaddr[NHB];
+    {
+      const int G = lane >> 4, j = lane & 15;
+      const int row0 = 8 * (G >> 1) + (j >> 2);
+      const int clow = 2 * (G & 1) + ((j & 3) >> 1);
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) vaddr[hb] = row0 * KROWB + (((hb * 4 + clow) ^ vswz<HD>(row0)) * 16) + 8 * (j & 1);
+    }
+
+    // window and block AHEAD blocks ahead in the stream, and that window's map
+    int ps3 = AHEAD / nkb, kb3 = AHEAD % nkb;
+    const int* map3 = p.rows + int64_t(tile_of(min(ps3, npass - 1))) * n;
+    for (int ps = 0; ps < npass; ++ps) {
+     window_init(tile_of(ps));
+     for (int kb = 0; kb < nkb; ++kb) {
+      const int gb = ps * nkb + kb;  // position in the stream of key blocks
+      const int cur = gb % NST;
+      {
+        // key rows of block gb+AHEAD: wavefront 0 copies them from the row map
+        // straight into the ring (no registers, so nothing waits on them before
+        // the block-end wait), ahead of this block's K / V loads so that wait
+        // covers them
+        int rr[KDI];
+        if (gb + DEPTH < nblocks) dma_rows(gb + DEPTH, rr);
+        if (gb + AHEAD < nblocks) {
+          if (wv == 0) {
+            const int j = min(kb3 * KB + lane, n - 1);
+            __builtin_amdgcn_global_load_lds((const void*)(map3 + j), (TS_LDS void*)(&idx_s[(gb + AHEAD) % NSL][0]),
+                                             4, 0, 0);
+          }
+          // the stream position AHEAD blocks on: its window's map is read only
+          // when it enters a new window
+          if (++kb3 == nkb) {
+            kb3 = 0;
+            if (++ps3 < npass) map3 = p.rows + int64_t(tile_of(ps3)) * n;
           }
         }
-    }
-    if (last && p.amax) wave_amax(p.amax, am, int(blockIdx.x) * NW + wave);
-  };
-
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's DMA of the first blocks landed
-  __syncthreads();
-  const int krow_a = swap23(l32);  // key row this lane feeds as MFMA A row
-  // V^T fragment addresses: lane 16G + j reads key row 8 (G / 2) + j / 4 (+16
-  // per 16-key chunk, +4 for the second read) at hd dims hb*32 + 16 (G % 2) +
-  // 4 (j % 4) .. +3; the swizzle depends only on the row's low bits, which
-  // the chunk and read offsets keep
-  int vaddr[NHB];
-  {
-    const int G = lane >> 4, j = lane & 15;
-    const int row0 = 8 * (G >> 1) + (j >> 2);
-    const int clow = 2 * (G & 1) + ((j & 3) >> 1);
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) vaddr[hb] = row0 * KROWB + (((hb * 4 + clow) ^ vswz<HD>(row0)) * 16) + 8 * (j & 1);
-  }
-
-  // window and block AHEAD blocks ahead in the stream, and that window's map
-  int ps3 = AHEAD / nkb, kb3 = AHEAD % nkb;
-  const int* map3 = p.rows + int64_t(tile_of(min(ps3, npass - 1))) * n;
-  for (int ps = 0; ps < npass; ++ps) {
-   window_init(tile_of(ps));
-   for (int kb = 0; kb < nkb; ++kb) {
-    const int gb = ps * nkb + kb;  // position in the stream of key blocks
-    const int cur = gb % NST;
-    {
-      // key rows of block gb+AHEAD: wavefront 0 copies them from the row map
-      // straight into the ring (no registers, so nothing waits on them before
-      // the block-end wait), ahead of this block's K / V loads so that wait
-      // covers them
-      int rr[KDI];
-      if (gb + DEPTH < nblocks) dma_rows(gb + DEPTH, rr);
-      if (gb + AHEAD < nblocks) {
-        if (wv == 0) {
-          const int j = min(kb3 * KB + lane, n - 1);
-          __builtin_amdgcn_global_load_lds((const void*)(map3 + j), (TS_LDS void*)(&idx_s[(gb + AHEAD) % NSL][0]),
-                                           4, 0, 0);
-        }
-        // the stream position AHEAD blocks on: its window's map is read only
-        // when it enters a new window
-        if (++kb3 == nkb) {
-          kb3 = 0;
-          if (++ps3 < npass) map3 = p.rows + int64_t(tile_of(ps3)) * n;
-        }
+        if (gb + DEPTH < nblocks) dma(gb + DEPTH, rr);
       }
-      if (gb + DEPTH < nblocks) dma(gb + DEPTH, rr);
-    }
-    const char* ks = Ks[cur];
-    const char* vs = Vs[cur];
-    const int j0 = kb * KB;
+      const char* ks = Ks[cur];
+      const char* vs = Vs[cur];
+      const int j0 = kb * KB;
 
-    // ---- S^T = K Q^T for the 64 keys: two 32-key chains, K fragments read
-    // ahead of the MFMAs that use them (four LDS reads kept in flight)
-    f32x16 sacc[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int kr = sb * 32 + krow_a;
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(ks + kr * KROWB + (((2 * s + g) ^ kswz<HD>(kr)) * 16));
-        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sb], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
-#pragma unroll
-    for (int i = 0; i < 2 * KSTEPS - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    if (j0 + KB > n) {  // keys past the window end (last block of a window only)
-      // accumulator row 8(r/4)+4g+(r%4) holds key swap23(that row) =
-      // 16(r/8) + 4((r/4)%2) + r%4 + 8g: one per-lane limit, constant offsets
-      const int lim = n - j0 - 8 * g;
+      // ---- S^T = K Q^T for the 64 keys: two 32-key chains, K fragments read
+      // ahead of the MFMAs that use them (four LDS reads kept in flight)
+      f32x16 sacc[2];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (sb * 32 + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3) >= lim) sacc[sb][r] = -INFINITY;
-    }
-    // ---- online softmax over the block (one rescale check per block)
-    bf16x8 pf[4];
-    {
-      float mx = -INFINITY;
+        for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.f;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * C;
-      // rescale only when some query's block max passes its running max by 2^8
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_LOG2) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) oacc[hb] *= alpha;
-      }
-      const float mneg = -m_run;
-      float lsum = 0.f;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[sb][r], C, mneg));
-          lsum += pv;
-          pf[sb * 2 + (r >> 3)][r & 7] = bf16(pv);
+        for (int sb = 0; sb < 2; ++sb) {
+          const int kr = sb * 32 + krow_a;
+          const bf16x8 kf =
+              *reinterpret_cast<const bf16x8*>(ks + kr * KROWB + (((2 * s + g) ^ kswz<HD>(kr)) * 16));
+          sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sb], 0, 0, 0);
         }
-      l_run += lsum;
-    }
-    // ---- O^T += V^T P^T over four 16-key chunks (NHB independent chains).
-    // The transposing reads take no immediate offset, so their 8*NHB
-    // addresses would all be precomputed and held across the loop; the empty
-    // asm makes the NHB per-lane bases opaque here, so each address is one
-    // add from a base inside the block instead.
-    int vb[NHB];
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-      vb[hb] = vaddr[hb];
-      asm volatile("" : "+v"(vb[hb]));
-    }
+      for (int i = 0; i < 2 * KSTEPS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (j0 + KB > n) {  // keys past the window end (last block of a window only)
+        // accumulator row 8(r/4)+4g+(r%4) holds key swap23(that row) =
+        // 16(r/8) + 4((r/4)%2) + r%4 + 8g: one per-lane limit, constant offsets
+        const int lim = n - j0 - 8 * g;
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (sb * 32 + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3) >= lim) sacc[sb][r] = -INFINITY;
+      }
+      // ---- online softmax over the block (one rescale check per block)
+      bf16x8 pf[4];
+      {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * C;
+        // rescale only when some query's block max passes its running max by 2^8
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_LOG2) != 0) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) oacc[hb] *= alpha;
+        }
+        const float mneg = -m_run;
+        float lsum = 0.f;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[sb][r], C, mneg));
+            lsum += pv;
+            pf[sb * 2 + (r >> 3)][r & 7] = bf16(pv);
+          }
+        l_run += lsum;
+      }
+      // ---- O^T += V^T P^T over four 16-key chunks (NHB independent chains).
+      // The transposing reads take no immediate offset, so their 8*NHB
+      // addresses would all be precomputed and held across the loop; the empty
+      // asm makes the NHB per-lane bases opaque here, so each address is one
+      // add from a base inside the block instead.
+      int vb[NHB];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) {
-        const char* a = vs + vb[hb] + 16 * cc * KROWB;
-        const bf16x8 vf = v_fragment(a, a + 4 * KROWB);
-        oacc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], oacc[hb], 0, 0, 0);
+        vb[hb] = vaddr[hb];
+        asm volatile("" : "+v"(vb[hb]));
       }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 4 fragments (8 reads) ahead
 #pragma unroll
-    for (int i = 0; i < 4 * NHB - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          const char* a = vs + vb[hb] + 16 * cc * KROWB;
+          const bf16x8 vf = v_fragment(a, a + 4 * KROWB);
+          oacc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], oacc[hb], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 4 fragments (8 reads) ahead
+#pragma unroll
+      for (int i = 0; i < 4 * NHB - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
-    // this wavefront's loads of block gb+1 have landed (the newer blocks'
-    // may still be in flight) and its LDS traffic is done; then a barrier
-    // without the fence of __syncthreads, which would also wait for those.
-    // Vector memory operations complete in issue order, so the count also
-    // covers the previous window's output loads and stores.
-    if (gb + DEPTH < nblocks) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((DEPTH - 1) * 2 * KDI) : "memory");
-    else if (DEPTH == 3 && gb + 2 < nblocks) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * KDI) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-   }
-   window_finish(ps);
-  }
+      // this wavefront's loads of block gb+1 have landed (the newer blocks'
+      // may still be in flight) and its LDS traffic is done; then a barrier
+      // without the fence of __syncthreads, which would also wait for those.
+      // Vector memory operations complete in issue order, so the count also
+      // covers the previous window's output loads and stores.
+      if (gb + DEPTH < nblocks) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((DEPTH - 1) * 2 * KDI) : "memory");
+      else if (DEPTH == 3 && gb + 2 < nblocks) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * KDI) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+     }
+     window_finish(ps);
+    }
+  }  // jobs
 }
 
 // Global-token query row of one (head, tile), over the window keys
@@ -762,9 +787,37 @@ namespace tsk {
 
 static AttnP make_params(const AttnArgs& a) {
   return AttnP{a.qkv,       a.out,       a.part, a.rows, a.g0, a.gstep, a.blk_nt, a.blk_tiles, a.blk_rows, a.blk_w, a.nblk, a.maxc,
-               a.blk_order, a.blk_cls,   a.ncls,
+               a.blk_order, a.blk_cls,   a.ncls,           a.half_a, a.jobs,
                a.n_union,   a.d,         a.H,    a.n_tiles,        a.n,
                1.4426950408889634f / sqrtf(float(a.hd)),           a.amax};
+}
+
+__global__ void k_zero_jobs(unsigned* jobs) {
+  if (threadIdx.x < tsk::JOB_COUNTERS_BYTES / 4) jobs[threadIdx.x] = 0u;
+}
+
+// Workgroups of the blended bf16 kernel that the current device holds at
+// once: CUs x resident workgroups per CU, rounded down to a multiple of 8
+// (at least 8).  Cached per device.
+hipError_t blend_slots(int hd, int* out) {
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({dev, hd});
+  if (it == cache.end()) {
+    int cus = 0, per_cu = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    e = hd == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_bf16<64, true>, NW * 64, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_bf16<128, true>, NW * 64, 0);
+    if (e != hipSuccess) return e;
+    const int slots = std::max(8, (std::max(1, cus) * std::max(1, per_cu)) / 8 * 8);
+    it = cache.emplace(std::make_pair(dev, hd), slots).first;
+  }
+  *out = it->second;
+  return hipSuccess;
 }
 
 hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
@@ -786,28 +839,24 @@ hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
 #undef TS_F32A
     return hipGetLastError();
   }
-  int nwg = njob * a.H;
-  if (blend) {
-    // every XCD is dealt the same number of workgroups; the XCD with the
-    // most jobs sets it, the others' spare workgroups exit
-    if (!a.blk_order || !a.blk_cls || a.ncls < 1) return hipErrorInvalidValue;
-    int most = 0;
-    for (int x = 0; x < 8; ++x) {
-      const HalfRange r = xcd_halves(a.H, x);
-      most = std::max(most, r.na * a.half_a + r.nb * (a.nblk - a.half_a));
-    }
-    nwg = 8 * most;
+  if (a.hd != 64 && a.hd != 128) return hipErrorInvalidValue;
+  const dim3 block(NW * 64);
+  if (!blend) {
+    const dim3 grid(njob * a.H);
+    if (a.hd == 64) hipLaunchKernelGGL((k_attn_bf16<64, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_attn_bf16<128, false>), grid, block, 0, s, p);
+    return hipGetLastError();
   }
-  const dim3 grid(nwg), block(NW * 64);
-#define TS_BFA(HD)                                                                 \
-  do {                                                                             \
-    if (blend) hipLaunchKernelGGL((k_attn_bf16<HD, true>), grid, block, 0, s, p); \
-    else hipLaunchKernelGGL((k_attn_bf16<HD, false>), grid, block, 0, s, p);      \
-  } while (0)
-  if (a.hd == 64) TS_BFA(64);
-  else if (a.hd == 128) TS_BFA(128);
-  else return hipErrorInvalidValue;
-#undef TS_BFA
+  // blended: as many workgroups as the CUs hold at once (a multiple of 8, so
+  // every XCD holds the same number), counters zeroed first
+  if (!a.blk_order || !a.blk_cls || a.ncls < 1 || !a.jobs) return hipErrorInvalidValue;
+  int slots = 0;
+  hipError_t e = blend_slots(a.hd, &slots);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_zero_jobs, dim3(1), dim3(64), 0, s, a.jobs);
+  const dim3 grid(slots);
+  if (a.hd == 64) hipLaunchKernelGGL((k_attn_bf16<64, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((k_attn_bf16<128, true>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

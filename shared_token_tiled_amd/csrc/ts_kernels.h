@@ -87,6 +87,8 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
 // ---- attn.hip ----
 // Query rows per attention workgroup, and per query block of the plan.
 constexpr int QBLOCK = 256;
+// bytes of the blended attention's job counters: 8 XCDs, 32 bytes apart
+constexpr int JOB_COUNTERS_BYTES = 256;
 // q and k of qkv are as qk_prep left them (normalised, rotated by grid
 // coordinates).  Window token j of tile t is qkv row rows[t*n + j], its global
 // token row g0 + gstep*t.  Layouts (see attn.hip):
@@ -111,6 +113,7 @@ struct AttnArgs {
   const int* blk_order = nullptr;  // [nblk] blocks of the halves A, B of a head (bf16 job order)
   const int* blk_cls = nullptr;    // [ncls*4] per class of equal windows: count, offset in A; in B
   int ncls = 0, half_a = 0;        // classes; blocks in half A (half B: nblk - half_a)
+  unsigned* jobs = nullptr;        // bf16 blended: per-XCD job counters (JOB_COUNTERS_BYTES), zeroed by attention()
   int n_union, d, H, hd, n_tiles, n;
   unsigned* amax = nullptr;        // optional (bf16): max |out| as stored
 };
