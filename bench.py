@@ -163,6 +163,9 @@ def main():
                          "(the tiled baseline stays as released)")
     ap.add_argument("--partial-share", default=None, metavar="OPS",
                     help="time partial sharing from layer k with per-tile streams; OPS from q, o, m (e.g. qo)")
+    ap.add_argument("--enc", action="store_true",
+                    help="time the pipeline: the config's encoder stack, then the decoder, TileShare in both "
+                         "(the encoder at its own k) against tiled in both")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path's sharding across "
@@ -174,6 +177,15 @@ def main():
     from synth import configs
 
     cfg = configs.get(args.config)
+    enc_cfg = None
+    if args.enc:
+        if args.config not in configs.ENCODERS:
+            print(f"bench.py: no encoder is defined for {args.config}", file=sys.stderr)
+            sys.exit(2)
+        if args.merge_once is not None or args.partial_share is not None:
+            print("bench.py: --enc times TileShare-k stacks only", file=sys.stderr)
+            sys.exit(2)
+        enc_cfg = configs.get(configs.ENCODERS[args.config])
     if args.fp8_gemms:
         cfg["fp8_gemms"] = tuple(args.fp8_gemms.split(","))
     cfg["fp8_per_tile"] = args.fp8_per_tile
@@ -192,6 +204,16 @@ def main():
     model_base = ts.model_desc(dict(cfg, layer0_dedup=False))
     x, g, tens, structs = device_inputs(cfg, cfg.get("seed", 0), dev)
     ws_bytes = max(ts.ts_workspace_size(model, plan, kk) for kk in (k, L, -1))
+    if enc_cfg is not None:
+        # the encoder: same grid, tiling and width, its own weights; its output
+        # rows are the decoder's input tokens, the global tokens stay learned
+        k_enc = enc_cfg["k_values"][0]
+        enc_model = ts.model_desc(enc_cfg)
+        ex, _, enc_tens, enc_structs = device_inputs(enc_cfg, enc_cfg.get("seed", 1), dev)
+        ws_bytes = max(ws_bytes, *(ts.ts_workspace_size(enc_model, plan, kk)
+                                   for kk in (k_enc, enc_cfg["n_layers"])))
+        x_lat = torch.empty_like(ex)
+        g_lat = torch.empty(info.n_tiles, cfg["d"], device=dev)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     xo = torch.empty_like(x)
     go = torch.empty(info.n_tiles, cfg["d"], device=dev)
@@ -205,11 +227,18 @@ def main():
             ts.ts_merge_once_forward(model, structs, plan, args.merge_once, x, g, xo, go, ws)
         elif args.partial_share is not None:
             ts.ts_partial_share_forward(model, structs, plan, k, share_mask, x, g, xo, go, ws)
+        elif enc_cfg is not None:
+            ts.ts_stack_forward(enc_model, enc_structs, plan, k_enc, ex, g, x_lat, g_lat, ws)
+            ts.ts_stack_forward(model, structs, plan, k, x_lat, g, xo, go, ws)
         else:
             ts.ts_stack_forward(model, structs, plan, k, x, g, xo, go, ws)
 
     def step_base():
-        ts.ts_tiled_forward(model_base, structs, plan, x, g, xo, go, ws)
+        if enc_cfg is not None:
+            ts.ts_tiled_forward(enc_model, enc_structs, plan, ex, g, x_lat, g_lat, ws)
+            ts.ts_tiled_forward(model_base, structs, plan, x_lat, g, xo, go, ws)
+        else:
+            ts.ts_tiled_forward(model_base, structs, plan, x, g, xo, go, ws)
 
     def timed(fn, steps, warmup, profile):
         for _ in range(warmup):
@@ -272,6 +301,8 @@ def main():
                 if args.merge_once is not None else
                 decode_flops(cfg, pl, k, args.partial_share if args.partial_share is not None else "qom",
                              dedup0=args.layer0_dedup))
+    if enc_cfg is not None:
+        pl_flops += decode_flops(enc_cfg, pl, k_enc)
     mode = (f"merge once at layer {args.merge_once}, then per tile" if args.merge_once is not None
             else (f"per-tile streams from layer {k} sharing {args.partial_share or 'nothing'}"
                   if args.partial_share is not None else f"TileShare-{k}"))
@@ -280,6 +311,9 @@ def main():
         extras.append("hard stitching")
     if args.layer0_dedup:
         extras.append("layer 0 Norm1/QKV/QK-norm once per token")
+    if enc_cfg is not None:
+        extras.append(f"pipeline: {enc_cfg['name']} encoder ({enc_cfg['n_layers']} blocks, TileShare-{k_enc}) "
+                      f"before the decoder; tiled baseline tiled in both")
     if cfg["gemm_shared"] == "fp8":
         extras.append(f"fp8 GEMMs {','.join(cfg.get('fp8_gemms') or ('qkv', 'out', 'fc1', 'fc2'))} in shared"
                       + (" and per-tile" if args.fp8_per_tile else "") + " layers")

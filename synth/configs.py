@@ -1,4 +1,4 @@
-"""Workload definitions: the five synthetic decoder configurations.
+"""Workload definitions: the synthetic decoder configurations and one encoder.
 
 Pure data, no arithmetic of the method.  Each entry gives the token grid, the
 tiling (tile extent and stride per axis, T/H/W order), the transformer block
@@ -38,9 +38,22 @@ CONFIGS = {
         n_layers=24, d=1024, n_heads=16, head_dim=64, mlp_hidden=4096,
         norm="ln", qk_norm=False, dtype="bf16", gemm_shared="bf16",
         k_values=(0, 24), seed=0),
+    # The encoder of the ViTok-like 4K pipeline ("+enc": TileShare also in the
+    # encoder).  Same token grid, tiling and block shape as the decoder; the
+    # pages give no encoder shape, and its depth is read off the tiled
+    # timings: pipeline minus decoder is about a fifth of the decoder's time,
+    # so five blocks against the decoder's 24.
+    "vitok4k_enc": dict(
+        ndim=2, grid=(1, 135, 240), tile=(1, 64, 64), stride=(1, 48, 48),
+        n_layers=5, d=1024, n_heads=16, head_dim=64, mlp_hidden=4096,
+        norm="ln", qk_norm=False, dtype="bf16", gemm_shared="bf16",
+        k_values=(0, 5), seed=1),
 }
 
-ORDER = ("tiny2d", "small_video", "minimax_h3", "minimax_h3_fp8", "vitok4k")
+# decoder workload -> the encoder that runs before it in the pipeline
+ENCODERS = {"vitok4k": "vitok4k_enc"}
+
+ORDER = ("tiny2d", "small_video", "minimax_h3", "minimax_h3_fp8", "vitok4k", "vitok4k_enc")
 
 ROPE_BASE = 10000.0
 EPS = 1e-6

@@ -24,6 +24,8 @@ REDUCED = {
                         n_layers=2),
     "vitok4k": dict(grid=(1, 20, 36), tile=(1, 16, 16), stride=(1, 12, 12), d=256, n_heads=4, mlp_hidden=1024,
                     n_layers=2),
+    "vitok4k_enc": dict(grid=(1, 20, 36), tile=(1, 16, 16), stride=(1, 12, 12), d=256, n_heads=4, mlp_hidden=1024,
+                        n_layers=2),
 }
 
 
@@ -44,7 +46,7 @@ CASES = [("tiny2d", None, 0), ("tiny2d", None, 1),
 
 
 @pytest.mark.parametrize("name,size,k", CASES)
-@pytest.mark.parametrize("qk_scale", [1.0, 4.0])
+@pytest.mark.parametrize("qk_scale", [1.0, 4.0, 8.0])
 def test_stack_against_oracle(name, size, k, qk_scale):
     cfg = configs.get(name) if size is None else reduced(name)
     say(f"stack {name} {'reduced' if size else 'full'} k={k} qk_scale={qk_scale} grid={cfg['grid']}")
@@ -306,3 +308,31 @@ def test_layer0_dedup_against_oracle_and_per_tile_rows(entry, name, size, k):
     # the same kernels on the same values: equal up to the summation order of
     # rows that fall into the ragged-row GEMM in one layout and not the other
     assert ep < 1e-3
+
+
+@pytest.mark.parametrize("k_enc,k_dec", [(0, 0), (2, 2), (0, 1)])
+def test_encoder_then_decoder(k_enc, k_dec):
+    """TileShare also in the encoder (paper page, Tables S11 and S12, "+enc"):
+    the encoder stack's output rows are the decoder's input tokens.  Each
+    stack is held to the per-stack tolerance: the encoder against the oracle
+    on the same inputs, the decoder against the oracle fed the GPU encoder's
+    output; the end-to-end difference is reported."""
+    enc, dec = reduced("vitok4k_enc"), reduced("vitok4k")
+    say(f"pipeline encoder k={k_enc} then decoder k={k_dec} grid={dec['grid']}")
+    xe, g, le = make_inputs(enc)
+    _, _, ld = make_inputs(dec)
+    run_e, run_d = Run(enc, le), Run(dec, ld)
+    try:
+        lat, _ = run_e.stack(xe, g, k_enc)
+        got, ggot = run_d.stack(lat, g, k_dec)
+    finally:
+        run_e.close()
+        run_d.close()
+    ref_lat, _ = _oracle(enc, xe, g, le, k_enc)
+    ref, gref = _oracle(dec, lat, g, ld, k_dec)
+    end, _ = _oracle(dec, ref_lat, g, ld, k_dec)
+    tol = TOL[dec["dtype"]]
+    e_enc, e_dec, eg = max_rel(lat, ref_lat), max_rel(got, ref), max_rel(ggot, gref)
+    print(f"  encoder {e_enc:.3e}, decoder {e_dec:.3e} (globals {eg:.3e}), end to end {max_rel(got, end):.3e}; "
+          f"tolerance {tol} per stack")
+    assert e_enc < tol and e_dec < tol and eg < tol
