@@ -316,18 +316,21 @@ ts_status ts_op_gemm_ws(int32_t dtype, int32_t epilogue, const void* a, const vo
  *  shared = 0: per-tile layout, rows = n_tiles*(tile_tokens+1) (tile t at
  *    t*(tile_tokens+1), its global token last); out in the same layout.
  * ws: device workspace of at least ts_workspace_size(model, plan, n_layers)
- * bytes, 256-byte aligned.  Asynchronous. */
+ * bytes, 256-byte aligned.  Asynchronous.  bf16: the qkv array of either
+ * layout must stay below 4 GiB (rows * 6 * d bytes < 2^32; every forward call
+ * returns TS_ESHAPE otherwise). */
 ts_status ts_op_attention(const ts_model_desc* model, const ts_plan* plan, int32_t shared, void* qkv,
                           const float* q_g, const float* k_g, void* out, void* ws, size_t ws_bytes,
                           void* stream);
 
 /* For callers that cannot allocate device memory (code under graph capture,
  * serving loops, harnesses that forbid hipMalloc): ts_op_attention with no
- * workspace argument.  Its scratch -- the fp32 partial blends of the shared
- * layout (n_union * d * 4 bytes) and the global rows' split states -- lives
+ * workspace argument.  Its scratch -- 256 bytes of job counters (zeroed by
+ * the call), the fp32 partial blends of the shared layout (n_union * d * 4
+ * bytes) and the global rows' split states -- lives
  * in a file-scope device array of TS_NOALLOC_SCRATCH_BYTES that every GPU the
  * library runs on holds until the process ends; the call allocates nothing.
- * A request whose partial blends exceed the array returns TS_EWORKSPACE
+ * A request whose counters and partial blends exceed the array returns TS_EWORKSPACE
  * (the per-tile layout, shared = 0, needs none).  All calls on one GPU share
  * its array: calls that overlap on one GPU (on different streams, or from
  * different threads) race and must be serialised by the caller.  Nothing in

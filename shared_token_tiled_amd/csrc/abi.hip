@@ -132,6 +132,11 @@ ts_status check_plan(const ts_plan* p, const ts_model_desc* m) {
   if (!p->uploaded) return fail(TS_EINVAL, "plan not uploaded (call ts_plan_upload)");
   if (p->rope_hd != m->head_dim || p->rope_base != m->rope_base)
     return fail(TS_EINVAL, "plan RoPE table was uploaded for another head_dim or base");
+  // the bf16 attention stages K and V with 32-bit byte offsets into qkv
+  const int64_t rows = std::max(int64_t(p->n_tiles) * (p->n + 1), int64_t(p->n_union) + p->n_tiles);
+  if (m->act_dtype == TS_BF16 && rows * 6 * int64_t(m->d) >= (int64_t(1) << 32))
+    return fail(TS_ESHAPE, "the qkv array (" + std::to_string(rows) + " rows x 3d bf16) reaches 4 GiB; the "
+                           "attention's K/V staging takes 32-bit offsets");
   return TS_OK;
 }
 

@@ -355,16 +355,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         rr[i] = idx_s[gb % NSL][row];
       }
     };
+    // DMA source offsets in bytes, 32-bit: a row index times the row pitch by
+    // a 24-bit multiply (one full-rate instruction, where a 64-bit product
+    // takes three quarter-rate ones; the launcher checks that the qkv array
+    // is below 4 GiB), plus this lane's swizzled chunk
+    const uint32_t ldb = uint32_t(ld) * 2u;
+    const char* kb8 = (const char*)kbase;
+    const char* vb8 = (const char*)vbase;
+    uint32_t kch[KDI], vch[KDI];
+#pragma unroll
+    for (int i = 0; i < KDI; ++i) {
+      const int b = (wv * KDI + i) * 1024 + 16 * lane;
+      const int row = b / KROWB, slot = (b % KROWB) / 16;
+      kch[i] = uint32_t((slot ^ kswz<HD>(row)) * 16);
+      vch[i] = uint32_t((slot ^ vswz<HD>(row)) * 16);
+    }
     auto dma = [&](int gb, const int (&rr)[KDI]) {
       const int st = gb % NST;
 #pragma unroll
       for (int i = 0; i < KDI; ++i) {
-        const int b = (wv * KDI + i) * 1024 + 16 * lane;
-        const int row = b / KROWB, slot = (b % KROWB) / 16;
-        __builtin_amdgcn_global_load_lds((const void*)(kbase + int64_t(rr[i]) * ld + (slot ^ kswz<HD>(row)) * 8),
-                                         (TS_LDS void*)(&Ks[st][(wv * KDI + i) * 1024]), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vbase + int64_t(rr[i]) * ld + (slot ^ vswz<HD>(row)) * 8),
-                                         (TS_LDS void*)(&Vs[st][(wv * KDI + i) * 1024]), 16, 0, 0);
+        const uint32_t ro = __umul24(uint32_t(rr[i]), ldb);
+        __builtin_amdgcn_global_load_lds((const void*)(kb8 + (ro + kch[i])), (TS_LDS void*)(&Ks[st][(wv * KDI + i) * 1024]),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vb8 + (ro + vch[i])), (TS_LDS void*)(&Vs[st][(wv * KDI + i) * 1024]),
+                                         16, 0, 0);
       }
     };
 
@@ -840,6 +854,10 @@ hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
     return hipGetLastError();
   }
   if (a.hd != 64 && a.hd != 128) return hipErrorInvalidValue;
+  // the K / V staging takes 32-bit byte offsets into qkv: its rows (the last
+  // is tile n_tiles-1's global row) must span less than 4 GiB
+  const int64_t qkv_rows = int64_t(a.g0) + int64_t(a.gstep) * (a.n_tiles - 1) + 1;
+  if (qkv_rows * 6 * int64_t(a.d) >= (int64_t(1) << 32)) return hipErrorInvalidValue;
   const dim3 block(NW * 64);
   if (!blend) {
     const dim3 grid(njob * a.H);
