@@ -283,9 +283,13 @@ tsk::RopeRows rope_rows(const ts_plan* p, bool shared) {
 // bf16): max |output| as stored.
 enum AttnLayout { ATT_TILED, ATT_SHARED_ROWS, ATT_BLENDED };
 ts_status window_attention(const ts_model_desc* m, const ts_plan* p, AttnLayout lay, const void* qkv, void* out,
-                           float* part, unsigned* jobs, unsigned* amax, hipStream_t s, float* gscratch = nullptr,
-                           int64_t gscratch_floats = 0) {
+                           float* part, unsigned* jobs, unsigned* amax, hipStream_t s, float* gscratch,
+                           int64_t gscratch_floats, const float* q_g, const float* k_g) {
   tsk::AttnArgs a;
+  if (m->qk_norm) {
+    a.qg = q_g;
+    a.kg = k_g;
+  }
   a.qkv = qkv;
   a.out = out;
   a.part = part;
@@ -390,7 +394,7 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
   const void* aout = shared ? ws.h : ws.o;
   if ((st = window_attention(m, p, shared ? ATT_BLENDED : (qsh ? ATT_SHARED_ROWS : ATT_TILED), ws.big,
                              const_cast<void*>(aout), (float*)ws.o, ws.jobs, am_out, c.s, ws.gpart,
-                             ws.gpart_floats)) != TS_OK)
+                             ws.gpart_floats, w.q_g, w.k_g)) != TS_OK)
     return st;
   if ((st = proj(c, ws, (f8 & TS_FP8_OUT) != 0, "out", tsk::EPI_RESID, aout, M, d, d, w.w_o, w.w_o_f8,
                  w.w_scale_f8 ? w.w_scale_f8 + 1 : nullptr, w.b_o, x, am_out != nullptr)) != TS_OK)
@@ -458,7 +462,7 @@ ts_status run_layer_partial(const Ctx& c, const ts_layer_weights& w, float* X, i
            "qk_prep");
   }
   if ((st = window_attention(m, p, sq ? ATT_SHARED_ROWS : ATT_TILED, ws.big, ws.o, nullptr, nullptr, nullptr, c.s,
-                             ws.gpart, ws.gpart_floats)) != TS_OK)
+                             ws.gpart, ws.gpart_floats, w.q_g, w.k_g)) != TS_OK)
     return st;
   // out-projection
   if (so) {
@@ -686,7 +690,7 @@ ts_status op_attention_impl(const ts_model_desc* m, const ts_plan* p, bool share
            "qk_prep");
   }
   return window_attention(m, p, shared ? ATT_BLENDED : ATT_TILED, qkv, out, part, jobs, nullptr, s, gpart,
-                          gpart_floats);
+                          gpart_floats, q_g, k_g);
 }
 
 // ---- scratch of the no-allocation entry point --------------------------

@@ -63,6 +63,8 @@ struct AttnP {
   int n_union, d, H, n_tiles, n;
   float scale_log2;  // log2(e) / sqrt(hd)
   unsigned* amax;
+  const float* qg;   // QK-norm gains [hd] or null
+  const float* kg;
 };
 
 constexpr int QB = 256;  // query rows per workgroup (both kernels)
@@ -187,6 +189,10 @@ constexpr int AHEAD = 2 * DEPTH - 1;   // blocks ahead the key rows are fetched
 constexpr int NSL = 8;                 // slots of the key-row ring (>= AHEAD + 1)
 static_assert(NSL >= AHEAD + 1 && DEPTH >= 2 && DEPTH <= 3, "staging pipeline");
 constexpr float RESCALE_LOG2 = 8.0f;   // keep a stale running max until a block exceeds it by 2^8
+// Largest static score bound used as the softmax offset: weights >= 2^-64,
+// and the fp32 argument score*C - bound of a weight that matters (|.| < 32)
+// is rounded to 2^-20, about as finely as against a running max.
+constexpr float FIXED_MAX_LIMIT = 32.f;
 static_assert(QB == 32 * NW, "32 query rows per wavefront");
 static_assert(QB == tsk::QBLOCK, "query blocks of the plan");
 
@@ -298,6 +304,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // job on one engine would hold back the launch of every later workgroup.
   // Pulled jobs keep every CU busy until its XCD's list is done.
   const int xcd = blockIdx.x & 7;
+  // With QK-RMSNorm a q or k head row has norm at most sqrt(hd) max|gain|
+  // (the RMS-normalised vector has norm sqrt(hd), RoPE rotates it, bf16
+  // rounding adds < 0.4 %), so every score times C lies within +-bnd.  For
+  // bnd <= FIXED_MAX_LIMIT the softmax subtracts bnd instead of a running
+  // max: every weight is in [2^-2bnd, 1], and the per-block max and rescale
+  // go away.  bnd is an integer, so a weight is
+  // 2^score scaled exactly and rounds to bf16 as 2^score would.
+  bool fixedm = false;
+  float bnd = 0.f;
+  if (p.qg) {
+    float gq = 0.f, gk = 0.f;
+    for (int e = lane; e < HD; e += 64) {
+      gq = fmaxf(gq, fabsf(p.qg[e]));
+      gk = fmaxf(gk, fabsf(p.kg[e]));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      gq = fmaxf(gq, __shfl_xor(gq, o, 64));
+      gk = fmaxf(gk, __shfl_xor(gk, o, 64));
+    }
+    bnd = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                                         int, ceilf(1.01f * float(HD) * p.scale_log2 * gq * gk + 1e-3f))));
+    fixedm = bnd <= FIXED_MAX_LIMIT;
+  }
   int njx = 0;  // blended: the XCD's job count
   if constexpr (BLEND) {
     const HalfRange xr = xcd_halves(p.H, xcd);
@@ -429,15 +459,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int e = 0; e < 8; ++e) sg += float(q[e]) * float(kg[e]);
       }
       sg += __shfl_xor(sg, 32, 64);
-      m_run = sg * C;
-      l_run = g == 0 ? 1.f : 0.f;
+      // weight of the global key: 1 against a running max started at its
+      // score, or 2^(score - bnd) against the fixed offset
+      m_run = fixedm ? bnd : sg * C;
+      const float w0 = fixedm ? __builtin_amdgcn_exp2f(sg * C - bnd) : 1.f;
+      l_run = g == 0 ? w0 : 0.f;
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const bf16x4 v = *reinterpret_cast<const bf16x4*>(vgp + hb * 32 + 8 * r4 + 4 * g);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) oacc[hb][4 * r4 + e] = float(v[e]);
+          for (int e = 0; e < 4; ++e) oacc[hb][4 * r4 + e] = float(v[e]) * w0;
         }
     };
     // the window's output o = O / l: written (per-tile layouts), or weighted by
@@ -590,23 +623,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           for (int r = 0; r < 16; ++r)
             if (sb * 32 + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3) >= lim) sacc[sb][r] = -INFINITY;
       }
-      // ---- online softmax over the block (one rescale check per block)
+      // ---- softmax over the block: against the fixed offset, or online
+      // (one rescale check per block)
       bf16x8 pf[4];
       {
-        float mx = -INFINITY;
+        if (!fixedm) {
+          float mx = -INFINITY;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+          for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * C;
-        // rescale only when some query's block max passes its running max by 2^8
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_LOG2) != 0) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * C;
+          // rescale only when some query's block max passes its running max by 2^8
+          if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_LOG2) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
-          for (int hb = 0; hb < NHB; ++hb) oacc[hb] *= alpha;
+            for (int hb = 0; hb < NHB; ++hb) oacc[hb] *= alpha;
+          }
         }
         const float mneg = -m_run;
         float lsum = 0.f;
@@ -803,7 +839,7 @@ static AttnP make_params(const AttnArgs& a) {
   return AttnP{a.qkv,       a.out,       a.part, a.rows, a.g0, a.gstep, a.blk_nt, a.blk_tiles, a.blk_rows, a.blk_w, a.nblk, a.maxc,
                a.blk_order, a.blk_cls,   a.ncls,           a.half_a, a.jobs,
                a.n_union,   a.d,         a.H,    a.n_tiles,        a.n,
-               1.4426950408889634f / sqrtf(float(a.hd)),           a.amax};
+               1.4426950408889634f / sqrtf(float(a.hd)),           a.amax, a.qg, a.kg};
 }
 
 __global__ void k_zero_jobs(unsigned* jobs) {

@@ -116,6 +116,10 @@ struct AttnArgs {
   unsigned* jobs = nullptr;        // bf16 blended: per-XCD job counters (JOB_COUNTERS_BYTES), zeroed by attention()
   int n_union, d, H, hd, n_tiles, n;
   unsigned* amax = nullptr;        // optional (bf16): max |out| as stored
+  // QK-RMSNorm gains [hd] of q and k, or null: with them every score obeys
+  // |q.k| <= hd max|q_g| max|k_g|, a fixed softmax offset (bf16 kernel)
+  const float* qg = nullptr;
+  const float* kg = nullptr;
 };
 // fp32: every query row, the global rows included.  bf16: the tile-token
 // query rows; the global-token rows are attention_global's.

@@ -11,11 +11,14 @@ The step (``ts_op_attention``, and the attention of every layer) rounds at:
      equals the pages' tile-local rotation before rounding (Table S1: RoPE per
      tile on tile coordinates);
   2. the softmax weights of the window's tile tokens: 2^(s*log2(e)/sqrt(hd) - m)
-     rounded to bf16 as the P operand of the PV product, where m is a running
-     maximum that is raised only when some query of the 32 handled together
-     sees a block of 64 keys exceed it by 2^8 (then each of those queries takes
-     the larger of its running and block maximum); the weight sum uses the
-     unrounded weights; the global key's weight is never rounded;
+     rounded to bf16 as the P operand of the PV product; the weight sum uses
+     the unrounded weights; the global key's weight is never rounded.  With
+     QK-RMSNorm every score obeys |s| <= hd max|q_g| max|k_g| (normalised rows
+     have norm sqrt(hd), RoPE rotates them), and m is that bound, rounded up
+     to an integer (with a 1 % margin), when it is at most 32.  Otherwise m
+     is a running maximum that is raised only when some query of the 32
+     handled together sees a block of 64 keys exceed it by 2^8 (then each of
+     those queries takes the larger of its running and block maximum);
   3. the output: the window output o = O / l (shared layers: the w-bar sum of
      the windows' outputs, in ascending tile order) rounded once to bf16.
 The global token's own query row keeps fp32 weights (rounding 3 only).
@@ -33,6 +36,21 @@ from synth import round_bf16
 
 QB, WAVE, KB = 256, 32, 64
 RESCALE_LOG2 = 8.0
+FIXED_MAX_LIMIT = 32.0
+AMBIG_TOL = 2.0 ** -15   # relative distance of a weight from a bf16 rounding midpoint
+
+
+def fixed_offset(cfg, q_g, k_g):
+    """The fixed softmax offset of the bf16 kernel under QK-RMSNorm (log2
+    domain): ceil(1.01 hd C max|q_g| max|k_g| + 1e-3) with C = log2(e)/sqrt(hd)
+    as the library forms it in fp32, when at most FIXED_MAX_LIMIT; else None
+    (running maximum)."""
+    if not cfg.get("qk_norm") or q_g is None or k_g is None:
+        return None
+    hd = cfg["head_dim"]
+    C = float(np.float32(1.4426950408889634) / np.sqrt(np.float32(hd)))
+    b = math.ceil(1.01 * hd * C * float(np.max(np.abs(q_g))) * float(np.max(np.abs(k_g))) + 1e-3)
+    return float(b) if b <= FIXED_MAX_LIMIT else None
 
 
 def _bf16(a):
@@ -101,17 +119,46 @@ def qk_prep(qkv, cfg, plan, shared, q_g=None, k_g=None, bf16=True, terms=False):
     return (x.astype(np.float64), mag) if terms else x.astype(np.float64)
 
 
-def _window(qs, K, V, kg, vg, hd, groups, round_p=True):
+def _ambiguous_ulp(p):
+    """The bf16 spacing at each weight p > 0 where p lies within AMBIG_TOL
+    (relative) of a rounding midpoint, else 0: there the GPU's fp32 weight,
+    a few 1e-6 away from this float64 one (the fp32 score and its exponent
+    argument), may round to the other neighbour, one ulp away."""
+    p = np.asarray(p, np.float64)
+    pos = p > 0
+    e = np.floor(np.log2(np.where(pos, p, 1.0)))
+    ulp = np.exp2(e - 7)
+    mid = np.floor(p / ulp) * ulp + ulp / 2
+    return np.where(pos & (np.abs(p - mid) < AMBIG_TOL * p), ulp, 0.0)
+
+
+def _window(qs, K, V, kg, vg, hd, groups, round_p=True, fixed=None):
     """Unnormalised output and weight sum of queries qs [nq, hd] over one
-    window (tile keys K, V [n, hd], global key kg, vg), with the running
-    maximum shared by the queries of each group (list of index arrays).
-    Returns o = O / l [nq, hd] in float64."""
+    window (tile keys K, V [n, hd], global key kg, vg), against the fixed
+    offset ``fixed`` or with the running maximum shared by the queries of each
+    group (list of index arrays).  Returns o = O / l [nq, hd] and the bound
+    sum_j ulp_j |V_j| / l over the weights whose rounding is ambiguous
+    (_ambiguous_ulp), both float64."""
     C = (1.0 / math.log(2.0)) / math.sqrt(hd)
     n = K.shape[0]
+    aV = np.abs(V)
     sl = (qs @ K.T) * C                         # scores, log2 domain
+    if fixed is not None:
+        wg = np.exp2((qs @ kg) * C - fixed)     # global key weight
+        O = wg[:, None] * vg[None, :]
+        A = np.zeros_like(O)
+        L = wg.copy()
+        for j0 in range(0, n, KB):
+            p = np.exp2(sl[:, j0:j0 + KB] - fixed)
+            O += (_bf16(p) if round_p else p) @ V[j0:j0 + KB]
+            if round_p:
+                A += _ambiguous_ulp(p) @ aV[j0:j0 + KB]
+            L += p.sum(axis=1)
+        return O / L[:, None], A / L[:, None]
     m = (qs @ kg) * C                           # running max starts at the global key's score
     wg = np.ones(len(qs))                       # global key weight relative to m
     O = wg[:, None] * vg[None, :]
+    A = np.zeros_like(O)
     L = wg.copy()
     for j0 in range(0, n, KB):
         blk = sl[:, j0:j0 + KB]
@@ -123,12 +170,15 @@ def _window(qs, K, V, kg, vg, hd, groups, round_p=True):
         m_new = np.where(raise_any, np.maximum(m, bm), m)
         alpha = np.exp2(m - m_new)
         O *= alpha[:, None]
+        A *= alpha[:, None]
         L *= alpha
         m = m_new
         p = np.exp2(blk - m[:, None])
         O += (_bf16(p) if round_p else p) @ V[j0:j0 + KB]
+        if round_p:
+            A += _ambiguous_ulp(p) @ aV[j0:j0 + KB]
         L += p.sum(axis=1)
-    return O / L[:, None]
+    return O / L[:, None], A / L[:, None]
 
 
 def _global_row(qg, K, V, kg, vg, hd):
@@ -161,13 +211,17 @@ def query_blocks(plan):
     return out
 
 
-def attention(qkv_r, cfg, plan, shared, bf16=True, blocks=None):
+def attention(qkv_r, cfg, plan, shared, bf16=True, blocks=None, q_g=None, k_g=None, ambiguity=False):
     """The attention step on qkv_r (float64 array with q, k already as
     ``qk_prep`` returns them).  shared: blended rows [n_union + n_tiles, d];
     else per-tile rows [n_tiles*(n+1), d].  ``blocks`` (shared only): indices
     into query_blocks(plan) to evaluate (default all); rows of other blocks
-    are left NaN.  Output values rounded to bf16 when ``bf16``."""
+    are left NaN.  Output values rounded to bf16 when ``bf16``.  q_g, k_g:
+    the QK-norm gains qkv_r was prepared with (they set the softmax offset).
+    ambiguity: also return, per output element, the bound on what softmax
+    weights of ambiguous rounding can move it (zero on the global rows)."""
     d, hd, H = cfg["d"], cfg["head_dim"], cfg["n_heads"]
+    fixed = fixed_offset(cfg, q_g, k_g)
     n, nt = plan.tile_tokens, plan.n_tiles
     rnd = _bf16 if bf16 else (lambda a: a)
     q, k, v = qkv_r[:, :d], qkv_r[:, d:2 * d], qkv_r[:, 2 * d:]
@@ -177,6 +231,7 @@ def attention(qkv_r, cfg, plan, shared, bf16=True, blocks=None):
     else:
         out = np.full((nt * (n + 1), d), np.nan)
         win = [np.arange(t * (n + 1), (t + 1) * (n + 1)) for t in range(nt)]
+    amb = np.zeros_like(out)
     for h in range(H):
         cs = slice(h * hd, (h + 1) * hd)
         for t in range(nt):                      # global query rows
@@ -193,14 +248,17 @@ def attention(qkv_r, cfg, plan, shared, bf16=True, blocks=None):
                 ext = _pad_to_wave(rows, rows[0])
                 groups = [np.arange(w0, w0 + WAVE) for w0 in range(0, len(ext), WAVE)]
                 acc = np.zeros((len(rows), hd))
+                acc_a = np.zeros((len(rows), hd))
                 for t in tiles:
                     K, V = k[win[t][:n], cs], v[win[t][:n], cs]
                     g = win[t][n]
-                    o = _window(q[ext, cs], K, V, k[g, cs], v[g, cs], hd, groups, bf16)[:len(rows)]
+                    o, a = _window(q[ext, cs], K, V, k[g, cs], v[g, cs], hd, groups, bf16, fixed)
                     wts = np.array([dict((tt, w) for tt, _, w in plan.cover_of(int(r)))[t] for r in rows],
                                    np.float32).astype(np.float64)
-                    acc += wts[:, None] * o
+                    acc += wts[:, None] * o[:len(rows)]
+                    acc_a += wts[:, None] * a[:len(rows)]
                 out[rows, cs] = rnd(acc)
+                amb[rows, cs] = acc_a
         else:
             for t in range(nt):
                 K, V = k[win[t][:n], cs], v[win[t][:n], cs]
@@ -209,5 +267,7 @@ def attention(qkv_r, cfg, plan, shared, bf16=True, blocks=None):
                 # query slots past the window end run its last token
                 ext = _pad_to_wave(rows, rows[-1])
                 groups = [np.arange(w0, w0 + WAVE) for w0 in range(0, len(ext), WAVE)]
-                out[rows, cs] = rnd(_window(q[ext, cs], K, V, k[g, cs], v[g, cs], hd, groups, bf16)[:n])
-    return out
+                o, a = _window(q[ext, cs], K, V, k[g, cs], v[g, cs], hd, groups, bf16, fixed)
+                out[rows, cs] = rnd(o[:n])
+                amb[rows, cs] = a[:n]
+    return (out, amb) if ambiguity else out

@@ -24,7 +24,8 @@ def test_model_without_rounding_is_the_oracle(case, shared):
     cfg = case_cfg(*case)
     pl, qkv, qg, kg = case_inputs(cfg, shared, 3.0)
     ref = oracle_attention(qkv, cfg, pl, shared, qg, kg)
-    got = AR.attention(AR.qk_prep(qkv, cfg, pl, shared, qg, kg, bf16=False), cfg, pl, shared, bf16=False)
+    got = AR.attention(AR.qk_prep(qkv, cfg, pl, shared, qg, kg, bf16=False), cfg, pl, shared, bf16=False,
+                       q_g=qg, k_g=kg)
     assert rel(got, ref) < 2e-5
 
 
@@ -35,12 +36,42 @@ def test_rounding_points_stay_under_the_caps(case, shared, qk_scale):
     cfg = case_cfg(*case)
     pl, qkv, qg, kg = case_inputs(cfg, shared, qk_scale)
     ref = oracle_attention(qkv, cfg, pl, shared, qg, kg)
-    got = AR.attention(AR.qk_prep(qkv, cfg, pl, shared, qg, kg), cfg, pl, shared)
+    got = AR.attention(AR.qk_prep(qkv, cfg, pl, shared, qg, kg), cfg, pl, shared, q_g=qg, k_g=kg)
     e = rel(got, ref)
     print(f"  rounding model max|err|/rms {e:.3e} (cap {CAP[qk_scale]})")
     assert e * 1.25 < CAP[qk_scale]
     # and the roundings are not vacuous: the model differs from the exact values
     assert e > 1e-3
+
+
+@pytest.mark.parametrize("gain", [1.0, 1.3, 1.8])
+@pytest.mark.parametrize("shared", [True, False])
+def test_fixed_offset_bounds_every_score(gain, shared):
+    """The premise of the bf16 kernel's fixed softmax offset under QK-RMSNorm:
+    on q and k as the library stores them (normalised, gains, RoPE, bf16),
+    every score times log2(e)/sqrt(hd) lies within the offset; past the limit
+    (gains x1.8) there is no offset and the kernel keeps a running maximum."""
+    case = [c for c in CASES if c[6] and c[7] == "bf16"][0]
+    cfg = case_cfg(*case)
+    pl, qkv, qg, kg = case_inputs(cfg, shared, 3.0)
+    qg, kg = (qg * np.float32(gain)).astype(np.float32), (kg * np.float32(gain)).astype(np.float32)
+    off = AR.fixed_offset(cfg, qg, kg)
+    if gain > 1.5:
+        assert off is None
+        return
+    assert off is not None and off == int(off)
+    x = AR.qk_prep(qkv, cfg, pl, shared, qg, kg)
+    d, hd = cfg["d"], cfg["head_dim"]
+    C = 1.0 / np.log(2.0) / np.sqrt(hd)
+    worst = 0.0
+    for h in range(cfg["n_heads"]):
+        q, k = x[:, h * hd:(h + 1) * hd], x[:, d + h * hd:d + (h + 1) * hd]
+        worst = max(worst, float(np.max(np.abs(q @ k.T))) * C)
+    print(f"  offset {off}, largest |score| x C {worst:.3f}")
+    assert worst <= off
+    # the row norms the bound rests on: at most sqrt(hd) max|q_g|, plus bf16 rounding
+    qn = np.linalg.norm(x[:, :hd], axis=1)
+    assert np.max(qn) <= np.sqrt(hd) * float(np.max(np.abs(qg))) * 1.005
 
 
 @pytest.mark.parametrize("grid,tile,stride,blend", [((2, 12, 20), (2, 8, 8), (2, 6, 6), "ramp"),

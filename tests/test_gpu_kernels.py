@@ -233,13 +233,16 @@ def check_attention(cfg, pl, qkv, q_g, k_g, shared, got, qkv_gpu, ref, emu_block
     assert np.array_equal(qkv_gpu[:, 2 * d:], np.asarray(qkv, np.float64)[:, 2 * d:])
     # 2. the attention on those q and k against the rounding model, element by
     #    element: one output rounding decision (2^-7 relative) plus fp32
-    #    accumulation and rare softmax-weight rounding decisions
-    emu = AR.attention(qkv_gpu, cfg, pl, shared, blocks=emu_blocks)
+    #    accumulation, plus one bf16 ulp of every softmax weight that lies too
+    #    close to a rounding midpoint for the model to tell which way the
+    #    GPU's fp32 weight rounds (attn_rounding._ambiguous_ulp)
+    emu, amb = AR.attention(qkv_gpu, cfg, pl, shared, blocks=emu_blocks, q_g=q_g, k_g=k_g, ambiguity=True)
     rms = float(np.sqrt(np.nanmean(emu[sel] ** 2)))
-    bound = 2.0 ** -7 * np.abs(emu[sel]) + 4e-3 * rms
+    bound = 2.0 ** -7 * np.abs(emu[sel]) + 4e-3 * rms + amb[sel]
     dev = np.abs(got[sel] - emu[sel])
     print(f"  qk bit-identical {same:.5f}; max|gpu-model|/rms {np.max(dev) / rms:.3e}, "
-          f"worst fraction of bound {np.max(dev / bound):.3f}")
+          f"worst fraction of bound {np.max(dev / bound):.3f}; ambiguous-weight term max/rms "
+          f"{np.max(amb[sel]) / rms:.2e}")
     bad = np.argwhere(dev > bound)
     assert len(bad) == 0, (len(bad), [(int(r), int(c), got[sel][r, c], emu[sel][r, c]) for r, c in bad[:5]])
     # 3. against the oracle, element by element: within what the rounding
@@ -272,6 +275,27 @@ def test_attention_step_against_oracle(case, shared, qk_scale):
     if cfg["dtype"] == "bf16":
         print(f"  max|gpu-oracle|/rms {e:.3e} (cap {AC.CAP[qk_scale]})")
         assert e < AC.CAP[qk_scale]
+
+
+@pytest.mark.parametrize("gain", [1.3, 1.8])
+@pytest.mark.parametrize("shared", [True, False])
+def test_attention_softmax_offset_edges(gain, shared):
+    """QK-norm gains scaled to near the fixed softmax offset's limit (1.3:
+    an offset of 31, weights down to 2^-62) and past it (1.8: the running
+    maximum under QK-norm), checked as the other attention cases; the logits
+    grow by gain^2, within the cap of qk_scale 3."""
+    cfg = AC.case_cfg(*AC.CASES[0])
+    assert cfg["qk_norm"]
+    say(f"attention step, QK-norm gains x{gain}, shared={shared}")
+    pl, qkv, q_g, k_g = AC.case_inputs(cfg, shared, 1.0)
+    q_g, k_g = (q_g * np.float32(gain)).astype(np.float32), (k_g * np.float32(gain)).astype(np.float32)
+    off = AR.fixed_offset(cfg, q_g, k_g)
+    assert (off is not None) == (gain < 1.5), off
+    got, qkv_gpu = run_attention_op(cfg, pl, qkv, q_g, k_g, shared)
+    ref = AC.oracle_attention(qkv, cfg, pl, shared, q_g, k_g)
+    e = check_attention(cfg, pl, qkv, q_g, k_g, shared, got, qkv_gpu, ref)
+    print(f"  offset {off}: max|gpu-oracle|/rms {e:.3e} (cap {AC.CAP[3.0]})")
+    assert e < AC.CAP[3.0]
 
 
 def test_attention_hard_stitching_blocks():
