@@ -307,7 +307,12 @@ ts_status ts_op_gemm_ws(int32_t dtype, int32_t epilogue, const void* a, const vo
  * RoPE -- then, for every tile t and head, dense softmax attention with scale
  * 1/sqrt(head_dim) over the tile's window (its tile_tokens rows plus its
  * global row).  qkv: device [rows, 3d] act_dtype, q | k | v as the QKV
- * projection writes them.
+ * projection writes them; with bf16 the q section is left multiplied by the
+ * softmax scale in the log2 domain, log2(e)/sqrt(head_dim), before its bf16
+ * rounding (the kernels' scores are then q.k), with fp32 it is left
+ * unscaled.  With QK-norm the softmax subtracts the static bound on the
+ * scores that the gains give (|q.k| <= head_dim max|q_g| max|k_g| times the
+ * scale) instead of a running maximum when that bound is at most 32.
  *  shared = 1: rows = n_union + n_tiles (grid rows, then the global row of
  *    tile t at n_union + t); out: device [n_union + n_tiles, d] act_dtype,
  *    row p < n_union the w-bar blend of the outputs of every window holding p

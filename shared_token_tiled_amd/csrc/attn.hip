@@ -6,7 +6,9 @@
 // q and k arrive normalised and rotated by qk_prep, which rotates every row
 // once by its grid coordinate (a tile's global row by the tile's start): a
 // score depends only on the two coordinates' difference, the same in every
-// tile, so rows are read in place and no per-tile copies are made.
+// tile, so rows are read in place and no per-tile copies are made.  In bf16
+// q also carries the softmax scale log2(e)/sqrt(hd), so q.k is a score in the
+// log2 domain of the exponentials.
 //
 // Three layouts of the query rows and outputs:
 //  - per tile: qkv rows and outputs t*(n+1)+i (tile t's window token i, its
@@ -39,6 +41,7 @@
 #include <cstdlib>
 #include <map>
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 #include "ts_kernels.h"
@@ -306,7 +309,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int xcd = blockIdx.x & 7;
   // With QK-RMSNorm a q or k head row has norm at most sqrt(hd) max|gain|
   // (the RMS-normalised vector has norm sqrt(hd), RoPE rotates it, bf16
-  // rounding adds < 0.4 %), so every score times C lies within +-bnd.  For
+  // rounding adds < 0.4 %), so every score, q carrying the factor
+  // C = log2(e)/sqrt(hd), lies within +-bnd.  For
   // bnd <= FIXED_MAX_LIMIT the softmax subtracts bnd instead of a running
   // max: every weight is in [2^-2bnd, 1], and the per-block max and rescale
   // go away.  bnd is an integer, so a weight is
@@ -333,6 +337,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const HalfRange xr = xcd_halves(p.H, xcd);
     njx = xr.na * p.half_a + xr.nb * (p.nblk - p.half_a);
   }
+  // The job loop in two versions, each with its registers to its own code:
+  // against the fixed offset, and with a running max.
+  auto job_loop = [&](auto fixed_tag) {
+  constexpr bool FIXED = decltype(fixed_tag)::value;
   for (int it = 0;; ++it) {
     int h = 0, t0 = 0, qblk = 0, blk = 0, npass = 1;
     if constexpr (BLEND) {
@@ -439,7 +447,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * g);
     }
-    const float C = p.scale_log2;
     float m_run = 0.f, l_run = 0.f;
     f32x16 oacc[NHB];
     // the window's global key is the softmax's initial state: score, weight 1, value
@@ -459,10 +466,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int e = 0; e < 8; ++e) sg += float(q[e]) * float(kg[e]);
       }
       sg += __shfl_xor(sg, 32, 64);
-      // weight of the global key: 1 against a running max started at its
-      // score, or 2^(score - bnd) against the fixed offset
-      m_run = fixedm ? bnd : sg * C;
-      const float w0 = fixedm ? __builtin_amdgcn_exp2f(sg * C - bnd) : 1.f;
+      // weight of the global key (q carries C, so sg is in the log2 domain):
+      // 1 against a running max started at its score, or 2^(sg - bnd)
+      // against the fixed offset
+      m_run = FIXED ? bnd : sg;
+      const float w0 = FIXED ? __builtin_amdgcn_exp2f(sg - bnd) : 1.f;
       l_run = g == 0 ? w0 : 0.f;
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
@@ -542,6 +550,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's DMA of the first blocks landed
     __syncthreads();
     const int krow_a = swap23(l32);  // key row this lane feeds as MFMA A row
+    // start of every score chain: -bnd against the fixed offset, else 0
+    f32x16 sinit;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sinit[r] = FIXED ? -bnd : 0.f;
     // V^T fragment addresses: lane 16G + j reads key row 8 (G / 2) + j / 4 (+16
     // per 16-key chunk, +4 for the second read) at hd dims hb*32 + 16 (G % 2) +
     // 4 (j % 4) .. +3; the swizzle depends only on the row's low bits, which
@@ -593,9 +605,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // ahead of the MFMAs that use them (four LDS reads kept in flight)
       f32x16 sacc[2];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.f;
+      for (int sb = 0; sb < 2; ++sb) sacc[sb] = sinit;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
@@ -627,13 +637,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // (one rescale check per block)
       bf16x8 pf[4];
       {
-        if (!fixedm) {
+        if constexpr (!FIXED) {
           float mx = -INFINITY;
 #pragma unroll
           for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * C;
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
           // rescale only when some query's block max passes its running max by 2^8
           if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_LOG2) != 0) {
             const float m_new = fmaxf(m_run, mx);
@@ -644,13 +654,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             for (int hb = 0; hb < NHB; ++hb) oacc[hb] *= alpha;
           }
         }
-        const float mneg = -m_run;
+        // against the fixed offset the scores already hold s - bnd (the
+        // chains start from -bnd), so a weight is one exponential
         float lsum = 0.f;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[sb][r], C, mneg));
+            const float pv = __builtin_amdgcn_exp2f(FIXED ? sacc[sb][r] : sacc[sb][r] - m_run);
             lsum += pv;
             pf[sb * 2 + (r >> 3)][r & 7] = bf16(pv);
           }
@@ -698,6 +709,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
      window_finish(ps);
     }
   }  // jobs
+  };
+  if (fixedm) job_loop(std::true_type{});
+  else job_loop(std::false_type{});
 }
 
 // Global-token query row of one (head, tile), over the window keys
@@ -755,7 +769,7 @@ __global__ __launch_bounds__(NT) void k_attn_global_bf16(AttnP p, int split_keys
 #pragma unroll
       for (int o = 1; o < TPK; o <<= 1) sc += __shfl_xor(sc, o);
       if (sub == 0) {
-        s_s[jj] = sc * p.scale_log2;
+        s_s[jj] = sc;  // q carries log2(e)/sqrt(hd): the log2 domain
         r_s[jj] = int(r);
       }
     }

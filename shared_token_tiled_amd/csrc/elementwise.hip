@@ -2,6 +2,8 @@
 // blend (shared layers) and state merge (layer k), the per-tile gather, and
 // e4m3 quantisation.  All are one pass over HBM; rows are handled by whole
 // wavefronts with 16-byte (fp32) or 8-byte (bf16) vector accesses.
+#include <type_traits>
+
 #include "device_common.h"
 #include "ts_kernels.h"
 
@@ -190,6 +192,13 @@ __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int 
         const float x = v[2 * e], y = v[2 * e + 1];
         v[2 * e] = x * cs[e].x - y * cs[e].y;
         v[2 * e + 1] = x * cs[e].y + y * cs[e].x;
+      }
+      // bf16: q takes the softmax scale log2(e)/sqrt(hd) before its one
+      // rounding, so the attention's q.k is already in the log2 domain
+      if (std::is_same<T, bf16>::value && sl < H) {
+        constexpr float QSCALE = 1.4426950408889634f / (HD == 128 ? 11.313708498984761f : HD == 64 ? 8.0f : 5.656854249492381f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= QSCALE;
       }
       if (ok && sl < ns) store8(base + sl * HD, f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]});
     }

@@ -5,13 +5,16 @@ bf16 path rounds, so that the attention tests can bound the GPU's deviation
 from the oracle by what those roundings produce, element by element.
 
 The step (``ts_op_attention``, and the attention of every layer) rounds at:
-  1. q and k after QK-RMSNorm and RoPE: computed in fp32, stored as bf16.
-     RoPE turns every row by its grid coordinate (a tile's global row by the
-     tile's start); a score depends only on the coordinate difference, so this
-     equals the pages' tile-local rotation before rounding (Table S1: RoPE per
-     tile on tile coordinates);
+  1. q and k after QK-RMSNorm and RoPE: computed in fp32, stored as bf16, q
+     multiplied first by the softmax scale log2(e)/sqrt(hd) (fp32), so q.k is
+     a score s*log2(e)/sqrt(hd) in the log2 domain.  RoPE turns every row by
+     its grid coordinate (a tile's global row by the tile's start); a score
+     depends only on the coordinate difference, so this equals the pages'
+     tile-local rotation before rounding (Table S1: RoPE per tile on tile
+     coordinates);
   2. the softmax weights of the window's tile tokens: 2^(s*log2(e)/sqrt(hd) - m)
-     rounded to bf16 as the P operand of the PV product; the weight sum uses
+     rounded to bf16 as the P operand of the PV product (against the fixed
+     offset the MFMA chains start from -m); the weight sum uses
      the unrounded weights; the global key's weight is never rounded.  With
      QK-RMSNorm every score obeys |s| <= hd max|q_g| max|k_g| (normalised rows
      have norm sqrt(hd), RoPE rotates them), and m is that bound, rounded up
@@ -40,6 +43,12 @@ FIXED_MAX_LIMIT = 32.0
 AMBIG_TOL = 2.0 ** -15   # relative distance of a weight from a bf16 rounding midpoint
 
 
+def q_scale(hd):
+    """log2(e)/sqrt(hd) as the library forms it in fp32: the bf16 path's
+    q_prep multiplies q by it, so q.k is a score in the log2 domain."""
+    return np.float32(1.4426950408889634) / np.sqrt(np.float32(hd))
+
+
 def fixed_offset(cfg, q_g, k_g):
     """The fixed softmax offset of the bf16 kernel under QK-RMSNorm (log2
     domain): ceil(1.01 hd C max|q_g| max|k_g| + 1e-3) with C = log2(e)/sqrt(hd)
@@ -48,7 +57,7 @@ def fixed_offset(cfg, q_g, k_g):
     if not cfg.get("qk_norm") or q_g is None or k_g is None:
         return None
     hd = cfg["head_dim"]
-    C = float(np.float32(1.4426950408889634) / np.sqrt(np.float32(hd)))
+    C = float(q_scale(hd))
     b = math.ceil(1.01 * hd * C * float(np.max(np.abs(q_g))) * float(np.max(np.abs(k_g))) + 1e-3)
     return float(b) if b <= FIXED_MAX_LIMIT else None
 
@@ -115,6 +124,11 @@ def qk_prep(qkv, cfg, plan, shared, q_g=None, k_g=None, bf16=True, terms=False):
         out = np.empty_like(v)
         out[:, 0::2] = a * ang_c - b * ang_s
         out[:, 1::2] = a * ang_s + b * ang_c
+        if bf16 and sl < H:
+            # q takes the softmax scale log2(e)/sqrt(hd) (fp32) before its rounding
+            out = out * q_scale(hd)
+            if terms:
+                mag[:, cs] *= float(q_scale(hd))
         x[:, cs] = round_bf16(out) if bf16 else out
     return (x.astype(np.float64), mag) if terms else x.astype(np.float64)
 
@@ -132,14 +146,15 @@ def _ambiguous_ulp(p):
     return np.where(pos & (np.abs(p - mid) < AMBIG_TOL * p), ulp, 0.0)
 
 
-def _window(qs, K, V, kg, vg, hd, groups, round_p=True, fixed=None):
+def _window(qs, K, V, kg, vg, hd, groups, round_p=True, fixed=None, C=None):
     """Unnormalised output and weight sum of queries qs [nq, hd] over one
     window (tile keys K, V [n, hd], global key kg, vg), against the fixed
     offset ``fixed`` or with the running maximum shared by the queries of each
     group (list of index arrays).  Returns o = O / l [nq, hd] and the bound
     sum_j ulp_j |V_j| / l over the weights whose rounding is ambiguous
     (_ambiguous_ulp), both float64."""
-    C = (1.0 / math.log(2.0)) / math.sqrt(hd)
+    if C is None:
+        C = (1.0 / math.log(2.0)) / math.sqrt(hd)
     n = K.shape[0]
     aV = np.abs(V)
     sl = (qs @ K.T) * C                         # scores, log2 domain
@@ -181,10 +196,15 @@ def _window(qs, K, V, kg, vg, hd, groups, round_p=True, fixed=None):
     return O / L[:, None], A / L[:, None]
 
 
-def _global_row(qg, K, V, kg, vg, hd):
-    """The global token's query over its window, fp32 weights (not rounded)."""
-    s = np.concatenate([K @ qg, [kg @ qg]]) / math.sqrt(hd)
-    e = np.exp(s - s.max())
+def _global_row(qg, K, V, kg, vg, hd, log2_q=False):
+    """The global token's query over its window, fp32 weights (not rounded).
+    log2_q: qg carries log2(e)/sqrt(hd) (the bf16 path)."""
+    if log2_q:
+        s = np.concatenate([K @ qg, [kg @ qg]])
+        e = np.exp2(s - s.max())
+    else:
+        s = np.concatenate([K @ qg, [kg @ qg]]) / math.sqrt(hd)
+        e = np.exp(s - s.max())
     return (e[:-1] @ V + e[-1] * vg) / e.sum()
 
 
@@ -222,6 +242,8 @@ def attention(qkv_r, cfg, plan, shared, bf16=True, blocks=None, q_g=None, k_g=No
     weights of ambiguous rounding can move it (zero on the global rows)."""
     d, hd, H = cfg["d"], cfg["head_dim"], cfg["n_heads"]
     fixed = fixed_offset(cfg, q_g, k_g)
+    # bf16: q as qk_prep leaves it, carrying log2(e)/sqrt(hd); scores in the log2 domain
+    C = 1.0 if bf16 else None
     n, nt = plan.tile_tokens, plan.n_tiles
     rnd = _bf16 if bf16 else (lambda a: a)
     q, k, v = qkv_r[:, :d], qkv_r[:, d:2 * d], qkv_r[:, 2 * d:]
@@ -238,7 +260,7 @@ def attention(qkv_r, cfg, plan, shared, bf16=True, blocks=None, q_g=None, k_g=No
             K, V = k[win[t][:n], cs], v[win[t][:n], cs]
             g = win[t][n]
             row = plan.n_union + t if shared else g
-            out[row, cs] = rnd(_global_row(q[g, cs], K, V, k[g, cs], v[g, cs], hd))
+            out[row, cs] = rnd(_global_row(q[g, cs], K, V, k[g, cs], v[g, cs], hd, bf16))
         if shared:
             qb = query_blocks(plan)
             for bi in (range(len(qb)) if blocks is None else blocks):
@@ -252,7 +274,7 @@ def attention(qkv_r, cfg, plan, shared, bf16=True, blocks=None, q_g=None, k_g=No
                 for t in tiles:
                     K, V = k[win[t][:n], cs], v[win[t][:n], cs]
                     g = win[t][n]
-                    o, a = _window(q[ext, cs], K, V, k[g, cs], v[g, cs], hd, groups, bf16, fixed)
+                    o, a = _window(q[ext, cs], K, V, k[g, cs], v[g, cs], hd, groups, bf16, fixed, C)
                     wts = np.array([dict((tt, w) for tt, _, w in plan.cover_of(int(r)))[t] for r in rows],
                                    np.float32).astype(np.float64)
                     acc += wts[:, None] * o[:len(rows)]
@@ -267,7 +289,7 @@ def attention(qkv_r, cfg, plan, shared, bf16=True, blocks=None, q_g=None, k_g=No
                 # query slots past the window end run its last token
                 ext = _pad_to_wave(rows, rows[-1])
                 groups = [np.arange(w0, w0 + WAVE) for w0 in range(0, len(ext), WAVE)]
-                o, a = _window(q[ext, cs], K, V, k[g, cs], v[g, cs], hd, groups, bf16, fixed)
+                o, a = _window(q[ext, cs], K, V, k[g, cs], v[g, cs], hd, groups, bf16, fixed, C)
                 out[rows, cs] = rnd(o[:n])
                 amb[rows, cs] = a[:n]
     return (out, amb) if ambiguity else out
