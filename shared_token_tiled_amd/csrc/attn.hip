@@ -448,6 +448,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * g);
     }
     float m_run = 0.f, l_run = 0.f;
+    // start of every score chain, -m: the accumulators hold s - m and a
+    // weight is one exponential (-bnd against the fixed offset; with a
+    // running max, set by each window's start and each rescale)
+    f32x16 sinit;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sinit[r] = FIXED ? -bnd : 0.f;
     f32x16 oacc[NHB];
     // the window's global key is the softmax's initial state: score, weight 1, value
     auto window_init = [&](int t) {
@@ -471,6 +477,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // against the fixed offset
       m_run = FIXED ? bnd : sg;
       const float w0 = FIXED ? __builtin_amdgcn_exp2f(sg - bnd) : 1.f;
+      if constexpr (!FIXED) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sinit[r] = -sg;
+      }
       l_run = g == 0 ? w0 : 0.f;
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
@@ -550,10 +560,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's DMA of the first blocks landed
     __syncthreads();
     const int krow_a = swap23(l32);  // key row this lane feeds as MFMA A row
-    // start of every score chain: -bnd against the fixed offset, else 0
-    f32x16 sinit;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sinit[r] = FIXED ? -bnd : 0.f;
     // V^T fragment addresses: lane 16G + j reads key row 8 (G / 2) + j / 4 (+16
     // per 16-key chunk, +4 for the second read) at hd dims hb*32 + 16 (G % 2) +
     // 4 (j % 4) .. +3; the swizzle depends only on the row's low bits, which
@@ -638,30 +644,37 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       bf16x8 pf[4];
       {
         if constexpr (!FIXED) {
+          // the accumulators hold s - m: the block max past the running max
           float mx = -INFINITY;
 #pragma unroll
           for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
           mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          // rescale only when some query's block max passes its running max by 2^8
-          if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_LOG2) != 0) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
+          // rescale only when some query's block max passes its running max
+          // by 2^8: each query of the wavefront raises its max to its block
+          // max (if larger), and its scores follow
+          if (__builtin_amdgcn_ballot_w64(mx > RESCALE_LOG2) != 0) {
+            const float up = fmaxf(mx, 0.f);
+            const float alpha = __builtin_amdgcn_exp2f(-up);
+            m_run += up;
             l_run *= alpha;
 #pragma unroll
             for (int hb = 0; hb < NHB; ++hb) oacc[hb] *= alpha;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) sacc[sb] -= up;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sinit[r] = -m_run;
           }
         }
-        // against the fixed offset the scores already hold s - bnd (the
-        // chains start from -bnd), so a weight is one exponential
+        // the scores already hold s - m (the chains start from -m), so a
+        // weight is one exponential
         float lsum = 0.f;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(FIXED ? sacc[sb][r] : sacc[sb][r] - m_run);
+            const float pv = __builtin_amdgcn_exp2f(sacc[sb][r]);
             lsum += pv;
             pf[sb * 2 + (r >> 3)][r & 7] = bf16(pv);
           }
