@@ -34,9 +34,12 @@
 // and V blocks go from the qkv rows straight into LDS ([key][hd], 16-byte
 // chunks XOR-swizzled by key) with global_load_lds, three blocks in flight;
 // V^T fragments are read with the transposing LDS load ds_read_b64_tr_b16,
-// so V is never copied transposed.  The key rows of a window come through a
-// four-slot LDS ring filled three blocks ahead.  The windows of a query block
-// form one stream of key blocks, so the staging runs on across windows.
+// so V is never copied transposed.  The key rows of a window come through an
+// eight-slot LDS ring filled five blocks ahead.  The windows of a query block
+// form one stream of key blocks, so the staging runs on across windows.  The
+// score MFMA chains start from the softmax offset (-m), so a weight is one
+// exponential of an accumulator; under QK-norm that offset is a static bound
+// on the scores and needs no running max.
 #include <algorithm>
 #include <cstdlib>
 #include <map>

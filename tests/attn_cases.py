@@ -23,6 +23,7 @@ CASES = [
     (3, (2, 12, 28), (2, 12, 12), (2, 8, 8), 3, 64, False, "bf16"),
     (2, (1, 20, 36), (1, 16, 16), (1, 12, 12), 2, 64, False, "bf16"),
     (3, (2, 12, 20), (2, 8, 8), (2, 6, 6), 2, 128, False, "bf16"),
+    (2, (1, 20, 36), (1, 16, 16), (1, 12, 12), 2, 64, True, "bf16"),
     (2, (1, 16, 24), (1, 16, 16), (1, 8, 8), 2, 32, False, "f32"),
     (3, (2, 9, 10), (2, 7, 5), (2, 3, 3), 2, 64, False, "f32"),
 ]
