@@ -372,8 +372,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bf16* kbase = qkv + p.d + h * HD;
     const bf16* vbase = qkv + 2 * p.d + h * HD;
     const int nblocks = npass * nkb;  // key blocks streamed over all windows
+    // the job's window tiles: uniform plan data that no launch writes, read
+    // through the scalar cache, so that reading one (when the key-row stream
+    // enters the next window) waits on scalar loads only, not on the K / V
+    // loads in flight
     auto tile_of = [&](int ps) -> int {
-      if constexpr (BLEND) return p.blk_tiles[blk * p.maxc + ps];
+      if constexpr (BLEND)
+        return ((const __attribute__((address_space(4))) int*)p.blk_tiles)[__builtin_amdgcn_readfirstlane(blk * p.maxc + ps)];
       else return t0;
     };
 
