@@ -312,7 +312,9 @@ ts_status ts_op_gemm_ws(int32_t dtype, int32_t epilogue, const void* a, const vo
  * rounding (the kernels' scores are then q.k), with fp32 it is left
  * unscaled.  With QK-norm the softmax subtracts the static bound on the
  * scores that the gains give (|q.k| <= head_dim max|q_g| max|k_g| times the
- * scale) instead of a running maximum when that bound is at most 32.
+ * scale) instead of a running maximum when that bound is at most 32; in bf16
+ * without QK-norm, the bound max|q| max|k| over the q and k heads of all rows
+ * as stored (Cauchy-Schwarz), under the same limit.
  *  shared = 1: rows = n_union + n_tiles (grid rows, then the global row of
  *    tile t at n_union + t); out: device [n_union + n_tiles, d] act_dtype,
  *    row p < n_union the w-bar blend of the outputs of every window holding p
@@ -330,9 +332,10 @@ ts_status ts_op_attention(const ts_model_desc* model, const ts_plan* plan, int32
 
 /* For callers that cannot allocate device memory (code under graph capture,
  * serving loops, harnesses that forbid hipMalloc): ts_op_attention with no
- * workspace argument.  Its scratch -- 256 bytes of job counters (zeroed by
- * the call), the fp32 partial blends of the shared layout (n_union * d * 4
- * bytes) and the global rows' split states -- lives
+ * workspace argument.  Its scratch -- 256 bytes of job counters and 256 of
+ * the largest q and k head norms (both set by the call), the fp32 partial
+ * blends of the shared layout (n_union * d * 4 bytes) and the global rows'
+ * split states -- lives
  * in a file-scope device array of TS_NOALLOC_SCRATCH_BYTES that every GPU the
  * library runs on holds until the process ends; the call allocates nothing.
  * A request whose counters and partial blends exceed the array returns TS_EWORKSPACE

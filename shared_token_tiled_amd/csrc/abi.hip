@@ -155,6 +155,7 @@ struct WS {
   int64_t gpart_floats = 0;
   float* gsplit = nullptr;   // fp32 K-split parts of a GEMM's partial last round of tiles
   unsigned* jobs = nullptr;  // job counters of the blended attention
+  unsigned* qkn = nullptr;   // bf16 without QK-norm: qk_prep's largest q and k head norms
   size_t bytes = 0;
 };
 
@@ -193,6 +194,7 @@ WS layout(const ts_model_desc* m, const ts_plan* p, bool states, bool per_tile, 
   }
   if (m->act_dtype != TS_F32) w.gsplit = (float*)take(TS_GEMM_SPLIT_WS_BYTES);
   if (m->act_dtype == TS_BF16) w.jobs = (unsigned*)take(tsk::JOB_COUNTERS_BYTES);
+  if (m->act_dtype == TS_BF16 && !m->qk_norm) w.qkn = (unsigned*)take(tsk::QKN_BYTES);
   w.bytes = off;
   return w;
 }
@@ -284,11 +286,13 @@ tsk::RopeRows rope_rows(const ts_plan* p, bool shared) {
 enum AttnLayout { ATT_TILED, ATT_SHARED_ROWS, ATT_BLENDED };
 ts_status window_attention(const ts_model_desc* m, const ts_plan* p, AttnLayout lay, const void* qkv, void* out,
                            float* part, unsigned* jobs, unsigned* amax, hipStream_t s, float* gscratch,
-                           int64_t gscratch_floats, const float* q_g, const float* k_g) {
+                           int64_t gscratch_floats, const float* q_g, const float* k_g, const unsigned* qkn) {
   tsk::AttnArgs a;
   if (m->qk_norm) {
     a.qg = q_g;
     a.kg = k_g;
+  } else {
+    a.qkn = qkn;  // the score bound from qk_prep's largest norms (bf16)
   }
   a.qkv = qkv;
   a.out = out;
@@ -385,7 +389,7 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
   {
     Scope sc(c.s, "qk_prep", 0.0, double(Mq * 2 * d) * 2 * ab);
     TS_HIP(tsk::qk_prep(c.s, act, ws.big, int(Mq), d, H, hd, m->qk_norm ? w.q_g : nullptr, w.k_g, m->eps,
-                        rope_rows(p, qsh)),
+                        rope_rows(p, qsh), ws.qkn),
            "qk_prep");
   }
   // shared layers: the w-bar blend of the windows' outputs is formed by the
@@ -394,7 +398,7 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
   const void* aout = shared ? ws.h : ws.o;
   if ((st = window_attention(m, p, shared ? ATT_BLENDED : (qsh ? ATT_SHARED_ROWS : ATT_TILED), ws.big,
                              const_cast<void*>(aout), (float*)ws.o, ws.jobs, am_out, c.s, ws.gpart,
-                             ws.gpart_floats, w.q_g, w.k_g)) != TS_OK)
+                             ws.gpart_floats, w.q_g, w.k_g, ws.qkn)) != TS_OK)
     return st;
   if ((st = proj(c, ws, (f8 & TS_FP8_OUT) != 0, "out", tsk::EPI_RESID, aout, M, d, d, w.w_o, w.w_o_f8,
                  w.w_scale_f8 ? w.w_scale_f8 + 1 : nullptr, w.b_o, x, am_out != nullptr)) != TS_OK)
@@ -458,11 +462,11 @@ ts_status run_layer_partial(const Ctx& c, const ts_layer_weights& w, float* X, i
   {
     Scope sc(c.s, "qk_prep", 0.0, double(Mq * 2 * d) * 2 * ab);
     TS_HIP(tsk::qk_prep(c.s, act, ws.big, int(Mq), d, H, hd, m->qk_norm ? w.q_g : nullptr, w.k_g, m->eps,
-                        rope_rows(p, sq)),
+                        rope_rows(p, sq), ws.qkn),
            "qk_prep");
   }
   if ((st = window_attention(m, p, sq ? ATT_SHARED_ROWS : ATT_TILED, ws.big, ws.o, nullptr, nullptr, nullptr, c.s,
-                             ws.gpart, ws.gpart_floats, w.q_g, w.k_g)) != TS_OK)
+                             ws.gpart, ws.gpart_floats, w.q_g, w.k_g, ws.qkn)) != TS_OK)
     return st;
   // out-projection
   if (so) {
@@ -680,17 +684,17 @@ ts_status check_op_attention(const ts_model_desc* m, const ts_plan* p, void* qkv
 // attention (blended when shared), with the partial blends in `part` (fp32
 // [n_union, d], shared only) and the global rows' split states in gpart.
 ts_status op_attention_impl(const ts_model_desc* m, const ts_plan* p, bool shared, void* qkv, const float* q_g,
-                            const float* k_g, void* out, float* part, unsigned* jobs, float* gpart,
+                            const float* k_g, void* out, float* part, unsigned* jobs, unsigned* qkn, float* gpart,
                             int64_t gpart_floats, hipStream_t s) {
   const int64_t M = shared ? int64_t(p->n_union) + p->n_tiles : int64_t(p->n_tiles) * (p->n + 1);
   {
     Scope sc(s, "qk_prep", 0.0, double(M * 2 * m->d) * 2 * act_bytes(m->act_dtype));
     TS_HIP(tsk::qk_prep(s, m->act_dtype, qkv, int(M), m->d, m->n_heads, m->head_dim, m->qk_norm ? q_g : nullptr, k_g,
-                        m->eps, rope_rows(p, shared)),
+                        m->eps, rope_rows(p, shared), qkn),
            "qk_prep");
   }
   return window_attention(m, p, shared ? ATT_BLENDED : ATT_TILED, qkv, out, part, jobs, nullptr, s, gpart,
-                          gpart_floats, q_g, k_g);
+                          gpart_floats, q_g, k_g, qkn);
 }
 
 // ---- scratch of the no-allocation entry point --------------------------
@@ -977,18 +981,18 @@ ts_status ts_op_attention(const ts_model_desc* m, const ts_plan* p, int32_t shar
   WS w0 = layout(m, p, false, false, false, nullptr);
   if ((st = check_ws(ws, ws_bytes, w0.bytes)) != TS_OK) return st;
   WS w = layout(m, p, false, false, false, (char*)ws);
-  return op_attention_impl(m, p, shared != 0, qkv, q_g, k_g, out, (float*)w.o, w.jobs, w.gpart, w.gpart_floats,
-                           (hipStream_t)stream);
+  return op_attention_impl(m, p, shared != 0, qkv, q_g, k_g, out, (float*)w.o, w.jobs, w.qkn, w.gpart,
+                           w.gpart_floats, (hipStream_t)stream);
 }
 
 ts_status ts_op_attention_noalloc(const ts_model_desc* m, const ts_plan* p, int32_t shared, void* qkv,
                                   const float* q_g, const float* k_g, void* out, void* stream) {
   ts_status st;
   if ((st = check_op_attention(m, p, qkv, q_g, k_g, out)) != TS_OK) return st;
-  // the job counters, then the fp32 partial blends of the shared layout, the
-  // global rows' split states in the rest (the split count shrinks to what
-  // fits)
-  const size_t jobs_bytes = tsk::JOB_COUNTERS_BYTES;
+  // the job counters and the two largest head norms, then the fp32 partial
+  // blends of the shared layout, the global rows' split states in the rest
+  // (the split count shrinks to what fits)
+  const size_t jobs_bytes = tsk::JOB_COUNTERS_BYTES + tsk::QKN_BYTES;
   const size_t part_bytes = shared ? align256(size_t(p->n_union) * m->d * 4) : 0;
   if (jobs_bytes + part_bytes > TS_NOALLOC_SCRATCH_BYTES)
     return fail(TS_EWORKSPACE, "ts_op_attention_noalloc: the partial blends need " + std::to_string(part_bytes) +
@@ -997,7 +1001,9 @@ ts_status ts_op_attention_noalloc(const ts_model_desc* m, const ts_plan* p, int3
   char* base = nullptr;
   if ((st = noalloc_scratch(&base)) != TS_OK) return st;
   const int64_t gfloats = int64_t((TS_NOALLOC_SCRATCH_BYTES - jobs_bytes - part_bytes) / 4);
-  return op_attention_impl(m, p, shared != 0, qkv, q_g, k_g, out, (float*)(base + jobs_bytes), (unsigned*)base,
+  unsigned* qkn =
+      m->act_dtype == TS_BF16 && !m->qk_norm ? (unsigned*)(base + tsk::JOB_COUNTERS_BYTES) : nullptr;
+  return op_attention_impl(m, p, shared != 0, qkv, q_g, k_g, out, (float*)(base + jobs_bytes), (unsigned*)base, qkn,
                            (float*)(base + jobs_bytes + part_bytes), gfloats, (hipStream_t)stream);
 }
 

@@ -71,6 +71,7 @@ struct AttnP {
   unsigned* amax;
   const float* qg;   // QK-norm gains [hd] or null
   const float* kg;
+  const unsigned* qkn;  // without QK-norm: largest q and k head norms (float bits) or null
 };
 
 constexpr int QB = 256;  // query rows per workgroup (both kernels)
@@ -333,6 +334,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     bnd = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                                          int, ceilf(1.01f * float(HD) * p.scale_log2 * gq * gk + 1e-3f))));
+    fixedm = bnd <= FIXED_MAX_LIMIT;
+  } else if (p.qkn) {
+    // Without QK-norm, qk_prep's largest q and k head norms bound every score
+    // the same way (Cauchy-Schwarz; q carries C): |q.k| <= max|q| max|k|
+    const float qm = __uint_as_float(p.qkn[0]), km = __uint_as_float(p.qkn[1]);
+    bnd = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                        __builtin_bit_cast(int, ceilf(1.01f * qm * km + 1e-3f))));
     fixedm = bnd <= FIXED_MAX_LIMIT;
   }
   int njx = 0;  // blended: the XCD's job count
@@ -874,7 +882,7 @@ static AttnP make_params(const AttnArgs& a) {
   return AttnP{a.qkv,       a.out,       a.part, a.rows, a.g0, a.gstep, a.blk_nt, a.blk_tiles, a.blk_rows, a.blk_w, a.nblk, a.maxc,
                a.blk_order, a.blk_cls,   a.ncls,           a.half_a, a.jobs,
                a.n_union,   a.d,         a.H,    a.n_tiles,        a.n,
-               1.4426950408889634f / sqrtf(float(a.hd)),           a.amax, a.qg, a.kg};
+               1.4426950408889634f / sqrtf(float(a.hd)),           a.amax, a.qg, a.kg, a.qkn};
 }
 
 __global__ void k_zero_jobs(unsigned* jobs) {

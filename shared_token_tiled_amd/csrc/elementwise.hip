@@ -121,10 +121,14 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, int M
 // of pair i of axis a is coord_a * base^(-i / pairs_a), so the score of two
 // window tokens depends only on their coordinate difference, as with
 // tile-local positions, and the attention kernels stage keys unchanged.
+// qkn (optional): the largest q-head and k-head norms of the rows as stored,
+// as float bits (atomic max per workgroup, skipped where the slot already
+// holds more).
 template <typename T, int HD, bool NORM>
 __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int d, int H,
                                                 const float* __restrict__ qg,
-                                                const float* __restrict__ kg, float eps, tsk::RopeRows rr) {
+                                                const float* __restrict__ kg, float eps, tsk::RopeRows rr,
+                                                unsigned* __restrict__ qkn) {
   constexpr int LPS = HD / 8;    // lanes per row
   constexpr int RPW = 64 / LPS;  // rows per wavefront
   constexpr int U = 4;           // head slices in flight per lane
@@ -164,6 +168,7 @@ __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int 
   }
   T* base = qkv + int64_t(r) * 3 * d + sub * 8;
   const int ns = 2 * H;
+  float mq = 0.f, mk = 0.f;  // largest squared head norms as stored (qkn)
   for (int s0 = 0; s0 < ns; s0 += U) {
     f32x4 a[U], c[U];
 #pragma unroll
@@ -201,8 +206,44 @@ __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int 
         for (int e = 0; e < 8; ++e) v[e] *= QSCALE;
       }
       if (ok && sl < ns) store8(base + sl * HD, f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]});
+      if (qkn) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = float(T(v[e]));
+          ss += x * x;
+        }
+        ss = group_sum(ss, LPS);
+        if (ok && sl < ns) {
+          if (sl < H) mq = fmaxf(mq, ss);
+          else mk = fmaxf(mk, ss);
+        }
+      }
     }
   }
+  if (qkn) {  // uniform: a kernel argument
+    __shared__ float red[2][4];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      mq = fmaxf(mq, __shfl_xor(mq, o, 64));
+      mk = fmaxf(mk, __shfl_xor(mk, o, 64));
+    }
+    if (lane == 0) {
+      red[0][threadIdx.x >> 6] = mq;
+      red[1][threadIdx.x >> 6] = mk;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      const int t = threadIdx.x;
+      const float m = fmaxf(fmaxf(red[t][0], red[t][1]), fmaxf(red[t][2], red[t][3]));
+      const unsigned bits = __float_as_uint(sqrtf(m));
+      if (bits > __hip_atomic_load(qkn + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(qkn + t, bits);
+    }
+  }
+}
+
+__global__ void k_zero_qkn(unsigned* qkn) {
+  if (threadIdx.x < tsk::QKN_BYTES / 4) qkn[threadIdx.x] = 0u;
 }
 
 // ---- w-bar blend / state merge (Figure 2 caption: the only approximate step)
@@ -411,16 +452,17 @@ hipError_t norm(hipStream_t s, int act, bool rms, const float* x, int M, int d, 
 }
 
 hipError_t qk_prep(hipStream_t s, int act, void* qkv, int M, int d, int H, int hd, const float* qg,
-                   const float* kg, float eps, const RopeRows& rr) {
-  if (M <= 0) return hipSuccess;
+                   const float* kg, float eps, const RopeRows& rr, unsigned* qkn) {
+  if (qkn) hipLaunchKernelGGL(k_zero_qkn, dim3(1), dim3(64), 0, s, qkn);
+  if (M <= 0) return hipGetLastError();
   // four wavefronts per block, 512 / hd rows per wavefront
   const int64_t rows_per_block = 4 * (512 / hd);
   const dim3 grid(unsigned((M + rows_per_block - 1) / rows_per_block)), block(256);
   const bool norm = qg != nullptr;
 #define TS_QK(T, HD)                                                                                         \
   do {                                                                                                       \
-    if (norm) hipLaunchKernelGGL((k_qkprep<T, HD, true>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps, rr); \
-    else hipLaunchKernelGGL((k_qkprep<T, HD, false>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps, rr);    \
+    if (norm) hipLaunchKernelGGL((k_qkprep<T, HD, true>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps, rr, qkn); \
+    else hipLaunchKernelGGL((k_qkprep<T, HD, false>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps, rr, qkn);    \
   } while (0)
   if (act == ACT_F32) {
     if (hd == 32) TS_QK(float, 32); else if (hd == 64) TS_QK(float, 64); else TS_QK(float, 128);

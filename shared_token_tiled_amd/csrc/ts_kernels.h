@@ -39,9 +39,13 @@ struct RopeRows {
   int off[3], pairs[3];
 };
 // In place on the q and k heads of qkv [M, 3d]: QK-RMSNorm with gains qg, kg
-// (skipped when qg is null), then RoPE by the rows' coordinates.
+// (skipped when qg is null), then RoPE by the rows' coordinates.  qkn
+// (optional, bf16, without QK-norm; QKN_BYTES): set to the largest norm of a
+// q head and of a k head over all M rows as stored (float bits in qkn[0],
+// qkn[1]), zeroed first by qk_prep itself.
+constexpr int QKN_BYTES = 256;
 hipError_t qk_prep(hipStream_t s, int act, void* qkv, int M, int d, int H, int hd, const float* qg,
-                   const float* kg, float eps, const RopeRows& rr);
+                   const float* kg, float eps, const RopeRows& rr, unsigned* qkn = nullptr);
 // out_union[p] = sum_e w[e] * in[entry_row[e]] over cover_ptr[p]..cover_ptr[p+1];
 // out_global[t] = in[t*(n+1)+n] (skipped when out_global is null).
 // amax (optional): atomic max of |output| as stored, over both outputs.
@@ -120,6 +124,9 @@ struct AttnArgs {
   // |q.k| <= hd max|q_g| max|k_g|, a fixed softmax offset (bf16 kernel)
   const float* qg = nullptr;
   const float* kg = nullptr;
+  // without QK-norm (bf16): qk_prep's largest q and k head norms, or null:
+  // every score obeys |q.k| <= max|q| max|k| (Cauchy-Schwarz), the same use
+  const unsigned* qkn = nullptr;
 };
 // fp32: every query row, the global rows included.  bf16: the tile-token
 // query rows; the global-token rows are attention_global's.

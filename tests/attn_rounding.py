@@ -62,6 +62,21 @@ def fixed_offset(cfg, q_g, k_g):
     return float(b) if b <= FIXED_MAX_LIMIT else None
 
 
+def norm_offset(q, k, H, hd):
+    """The fixed softmax offset of the bf16 kernel without QK-norm (log2
+    domain; q carries log2(e)/sqrt(hd)): by Cauchy-Schwarz every score obeys
+    |q.k| <= max|q_h| max|k_h| over all rows and heads of q, k as qk_prep
+    stored them; the offset is ceil(1.01 max|q| max|k| + 1e-3), norms and
+    product in fp32 as the library forms them, when at most FIXED_MAX_LIMIT;
+    else None (running maximum)."""
+    def top(a):
+        a = np.asarray(a, np.float32).reshape(len(a), H, hd)
+        return np.float32(np.sqrt((a * a).sum(axis=-1, dtype=np.float32)).max())
+    qm, km = top(q), top(k)
+    b = math.ceil(float(np.float32(np.float32(1.01) * qm) * km + np.float32(1e-3)))
+    return float(b) if b <= FIXED_MAX_LIMIT else None
+
+
 def _bf16(a):
     return round_bf16(np.asarray(a, np.float32)).astype(np.float64)
 
@@ -241,12 +256,14 @@ def attention(qkv_r, cfg, plan, shared, bf16=True, blocks=None, q_g=None, k_g=No
     ambiguity: also return, per output element, the bound on what softmax
     weights of ambiguous rounding can move it (zero on the global rows)."""
     d, hd, H = cfg["d"], cfg["head_dim"], cfg["n_heads"]
+    q, k, v = qkv_r[:, :d], qkv_r[:, d:2 * d], qkv_r[:, 2 * d:]
     fixed = fixed_offset(cfg, q_g, k_g)
+    if bf16 and not cfg.get("qk_norm"):
+        fixed = norm_offset(q, k, H, hd)
     # bf16: q as qk_prep leaves it, carrying log2(e)/sqrt(hd); scores in the log2 domain
     C = 1.0 if bf16 else None
     n, nt = plan.tile_tokens, plan.n_tiles
     rnd = _bf16 if bf16 else (lambda a: a)
-    q, k, v = qkv_r[:, :d], qkv_r[:, d:2 * d], qkv_r[:, 2 * d:]
     if shared:
         out = np.full((plan.n_union + nt, d), np.nan)
         win = [np.concatenate([plan.tile_rows[t].astype(np.int64), [plan.n_union + t]]) for t in range(nt)]

@@ -60,18 +60,53 @@ def test_fixed_offset_bounds_every_score(gain, shared):
         assert off is None
         return
     assert off is not None and off == int(off)
+    # bf16: q as stored carries C = log2(e)/sqrt(hd), so q.k is the score times C
     x = AR.qk_prep(qkv, cfg, pl, shared, qg, kg)
     d, hd = cfg["d"], cfg["head_dim"]
     C = 1.0 / np.log(2.0) / np.sqrt(hd)
     worst = 0.0
     for h in range(cfg["n_heads"]):
         q, k = x[:, h * hd:(h + 1) * hd], x[:, d + h * hd:d + (h + 1) * hd]
-        worst = max(worst, float(np.max(np.abs(q @ k.T))) * C)
+        worst = max(worst, float(np.max(np.abs(q @ k.T))))
     print(f"  offset {off}, largest |score| x C {worst:.3f}")
     assert worst <= off
-    # the row norms the bound rests on: at most sqrt(hd) max|q_g|, plus bf16 rounding
+    # not vacuous: the scores reach a fair part of the bound
+    assert worst > 0.3 * off
+    # the row norms the bound rests on: at most sqrt(hd) max|gain| (times C for
+    # q), plus bf16 rounding
     qn = np.linalg.norm(x[:, :hd], axis=1)
-    assert np.max(qn) <= np.sqrt(hd) * float(np.max(np.abs(qg))) * 1.005
+    kn = np.linalg.norm(x[:, d:d + hd], axis=1)
+    assert np.max(qn) <= np.sqrt(hd) * float(np.max(np.abs(qg))) * C * 1.005
+    assert np.max(kn) <= np.sqrt(hd) * float(np.max(np.abs(kg))) * 1.005
+
+
+@pytest.mark.parametrize("qk_scale", [1.0, 3.0, 8.0])
+@pytest.mark.parametrize("shared", [True, False])
+def test_norm_offset_bounds_every_score(qk_scale, shared):
+    """The bf16 kernel's fixed softmax offset without QK-norm: the largest q
+    and k head norms as stored bound every score (Cauchy-Schwarz), so every
+    score (times C, which q carries) lies within the offset; when the bound
+    passes the limit there is no offset and the kernel keeps a running
+    maximum."""
+    case = [c for c in CASES if not c[6] and c[7] == "bf16"][0]
+    cfg = case_cfg(*case)
+    pl, qkv, qg, kg = case_inputs(cfg, shared, qk_scale)
+    x = AR.qk_prep(qkv, cfg, pl, shared)
+    d, hd, H = cfg["d"], cfg["head_dim"], cfg["n_heads"]
+    q, k = x[:, :d], x[:, d:2 * d]
+    off = AR.norm_offset(q, k, H, hd)
+    qm = max(float(np.max(np.linalg.norm(q[:, h * hd:(h + 1) * hd], axis=1))) for h in range(H))
+    km = max(float(np.max(np.linalg.norm(k[:, h * hd:(h + 1) * hd], axis=1))) for h in range(H))
+    worst = max(float(np.max(np.abs(q[:, h * hd:(h + 1) * hd] @ k[:, h * hd:(h + 1) * hd].T))) for h in range(H))
+    print(f"  offset {off}, bound {qm * km:.3f}, largest |score| x C {worst:.3f}")
+    assert worst <= qm * km * (1 + 1e-9)
+    if qm * km * 1.01 + 1e-3 > AR.FIXED_MAX_LIMIT:
+        assert off is None
+        return
+    assert off is not None and off == int(off) and off >= qm * km * 1.01
+    assert worst <= off
+    # with the 1 % margin and the rounding up, the offset is the bound's ceiling
+    assert off <= qm * km * 1.01 + 1e-3 + 1
 
 
 @pytest.mark.parametrize("grid,tile,stride,blend", [((2, 12, 20), (2, 8, 8), (2, 6, 6), "ramp"),
