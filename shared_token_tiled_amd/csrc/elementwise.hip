@@ -121,10 +121,10 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, int M
 // of pair i of axis a is coord_a * base^(-i / pairs_a), so the score of two
 // window tokens depends only on their coordinate difference, as with
 // tile-local positions, and the attention kernels stage keys unchanged.
-// qkn (optional): the largest q-head and k-head norms of the rows as stored,
-// as float bits (atomic max per workgroup, skipped where the slot already
-// holds more).
-template <typename T, int HD, bool NORM>
+// QKN: the largest q-head and k-head norms of the rows as stored into qkn[0],
+// qkn[1], as float bits (atomic max per workgroup, skipped where the slot
+// already holds more); a template flag, so the other versions carry none of it.
+template <typename T, int HD, bool NORM, bool QKN>
 __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int d, int H,
                                                 const float* __restrict__ qg,
                                                 const float* __restrict__ kg, float eps, tsk::RopeRows rr,
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int 
         for (int e = 0; e < 8; ++e) v[e] *= QSCALE;
       }
       if (ok && sl < ns) store8(base + sl * HD, f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]});
-      if (qkn) {
+      if constexpr (QKN) {
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void k_qkprep(T* __restrict__ qkv, int M, int 
       }
     }
   }
-  if (qkn) {  // uniform: a kernel argument
+  if constexpr (QKN) {
     __shared__ float red[2][4];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -459,10 +459,11 @@ hipError_t qk_prep(hipStream_t s, int act, void* qkv, int M, int d, int H, int h
   const int64_t rows_per_block = 4 * (512 / hd);
   const dim3 grid(unsigned((M + rows_per_block - 1) / rows_per_block)), block(256);
   const bool norm = qg != nullptr;
-#define TS_QK(T, HD)                                                                                         \
-  do {                                                                                                       \
-    if (norm) hipLaunchKernelGGL((k_qkprep<T, HD, true>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps, rr, qkn); \
-    else hipLaunchKernelGGL((k_qkprep<T, HD, false>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps, rr, qkn);    \
+#define TS_QK(T, HD)                                                                                              \
+  do {                                                                                                            \
+    if (norm) hipLaunchKernelGGL((k_qkprep<T, HD, true, false>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps, rr, qkn); \
+    else if (qkn) hipLaunchKernelGGL((k_qkprep<T, HD, false, true>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps, rr, qkn); \
+    else hipLaunchKernelGGL((k_qkprep<T, HD, false, false>), grid, block, 0, s, (T*)qkv, M, d, H, qg, kg, eps, rr, qkn); \
   } while (0)
   if (act == ACT_F32) {
     if (hd == 32) TS_QK(float, 32); else if (hd == 64) TS_QK(float, 64); else TS_QK(float, 128);
