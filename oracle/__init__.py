@@ -13,8 +13,7 @@ captions (which operations are shared from layer k on) and Table S1 (each
 operation of a block under TileShare).  The oracle writes that definition out
 directly in numpy, in float64, with plain loops over tiles and heads and no
 blocking or fusion.  Where the pages leave a step open the oracle takes one
-reading; every reading is listed in the design doc and named in the docstring of
-the function that takes it.
+reading, named in the docstring of the module or function that takes it.
 
 Modules
 -------

@@ -2,7 +2,7 @@
 
 Pages: FP8 appears as "V0 + FP8" (Table S5), "FP8 MLP layers only" and
 "TileShare-4 + FP8" (Table S2) and "up to 1.96x with FP8" (abstract); the
-format and the scaling are not given.  Reading: OCP e4m3 (1 sign,
+format and the scaling are not given.  Reading taken here: OCP e4m3 (1 sign,
 4 exponent bits with bias 7, 3 mantissa bits, largest finite 448, no
 infinities, S.1111.111 is NaN); one scale per operand tensor of each GEMM
 call, s = absmax/448 (s = 1 when the tensor is all zero); codes by round to

@@ -11,7 +11,7 @@ come from the shared states; the blend of attention outputs happens in every
 layer >= k.  Abstract and Table 1 caption: TileShare-k keeps the first k
 layers per tile (per-tile residual streams).
 
-Readings taken (the design doc lists them with reasons): pre-norm block
+Readings taken where the pages leave a step open: pre-norm block
 x += Attn(Norm1(x)); x += MLP(Norm2(x)); MLP = fc1 -> exact erf GELU -> fc2;
 LayerNorm for the ViT-style configurations, RMSNorm plus per-head
 QK-RMSNorm for the MiniMax-style ones; eps 1e-6; q|k|v split of the QKV

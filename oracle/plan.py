@@ -6,7 +6,7 @@ with the released weights w-bar), Figure 5 ("tiles per pixel", tile-start
 lines) and Table S10 (tile size and overlap as the tiling's parameters).
 
 The pages give neither a clamp rule for the last tile nor the ramp formula of
-w-bar.  Readings taken here (listed in the design doc):
+w-bar.  Readings taken here:
 
 * per axis of length N with tile extent L and stride S: one tile of extent N
   if N <= L, else starts min(i*S, N-L) for i = 0 .. ceil((N-L)/S), i.e. the

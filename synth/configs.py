@@ -3,8 +3,8 @@
 Pure data, no arithmetic of the method.  Each entry gives the token grid, the
 tiling (tile extent and stride per axis, T/H/W order), the transformer block
 shape and the variants that are compared.  Shapes follow the decoders the
-TileShare paper page times (MiniMax-H3, ViTok-v2; Tables S5, S6, S12), scaled
-to the synthetic workloads described in the design doc.
+TileShare paper page times (MiniMax-H3, ViTok-v2; Tables S5, S6, S12), with
+random-initialised weights and seeded synthetic inputs of those shapes.
 """
 
 CONFIGS = {
