@@ -11,7 +11,7 @@ Inputs are synthetic and seeded: weights N(0, 0.02) (norm gains 1 + N(0, 0.02))
 rounded to bf16, tokens N(0, 1), drawn on the GPU; they are resident in HBM
 before the timed region starts.
 
-Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  --gpus N with N > 1 exits: the library runs on one GPU.
 """
 import argparse
 import json
@@ -168,8 +168,8 @@ def main():
                          "(the encoder at its own k) against tiled in both")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path's sharding across "
-              f"GPUs is a design note, not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
+              f"multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
