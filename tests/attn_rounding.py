@@ -62,18 +62,22 @@ def fixed_offset(cfg, q_g, k_g):
     return float(b) if b <= FIXED_MAX_LIMIT else None
 
 
-def norm_offset(q, k, H, hd):
-    """The fixed softmax offset of the bf16 kernel without QK-norm (log2
-    domain; q carries log2(e)/sqrt(hd)): by Cauchy-Schwarz every score obeys
-    |q.k| <= max|q_h| max|k_h| over all rows and heads of q, k as qk_prep
-    stored them; the offset is ceil(1.01 max|q| max|k| + 1e-3), norms and
-    product in fp32 as the library forms them, when at most FIXED_MAX_LIMIT;
-    else None (running maximum)."""
+def norm_bound(q, k, H, hd):
+    """1.01 max|q_h| max|k_h| over all rows and heads of q, k as qk_prep
+    stored them (fp32 norms and product, as the library forms them): with q
+    carrying log2(e)/sqrt(hd), by Cauchy-Schwarz a bound on every score in the
+    log2 domain, with a 1 % margin."""
     def top(a):
         a = np.asarray(a, np.float32).reshape(len(a), H, hd)
         return np.float32(np.sqrt((a * a).sum(axis=-1, dtype=np.float32)).max())
-    qm, km = top(q), top(k)
-    b = math.ceil(float(np.float32(np.float32(1.01) * qm) * km + np.float32(1e-3)))
+    return float(np.float32(np.float32(1.01) * top(q)) * top(k))
+
+
+def norm_offset(q, k, H, hd):
+    """The fixed softmax offset of the bf16 kernel without QK-norm:
+    ceil(norm_bound + 1e-3) when at most FIXED_MAX_LIMIT; else None (running
+    maximum)."""
+    b = math.ceil(float(np.float32(norm_bound(q, k, H, hd)) + np.float32(1e-3)))
     return float(b) if b <= FIXED_MAX_LIMIT else None
 
 

@@ -298,6 +298,32 @@ def test_attention_softmax_offset_edges(gain, shared):
     assert e < AC.CAP[3.0]
 
 
+@pytest.mark.parametrize("target", [31.5, 33.0])
+@pytest.mark.parametrize("shared", [True, False])
+def test_attention_norm_offset_edges(target, shared):
+    """Without QK-norm: q and k scaled so that the score bound from the
+    largest head norms (1.01 max|q| max|k|) is 31.5, an offset of 32 at the
+    limit (weights down to 2^-64), or 33, past it (the running maximum);
+    checked as the other attention cases.  The logits grow by the square of
+    the scale, about 1.6, within the cap of qk_scale 3."""
+    case = [c for c in AC.CASES if not c[6] and c[7] == "bf16"][0]
+    cfg = AC.case_cfg(*case)
+    d, H, hd = cfg["d"], cfg["n_heads"], cfg["head_dim"]
+    pl, qkv, _, _ = AC.case_inputs(cfg, shared, 1.0)
+    x = AR.qk_prep(qkv, cfg, pl, shared)
+    scale = float(np.sqrt(target / AR.norm_bound(x[:, :d], x[:, d:2 * d], H, hd)))
+    say(f"attention step, no QK-norm, score bound {target} (q, k x{scale:.3f}), shared={shared}")
+    pl, qkv, _, _ = AC.case_inputs(cfg, shared, scale)
+    x = AR.qk_prep(qkv, cfg, pl, shared)
+    off = AR.norm_offset(x[:, :d], x[:, d:2 * d], H, hd)
+    assert (off is not None) == (target < AR.FIXED_MAX_LIMIT), off
+    got, qkv_gpu = run_attention_op(cfg, pl, qkv, None, None, shared)
+    ref = AC.oracle_attention(qkv, cfg, pl, shared)
+    e = check_attention(cfg, pl, qkv, None, None, shared, got, qkv_gpu, ref)
+    print(f"  offset {off}: max|gpu-oracle|/rms {e:.3e} (cap {AC.CAP[3.0]})")
+    assert e < AC.CAP[3.0]
+
+
 def test_attention_hard_stitching_blocks():
     """Hard stitching: every grid row's query block holds one tile (the one of
     weight 1), so a shared layer attends each row once; the output is that
