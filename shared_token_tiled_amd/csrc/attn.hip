@@ -43,6 +43,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <map>
+#include <tuple>
 #include <mutex>
 #include <type_traits>
 
@@ -196,6 +197,19 @@ constexpr int AHEAD = 2 * DEPTH - 1;   // blocks ahead the key rows are fetched
 constexpr int NSL = 8;                 // slots of the key-row ring (>= AHEAD + 1)
 static_assert(NSL >= AHEAD + 1 && DEPTH >= 2 && DEPTH <= 3, "staging pipeline");
 constexpr float RESCALE_LOG2 = 8.0f;   // keep a stale running max until a block exceeds it by 2^8
+// The bf16 kernel comes in three modes: 0 takes the fixed softmax offset or
+// the running max as the launch's scores allow, 1 runs only against the fixed
+// offset and 2 only with a running max (each returns at once otherwise, so
+// that launching 1 and then 2 runs exactly one of them): one version of the
+// job loop per kernel, so neither carries the other's registers.
+// Wavefronts per SIMD: at head size 64 a workgroup's LDS (67.6 KB) lets two
+// workgroups share a CU, so with the fixed offset four wavefronts per SIMD
+// (at most 128 VGPRs, no spills); their phases drift apart, so one
+// workgroup's MFMAs run beside the other's softmax.  The running max needs
+// more registers (two wavefronts per SIMD), and at head size 128 (133 KB of
+// LDS) one workgroup fills a CU.
+template <int HD, int MODE>
+constexpr int WPS = HD == 64 && MODE == 1 ? 4 : 2;
 // Largest static score bound used as the softmax offset: weights >= 2^-64,
 // and the fp32 argument score*C - bound of a weight that matters (|.| < 32)
 // is rounded to 2^-20, about as finely as against a running max.
@@ -280,11 +294,16 @@ __device__ __forceinline__ bool blend_job(const AttnP& p, int b, int& blk, int& 
   return false;
 }
 
-template <int HD, bool BLEND>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(AttnP p) {
+template <int HD, bool BLEND, int MODE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPS<HD, MODE>, WPS<HD, MODE>))) void k_attn_bf16(AttnP p) {
   constexpr int KROWB = HD * 2;       // bytes per staged key row
   constexpr int NHB = HD / 32;        // 32-row hd blocks of O^T
   constexpr int KSTEPS = HD / 16;     // MFMA k-steps of S^T
+  // LDS fragment reads kept ahead of their MFMAs: K fragments (reads) in the
+  // score phase, V^T fragments in the output phase; fewer at head size 64,
+  // where four wavefronts share a SIMD and cover each other's reads
+  constexpr int SRA = WPS<HD, MODE> == 4 ? 2 : 4;
+  constexpr int VRA = WPS<HD, MODE> == 4 ? 2 : 4;
   // global_load_lds: lane l of a wavefront instruction writes 16 bytes at LDS
   // base + 16*l; instruction i of wavefront w fills bytes [(w*KDI + i) KB,
   // +1 KB) of a stage, i.e. key row b / KROWB, slot (b % KROWB) / 16 for lane
@@ -353,6 +372,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto job_loop = [&](auto fixed_tag) {
   constexpr bool FIXED = decltype(fixed_tag)::value;
   for (int it = 0;; ++it) {
+    int tid_j = int(threadIdx.x);
+    if constexpr (WPS<HD, MODE> == 4) asm volatile("" : "+v"(tid_j));
+    const int tid = tid_j, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
     int h = 0, t0 = 0, qblk = 0, blk = 0, npass = 1;
     if constexpr (BLEND) {
       // take the XCD's next job; every thread has read job_s before the job's
@@ -476,10 +498,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int64_t gr = gkey_row(p, t);
       const bf16* kgp = kbase + gr * ld;
       const bf16* vgp = vbase + gr * ld;
+      // four wavefronts per SIMD: this lane's column offsets anew (opaque), so
+      // that no lane address is formed once per job and held across windows
+      int gw = g;
+      if constexpr (WPS<HD, MODE> == 4) asm volatile("" : "+v"(gw));
       float sg = 0.f;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8 kg = *reinterpret_cast<const bf16x8*>(kgp + 16 * s + 8 * g);
+        const bf16x8 kg = *reinterpret_cast<const bf16x8*>(kgp + 16 * s + 8 * gw);
         // q opaque here: its fp32 copy (64 registers) would otherwise be made
         // once and held across every window
         bf16x8 q = qf[s];
@@ -502,7 +528,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const bf16x4 v = *reinterpret_cast<const bf16x4*>(vgp + hb * 32 + 8 * r4 + 4 * g);
+          const bf16x4 v = *reinterpret_cast<const bf16x4*>(vgp + hb * 32 + 8 * r4 + 4 * gw);
 #pragma unroll
           for (int e = 0; e < 4; ++e) oacc[hb][4 * r4 + e] = float(v[e]) * w0;
         }
@@ -518,10 +544,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       bool valid;
       float coef;
       if constexpr (BLEND) {
-        const int r = p.blk_rows[blk * QB + slot];
+        // four wavefronts per SIMD: the slot index anew (opaque), so that
+        // nothing formed from it at the job's start is held across the key loop
+        int sl = slot;
+        if constexpr (WPS<HD, MODE> == 4) asm volatile("" : "+v"(sl));
+        const int r = p.blk_rows[blk * QB + sl];
         valid = r >= 0;
         orw = valid ? r : p.blk_rows[blk * QB];
-        coef = p.blk_w[(int64_t(blk) * p.maxc + ps) * QB + slot] / l_tot;
+        coef = p.blk_w[(int64_t(blk) * p.maxc + ps) * QB + sl] / l_tot;
       } else {
         const int qi = qblk * QB + slot;
         valid = qi < n;
@@ -638,13 +668,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sb], 0, 0, 0);
         }
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, SRA, 0);  // SRA LDS reads
 #pragma unroll
-      for (int i = 0; i < 2 * KSTEPS - 4; ++i) {
+      for (int i = 0; i < 2 * KSTEPS - SRA; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next LDS read
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, SRA, 0);
       if (j0 + KB > n) {  // keys past the window end (last block of a window only)
         // accumulator row 8(r/4)+4g+(r%4) holds key swap23(that row) =
         // 16(r/8) + 4((r/4)%2) + r%4 + 8g: one per-lane limit, constant offsets
@@ -716,13 +746,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           oacc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], oacc[hb], 0, 0, 0);
         }
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 4 fragments (8 reads) ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * VRA, 0);  // VRA fragments (2 VRA reads) ahead
 #pragma unroll
-      for (int i = 0; i < 4 * NHB - 4; ++i) {
+      for (int i = 0; i < 4 * NHB - VRA; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, VRA, 0);
 
       // this wavefront's loads of block gb+1 have landed (the newer blocks'
       // may still be in flight) and its LDS traffic is done; then a barrier
@@ -739,8 +769,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }  // jobs
   };
-  if (fixedm) job_loop(std::true_type{});
-  else job_loop(std::false_type{});
+  if constexpr (MODE == 0) {
+    if (fixedm) job_loop(std::true_type{});
+    else job_loop(std::false_type{});
+  } else if constexpr (MODE == 1) {
+    if (fixedm) job_loop(std::true_type{});
+  } else {
+    if (!fixedm) job_loop(std::false_type{});
+  }
 }
 
 // Global-token query row of one (head, tile), over the window keys
@@ -892,22 +928,25 @@ __global__ void k_zero_jobs(unsigned* jobs) {
 // Workgroups of the blended bf16 kernel that the current device holds at
 // once: CUs x resident workgroups per CU, rounded down to a multiple of 8
 // (at least 8).  Cached per device.
-hipError_t blend_slots(int hd, int* out) {
+hipError_t blend_slots(int hd, int mode, int* out) {
   static std::mutex mu;
-  static std::map<std::pair<int, int>, int> cache;
+  static std::map<std::tuple<int, int, int>, int> cache;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find({dev, hd});
+  auto it = cache.find({dev, hd, mode});
   if (it == cache.end()) {
     int cus = 0, per_cu = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    e = hd == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_bf16<64, true>, NW * 64, 0)
-                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_bf16<128, true>, NW * 64, 0);
+    if (hd == 64)
+      e = mode == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_bf16<64, true, 1>, NW * 64, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_bf16<64, true, 2>, NW * 64, 0);
+    else
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_bf16<128, true, 0>, NW * 64, 0);
     if (e != hipSuccess) return e;
     const int slots = std::max(8, (std::max(1, cus) * std::max(1, per_cu)) / 8 * 8);
-    it = cache.emplace(std::make_pair(dev, hd), slots).first;
+    it = cache.emplace(std::make_tuple(dev, hd, mode), slots).first;
   }
   *out = it->second;
   return hipSuccess;
@@ -940,20 +979,31 @@ hipError_t attention(hipStream_t s, int act, const AttnArgs& a) {
   const dim3 block(NW * 64);
   if (!blend) {
     const dim3 grid(njob * a.H);
-    if (a.hd == 64) hipLaunchKernelGGL((k_attn_bf16<64, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_attn_bf16<128, false>), grid, block, 0, s, p);
+    if (a.hd == 64) {  // the fixed-offset kernel, then the running-max one: one of them runs
+      hipLaunchKernelGGL((k_attn_bf16<64, false, 1>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((k_attn_bf16<64, false, 2>), grid, block, 0, s, p);
+    } else {
+      hipLaunchKernelGGL((k_attn_bf16<128, false, 0>), grid, block, 0, s, p);
+    }
     return hipGetLastError();
   }
   // blended: as many workgroups as the CUs hold at once (a multiple of 8, so
   // every XCD holds the same number), counters zeroed first
   if (!a.blk_order || !a.blk_cls || a.ncls < 1 || !a.jobs) return hipErrorInvalidValue;
-  int slots = 0;
-  hipError_t e = blend_slots(a.hd, &slots);
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_zero_jobs, dim3(1), dim3(64), 0, s, a.jobs);
-  const dim3 grid(slots);
-  if (a.hd == 64) hipLaunchKernelGGL((k_attn_bf16<64, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((k_attn_bf16<128, true>), grid, block, 0, s, p);
+  if (a.hd == 64) {  // the fixed-offset kernel, then the running-max one: one of them takes the jobs
+    int s1 = 0, s2 = 0;
+    hipError_t e = blend_slots(64, 1, &s1);
+    if (e == hipSuccess) e = blend_slots(64, 2, &s2);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_attn_bf16<64, true, 1>), dim3(s1), block, 0, s, p);
+    hipLaunchKernelGGL((k_attn_bf16<64, true, 2>), dim3(s2), block, 0, s, p);
+  } else {
+    int slots = 0;
+    hipError_t e = blend_slots(128, 0, &slots);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_attn_bf16<128, true, 0>), dim3(slots), block, 0, s, p);
+  }
   return hipGetLastError();
 }
 
