@@ -141,6 +141,19 @@ ts_status check_plan(const ts_plan* p, const ts_model_desc* m) {
 }
 
 // ------------------------------------------------------------ workspace
+// Row pitch (elements) of the MLP hidden activations, written by fc1 and read
+// as fc2's A operand.  A bf16 row of a multiple of 4 KB is padded by 128
+// bytes: an isolated fc2-shaped GEMM (hidden 10240) runs 3-4 % faster with A
+// rows 20608 bytes apart than 20480 (likely because the 128-byte slices that
+// a K block takes from a panel's 256 rows then spread over more memory
+// channels).  An fp8 fc2 quantises the hidden as one contiguous array, so it
+// keeps the plain pitch.
+int64_t mlp_pitch(const ts_model_desc* m, bool fc2_fp8) {
+  const int64_t dm = m->mlp_hidden;
+  if (m->act_dtype != TS_BF16 || fc2_fp8 || (dm * 2) % 4096 != 0) return dm;
+  return dm + 64;
+}
+
 struct WS {
   unsigned* amax = nullptr;  // fp8 scratch: amax bits
   float* sa = nullptr;       // fp8 scratch: activation scale
@@ -166,7 +179,7 @@ WS layout(const ts_model_desc* m, const ts_plan* p, bool states, bool per_tile, 
   const int64_t Mt = int64_t(p->n_tiles) * (p->n + 1);
   const int64_t Ms = int64_t(p->n_union) + p->n_tiles;
   const int64_t Mmax = per_tile ? std::max(Mt, Ms) : Ms;
-  const int64_t d = m->d, wide = std::max<int64_t>(3 * d, m->mlp_hidden);
+  const int64_t d = m->d, wide = std::max<int64_t>(3 * d, mlp_pitch(m, false));
   const int ab = act_bytes(m->act_dtype);
   WS w;
   size_t off = 0;
@@ -210,9 +223,10 @@ double gemm_bytes(int64_t M, int64_t N, int64_t K, int ab, int ob, bool resid) {
   return double(M * K + N * K) * ab + double(M * N) * ob * (resid ? 2 : 1);
 }
 
-// The MFMA GEMM addresses each operand with 32-bit byte offsets.
-bool gemm_offsets_fit(int64_t M, int64_t N, int64_t K, int esz) {
-  return M * K * esz < (int64_t(1) << 32) && N * K * esz < (int64_t(1) << 32);
+// The MFMA GEMM addresses each operand with 32-bit byte offsets (A with row
+// pitch lda >= K).
+bool gemm_offsets_fit(int64_t M, int64_t N, int64_t K, int esz, int64_t lda = 0) {
+  return M * std::max(lda, K) * esz < (int64_t(1) << 32) && N * K * esz < (int64_t(1) << 32);
 }
 
 // The producer of an fp8 GEMM operand (a norm, the blend, a bf16-output
@@ -227,11 +241,14 @@ bool fused_amax() {
 // y = A W^T (+ epilogue) for one projection; fp8 quantises A first.
 // amax_ready: ws.amax already holds max |A| (see fused_amax).  out_amax: the
 // epilogue takes max |C| into it (for the next projection's quantisation).
+// lda, ldc: row pitches of A and C in elements (0: K and N; fp8 takes A
+// contiguous).
 ts_status proj(const Ctx& c, const WS& ws, bool f8, const char* role, int epi, const void* A, int64_t M,
                int N, int K, const void* Wt, const uint8_t* W8, const float* w8scale, const float* bias,
-               void* C, bool amax_ready = false, unsigned* out_amax = nullptr) {
+               void* C, bool amax_ready = false, unsigned* out_amax = nullptr, int lda = 0, int ldc = 0) {
   const int act = c.m->act_dtype;
-  if (act != TS_F32 && !gemm_offsets_fit(M, N, K, f8 ? 1 : 2))
+  if (f8 && lda != 0 && lda != K) return fail(TS_EINVAL, std::string("fp8 GEMM operand with a row pitch (") + role + ")");
+  if (act != TS_F32 && !gemm_offsets_fit(M, N, K, f8 ? 1 : 2, lda))
     return fail(TS_ESHAPE, std::string("GEMM operand larger than 4 GiB (") + role + ")");
   const int ob = (epi == tsk::EPI_RESID || epi == tsk::EPI_F32) ? 4 : act_bytes(act);
   std::string name = std::string(f8 ? "gemm_fp8[" : (act == TS_F32 ? "gemm_f32[" : "gemm_bf16[")) + role + "]";
@@ -245,14 +262,14 @@ ts_status proj(const Ctx& c, const WS& ws, bool f8, const char* role, int epi, c
     if (out_amax) TS_HIP(tsk::zero_amax(c.s, out_amax), "amax reset");  // after the quantisation read it
     Scope sc(c.s, name.c_str(), 2.0 * M * N * K, gemm_bytes(M, N, K, 1, ob, epi == tsk::EPI_RESID));
     TS_HIP(tsk::gemm(c.s, tsk::ACT_FP8, epi, ws.q8, W8, int(M), N, K, bias, C, ws.sa, w8scale, ws.gsplit,
-                   TS_GEMM_SPLIT_WS_BYTES, out_amax),
+                   TS_GEMM_SPLIT_WS_BYTES, out_amax, 0, ldc),
          "fp8 gemm");
     return TS_OK;
   }
   if (out_amax) TS_HIP(tsk::zero_amax(c.s, out_amax), "amax reset");
   Scope sc(c.s, name.c_str(), 2.0 * M * N * K, gemm_bytes(M, N, K, act_bytes(act), ob, epi == tsk::EPI_RESID));
   TS_HIP(tsk::gemm(c.s, act, epi, A, Wt, int(M), N, K, bias, C, nullptr, nullptr, ws.gsplit, TS_GEMM_SPLIT_WS_BYTES,
-                   out_amax),
+                   out_amax, lda, ldc),
          "gemm");
   return TS_OK;
 }
@@ -408,11 +425,12 @@ ts_status run_layer(const Ctx& c, const ts_layer_weights& w, float* x, bool shar
     Scope sc(c.s, "norm", 0.0, double(M * d) * (4 + ab));
     TS_HIP(tsk::norm(c.s, act, rms, x, int(M), d, w.norm2_g, w.norm2_b, m->eps, ws.h, am_fc1), "norm2");
   }
+  const int hp = int(mlp_pitch(m, (f8 & TS_FP8_FC2) != 0));
   if ((st = proj(c, ws, (f8 & TS_FP8_FC1) != 0, "fc1", tsk::EPI_BIAS_GELU, ws.h, M, dm, d, w.w_1, w.w_1_f8,
-                 w.w_scale_f8 ? w.w_scale_f8 + 2 : nullptr, w.b_1, ws.big, am_fc1 != nullptr, am_fc2)) != TS_OK)
+                 w.w_scale_f8 ? w.w_scale_f8 + 2 : nullptr, w.b_1, ws.big, am_fc1 != nullptr, am_fc2, 0, hp)) != TS_OK)
     return st;
   if ((st = proj(c, ws, (f8 & TS_FP8_FC2) != 0, "fc2", tsk::EPI_RESID, ws.big, M, d, dm, w.w_2, w.w_2_f8,
-                 w.w_scale_f8 ? w.w_scale_f8 + 3 : nullptr, w.b_2, x, am_fc2 != nullptr)) != TS_OK)
+                 w.w_scale_f8 ? w.w_scale_f8 + 3 : nullptr, w.b_2, x, am_fc2 != nullptr, nullptr, hp)) != TS_OK)
     return st;
   return TS_OK;
 }
@@ -492,17 +510,19 @@ ts_status run_layer_partial(const Ctx& c, const ts_layer_weights& w, float* X, i
     Scope sc(c.s, "norm", 0.0, double(Mm * d) * (4 + ab));
     TS_HIP(tsk::norm(c.s, act, rms, sm ? ws.xs : X, int(Mm), d, w.norm2_g, w.norm2_b, m->eps, ws.h), "norm2");
   }
+  const int hp = int(mlp_pitch(m, false));
   if ((st = proj(c, ws, false, "fc1", tsk::EPI_BIAS_GELU, ws.h, Mm, dm, d, w.w_1, nullptr, nullptr, w.b_1,
-                 ws.big)) != TS_OK)
+                 ws.big, false, nullptr, 0, hp)) != TS_OK)
     return st;
   if (sm) {
     // the blended state in xs has been consumed by Norm2: xs takes the MLP result
     if ((st = proj(c, ws, false, "fc2", tsk::EPI_F32, ws.big, Ms, d, dm, w.w_2, nullptr, nullptr, w.b_2,
-                   ws.xs)) != TS_OK)
+                   ws.xs, false, nullptr, hp)) != TS_OK)
       return st;
     return add_back();
   }
-  return proj(c, ws, false, "fc2", tsk::EPI_RESID, ws.big, Mt, d, dm, w.w_2, nullptr, nullptr, w.b_2, X);
+  return proj(c, ws, false, "fc2", tsk::EPI_RESID, ws.big, Mt, d, dm, w.w_2, nullptr, nullptr, w.b_2, X, false,
+              nullptr, hp);
 }
 
 ts_status check_ws(void* ws, size_t ws_bytes, size_t need) {

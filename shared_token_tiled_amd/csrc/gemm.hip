@@ -49,6 +49,8 @@ struct GemmP {
   // float bits (all values are >= 0, so integer order is float order); the
   // fp8 quantisation of this output then needs no separate max pass
   unsigned* amax;
+  // row pitches in elements of A (>= K) and C (>= N); B is [N, K] contiguous
+  int lda, ldc;
 };
 
 // Output stores of the tile epilogue, non-temporal: every output (qkv, the
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmP p) {
     for (int e = 0; e < 4; ++e) {
       const int k = k0 + lk + e;
       const int am = m0 + lr, bn = n0 + lr;
-      As[lk + e][lr] = (am < p.M && k < p.K) ? A[size_t(am) * p.K + k] : 0.f;
+      As[lk + e][lr] = (am < p.M && k < p.K) ? A[size_t(am) * p.lda + k] : 0.f;
       Bs[lk + e][lr] = (bn < p.N && k < p.K) ? B[size_t(bn) * p.K + k] : 0.f;
     }
     __syncthreads();
@@ -162,8 +164,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmP p) {
       const int n = n0 + tx * 4 + j;
       if (n >= p.N) continue;
       const float v = epi_value<EPI>(acc[i][j], 1.0f, p.bias ? p.bias[n] : 0.f);
-      if (EPI == EPI_RESID) C[size_t(m) * p.N + n] += v;
-      else C[size_t(m) * p.N + n] = v;
+      if (EPI == EPI_RESID) C[size_t(m) * p.ldc + n] += v;
+      else C[size_t(m) * p.ldc + n] = v;
     }
   }
 }
@@ -394,7 +396,8 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int ESZ = FP8 ? 1 : 2;               // element bytes
-  const uint32_t ldab = uint32_t(p.K) * ESZ; // row pitch of A and B in bytes
+  const uint32_t lda8 = uint32_t(p.lda) * ESZ; // row pitches of A and B in bytes
+  const uint32_t ldb8 = uint32_t(p.K) * ESZ;
   const char* A = (const char*)p.A;
   const char* B = (const char*)p.B;
 
@@ -409,8 +412,8 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
   uint32_t offA[LPO], offB[LPO];  // byte offsets (the host checks they fit)
 #pragma unroll
   for (int i = 0; i < LPO; ++i) {
-    offA[i] = uint32_t(min(m0 + lrow + 8 * NW * i, p.M - 1)) * ldab + lchunk * 16;
-    offB[i] = uint32_t(min(n0 + lrow + 8 * NW * i, p.N - 1)) * ldab + lchunk * 16;
+    offA[i] = uint32_t(min(m0 + lrow + 8 * NW * i, p.M - 1)) * lda8 + lchunk * 16;
+    offB[i] = uint32_t(min(n0 + lrow + 8 * NW * i, p.N - 1)) * ldb8 + lchunk * 16;
   }
   auto gload = [&](int kt, int st) {   // K block kb0 + kt into stage st
     const uint32_t kb = uint32_t(kb0 + kt) * ROWB;
@@ -431,7 +434,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
     if constexpr (EPI == EPI_RAW)
       store_tile<EPI, FP8, NB>(p, ac, stg, p.part + int64_t(blockIdx.x) * (BM * BN), BN, BM, BN, arow, brow, lane);
     else
-      store_tile<EPI, FP8, NB>(p, ac, stg, p.C, p.N, p.M, p.N, m0 + arow, n0 + brow, lane);
+      store_tile<EPI, FP8, NB>(p, ac, stg, p.C, p.ldc, p.M, p.N, m0 + arow, n0 + brow, lane);
   };
   f32x16 acc[4][NB];
 #pragma unroll
@@ -538,9 +541,8 @@ __global__ __launch_bounds__(512) void k_gemm_rows(GemmP p) {
   const int l32 = lane & 31, g = lane >> 5;
   const int n0 = blockIdx.x * 32;
   const int ESZ = FP8 ? 1 : 2;
-  const int64_t ld = int64_t(p.K) * ESZ;
-  const char* ar = (const char*)p.A + int64_t(min(l32, p.M - 1)) * ld;
-  const char* br = (const char*)p.B + int64_t(min(n0 + l32, p.N - 1)) * ld;
+  const char* ar = (const char*)p.A + int64_t(min(l32, p.M - 1)) * p.lda * ESZ;
+  const char* br = (const char*)p.B + int64_t(min(n0 + l32, p.N - 1)) * p.K * ESZ;
   // byte offsets of this lane's four 16-byte chunks in a k-group: bf16 k-step
   // j takes chunk j (k 16j + 8g ..); fp8 k-step j2 takes chunks 2j2, 2j2+1
   // (k 64 j2 + 32 g ..); A and B use the same assignment
@@ -599,7 +601,7 @@ __global__ __launch_bounds__(512) void k_gemm_rows(GemmP p) {
       f32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, p.bias ? p.bias[col + e] : 0.f);
-      const int64_t off = int64_t(row) * p.N + col;
+      const int64_t off = int64_t(row) * p.ldc + col;
       if (EPI == EPI_RESID) {
         float* C = (float*)p.C;
         store4(C + off, load4(C + off) + o);
@@ -635,7 +637,7 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmP p) {
     f32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = epi_value<EPI, true>(v[e], alpha, p.bias ? p.bias[col + e] : 0.f);
-    const int64_t off = int64_t(row) * p.N + col;
+    const int64_t off = int64_t(row) * p.ldc + col;
     if (EPI == EPI_RESID) {
       store4((float*)p.C + off, load4((const float*)p.C + off) + o);
     } else if (EPI == EPI_F32) {
@@ -676,10 +678,13 @@ namespace tsk {
 
 hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, int M, int N, int K,
                 const float* bias, void* C, const float* sa, const float* sb, float* ws, size_t ws_bytes,
-                unsigned* amax) {
+                unsigned* amax, int lda, int ldc) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (lda == 0) lda = K;
+  if (ldc == 0) ldc = N;
+  if (lda < K || ldc < N || lda % 8 != 0 || ldc % 4 != 0) return hipErrorInvalidValue;
   if (act == ACT_F32) {
-    GemmP p{A, B, C, bias, sa, sb, M, N, K, 0, 0, 1, nullptr};
+    GemmP p{A, B, C, bias, sa, sb, M, N, K, 0, 0, 1, nullptr, nullptr, lda, ldc};
     const dim3 grid((N + FT - 1) / FT, (M + FT - 1) / FT), block(256);
     switch (epi) {
       case EPI_BIAS: hipLaunchKernelGGL(k_gemm_f32<EPI_BIAS>, grid, block, 0, s, p); break;
@@ -723,10 +728,10 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
       }
     }
   }
-  GemmP pm{A, B, C, bias, sa, sb, Mm, N, K, int(Tm), 0, 1, nullptr, amax};
-  GemmP ps{A, B, C, bias, sa, sb, Mm, N, K, 0, int(Tm), ks, ws, amax};
-  GemmP pt{(const char*)A + int64_t(Mm) * K * esz, B, (char*)C + int64_t(Mm) * N * osz, bias, sa, sb, M - Mm, N, K,
-           0, 0, 1, nullptr, amax};
+  GemmP pm{A, B, C, bias, sa, sb, Mm, N, K, int(Tm), 0, 1, nullptr, amax, lda, ldc};
+  GemmP ps{A, B, C, bias, sa, sb, Mm, N, K, 0, int(Tm), ks, ws, amax, lda, ldc};
+  GemmP pt{(const char*)A + int64_t(Mm) * lda * esz, B, (char*)C + int64_t(Mm) * ldc * osz, bias, sa, sb, M - Mm, N, K,
+           0, 0, 1, nullptr, amax, lda, ldc};
   const int wn = gemm_waves_n();
   const dim3 grid(static_cast<unsigned>(Tm)), block(128 * wn), tgrid((N + 31) / 32);
   const dim3 sgrid(static_cast<unsigned>((T - Tm) * ks)), rgrid(static_cast<unsigned>((T - Tm) * (BM / 4)));

@@ -84,9 +84,11 @@ hipError_t zero_amax(hipStream_t s, unsigned* p);
 // ws (fp32, ws_bytes; may be null): scratch for the K-split parts of a
 // partial last round of tiles (up to 8 x 256 KB per tile of that round).
 // amax (optional, bf16-output epilogues): atomic max of |C| as stored.
+// lda, ldc: row pitches of A and C in elements (0: K and N; lda a multiple of
+// 8, ldc of 4); B is [N, K] contiguous.
 hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, int M, int N, int K,
                 const float* bias, void* C, const float* sa, const float* sb, float* ws = nullptr,
-                size_t ws_bytes = 0, unsigned* amax = nullptr);
+                size_t ws_bytes = 0, unsigned* amax = nullptr, int lda = 0, int ldc = 0);
 
 // ---- attn.hip ----
 // Query rows per attention workgroup, and per query block of the plan.
