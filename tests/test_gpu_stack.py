@@ -64,6 +64,26 @@ def test_stack_against_oracle(name, size, k, qk_scale):
     assert e < tol and eg < tol
 
 
+@pytest.mark.parametrize("name", ["minimax_h3", "minimax_h3_fp8"])
+def test_stack_with_padded_hidden_rows(name):
+    # a bf16 MLP hidden row of 4 KB (2048 channels) is stored at a padded
+    # pitch, written by fc1 and read by fc2 with it; an fp8 fc2 (the shared
+    # layers of the fp8 workload) takes the hidden unpadded
+    cfg = configs.get(name, **dict(REDUCED[name], mlp_hidden=2048, n_layers=2))
+    say(f"stack {name} reduced, hidden 2048, k=1")
+    x, g, layers = make_inputs(cfg)
+    ref, gref = _oracle(cfg, x, g, layers, 1)
+    run = Run(cfg, layers)
+    try:
+        got, ggot = run.stack(x, g, 1)
+    finally:
+        run.close()
+    tol = TOL["fp8" if cfg["gemm_shared"] == "fp8" else cfg["dtype"]]
+    e, eg = max_rel(got, ref), max_rel(ggot, gref)
+    print(f"  max|err|/rms = {e:.3e} (globals {eg:.3e}), tolerance {tol}")
+    assert e < tol and eg < tol
+
+
 @pytest.mark.parametrize("name", ["minimax_h3", "vitok4k", "tiny2d"])
 def test_shared_layer_against_oracle(name):
     cfg = configs.get(name) if name == "tiny2d" else reduced(name)
