@@ -682,7 +682,11 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
   if (M <= 0 || N <= 0) return hipSuccess;
   if (lda == 0) lda = K;
   if (ldc == 0) ldc = N;
-  if (lda < K || ldc < N || lda % 8 != 0 || ldc % 4 != 0) return hipErrorInvalidValue;
+  if (lda < K || ldc < N) return hipErrorInvalidValue;
+  // MFMA kernels: rows of A start on 16 bytes (staged and read in 16-byte
+  // chunks), and the epilogue writes 4 elements per lane
+  if (act != ACT_F32 && ((int64_t(lda) * (act == ACT_FP8 ? 1 : 2)) % 16 != 0 || ldc % 4 != 0))
+    return hipErrorInvalidValue;
   if (act == ACT_F32) {
     GemmP p{A, B, C, bias, sa, sb, M, N, K, 0, 0, 1, nullptr, nullptr, lda, ldc};
     const dim3 grid((N + FT - 1) / FT, (M + FT - 1) / FT), block(256);
