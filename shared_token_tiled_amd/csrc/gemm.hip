@@ -39,10 +39,10 @@ struct GemmP {
   const float* sa;
   const float* sb;
   int M, N, K;
-  // tile kernels: this launch covers tile ids [0, ntiles) of the XCD-aware
-  // order (ksplit = 1), or the tiles tile0 + b / ksplit with K split
-  // ksplit ways (workgroup b takes part b % ksplit and writes its raw 256x256
-  // fp32 partial product to part + b * 65536)
+  // tile kernels: workgroups b < nlead take K-split parts: part b % ksplit
+  // of tile tile0 + b / ksplit (K split ksplit ways), writing the raw
+  // 256x256 fp32 partial product to part + b * 65536; workgroups b >= nlead
+  // take tile b - nlead of the XCD-aware order over tile ids [0, ntiles)
   int ntiles, tile0, ksplit;
   float* part;
   // when set (bf16 output epilogues): atomic max of |output| as stored, in
@@ -51,6 +51,7 @@ struct GemmP {
   unsigned* amax;
   // row pitches in elements of A (>= K) and C (>= N); B is [N, K] contiguous
   int lda, ldc;
+  int nlead;
 };
 
 // Output stores of the tile epilogue, non-temporal: every output (qkv, the
@@ -386,13 +387,14 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
   int tm, tn;
   const int KTT = p.K * (FP8 ? 1 : 2) / ROWB;  // K blocks of the whole product
   int kb0 = 0, kb1 = KTT;                      // this workgroup's K blocks
-  if (p.ksplit > 1) {
+  const bool is_part = int(blockIdx.x) < p.nlead;
+  if (is_part) {
     const int part = blockIdx.x % p.ksplit;
     group_tile(p.tile0 + blockIdx.x / p.ksplit, tiles_m, tiles_n, tm, tn);
     kb0 = int(int64_t(KTT) * part / p.ksplit);
     kb1 = int(int64_t(KTT) * (part + 1) / p.ksplit);
   } else {
-    tile_coords(blockIdx.x, p.ntiles, tiles_m, tiles_n, tm, tn);
+    tile_coords(blockIdx.x - p.nlead, p.ntiles, tiles_m, tiles_n, tm, tn);
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int ESZ = FP8 ? 1 : 2;               // element bytes
@@ -431,8 +433,8 @@ __global__ __launch_bounds__(128 * WN, 1) void k_gemm_mfma(GemmP p) {
   // epilogue: the C tile, or this part's raw sums for a split launch
   auto store = [&](const f32x16 (&ac)[4][NB]) {
     float* stg = reinterpret_cast<float*>(smem) + wave * (32 * (WCOLS + 8));
-    if constexpr (EPI == EPI_RAW)
-      store_tile<EPI, FP8, NB>(p, ac, stg, p.part + int64_t(blockIdx.x) * (BM * BN), BN, BM, BN, arow, brow, lane);
+    if (EPI == EPI_RAW || is_part)
+      store_tile<EPI_RAW, FP8, NB>(p, ac, stg, p.part + int64_t(blockIdx.x) * (BM * BN), BN, BM, BN, arow, brow, lane);
     else
       store_tile<EPI, FP8, NB>(p, ac, stg, p.C, p.ldc, p.M, p.N, m0 + arow, n0 + brow, lane);
   };
@@ -672,6 +674,16 @@ int gemm_waves_n() {
   return v;
 }
 
+// K-split lead parts for short-K residual GEMMs (the out-projection);
+// TS_GEMM_LEAD_SPLIT=0 turns them off, for measurements.
+bool lead_split() {
+  static const bool v = [] {
+    const char* e = getenv("TS_GEMM_LEAD_SPLIT");
+    return !(e && atoi(e) == 0);
+  }();
+  return v;
+}
+
 }  // namespace
 
 namespace tsk {
@@ -688,7 +700,7 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
   if (act != ACT_F32 && ((int64_t(lda) * (act == ACT_FP8 ? 1 : 2)) % 16 != 0 || ldc % 4 != 0))
     return hipErrorInvalidValue;
   if (act == ACT_F32) {
-    GemmP p{A, B, C, bias, sa, sb, M, N, K, 0, 0, 1, nullptr, nullptr, lda, ldc};
+    GemmP p{A, B, C, bias, sa, sb, M, N, K, 0, 0, 1, nullptr, nullptr, lda, ldc, 0};
     const dim3 grid((N + FT - 1) / FT, (M + FT - 1) / FT), block(256);
     switch (epi) {
       case EPI_BIAS: hipLaunchKernelGGL(k_gemm_f32<EPI_BIAS>, grid, block, 0, s, p); break;
@@ -722,6 +734,7 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
   const int KTT = K * esz / ROWB;
   int64_t Tm = T;
   int ks = 1;
+  bool lead = false;
   if (ws && T > 0 && KTT >= 64) {
     const int64_t ncu = device_cus(), rem = T % ncu;
     if (rem > 0) {
@@ -731,21 +744,34 @@ hipError_t gemm(hipStream_t s, int act, int epi, const void* A, const void* B, i
         Tm = T - rem;
       }
     }
+  } else if (ws && T > 0 && epi == EPI_RESID && lead_split()) {
+    // Short K, residual epilogue: the tiles of the partial last round run
+    // first, as two K halves each, in the same launch as the full tiles.
+    // The CUs that start with a half tile reach every later epilogue half a
+    // tile after the others, so the HBM-bound fp32 residual epilogues of a
+    // round no longer all run at once, and the rounds end together.
+    const int64_t ncu = device_cus(), rem = T % ncu;
+    if (rem > 0 && 2 * rem <= ncu && size_t(rem) * 2 * BM * BN * 4 <= ws_bytes && KTT >= 8) {
+      ks = 2;
+      Tm = T - rem;
+      lead = true;
+    }
   }
-  GemmP pm{A, B, C, bias, sa, sb, Mm, N, K, int(Tm), 0, 1, nullptr, amax, lda, ldc};
-  GemmP ps{A, B, C, bias, sa, sb, Mm, N, K, 0, int(Tm), ks, ws, amax, lda, ldc};
+  const int nlead = lead ? int((T - Tm) * ks) : 0;
+  GemmP pm{A, B, C, bias, sa, sb, Mm, N, K, int(Tm), int(Tm), ks, ws, amax, lda, ldc, nlead};
+  GemmP ps{A, B, C, bias, sa, sb, Mm, N, K, 0, int(Tm), ks, ws, amax, lda, ldc, int((T - Tm) * ks)};
   GemmP pt{(const char*)A + int64_t(Mm) * lda * esz, B, (char*)C + int64_t(Mm) * ldc * osz, bias, sa, sb, M - Mm, N, K,
-           0, 0, 1, nullptr, amax, lda, ldc};
-  const int wn = gemm_waves_n();
-  const dim3 grid(static_cast<unsigned>(Tm)), block(128 * wn), tgrid((N + 31) / 32);
+           0, 0, 1, nullptr, amax, lda, ldc, 0};
+  const int wn = lead ? 4 : gemm_waves_n();
+  const dim3 grid(static_cast<unsigned>(Tm + nlead)), block(128 * wn), tgrid((N + 31) / 32);
   const dim3 sgrid(static_cast<unsigned>((T - Tm) * ks)), rgrid(static_cast<unsigned>((T - Tm) * (BM / 4)));
 #define TS_G(E, F8)                                                                          \
   do {                                                                                       \
-    if (Tm == 0) {                                                                           \
+    if (Tm + nlead == 0) {                                                                   \
     } else if (wn == 2) hipLaunchKernelGGL((k_gemm_mfma<E, F8, 2>), grid, block, 0, s, pm);   \
     else hipLaunchKernelGGL((k_gemm_mfma<E, F8, 4>), grid, block, 0, s, pm);                  \
     if (Tm < T) {                                                                            \
-      hipLaunchKernelGGL((k_gemm_mfma<EPI_RAW, F8, 4>), sgrid, dim3(512), 0, s, ps);          \
+      if (!lead) hipLaunchKernelGGL((k_gemm_mfma<EPI_RAW, F8, 4>), sgrid, dim3(512), 0, s, ps); \
       hipLaunchKernelGGL((k_gemm_reduce<E, F8>), rgrid, dim3(256), 0, s, ps);                 \
     }                                                                                        \
     if (Mm < M) hipLaunchKernelGGL((k_gemm_rows<E, F8>), tgrid, dim3(512), 0, s, pt);         \

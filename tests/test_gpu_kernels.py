@@ -67,11 +67,14 @@ def test_gemm_against_oracle(M_, N, K, epi, dtype, ws):
 
 @pytest.mark.parametrize("M_,N,K", [(40 * 256 + 100, 2048, 256), (40 * 256, 2048, 192)])
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
-def test_gemm_many_tiles(M_, N, K, epi):
+@pytest.mark.parametrize("ws", [False, True])
+def test_gemm_many_tiles(M_, N, K, epi, ws):
     """More 256x256 tiles than compute units (several rounds), an even and an
     odd K block count, and (first shape) a partial last row tile, whose lanes
-    past the last row store into the epilogue's sink instead of C."""
-    test_gemm_against_oracle(M_, N, K, epi, "bf16", False)
+    past the last row store into the epilogue's sink instead of C.  With a
+    workspace the residual epilogue's partial last round runs first as K
+    halves in the same launch as the full tiles."""
+    test_gemm_against_oracle(M_, N, K, epi, "bf16", ws)
 
 
 @pytest.mark.parametrize("M_", [5, 512 + 7, 256 + 32])
