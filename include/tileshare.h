@@ -288,11 +288,14 @@ ts_status ts_op_gemm(int32_t dtype, int32_t epilogue, const void* a, const void*
                      const float* scale_b, void* stream);
 /* The same GEMM with a device workspace (ws, ws_bytes; 256-byte aligned, may
  * be NULL / 0): the 256x256 output tiles of a partial last round over the
- * compute units are split along k into up to 8 parts run side by side, their
- * fp32 partial sums kept in ws and added in part order (the result does not
- * vary from run to run).  Uses at most ws_bytes; with less than two parts'
- * room for that round it runs unsplit.  8 x 256 KB per compute unit (64 MiB
- * on MI355X) allows every split.  The forward calls pass their workspace. */
+ * compute units are split along k, their fp32 partial sums kept in ws and
+ * added in part order (the result does not vary from run to run).  Long k
+ * (>= 64 blocks of 128 bytes): up to 8 parts per tile, run after the full
+ * tiles.  Short k with TS_EPI_RESIDUAL: two halves per tile, run first in the
+ * same launch as the full tiles, so the residual epilogues of the later
+ * tiles are staggered.  Uses at most ws_bytes; with less room it runs
+ * unsplit.  8 x 256 KB per compute unit (64 MiB on MI355X) allows every
+ * split.  The forward calls pass their workspace. */
 #define TS_GEMM_SPLIT_WS_BYTES (64u << 20)
 ts_status ts_op_gemm_ws(int32_t dtype, int32_t epilogue, const void* a, const void* b, int32_t m,
                         int32_t n, int32_t k, const float* bias, void* c, const float* scale_a,
